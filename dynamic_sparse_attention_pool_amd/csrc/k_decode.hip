@@ -1,0 +1,571 @@
+// Gathered attention: clustered-context decode and token-gathered prefill,
+// plus the offline cluster-major packing of a fixed context.
+//
+// Squeezed Attention page, §技术方案: offline, keys are clustered and each
+// key is mapped to its cluster; online, a query attends only the key/value
+// pairs of its top-K clusters.  IndexCache article, §长文本的算力困境 and
+// §"偷懒"的艺术: every query token attends its indexer-selected token subset,
+// and shared layers reuse a full layer's subset.
+//
+// Cluster decode is bound by HBM bandwidth.  The context is stored cluster by
+// cluster, so the union of all selected clusters can be streamed once: each
+// workgroup sweeps a contiguous range of packed rows, skips 64-row tiles that
+// no query of the KV head selected, and runs all of the head's queries
+// (<= 64, here 8 tokens x 4 grouped heads) against each tile with a
+// per-(query, row) selection mask.  Partial (max, sum, output) per range are
+// merged by a second, fixed-order kernel.
+//
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16, queries as the N dimension):
+//   S^T[key][query] = K . Q^T  — K rows go straight from memory into the A
+//   operand (each lane reads 128 contiguous bytes of one key row; Q^T uses
+//   the same dimension order), V is transposed through LDS for O^T = V^T P^T.
+// The token gather uses v_mfma_f32_16x16x32_bf16 with the 16 query heads of
+// one token as the N dimension.
+#include <algorithm>
+#include <climits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+constexpr int kBlk = 64;
+constexpr int kD = 128;
+constexpr int kVS = kBlk + 8;  // V^T row stride (elements)
+
+// ================================================================ cluster pack
+constexpr int kSeg = 2048;
+
+__global__ __launch_bounds__(256) void k_pack_count(const int32_t* __restrict__ labels, int64_t n, int C, int nseg,
+                                                    int32_t* __restrict__ segcnt, int32_t* err) {
+  extern __shared__ int32_t hist[];
+  const int g = blockIdx.x / nseg, s = blockIdx.x % nseg;
+  for (int c = threadIdx.x; c < C; c += blockDim.x) hist[c] = 0;
+  __syncthreads();
+  const int64_t t0 = (int64_t)s * kSeg, t1 = min(n, t0 + kSeg);
+  bool bad = false;
+  for (int64_t t = t0 + threadIdx.x; t < t1; t += blockDim.x) {
+    const int c = labels[(int64_t)g * n + t];
+    if (c < 0 || c >= C) bad = true;
+    else atomicAdd(&hist[c], 1);
+  }
+  if (bad && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += blockDim.x) segcnt[((int64_t)g * nseg + s) * C + c] = hist[c];
+}
+
+// Exclusive scan in (cluster, segment) order -> per-segment bases and cluster_ptr.
+__global__ __launch_bounds__(64) void k_pack_scan(int C, int nseg, int32_t* __restrict__ seg, int32_t* __restrict__ ptr) {
+  const int g = blockIdx.x;
+  if (threadIdx.x != 0) return;
+  int32_t run = 0;
+  for (int c = 0; c < C; ++c) {
+    ptr[(int64_t)g * (C + 1) + c] = run;
+    for (int s = 0; s < nseg; ++s) {
+      int32_t* e = &seg[((int64_t)g * nseg + s) * C + c];
+      const int32_t x = *e;
+      *e = run;
+      run += x;
+    }
+  }
+  ptr[(int64_t)g * (C + 1) + C] = run;
+}
+
+// Each thread owns clusters; walking the segment in token order keeps the sort stable.
+__global__ __launch_bounds__(256) void k_pack_scatter(const int32_t* __restrict__ labels, int64_t n, int C, int nseg,
+                                                      const int32_t* __restrict__ seg, int32_t* __restrict__ perm) {
+  __shared__ int32_t lab[kSeg];
+  const int g = blockIdx.x / nseg, s = blockIdx.x % nseg;
+  const int64_t t0 = (int64_t)s * kSeg, t1 = min(n, t0 + kSeg);
+  const int len = (int)(t1 - t0);
+  for (int t = threadIdx.x; t < len; t += blockDim.x) lab[t] = labels[(int64_t)g * n + t0 + t];
+  __syncthreads();
+  for (int c = threadIdx.x; c < C; c += blockDim.x) {
+    int32_t pos = seg[((int64_t)g * nseg + s) * C + c];
+    for (int t = 0; t < len; ++t)
+      if (lab[t] == c) perm[(int64_t)g * n + pos++] = (int32_t)(t0 + t);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_pack_copy(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                   const int32_t* __restrict__ perm, const int32_t* __restrict__ ptr,
+                                                   int64_t n, int C, int row_bytes, int64_t total_chunks) {
+  const int cpr = row_bytes / 16;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total_chunks;
+       e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = e / cpr;  // packed row over all heads
+    const int ch = (int)(e % cpr);
+    const int64_t g = row / n, p = row % n;
+    if (p >= ptr[g * (C + 1) + C]) continue;  // rows dropped for invalid labels
+    const int64_t srow = g * n + perm[row];
+    stg16(dst + row * row_bytes + ch * 16, ldg16(src + srow * row_bytes + ch * 16));
+  }
+}
+
+// ================================================================ shared tile helpers
+// V tile of 64 rows -> registers (each lane: 4 groups of 4 rows x 16 bytes).
+struct VRegs {
+  u32x4 v[4][4];
+};
+
+__device__ __forceinline__ void v_fetch(VRegs& R, const uint16_t* vb, const int* rows, int lane) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int gidx = lane + 64 * n;
+    const int kg = gidx % 16, dc = gidx / 16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) R.v[n][e] = ldg16(vb + (int64_t)rows[4 * n + e] * kD + 8 * dc);
+  }
+}
+
+// rows[] for v_fetch: the 16 rows this lane loads (4 groups of 4 consecutive slots)
+__device__ __forceinline__ int v_slot(int lane, int n, int e) { return 4 * ((lane + 64 * n) % 16) + e; }
+
+// Store V^T: POS maps a 4-key group index to its LDS position.
+template <int LAYOUT>
+__device__ __forceinline__ int vt_pos(int kg) {
+  if (LAYOUT == 32) {  // 32x32x16 consumers: groups swap 1 <-> 2 inside each 16-key block
+    const int q4 = kg & 3;
+    return 16 * (kg >> 2) + 4 * ((q4 == 1) ? 2 : (q4 == 2) ? 1 : q4);
+  }
+  // 16x16x32 consumers: key 32ks + 16a + 4b + c sits at 32ks + 8b + 4a + c
+  return 32 * (kg >> 3) + 8 * (kg & 3) + 4 * ((kg & 7) >> 2);
+}
+
+template <int LAYOUT>
+__device__ __forceinline__ void v_store(uint16_t* vt, const VRegs& R, int lane) {
+#pragma unroll
+  for (int n = 0; n < 4; ++n) {
+    const int gidx = lane + 64 * n;
+    const int kg = gidx % 16, dc = gidx / 16;
+    const int pos = vt_pos<LAYOUT>(kg);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      u32x2 pk;
+      pk[0] = ((R.v[n][0][w] >> sh) & 0xffffu) | (((R.v[n][1][w] >> sh) & 0xffffu) << 16);
+      pk[1] = ((R.v[n][2][w] >> sh) & 0xffffu) | (((R.v[n][3][w] >> sh) & 0xffffu) << 16);
+      *reinterpret_cast<u32x2*>(&vt[(8 * dc + e) * kVS + pos]) = pk;
+    }
+  }
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// ================================================================ cluster decode
+constexpr int kDecWaves = 4;
+constexpr int kRowsPerSplit = 2048;
+
+int decode_splits(int64_t n_ctx) { return (int)((n_ctx + kRowsPerSplit - 1) / kRowsPerSplit); }
+
+__global__ void k_fill_u64(uint64_t* p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0ull;
+}
+
+// mask[g][c] bit j <=> query j of KV head g (j = t*grp + head-in-group) selected cluster c
+__global__ void k_decode_mask(const int32_t* __restrict__ sel, int T, int hq, int hkv, int C, int n_sel,
+                              uint64_t* __restrict__ mask) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)T * hq * n_sel) return;
+  const int th = (int)(e / n_sel);
+  const int t = th / hq, h = th % hq;
+  const int grp = hq / hkv;
+  const int g = h / grp;
+  const int c = sel[e];
+  if (c < 0 || c >= C) return;
+  atomicOr(reinterpret_cast<unsigned long long*>(&mask[(int64_t)g * C + c]), 1ull << (t * grp + (h - g * grp)));
+}
+
+struct DecLds {
+  uint16_t vt[kD * kVS];
+  uint64_t rmask[kBlk];
+};
+
+// One workgroup per (KV head, packed-row range); NQT = query tiles of 32.
+template <int NQT>
+__global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p, const uint64_t* __restrict__ mask,
+                                                                 float* __restrict__ part, int nsplit) {
+  __shared__ DecLds L[kDecWaves];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int g = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
+  const int grp = p.hq / p.hkv;
+  const int nq = p.T * grp;
+  const int64_t N = p.n_ctx;
+  const int* ptr = p.cluster_ptr + (int64_t)g * (p.C + 1);
+  const uint64_t* gm = mask + (int64_t)g * p.C;
+  const uint16_t* kb = p.k + (int64_t)g * N * kD;
+  const uint16_t* vb = p.v + (int64_t)g * N * kD;
+  const int64_t p0 = (int64_t)split * kRowsPerSplit;
+  const int64_t p1 = min(N, p0 + kRowsPerSplit);
+  const int ntile = (int)((p1 - p0 + kBlk - 1) / kBlk);
+  const float sl2 = p.scale * kLog2e;
+
+  // Q^T: lane holds query 32nt+l32, dims 64hf + 8s .. +7 at step s
+  bf16x8 qv[NQT][8];
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const int qi = min(32 * nt + l32, nq - 1);
+    const int t = qi / grp, h = g * grp + qi % grp;
+    const uint16_t* qr = p.q + ((int64_t)t * p.hq + h) * kD + 64 * hf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qv[nt][s] = as_bf16x8(ldg16(qr + 8 * s));
+  }
+  f32x16 o[NQT][4];
+  float m[NQT], l[NQT];
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    m[nt] = -INFINITY;
+    l[nt] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[nt][dt][r] = 0.f;
+  }
+
+  for (int t = w; t < ntile; t += kDecWaves) {
+    const int64_t base = p0 + (int64_t)t * kBlk;
+    const int len = (int)min((int64_t)kBlk, p1 - base);
+    // cluster of this lane's row: last c with ptr[c] <= row
+    const int64_t myrow = base + min(lane, len - 1);
+    int lo = 0, hi = p.C - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ptr[mid] <= myrow) lo = mid;
+      else hi = mid - 1;
+    }
+    const uint64_t rm = lane < len ? gm[lo] : 0ull;
+    if (!__any(rm != 0ull)) continue;  // nobody selected any row of this tile
+    L[w].rmask[lane] = rm;
+    // V rows -> LDS (transposed), K rows -> A operand registers
+    int rows[16];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) rows[4 * n + e] = (int)(base + min(v_slot(lane, n, e), len - 1));
+    VRegs VR;
+    v_fetch(VR, vb, rows, lane);
+    bf16x8 ka[2][8];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int64_t row = base + min(32 * mt + l32, len - 1);
+      const uint16_t* kr = kb + row * kD + 64 * hf;
+#pragma unroll
+      for (int s = 0; s < 8; ++s) ka[mt][s] = as_bf16x8(ldg16(kr + 8 * s));
+    }
+    v_store<32>(L[w].vt, VR, lane);
+    wave_sync();
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      f32x16 s0, s1;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        s0[r] = 0.f;
+        s1[r] = 0.f;
+      }
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        s0 = mfma32x32x16(ka[0][s], qv[nt][s], s0);
+        s1 = mfma32x32x16(ka[1][s], qv[nt][s], s1);
+      }
+      const int qi = 32 * nt + l32;
+      float x[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const int slot = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
+        const float sv = (r < 16 ? s0[r] : s1[r - 16]) * sl2;
+        const bool keep = qi < nq && ((L[w].rmask[slot] >> qi) & 1ull);
+        x[r] = keep ? sv : -INFINITY;
+      }
+      float mx = x[0];
+#pragma unroll
+      for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[nt], mx);
+      const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+      const float alpha = fast_exp2(m[nt] - muse);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        x[r] = fast_exp2(x[r] - muse);
+        ps += x[r];
+      }
+      ps += __shfl_xor(ps, 32);
+      l[nt] = l[nt] * alpha + ps;
+      m[nt] = mnew;
+      bf16x8 pv[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4 u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
+        pv[ks] = as_bf16x8(u);
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[nt][dt][r] *= alpha;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&L[w].vt[(32 * dt + l32) * kVS + 16 * ks + 8 * hf]));
+          o[nt][dt] = mfma32x32x16(a, pv[ks], o[nt][dt]);
+        }
+      }
+    }
+    wave_sync();
+  }
+
+  // ---- this wave's partial (max, sum, unnormalised output) for its queries
+  float* pw = part + (((int64_t)g * nsplit + split) * kDecWaves + w) * 64 * (kD + 2);
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const int qi = 32 * nt + l32;
+    if (qi < nq) {
+      float* pp = pw + qi * (kD + 2);
+      if (hf == 0) {
+        pp[0] = m[nt];
+        pp[1] = l[nt];
+      }
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) pp[2 + 32 * dt + 8 * (r / 4) + 4 * hf + (r % 4)] = o[nt][dt][r];
+    }
+  }
+}
+
+// Fixed-order merge of the partials of every (range, wave) slot.
+__global__ __launch_bounds__(128) void k_decode_combine(GatherParams p, const float* __restrict__ part, int nslot) {
+  const int grp = p.hq / p.hkv;
+  const int th = blockIdx.x;  // (t, h)
+  const int t = th / p.hq, h = th % p.hq;
+  const int g = h / grp;
+  const int qi = t * grp + (h - g * grp);
+  const int d = threadIdx.x;
+  float M = -INFINITY;
+  for (int s = 0; s < nslot; ++s) M = fmaxf(M, part[(((int64_t)g * nslot + s) * 64 + qi) * (kD + 2)]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float Ls = 0.f, Os = 0.f;
+  for (int s = 0; s < nslot; ++s) {
+    const float* pp = part + (((int64_t)g * nslot + s) * 64 + qi) * (kD + 2);
+    const float f = fast_exp2(pp[0] - Mu);
+    Ls += pp[1] * f;
+    Os += pp[2 + d] * f;
+  }
+  const float val = Ls > 0.f ? Os / Ls : 0.f;
+  const int64_t o = (int64_t)th * kD + d;
+  if (p.out_bf16) reinterpret_cast<uint16_t*>(p.out)[o] = (uint16_t)f2bf(val);
+  else reinterpret_cast<float*>(p.out)[o] = val;
+  if (p.lse != nullptr && d == 0) p.lse[th] = Ls > 0.f ? (M + __log2f(Ls)) * kLn2 : -INFINITY;
+}
+
+// ================================================================ token gather (16 heads per KV head)
+constexpr int kGatherWaves = 4;
+
+__global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams p) {
+  __shared__ uint16_t VT[kGatherWaves][kD * kVS];
+  __shared__ int32_t KEYS[kGatherWaves][kBlk];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, l16 = lane & 15, qd = lane >> 4;
+  const int64_t item = (int64_t)blockIdx.x * kGatherWaves + w;  // (t, g)
+  if (item >= (int64_t)p.T * p.hkv) return;
+  const int t = (int)(item / p.hkv), g = (int)(item % p.hkv);
+  const int64_t N = p.n_ctx;
+  const uint16_t* kb = p.k + (int64_t)g * N * kD;
+  const uint16_t* vb = p.v + (int64_t)g * N * kD;
+  const int32_t* ids = p.tok_idx + (int64_t)t * p.n_tok;
+  const int h = g * 16 + l16;
+  const float sl2 = p.scale * kLog2e;
+  // Q^T: lane holds head l16, dims 32qd + 8s .. +7 at step s
+  bf16x8 qv[4];
+  {
+    const uint16_t* qr = p.q + ((int64_t)t * p.hq + h) * kD + 32 * qd;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[s] = as_bf16x8(ldg16(qr + 8 * s));
+  }
+  f32x4 o[8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const int ntile = (p.n_tok + kBlk - 1) / kBlk;
+  for (int tt = 0; tt < ntile; ++tt) {
+    const int base = tt * kBlk;
+    const int len = min(kBlk, p.n_tok - base);
+    const int myid = lane < len ? ids[base + lane] : -1;
+    KEYS[w][lane] = myid;
+    wave_sync();
+    // rows to load (invalid slots read row 0 of a valid key; they are masked)
+    int first = KEYS[w][0] >= 0 ? KEYS[w][0] : 0;
+    int rows[16];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int id = KEYS[w][v_slot(lane, n, e)];
+        rows[4 * n + e] = id >= 0 ? id : first;
+      }
+    VRegs VR;
+    v_fetch(VR, vb, rows, lane);
+    bf16x8 ka[4][4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+      const int id = KEYS[w][16 * mt + l16];
+      const uint16_t* kr = kb + (int64_t)(id >= 0 ? id : first) * kD + 32 * qd;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) ka[mt][s] = as_bf16x8(ldg16(kr + 8 * s));
+    }
+    wave_sync();
+    v_store<16>(VT[w], VR, lane);
+    wave_sync();
+    f32x4 sc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[mt][r] = 0.f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sc[mt] = mfma16x16x32(ka[mt][s], qv[s], sc[mt]);
+    }
+    // element (mt, r): head l16, key slot 16mt + 4qd + r
+    float x[16];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int slot = 16 * mt + 4 * qd + r;
+        x[4 * mt + r] = KEYS[w][slot] >= 0 ? sc[mt][r] * sl2 : -INFINITY;
+      }
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = fast_exp2(m - muse);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = fast_exp2(x[r] - muse);
+      ps += x[r];
+    }
+    ps += __shfl_xor(ps, 16);
+    ps += __shfl_xor(ps, 32);
+    l = l * alpha + ps;
+    m = mnew;
+    // P^T for k-step ks: registers of M tiles 2ks and 2ks+1
+    bf16x8 pv[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
+      pv[ks] = as_bf16x8(u);
+    }
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[dt][r] *= alpha;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&VT[w][(16 * dt + l16) * kVS + 32 * ks + 8 * qd]));
+        o[dt] = mfma16x16x32(a, pv[ks], o[dt]);
+      }
+    }
+    wave_sync();
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t orow = (int64_t)t * p.hq + h;
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) {
+    const int d0 = 16 * dt + 4 * qd;
+    if (p.out_bf16) {
+      u32x2 pk;
+      pk[0] = pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv);
+      pk[1] = pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv);
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.out) + orow * kD + d0) = pk;
+    } else {
+      f32x4 v4;
+      for (int r = 0; r < 4; ++r) v4[r] = o[dt][r] * inv;
+      *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.out) + orow * kD + d0) = v4;
+    }
+  }
+  if (p.lse != nullptr && qd == 0) p.lse[orow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+}
+
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+// ---------------------------------------------------------------- launchers
+size_t cluster_pack_workspace_bytes(int64_t hkv, int64_t n, int C) {
+  const int64_t nseg = (n + kSeg - 1) / kSeg;
+  return a256((size_t)(hkv * nseg * C) * 4);
+}
+
+hipError_t launch_cluster_pack(const int32_t* labels, int64_t hkv, int64_t n, int C, int32_t* ptr, int32_t* perm,
+                               const void* k, const void* v, void* kp, void* vp, int head_dim, int elem_bytes,
+                               int32_t* err, void* ws, hipStream_t stream) {
+  const int nseg = (int)((n + kSeg - 1) / kSeg);
+  int32_t* seg = reinterpret_cast<int32_t*>(ws);
+  const dim3 grid((unsigned)(hkv * nseg));
+  hipLaunchKernelGGL(k_pack_count, grid, dim3(256), (size_t)C * 4, stream, labels, n, C, nseg, seg, err);
+  hipLaunchKernelGGL(k_pack_scan, dim3((unsigned)hkv), dim3(64), 0, stream, C, nseg, seg, ptr);
+  hipLaunchKernelGGL(k_pack_scatter, grid, dim3(256), 0, stream, labels, n, C, nseg, seg, perm);
+  if (kp != nullptr) {
+    const int row_bytes = head_dim * elem_bytes;
+    const int64_t chunks = hkv * n * (row_bytes / 16);
+    const unsigned blocks = (unsigned)std::min<int64_t>(8192, (chunks + 255) / 256);
+    hipLaunchKernelGGL(k_pack_copy, dim3(blocks), dim3(256), 0, stream, (const uint8_t*)k, (uint8_t*)kp, perm, ptr, n, C,
+                       row_bytes, chunks);
+    hipLaunchKernelGGL(k_pack_copy, dim3(blocks), dim3(256), 0, stream, (const uint8_t*)v, (uint8_t*)vp, perm, ptr, n, C,
+                       row_bytes, chunks);
+  }
+  return hipGetLastError();
+}
+
+size_t cluster_decode_workspace_bytes(int T, int hq, int hkv, int C, int64_t n_ctx) {
+  (void)T;
+  (void)hq;
+  return a256((size_t)hkv * C * 8) + a256((size_t)hkv * decode_splits(n_ctx) * kDecWaves * 64 * (kD + 2) * 4);
+}
+
+hipError_t launch_cluster_decode(const GatherParams& p, void* ws, hipStream_t stream) {
+  const int nsplit = decode_splits(p.n_ctx);
+  uint64_t* mask = reinterpret_cast<uint64_t*>(ws);
+  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + a256((size_t)p.hkv * p.C * 8));
+  const int64_t nm = (int64_t)p.hkv * p.C;
+  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)std::min<int64_t>(1024, (nm + 255) / 256)), dim3(256), 0, stream, mask, nm);
+  const int64_t ns = (int64_t)p.T * p.hq * p.n_sel;
+  hipLaunchKernelGGL(k_decode_mask, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, p.sel, p.T, p.hq, p.hkv,
+                     p.C, p.n_sel, mask);
+  const int nq = p.T * (p.hq / p.hkv);
+  const dim3 grid(p.hkv * nsplit);
+  if (nq <= 32)
+    hipLaunchKernelGGL((k_decode_split<1>), grid, dim3(64 * kDecWaves), 0, stream, p, mask, part, nsplit);
+  else
+    hipLaunchKernelGGL((k_decode_split<2>), grid, dim3(64 * kDecWaves), 0, stream, p, mask, part, nsplit);
+  hipLaunchKernelGGL(k_decode_combine, dim3(p.T * p.hq), dim3(kD), 0, stream, p, part, nsplit * kDecWaves);
+  return hipGetLastError();
+}
+
+size_t token_gather_workspace_bytes(int T, int hq, int n_tok) {
+  (void)T;
+  (void)hq;
+  (void)n_tok;
+  return 0;
+}
+
+hipError_t launch_token_gather(const GatherParams& p, void* ws, hipStream_t stream) {
+  (void)ws;
+  const int64_t items = (int64_t)p.T * p.hkv;
+  hipLaunchKernelGGL(k_token_gather, dim3((unsigned)((items + kGatherWaves - 1) / kGatherWaves)),
+                     dim3(64 * kGatherWaves), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa

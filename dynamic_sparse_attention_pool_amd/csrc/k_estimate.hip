@@ -1,0 +1,207 @@
+// Cheap estimators: block mean pooling and pooled block scores, and
+// query-centroid scores.
+//
+// "MInference 1.0" article, §方法介紹: block-sparse indices come from the
+// mean-pooled Q and K; pooling commutes with the product, so the pooled score
+// of a block pair is the mean of that 64x64 block of Q K^T.
+// Squeezed Attention page, §技术方案: every query is compared with every
+// cluster centroid, the centroids being held in on-chip shared memory.
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+constexpr int kBlk = 64;
+
+// ---------------------------------------------------------------- k_pool
+// One workgroup per (row of heads, block): 64 rows x D read with 16-byte
+// loads (HBM-streaming), fp32 partial sums per thread, a fixed-order
+// reduction through LDS, then the mean.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, int64_t seq, int nb,
+                                              float* __restrict__ out) {
+  constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
+  constexpr int CPR = D / E;         // chunks per row
+  constexpr int RPP = 256 / CPR;     // rows per pass
+  __shared__ float red[RPP][D];
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x / nb;
+  const int j = blockIdx.x % nb;
+  const int rp = tid / CPR, c = tid % CPR;
+  const T* base = x + (r * seq + (int64_t)j * kBlk) * D + c * E;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+#pragma unroll
+  for (int row = rp; row < kBlk; row += RPP) {
+    const u32x4 v = ldg16(base + (int64_t)row * D);
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += bf2f((uint16_t)((v[e >> 1] >> ((e & 1) * 16)) & 0xffffu));
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) red[rp][c * E + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    float s = 0.f;
+#pragma unroll
+    for (int q = 0; q < RPP; ++q) s += red[q][tid];
+    out[((int64_t)r * nb + j) * D + tid] = s * (1.0f / kBlk);
+  }
+}
+
+// ---------------------------------------------------------------- k_block_score
+// S[b,h,i,j] = pooled_q[b,h,i] . pooled_k[b,g(h),j] * scale for j <= i.
+// 64x64 output tile per workgroup, 4x4 per thread, fp32 FMAs in dimension
+// order.  Tiles strictly above the diagonal only write -inf.
+__global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ pq, const float* __restrict__ pk,
+                                                     int hq, int hkv, int nb, int D, float scale,
+                                                     float* __restrict__ S) {
+  __shared__ float Qs[64][33];
+  __shared__ float Ks[64][33];
+  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
+  const int nbt = (nb + 63) / 64;
+  const int bh = blockIdx.x / (nbt * nbt);
+  const int tile = blockIdx.x % (nbt * nbt);
+  const int ti = tile / nbt, tj = tile % nbt;
+  const int b = bh / hq, h = bh % hq;
+  const int g = (h * hkv) / hq;
+  float* Sb = S + (int64_t)bh * nb * nb;
+  if (tj > ti) {
+    for (int e = tid; e < 64 * 64; e += 256) {
+      const int i = ti * 64 + e / 64, j = tj * 64 + e % 64;
+      if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = -INFINITY;
+    }
+    return;
+  }
+  const float* Qb = pq + (int64_t)bh * nb * D;
+  const float* Kb = pk + ((int64_t)b * hkv + g) * nb * D;
+  float acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
+  for (int d0 = 0; d0 < D; d0 += 32) {
+    for (int e = tid; e < 64 * 32; e += 256) {
+      const int rr = e / 32, dd = e % 32;
+      const int qi = ti * 64 + rr, kj = tj * 64 + rr;
+      Qs[rr][dd] = qi < nb ? Qb[(int64_t)qi * D + d0 + dd] : 0.f;
+      Ks[rr][dd] = kj < nb ? Kb[(int64_t)kj * D + d0 + dd] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int dd = 0; dd < 32; ++dd) {
+      float qv[4], kv[4];
+#pragma unroll
+      for (int a = 0; a < 4; ++a) qv[a] = Qs[ty + 16 * a][dd];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) kv[c] = Ks[tx + 16 * c][dd];
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(qv[a], kv[c], acc[a][c]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int i = ti * 64 + ty + 16 * a, j = tj * 64 + tx + 16 * c;
+      if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = (j <= i) ? acc[a][c] * scale : -INFINITY;
+    }
+}
+
+// ---------------------------------------------------------------- k_centroid_score
+// One workgroup per (KV head, chunk of 32 centroids).  The chunk's centroids
+// and all queries of the KV head's group sit in LDS; each thread computes
+// (query, centroid) dot products in fp32.
+template <typename T>
+__global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q, const float* __restrict__ cent,
+                                                        int T_, int hq, int hkv, int C, int D, float scale,
+                                                        float* __restrict__ out) {
+  extern __shared__ float sm[];
+  const int grp = hq / hkv;
+  const int nq = T_ * grp;
+  const int nchunk = (C + 31) / 32;
+  const int g = blockIdx.x / nchunk, c0 = (blockIdx.x % nchunk) * 32;
+  float* Cs = sm;                 // [32][D+1]
+  float* Qs = sm + 32 * (D + 1);  // [nq][D+1]
+  for (int e = threadIdx.x; e < 32 * D; e += blockDim.x) {
+    const int c = e / D, d = e % D;
+    Cs[c * (D + 1) + d] = (c0 + c < C) ? cent[((int64_t)g * C + c0 + c) * D + d] : 0.f;
+  }
+  for (int e = threadIdx.x; e < nq * D; e += blockDim.x) {
+    const int qi = e / D, d = e % D;
+    const int t = qi / grp, h = g * grp + qi % grp;
+    const T* qp = q + ((int64_t)t * hq + h) * D + d;
+    float v;
+    if constexpr (sizeof(T) == 2) v = bf2f(*reinterpret_cast<const uint16_t*>(qp));
+    else v = *reinterpret_cast<const float*>(qp);
+    Qs[qi * (D + 1) + d] = v;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nq * 32; e += blockDim.x) {
+    const int qi = e / 32, c = e % 32;
+    if (c0 + c >= C) continue;
+    float acc = 0.f;
+    for (int d = 0; d < D; ++d) acc = fmaf(Qs[qi * (D + 1) + d], Cs[c * (D + 1) + d], acc);
+    const int t = qi / grp, h = g * grp + qi % grp;
+    out[((int64_t)t * hq + h) * C + c0 + c] = acc * scale;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_pool(const void* x, int64_t rows, int64_t seq, int head_dim, bool bf16, int block,
+                       float* out, hipStream_t stream) {
+  if (block != kBlk) return hipErrorInvalidValue;
+  const int nb = (int)(seq / kBlk);
+  const int64_t nblk = rows * nb;
+  if (nblk == 0) return hipSuccess;
+  const dim3 grid((unsigned)nblk);
+  if (bf16 && head_dim == 128)
+    hipLaunchKernelGGL((k_pool<uint16_t, 128>), grid, dim3(256), 0, stream, (const uint16_t*)x, seq, nb, out);
+  else if (bf16 && head_dim == 64)
+    hipLaunchKernelGGL((k_pool<uint16_t, 64>), grid, dim3(256), 0, stream, (const uint16_t*)x, seq, nb, out);
+  else if (!bf16 && head_dim == 128)
+    hipLaunchKernelGGL((k_pool<float, 128>), grid, dim3(256), 0, stream, (const float*)x, seq, nb, out);
+  else if (!bf16 && head_dim == 64)
+    hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, stream, (const float*)x, seq, nb, out);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, int nb,
+                              int head_dim, float scale, float* scores, hipStream_t stream) {
+  const int nbt = (nb + 63) / 64;
+  const int64_t n = (int64_t)batch * hq * nbt * nbt;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_block_score, dim3((unsigned)n), dim3(256), 0, stream, pq, pk, hq, hkv, nb, head_dim,
+                     scale, scores);
+  return hipGetLastError();
+}
+
+hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,
+                                 int C, int head_dim, float scale, float* out, hipStream_t stream) {
+  const int grp = hq / hkv;
+  const size_t lds = (size_t)(32 + T * grp) * (head_dim + 1) * sizeof(float);
+  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  const int nchunk = (C + 31) / 32;
+  const dim3 grid(hkv * nchunk);
+  if (q_bf16)
+    hipLaunchKernelGGL((k_centroid_score<uint16_t>), grid, dim3(256), lds, stream, (const uint16_t*)q, cent, T,
+                       hq, hkv, C, head_dim, scale, out);
+  else
+    hipLaunchKernelGGL((k_centroid_score<float>), grid, dim3(256), lds, stream, (const float*)q, cent, T, hq,
+                       hkv, C, head_dim, scale, out);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -1,0 +1,463 @@
+// Block-sparse / vertical-slash attention forward for gfx950.
+//
+// "MInference 1.0" article, §方法介紹: exact attention runs only over the
+// estimated blocks with a FlashAttention-style kernel; §延遲和內核中的稀疏模式,
+// Fig. 4: the vertical-slash kernel covers slash lines with 64x64 tiles and
+// vertical lines with 1x64 column pieces.  Both reduce to one loop: for a
+// 64-row query block, visit a list of 64-key tiles (contiguous ranges or
+// gathered columns), and fold each into an online softmax.
+//
+// bf16 kernel — one workgroup (2 waves) per (batch, head, query block); each
+// wave owns 32 query rows.  Per tile:
+//   S^T[key][query] = K_tile . Q^T          (v_mfma_f32_32x32x16_bf16, K from LDS,
+//                                            Q^T resident in VGPRs)
+//   online softmax along keys: every lane holds one query column, so the row
+//   statistics need a single exchange with lane^32
+//   O^T[d][query] += V^T . P^T               (V^T from LDS, P^T straight from the
+//                                            S^T accumulators, no shuffles)
+// The V tile is written to LDS transposed and with its keys permuted inside
+// each 16-key group so that the P^T register order lines up with it.
+// The next tile is fetched into VGPRs while the current one is computed.
+#include <climits>
+
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+constexpr int kBlk = 64;
+constexpr int kThreads = 128;
+
+template <int D>
+struct FwdLds {
+  static constexpr int KS = D + 8;      // K row stride (elements): 16 B pad against bank conflicts
+  static constexpr int VS = kBlk + 8;   // V^T row stride (elements)
+  uint16_t k[kBlk * KS];
+  uint16_t vt[D * VS];
+  int32_t key[kBlk];
+};
+
+// Tile source: either a contiguous key range or a gathered list of columns.
+struct TileRef {
+  int base;      // first key (contiguous) or offset into the column list (gathered)
+  int len;       // valid keys, 1..64
+  int gathered;  // 0 / 1
+  int diag;      // block mode: tile is the query block's own diagonal block
+};
+
+template <int MODE>
+struct TileIter {
+  // block mode
+  const int32_t* bidx = nullptr;
+  int cnt = 0, t = 0, iblk = 0;
+  // vertical-slash mode
+  const int32_t* iv = nullptr;
+  int n_iv = 0, cur_iv = 0, cur_off = 0;
+  int n_col = 0, col_off = 0;
+
+  __device__ bool next(TileRef& r) {
+    if (MODE == 0) {
+      if (t >= cnt) return false;
+      const int j = bidx[t++];
+      r.base = j * kBlk;
+      r.len = kBlk;
+      r.gathered = 0;
+      r.diag = (j == iblk);
+      return true;
+    }
+    if (cur_iv < n_iv) {
+      const int s = iv[2 * cur_iv], e = iv[2 * cur_iv + 1];
+      r.base = s + cur_off;
+      r.len = min(kBlk, e - r.base);
+      r.gathered = 0;
+      r.diag = 1;
+      cur_off += kBlk;
+      if (s + cur_off >= e) {
+        ++cur_iv;
+        cur_off = 0;
+      }
+      return true;
+    }
+    if (col_off < n_col) {
+      r.base = col_off;
+      r.len = min(kBlk, n_col - col_off);
+      r.gathered = 1;
+      r.diag = 1;
+      col_off += kBlk;
+      return true;
+    }
+    return false;
+  }
+};
+
+template <int D>
+struct TileRegs {
+  static constexpr int NK = D / 16;   // 16-byte K chunks per thread
+  static constexpr int NV = D / 64;   // (4 keys x 8 dims) V groups per thread
+  u32x4 k[NK];
+  u32x4 v[NV][4];
+  int32_t key;                        // absolute key of slot tid (tid < 64)
+};
+
+template <int D>
+__device__ __forceinline__ int tile_row(const TileRef& r, const int32_t* cols, int slot) {
+  const int s = min(slot, r.len - 1);
+  return r.gathered ? cols[r.base + s] : r.base + s;
+}
+
+template <int D>
+__device__ __forceinline__ void tile_fetch(TileRegs<D>& R, const TileRef& r, const uint16_t* kb,
+                                           const uint16_t* vb, const int32_t* cols, int tid) {
+  constexpr int CPR = D / 8;  // chunks per row
+#pragma unroll
+  for (int n = 0; n < TileRegs<D>::NK; ++n) {
+    const int c = tid + kThreads * n;
+    const int slot = c / CPR, dc = c % CPR;
+    const int row = tile_row<D>(r, cols, slot);
+    R.k[n] = ldg16(kb + (int64_t)row * D + 8 * dc);
+  }
+#pragma unroll
+  for (int n = 0; n < TileRegs<D>::NV; ++n) {
+    const int gidx = tid + kThreads * n;
+    const int kg = gidx % 16, dc = gidx / 16;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int row = tile_row<D>(r, cols, 4 * kg + e);
+      R.v[n][e] = ldg16(vb + (int64_t)row * D + 8 * dc);
+    }
+  }
+  if (tid < kBlk) {
+    R.key = tid < r.len ? (r.gathered ? cols[r.base + tid] : r.base + tid) : INT_MAX;
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_store(FwdLds<D>& L, const TileRegs<D>& R, int tid) {
+  constexpr int CPR = D / 8;
+#pragma unroll
+  for (int n = 0; n < TileRegs<D>::NK; ++n) {
+    const int c = tid + kThreads * n;
+    const int slot = c / CPR, dc = c % CPR;
+    *reinterpret_cast<u32x4*>(&L.k[slot * FwdLds<D>::KS + 8 * dc]) = R.k[n];
+  }
+#pragma unroll
+  for (int n = 0; n < TileRegs<D>::NV; ++n) {
+    const int gidx = tid + kThreads * n;
+    const int kg = gidx % 16, dc = gidx / 16;
+    // keys 4kg..4kg+3 sit at positions 16*(kg/4) + 4*swap(kg%4), swap = {0,2,1,3}
+    const int q4 = kg & 3;
+    const int pos = 16 * (kg >> 2) + 4 * ((q4 == 1) ? 2 : (q4 == 2) ? 1 : q4);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, sh = (e & 1) * 16;
+      const uint32_t x0 = (R.v[n][0][w] >> sh) & 0xffffu, x1 = (R.v[n][1][w] >> sh) & 0xffffu;
+      const uint32_t x2 = (R.v[n][2][w] >> sh) & 0xffffu, x3 = (R.v[n][3][w] >> sh) & 0xffffu;
+      u32x2 pk;
+      pk[0] = x0 | (x1 << 16);
+      pk[1] = x2 | (x3 << 16);
+      *reinterpret_cast<u32x2*>(&L.vt[(8 * dc + e) * FwdLds<D>::VS + pos]) = pk;
+    }
+  }
+  if (tid < kBlk) L.key[tid] = R.key;
+}
+
+template <int D, int MODE, bool OUT_BF16>
+__global__ __launch_bounds__(kThreads) void k_fwd_bf16(FwdParams p) {
+  __shared__ FwdLds<D> L;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int n_items = gridDim.x;
+  const int item = xcd_remap(blockIdx.x, n_items);
+  const int grp = p.heads_q / p.heads_kv;
+  int rest = item;
+  const int hh = rest % grp;
+  rest /= grp;
+  const int ii = rest % p.nqb;
+  rest /= p.nqb;
+  const int g = rest % p.heads_kv;
+  const int b = rest / p.heads_kv;
+  const int iblk = p.nqb - 1 - ii;  // long rows first
+  const int h = g * grp + hh;
+  const int64_t N = p.seq;
+  const int64_t row_id = ((int64_t)b * p.heads_q + h) * p.nqb + iblk;
+
+  const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (((int64_t)b * p.heads_q + h) * N + (int64_t)iblk * kBlk) * D;
+  const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + ((int64_t)b * p.heads_kv + g) * N * D;
+  const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + ((int64_t)b * p.heads_kv + g) * N * D;
+
+  TileIter<MODE> it;
+  const int32_t* cols = nullptr;
+  if (MODE == 0) {
+    it.bidx = p.block_idx + row_id * p.kmax;
+    it.cnt = p.block_cnt[row_id];
+    it.iblk = iblk;
+  } else {
+    it.iv = p.iv + row_id * p.max_iv * 2;
+    it.n_iv = p.iv_cnt[row_id];
+    it.n_col = p.col_cnt[row_id];
+    cols = p.col + row_id * p.max_col;
+  }
+
+  // Q^T operand: lane holds query row 32w+l32, dims 16s+8hf .. +7 of step s
+  bf16x8 qv[D / 16];
+  {
+    const uint16_t* qr = qb + (int64_t)(32 * w + l32) * D + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qv[s] = as_bf16x8(ldg16(qr + 16 * s));
+  }
+  const int qpos = iblk * kBlk + 32 * w + l32;  // absolute query row of this lane
+  const float sl2 = p.scale * kLog2e;
+
+  f32x16 o[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+  float m = -INFINITY, lsum = 0.f;
+
+  TileRegs<D> R;
+  TileRef cur, nxt;
+  bool have = it.next(cur);
+  if (have) tile_fetch<D>(R, cur, kb, vb, cols, tid);
+  while (have) {
+    __syncthreads();
+    tile_store<D>(L, R, tid);
+    __syncthreads();
+    const bool more = it.next(nxt);
+    if (more) tile_fetch<D>(R, nxt, kb, vb, cols, tid);
+
+    // ---- S^T = K . Q^T for the 64 keys of the tile (two 32-key M tiles)
+    f32x16 s0, s1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s0[r] = 0.f;
+      s1[r] = 0.f;
+    }
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&L.k[l32 * FwdLds<D>::KS + 16 * st + 8 * hf]));
+      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&L.k[(32 + l32) * FwdLds<D>::KS + 16 * st + 8 * hf]));
+      s0 = mfma32x32x16(a0, qv[st], s0);
+      s1 = mfma32x32x16(a1, qv[st], s1);
+    }
+
+    // ---- online softmax (log2 domain); element r of M tile mt is key slot
+    //      32*mt + 8*(r/4) + 4*hf + r%4
+    float x[32];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      x[r] = s0[r] * sl2;
+      x[16 + r] = s1[r] * sl2;
+    }
+    if (cur.diag) {
+      if (MODE == 0) {
+        const int lim = 32 * w + l32;  // slot index of this lane's own row
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          const int slot = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
+          if (slot > lim) x[r] = -INFINITY;
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 32; ++r) {
+          const int slot = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
+          const int key = L.key[slot];
+          if (key > qpos) x[r] = -INFINITY;  // empty slots hold INT_MAX
+        }
+      }
+    }
+    float mx = x[0];
+#pragma unroll
+    for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+    const float alpha = fast_exp2(m - muse);
+    float ps = 0.f;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      x[r] = fast_exp2(x[r] - muse);
+      ps += x[r];
+    }
+    ps += __shfl_xor(ps, 32);
+    lsum = lsum * alpha + ps;
+    m = mnew;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+
+    // ---- P^T operand for k-step ks = the 8 consecutive registers x[8ks .. 8ks+7]
+    bf16x8 pv[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      u32x4 u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
+      pv[ks] = as_bf16x8(u);
+    }
+    // ---- O^T += V^T . P^T
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&L.vt[(32 * dt + l32) * FwdLds<D>::VS + 16 * ks + 8 * hf]));
+        o[dt] = mfma32x32x16(a, pv[ks], o[dt]);
+      }
+    }
+    cur = nxt;
+    have = more;
+  }
+
+  // ---- epilogue: O = O^T / l, element (dt, r) is dim 32dt + 8(r/4) + 4hf + r%4
+  const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+  const int64_t orow = ((int64_t)b * p.heads_q + h) * N + qpos;
+  if (OUT_BF16) {
+    uint16_t* op = reinterpret_cast<uint16_t*>(p.out) + orow * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        u32x2 pk;
+        pk[0] = pack_bf16x2(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv);
+        pk[1] = pack_bf16x2(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
+        *reinterpret_cast<u32x2*>(op + 32 * dt + 8 * j + 4 * hf) = pk;
+      }
+  } else {
+    float* op = reinterpret_cast<float*>(p.out) + orow * D;
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        f32x4 v4;
+        for (int e = 0; e < 4; ++e) v4[e] = o[dt][4 * j + e] * inv;
+        *reinterpret_cast<f32x4*>(op + 32 * dt + 8 * j + 4 * hf) = v4;
+      }
+  }
+  if (p.lse != nullptr && hf == 0) p.lse[orow] = lsum > 0.f ? (m + __log2f(lsum)) * kLn2 : -INFINITY;
+}
+
+// ------------------------------------------------------------------ fp32 inputs
+// One workgroup of 64 threads per (batch, head, query block); each thread owns
+// one query row and folds the tile's keys one by one (fp32 throughout).
+template <int D, int MODE>
+__global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
+  __shared__ float Ks[kBlk][D];
+  __shared__ float Vs[kBlk][D];
+  __shared__ int32_t keyS[kBlk];
+  const int tid = threadIdx.x;
+  const int item = xcd_remap(blockIdx.x, gridDim.x);
+  const int grp = p.heads_q / p.heads_kv;
+  int rest = item;
+  const int hh = rest % grp;
+  rest /= grp;
+  const int ii = rest % p.nqb;
+  rest /= p.nqb;
+  const int g = rest % p.heads_kv;
+  const int b = rest / p.heads_kv;
+  const int iblk = p.nqb - 1 - ii;
+  const int h = g * grp + hh;
+  const int64_t N = p.seq;
+  const int64_t row_id = ((int64_t)b * p.heads_q + h) * p.nqb + iblk;
+  const int qpos = iblk * kBlk + tid;
+  const float* qr = reinterpret_cast<const float*>(p.q) + (((int64_t)b * p.heads_q + h) * N + qpos) * D;
+  const float* kb = reinterpret_cast<const float*>(p.k) + ((int64_t)b * p.heads_kv + g) * N * D;
+  const float* vb = reinterpret_cast<const float*>(p.v) + ((int64_t)b * p.heads_kv + g) * N * D;
+
+  TileIter<MODE> it;
+  const int32_t* cols = nullptr;
+  if (MODE == 0) {
+    it.bidx = p.block_idx + row_id * p.kmax;
+    it.cnt = p.block_cnt[row_id];
+    it.iblk = iblk;
+  } else {
+    it.iv = p.iv + row_id * p.max_iv * 2;
+    it.n_iv = p.iv_cnt[row_id];
+    it.n_col = p.col_cnt[row_id];
+    cols = p.col + row_id * p.max_col;
+  }
+  float q[D], o[D];
+  for (int d = 0; d < D; ++d) {
+    q[d] = qr[d];
+    o[d] = 0.f;
+  }
+  float m = -INFINITY, l = 0.f;
+  TileRef r;
+  while (it.next(r)) {
+    __syncthreads();
+    const int row = tile_row<D>(r, cols, tid);
+    for (int d = 0; d < D; d += 4) {
+      *reinterpret_cast<f32x4*>(&Ks[tid][d]) = *reinterpret_cast<const f32x4*>(kb + (int64_t)row * D + d);
+      *reinterpret_cast<f32x4*>(&Vs[tid][d]) = *reinterpret_cast<const f32x4*>(vb + (int64_t)row * D + d);
+    }
+    keyS[tid] = tid < r.len ? (r.gathered ? cols[r.base + tid] : r.base + tid) : INT_MAX;
+    __syncthreads();
+    float s[kBlk];
+    float mx = -INFINITY;
+    for (int c = 0; c < kBlk; ++c) {
+      float acc = 0.f;
+      for (int d = 0; d < D; ++d) acc = fmaf(q[d], Ks[c][d], acc);
+      s[c] = keyS[c] > qpos ? -INFINITY : acc * p.scale;
+      mx = fmaxf(mx, s[c]);
+    }
+    const float mnew = fmaxf(m, mx);
+    if (mnew == -INFINITY) continue;
+    const float alpha = expf(m - mnew);
+    l *= alpha;
+    for (int d = 0; d < D; ++d) o[d] *= alpha;
+    for (int c = 0; c < kBlk; ++c) {
+      const float pc = expf(s[c] - mnew);
+      l += pc;
+      for (int d = 0; d < D; ++d) o[d] = fmaf(pc, Vs[c][d], o[d]);
+    }
+    m = mnew;
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t orow = ((int64_t)b * p.heads_q + h) * N + qpos;
+  if (p.lse != nullptr) p.lse[orow] = l > 0.f ? m + logf(l) : -INFINITY;
+  float* op = reinterpret_cast<float*>(p.out) + orow * D;
+  for (int d = 0; d < D; d += 4) {
+    f32x4 v4 = {o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
+    *reinterpret_cast<f32x4*>(op + d) = v4;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, bool out_bf16,
+                      hipStream_t stream) {
+  const int n_items = p.batch * p.heads_q * p.nqb;
+  if (n_items == 0) return hipSuccess;
+  const dim3 grid(n_items);
+  if (in_bf16) {
+#define SA_FWD_CASE(D_, M_, OB_)                                                   \
+  if (head_dim == D_ && mode == M_ && out_bf16 == OB_) {                           \
+    hipLaunchKernelGGL((k_fwd_bf16<D_, M_, OB_>), grid, dim3(kThreads), 0, stream, p); \
+    return hipGetLastError();                                                      \
+  }
+    SA_FWD_CASE(128, 0, true)
+    SA_FWD_CASE(128, 0, false)
+    SA_FWD_CASE(128, 1, true)
+    SA_FWD_CASE(128, 1, false)
+    SA_FWD_CASE(64, 0, true)
+    SA_FWD_CASE(64, 0, false)
+    SA_FWD_CASE(64, 1, true)
+    SA_FWD_CASE(64, 1, false)
+#undef SA_FWD_CASE
+    return hipErrorInvalidValue;
+  }
+  if (out_bf16) return hipErrorInvalidValue;
+#define SA_FWD32_CASE(D_, M_)                                                   \
+  if (head_dim == D_ && mode == M_) {                                           \
+    hipLaunchKernelGGL((k_fwd_f32<D_, M_>), grid, dim3(64), 0, stream, p);      \
+    return hipGetLastError();                                                   \
+  }
+  SA_FWD32_CASE(64, 0)
+  SA_FWD32_CASE(64, 1)
+  SA_FWD32_CASE(128, 0)
+  SA_FWD32_CASE(128, 1)
+#undef SA_FWD32_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa

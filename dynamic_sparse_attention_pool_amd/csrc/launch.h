@@ -1,0 +1,95 @@
+// Internal interface between the C-ABI layer (sa_api.cpp) and the kernels.
+// Every launcher enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+// ---------------------------------------------------------------- forward
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* block_idx;
+  const int32_t* block_cnt;
+  const int32_t* iv;
+  const int32_t* iv_cnt;
+  const int32_t* col;
+  const int32_t* col_cnt;
+  int64_t seq;
+  int32_t batch, heads_q, heads_kv, nqb;
+  int32_t kmax, max_iv, max_col;
+  float scale;
+};
+hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, bool out_bf16,
+                      hipStream_t stream);
+
+// ---------------------------------------------------------------- estimate
+hipError_t launch_pool(const void* x, int64_t rows, int64_t seq, int head_dim, bool bf16, int block,
+                       float* out, hipStream_t stream);
+hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, int nb,
+                              int head_dim, float scale, float* scores, hipStream_t stream);
+hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,
+                                 int C, int head_dim, float scale, float* out, hipStream_t stream);
+hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
+                          int64_t pos0, float* out, hipStream_t stream);
+size_t vs_workspace_bytes(int64_t rows, int64_t seq);
+hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv, int64_t seq,
+                              int head_dim, int last_q, float scale, float* a_v, float* a_s, void* ws,
+                              hipStream_t stream);
+
+// ---------------------------------------------------------------- select
+struct SelectParams {
+  const float* scores;
+  int64_t rows, ncand, ld, period, offset;
+  int32_t causal, n_sink, n_local, k, rnum, rden, kmax;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* err;
+};
+hipError_t launch_select(const SelectParams& p, hipStream_t stream);
+
+struct VsBuildParams {
+  int64_t rows, seq;
+  int32_t bs, n_vert, n_slash;
+  const int32_t* vert;
+  const int32_t* vert_cnt;
+  const int32_t* slash;
+  const int32_t* slash_cnt;
+  int32_t* iv;
+  int32_t* iv_cnt;
+  int32_t* col;
+  int32_t* col_cnt;
+};
+hipError_t launch_vs_build(const VsBuildParams& p, hipStream_t stream);
+
+// ---------------------------------------------------------------- decode / gather
+struct GatherParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const int32_t* cluster_ptr;
+  const int32_t* sel;
+  const int32_t* tok_idx;
+  void* out;
+  float* lse;
+  int64_t n_ctx;
+  int32_t T, hq, hkv, C, n_sel, n_tok;
+  float scale;
+  bool out_bf16;
+};
+size_t cluster_decode_workspace_bytes(int T, int hq, int hkv, int C, int64_t n_ctx);
+hipError_t launch_cluster_decode(const GatherParams& p, void* ws, hipStream_t stream);
+size_t token_gather_workspace_bytes(int T, int hq, int n_tok);
+hipError_t launch_token_gather(const GatherParams& p, void* ws, hipStream_t stream);
+
+size_t cluster_pack_workspace_bytes(int64_t hkv, int64_t n, int C);
+hipError_t launch_cluster_pack(const int32_t* labels, int64_t hkv, int64_t n, int C, int32_t* ptr,
+                               int32_t* perm, const void* k, const void* v, void* kp, void* vp,
+                               int head_dim, int elem_bytes, int32_t* err, void* ws, hipStream_t stream);
+
+}  // namespace sa

@@ -1,0 +1,349 @@
+/*
+ * sa.h — C ABI of libsa: dynamic sparse attention on AMD Instinct MI355X (gfx950).
+ *
+ * The method (sources cited per entry point):
+ *   a cheap estimator scores key blocks, key clusters or key tokens; a per-row
+ *   top-k keeps a subset; exact softmax attention runs over the kept keys only.
+ *
+ * Conventions shared by every entry point
+ *   - Plain C.  Every tensor pointer is a DEVICE pointer owned by the caller.
+ *     The library never allocates or frees device memory: scratch space comes
+ *     from a caller-provided workspace whose size the matching
+ *     *_workspace_bytes() call returns (0 is a valid answer).
+ *   - Tensors are dense, row-major, in the documented shape order; the last
+ *     dimension is contiguous.  q, k, v, out pointers must be 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *     default stream).  No call synchronises the host.
+ *   - The return value is an sa_status.  Argument errors are detected on the
+ *     host before any launch and leave all outputs untouched; the message is
+ *     kept per thread and returned by sa_last_error().  SA_ERR_LAUNCH reports a
+ *     HIP launch failure.
+ *   - Outputs are bitwise deterministic run to run (no floating-point atomics).
+ *   - Element types: SA_F32 (float), SA_BF16 (bfloat16 bit patterns, uint16),
+ *     SA_I32 (int32).  Scores, pooled vectors and lse are always float.
+ *   - Grouped-query heads: query head h reads KV head floor(h*Hkv/Hq);
+ *     Hq must be a multiple of Hkv.
+ */
+#ifndef SA_H_
+#define SA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+typedef enum sa_status {
+  SA_OK = 0,
+  SA_ERR_NULL = 1,        /* a required pointer is NULL */
+  SA_ERR_SHAPE = 2,       /* a size is out of range or inconsistent */
+  SA_ERR_DTYPE = 3,       /* unsupported element type */
+  SA_ERR_ALIGN = 4,       /* pointer not 16-byte aligned */
+  SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
+  SA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  SA_ERR_LAUNCH = 7,      /* HIP reported an error at launch */
+  SA_ERR_VALUE = 8        /* a parameter value is invalid (e.g. scale, k) */
+} sa_status;
+
+typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_I32 = 2 } sa_dtype;
+
+/* ======================================================================
+ * sa_estimate — cheap scores that rank keys, blocks or clusters.
+ *
+ * kind = SA_EST_BLOCK_MEANPOOL
+ *   "MInference 1.0" article, §方法介紹: block-sparse indices are estimated
+ *   from mean-pooled Q and K (mean pooling commutes with the product).
+ *   q [B,Hq,N,d], k [B,Hkv,N,d] (F32 or BF16), N a multiple of block_size.
+ *   scores [B,Hq,nb,nb] float, nb = N/block_size:
+ *     scores[b,h,i,j] = mean(q rows of block i) . mean(k rows of block j) * scale
+ *     for j <= i, and -INFINITY for j > i.
+ *   pooled_q [B,Hq,nb,d] / pooled_k [B,Hkv,nb,d]: optional float outputs of the
+ *   block means; when NULL the means live in the workspace.
+ *
+ * kind = SA_EST_VSLASH
+ *   "MInference 1.0" article, §方法介紹: vertical and slash indices are
+ *   estimated from the attention of the last queries to all keys.
+ *   q [B,Hq,N,d], k [B,Hkv,N,d] (BF16).  The last `last_q` query rows, at
+ *   positions N-last_q .. N-1, attend keys causally: A = softmax(q k^T scale).
+ *   scores  [B,Hq,N] float: vertical score  a_v[c] = sum_r A[r,c]
+ *   scores2 [B,Hq,N] float: slash score     a_s[o] = sum_r A[r, pos_r - o]
+ *   Requires a workspace.
+ *
+ * kind = SA_EST_CENTROID
+ *   Squeezed Attention page, §技术方案: each query is compared with every
+ *   cluster centroid; §核心贡献/§技术方案 keep centroids in on-chip memory.
+ *   q [T,Hq,d] (BF16 or F32), centroids [Hkv,C,d] float.
+ *   scores [T,Hq,C] float = q[t,h] . centroids[g(h),c] * scale.
+ *
+ * kind = SA_EST_INDEXER
+ *   IndexCache article, §长文本的算力困境: a light indexer scores every key
+ *   token for every query.  Score of the synthetic workload:
+ *     I[t,s] = sum_h weights[h] * max(0, q[t,h,:] . k[s,:])   for s <= q_pos0 + t
+ *   q [T,Hi,di] (BF16; heads_q = Hi, head_dim = di, seq_q = T),
+ *   k [Nk,di] (BF16; seq_k = Nk, heads_kv = 1), weights [Hi] float.
+ *   scores [T,Nk] float, -INFINITY where s > q_pos0 + t.  No scale.
+ *   di must be 64; Hi a multiple of 8.
+ * ====================================================================== */
+enum { SA_EST_BLOCK_MEANPOOL = 0, SA_EST_VSLASH = 1, SA_EST_CENTROID = 2, SA_EST_INDEXER = 3 };
+
+typedef struct sa_estimate_args {
+  int32_t kind;
+  int32_t dtype;          /* element type of q and k */
+  int64_t batch;          /* B (BLOCK, VSLASH); ignored otherwise */
+  int64_t heads_q;        /* Hq, or Hi for INDEXER */
+  int64_t heads_kv;       /* Hkv; 1 for INDEXER */
+  int64_t seq_q;          /* N (BLOCK, VSLASH) or T (CENTROID, INDEXER) */
+  int64_t seq_k;          /* N, Nctx or Nk */
+  int64_t head_dim;       /* d (64 or 128), di for INDEXER */
+  int64_t n_centroids;    /* C (CENTROID) */
+  int64_t q_pos0;         /* INDEXER: absolute position of query 0 */
+  int32_t block_size;     /* BLOCK: 64 */
+  int32_t last_q;         /* VSLASH: 64 */
+  float scale;            /* BLOCK, VSLASH, CENTROID: > 0 */
+  int32_t reserved0;
+  const void* q;
+  const void* k;
+  const float* centroids; /* CENTROID */
+  const float* weights;   /* INDEXER */
+  float* scores;
+  float* scores2;         /* VSLASH slash scores */
+  float* pooled_q;        /* BLOCK, optional */
+  float* pooled_k;        /* BLOCK, optional */
+} sa_estimate_args;
+
+int sa_estimate_workspace_bytes(const sa_estimate_args* args, size_t* bytes);
+int sa_estimate(const sa_estimate_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * sa_select_topk — per-row top-k with forced members.
+ *
+ * The top subset by score is kept ("MInference 1.0" article, §方法介紹;
+ * Squeezed Attention page, §技术方案 "select the top-K clusters"; IndexCache
+ * article, §长文本的算力困境).  Local and global members are always attended
+ * ("稀疏注意力机制解析" explainer, §1.2), which gives the forced sets.
+ *
+ * scores: [rows, ld] float, row r reads scores[r*ld + 0 .. n_r-1].
+ * Candidates of row r: 0 .. n_r-1 with
+ *     n_r = causal ? min(ncand, (r % causal_period) + causal_offset + 1) : ncand
+ * Forced (always kept, not counted in k): 0 .. min(n_sink,n_r)-1 and
+ *     max(0, n_r-n_local) .. n_r-1.
+ * Budget: k_r = (ratio_den > 0 ? ceil(ratio_num*n_r/ratio_den) : k), capped at
+ *     the number of non-forced candidates.
+ * Order: higher score first; equal scores -> lower index first; -0 == +0.
+ * Output: idx [rows, kmax] int32 — the kept indices of row r ascending, padded
+ *     with -1; cnt [rows] int32 — the number kept.  The host checks that the
+ *     largest possible count fits kmax (SA_ERR_SHAPE otherwise).
+ * err_flag: optional device int32; set to 1 when a candidate score is NaN
+ *     (that row's output is then unspecified).  Never cleared by the library.
+ * Rows with up to 4096 candidates are ranked in LDS; longer rows (up to 2^24)
+ * with a multi-pass radix select that re-reads the row.
+ * ====================================================================== */
+typedef struct sa_select_args {
+  const float* scores;
+  int64_t rows;
+  int64_t ncand;
+  int64_t ld;
+  int64_t causal_period;
+  int64_t causal_offset;
+  int32_t causal;
+  int32_t n_sink;
+  int32_t n_local;
+  int32_t k;
+  int32_t ratio_num;
+  int32_t ratio_den;
+  int32_t kmax;
+  int32_t reserved0;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* err_flag;
+} sa_select_args;
+
+int sa_select_topk_workspace_bytes(const sa_select_args* args, size_t* bytes);
+int sa_select_topk(const sa_select_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * sa_vs_build — vertical-slash selections -> per-query-block key tables.
+ *
+ * "MInference 1.0" article, §延遲和內核中的稀疏模式, Fig. 4: vertical lines
+ * are computed in 1x64 pieces and slash lines in 64x64 blocks.  Reading: the
+ * slash at offset o covers, for query block i, the contiguous key tile
+ * [64i-o, 64i-o+64) clipped at 0 (the square tile whose diagonal is the line).
+ *
+ * rows = B*Hq; vert [rows, n_vert] ascending column indices with vert_cnt
+ * [rows]; slash [rows, n_slash] ascending offsets with slash_cnt [rows]
+ * (the outputs of sa_select_topk).  For every row and query block i < N/64:
+ *   iv  [rows, nqb, n_slash, 2]: the slash tiles united into disjoint
+ *       intervals [start, end), ascending; iv_cnt [rows, nqb].
+ *   col [rows, nqb, n_vert]: kept columns c <= 64i+63 outside those intervals,
+ *       ascending; col_cnt [rows, nqb].
+ * ====================================================================== */
+typedef struct sa_vs_build_args {
+  int64_t rows;
+  int64_t seq;
+  int32_t block_size;     /* 64 */
+  int32_t n_vert;
+  int32_t n_slash;
+  int32_t reserved0;
+  const int32_t* vert;
+  const int32_t* vert_cnt;
+  const int32_t* slash;
+  const int32_t* slash_cnt;
+  int32_t* iv;
+  int32_t* iv_cnt;
+  int32_t* col;
+  int32_t* col_cnt;
+} sa_vs_build_args;
+
+int sa_vs_build(const sa_vs_build_args* args, void* stream);
+
+/* ======================================================================
+ * sa_block_sparse_fwd — exact attention over the kept key sets.
+ *
+ * "MInference 1.0" article, §方法介紹 (block-sparse FlashAttention over the
+ * estimated block indices) and §延遲和內核中的稀疏模式, Fig. 4 (vertical-slash
+ * kernel).  FlashAttention tiling with an online softmax gives the exact
+ * softmax over the union of the listed keys.
+ *
+ * q [B,Hq,N,d], k and v [B,Hkv,N,d]; dtype SA_BF16 (d = 64 or 128, bf16
+ * matrix cores, fp32 accumulation) or SA_F32 (d = 64 or 128, fp32).
+ * out [B,Hq,N,d] of out_dtype (SA_F32 or SA_BF16); lse [B,Hq,N] float,
+ * optional (natural log of the softmax denominator, including the scale).
+ * Row r of query block i attends key c only when c <= r (token-causal).
+ * mode = SA_FWD_BLOCK: block_idx [B,Hq,nqb,kmax] ascending, -1 padded, and
+ *   block_cnt [B,Hq,nqb]; keys = union of blocks [64j, 64j+64).
+ *   Every listed block must satisfy 0 <= j <= i.
+ * mode = SA_FWD_VSLASH: the sa_vs_build tables (iv/iv_cnt with capacity
+ *   max_iv, col/col_cnt with capacity max_col); keys = intervals ∪ columns.
+ * A row with no admissible key gets out = 0 and lse = -INFINITY.
+ * ====================================================================== */
+enum { SA_FWD_BLOCK = 0, SA_FWD_VSLASH = 1 };
+
+typedef struct sa_fwd_args {
+  int32_t mode;
+  int32_t dtype;
+  int32_t out_dtype;
+  int32_t block_size;     /* 64 */
+  int64_t batch;
+  int64_t heads_q;
+  int64_t heads_kv;
+  int64_t seq;
+  int64_t head_dim;
+  float scale;
+  int32_t kmax;
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  float* lse;
+  const int32_t* block_idx;
+  const int32_t* block_cnt;
+  const int32_t* iv;
+  const int32_t* iv_cnt;
+  const int32_t* col;
+  const int32_t* col_cnt;
+  int32_t max_iv;
+  int32_t max_col;
+} sa_fwd_args;
+
+int sa_block_sparse_fwd_workspace_bytes(const sa_fwd_args* args, size_t* bytes);
+int sa_block_sparse_fwd(const sa_fwd_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * sa_gather_decode — exact attention over gathered keys.
+ *
+ * mode = SA_GATHER_CLUSTER (Squeezed Attention page, §技术方案: attention
+ *   only over the key/value pairs of the selected clusters).
+ *   q [T,Hq,d] BF16; k, v [Hkv,Nctx,d] BF16 in cluster-major order (as
+ *   written by sa_cluster_pack); cluster_ptr [Hkv,C+1] int32 (cluster c of
+ *   KV head g is rows cluster_ptr[g,c] .. cluster_ptr[g,c+1]-1); sel
+ *   [T,Hq,n_sel] int32 cluster ids (duplicates count once; -1 ignored).
+ *   T*Hq/Hkv (queries per KV head) must be <= 64.  No causal mask.
+ * mode = SA_GATHER_TOKEN (IndexCache article, §长文本的算力困境 and
+ *   §"偷懒"的艺术: attention over the indexer's token subset, which shared
+ *   layers reuse from the nearest full layer — the index cache is simply the
+ *   caller's tok_idx buffer passed to several layers).
+ *   q [T,Hq,d] BF16; k, v [Hkv,Nctx,d] BF16 in context order; tok_idx
+ *   [T,n_tok] int32, shared by all heads of token t, distinct, -1 padded.
+ * d = 128.  out [T,Hq,d] (out_dtype F32 or BF16); lse [T,Hq] optional.
+ * Both modes need a workspace.
+ * ====================================================================== */
+enum { SA_GATHER_CLUSTER = 0, SA_GATHER_TOKEN = 1 };
+
+typedef struct sa_gather_args {
+  int32_t mode;
+  int32_t dtype;
+  int32_t out_dtype;
+  int32_t n_clusters;
+  int64_t n_q;            /* T */
+  int64_t heads_q;
+  int64_t heads_kv;
+  int64_t n_ctx;
+  int64_t head_dim;
+  float scale;
+  int32_t n_sel;
+  int32_t n_tok;
+  int32_t reserved0;
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* cluster_ptr;
+  const int32_t* sel;
+  const int32_t* tok_idx;
+  void* out;
+  float* lse;
+} sa_gather_args;
+
+int sa_gather_decode_workspace_bytes(const sa_gather_args* args, size_t* bytes);
+int sa_gather_decode(const sa_gather_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * sa_cluster_pack — cluster-major layout of a fixed context (offline step).
+ *
+ * Squeezed Attention page, §技术方案, offline stage: keys are clustered and
+ * each key gets an index to its cluster.  This call turns labels into the
+ * cluster-major order the decode reads: a stable counting sort per KV head.
+ * labels [Hkv,Nctx] int32 in [0,C) -> cluster_ptr [Hkv,C+1] int32 and perm
+ * [Hkv,Nctx] int32 (perm[g,p] = context position of packed row p; token order
+ * kept inside a cluster).  When k/v and k_packed/v_packed are all non-NULL
+ * the rows are also copied: k_packed[g,p] = k[g,perm[g,p]] (same for v).
+ * Labels outside [0,C) give SA_ERR_VALUE through err_flag semantics: the
+ * optional err_flag device int32 is set to 1 and those tokens are dropped.
+ * ====================================================================== */
+typedef struct sa_cluster_pack_args {
+  int64_t heads_kv;
+  int64_t n_ctx;
+  int64_t head_dim;
+  int32_t n_clusters;
+  int32_t dtype;          /* of k / v when copied */
+  const int32_t* labels;
+  int32_t* cluster_ptr;
+  int32_t* perm;
+  const void* k;
+  const void* v;
+  void* k_packed;
+  void* v_packed;
+  int32_t* err_flag;
+} sa_cluster_pack_args;
+
+int sa_cluster_pack_workspace_bytes(const sa_cluster_pack_args* args, size_t* bytes);
+int sa_cluster_pack(const sa_cluster_pack_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * Library information.
+ * ====================================================================== */
+/* Message of the last failing call on this thread ("" if none). */
+const char* sa_last_error(void);
+/* SA_ABI_VERSION of the built library. */
+int sa_version(void);
+/* sizeof of the argument structs as compiled, so bindings can check layout:
+ * which = 0 estimate, 1 select, 2 vs_build, 3 fwd, 4 gather, 5 cluster_pack. */
+size_t sa_args_size(int which);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SA_H_ */

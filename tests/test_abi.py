@@ -1,0 +1,135 @@
+"""The C-ABI library loads, exports every entry point include/sa.h declares,
+agrees with the binding on struct layouts, and rejects bad arguments on the
+host before any launch.  CPU only: no call here reaches a kernel."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*|size_t)\s+(sa_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (load the HIP runtime the way the product does)
+    from dynamic_sparse_attention_pool_amd import _ffi
+    return _ffi.load()
+
+
+def test_header_declares_the_four_entry_points_and_helpers():
+    names = declared_functions()
+    for n in ["sa_estimate", "sa_select_topk", "sa_block_sparse_fwd", "sa_gather_decode", "sa_vs_build",
+              "sa_cluster_pack", "sa_last_error", "sa_version", "sa_args_size"]:
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+        assert n in _ffi.SYMBOLS, f"binding lacks {n}"
+
+
+def test_struct_layouts_and_version(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi
+    assert lib.sa_version() == _ffi.ABI_VERSION
+    for i, st in enumerate(_ffi.STRUCTS):
+        assert lib.sa_args_size(i) == C.sizeof(st)
+    assert lib.sa_args_size(99) == 0
+
+
+def _err(lib):
+    return lib.sa_last_error().decode()
+
+
+def test_fwd_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    a = F.FwdArgs()
+    assert lib.sa_block_sparse_fwd(None, None, 0, None) == 1
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 1   # q/k/v/out NULL
+    a.q = a.k = a.v = a.out = 256
+    a.dtype, a.out_dtype, a.block_size, a.head_dim = F.SA_BF16, F.SA_F32, 64, 128
+    a.batch, a.heads_q, a.heads_kv, a.seq, a.scale = 1, 4, 3, 128, 0.1
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 2   # 4 % 3
+    assert "multiple" in _err(lib)
+    a.heads_kv = 2
+    a.seq = 100
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 2
+    a.seq = 128
+    a.head_dim = 96
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 6
+    a.head_dim = 128
+    a.q = 264   # misaligned
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 4
+    a.q = 256
+    a.dtype = F.SA_I32
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 3
+    a.dtype = F.SA_BF16
+    a.scale = -1.0
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 8
+    a.scale = 0.1
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 1   # block tables missing
+    a.mode = 7
+    assert lib.sa_block_sparse_fwd(C.byref(a), None, 0, None) == 8
+
+
+def test_select_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    a = F.SelectArgs()
+    a.scores = a.idx = a.cnt = 256
+    a.rows, a.ncand, a.ld, a.k, a.kmax = 4, 10, 8, 2, 4
+    assert lib.sa_select_topk(C.byref(a), None, 0, None) == 2       # ld < ncand
+    a.ld = 10
+    a.n_sink, a.n_local, a.k, a.kmax = 1, 1, 3, 4
+    assert lib.sa_select_topk(C.byref(a), None, 0, None) == 2       # 1+1+3 > 4
+    assert "kmax" in _err(lib)
+    a.kmax = 5
+    n = C.c_size_t(7)
+    assert lib.sa_select_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0 and n.value == 0
+    a.causal, a.causal_period = 1, 0
+    assert lib.sa_select_topk(C.byref(a), None, 0, None) == 8
+    a.causal, a.causal_period, a.causal_offset = 1, 16, 0
+    a.ratio_num, a.ratio_den, a.n_sink, a.n_local, a.ncand, a.ld, a.rows = 10, 100, 1, 4, 16, 16, 16
+    a.kmax = 6   # row 15: 5 forced + ceil(1.6)=2 -> 7
+    assert lib.sa_select_topk(C.byref(a), None, 0, None) == 2
+    a.kmax = 7
+    assert lib.sa_select_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0
+
+
+def test_estimate_and_gather_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    e = F.EstimateArgs()
+    e.q = e.k = e.scores = 256
+    e.kind, e.dtype, e.batch, e.heads_q, e.heads_kv, e.seq_q, e.seq_k, e.head_dim = 0, F.SA_BF16, 1, 4, 2, 128, 128, 128
+    e.block_size, e.scale = 32, 0.1
+    assert lib.sa_estimate(C.byref(e), None, 0, None) == 6
+    e.block_size = 64
+    n = C.c_size_t(0)
+    assert lib.sa_estimate_workspace_bytes(C.byref(e), C.byref(n)) == 0
+    assert n.value == 2 * 1 * 4 * 128 * 4 + 2 * 1 * 2 * 128 * 4 or n.value >= (4 + 2) * 2 * 128 * 4
+    assert lib.sa_estimate(C.byref(e), None, 0, None) == 5           # workspace missing
+    e.kind = 3
+    e.head_dim = 32
+    e.weights = 256
+    assert lib.sa_estimate(C.byref(e), None, 0, None) == 6
+    e.kind = 9
+    assert lib.sa_estimate(C.byref(e), None, 0, None) == 8
+    g = F.GatherArgs()
+    g.q = g.k = g.v = g.out = 256
+    g.dtype, g.out_dtype, g.head_dim, g.n_q, g.heads_q, g.heads_kv, g.n_ctx, g.scale = F.SA_BF16, F.SA_F32, 128, 8, 32, 8, 1024, 0.1
+    g.mode = F.SA_GATHER_CLUSTER
+    assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 1      # cluster tables missing
+    g.cluster_ptr = g.sel = 256
+    g.n_clusters, g.n_sel = 16, 4
+    g.n_q = 32                                                        # 32*4 queries per KV head > 64
+    assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 6
+    g.mode = F.SA_GATHER_TOKEN
+    g.tok_idx, g.n_tok, g.heads_kv = 256, 64, 4                       # 8 heads per KV head
+    assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 6

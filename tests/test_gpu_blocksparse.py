@@ -1,0 +1,252 @@
+"""GPU parity of the block-sparse path: selection, pooled estimate and the
+sparse forward, each against the CPU oracle on the same seeded inputs."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import (assert_attention_close, assert_scores_close, certify_prefill, dev_bf16, dev_f32,
+                         dev_i32, host, pad_table, tie_tolerant_valid, torch)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import dynamic_sparse_attention_pool_amd as m
+    m.load()
+    return m
+
+
+def gpu_select(sa, scores_np, kmax, **kw):
+    t = torch()
+    s = dev_f32(scores_np)
+    idx = t.empty((scores_np.shape[0], kmax), dtype=t.int32, device=s.device)
+    cnt = t.empty(scores_np.shape[0], dtype=t.int32, device=s.device)
+    err = t.zeros(1, dtype=t.int32, device=s.device)
+    sa.sa_select_topk(s, idx, cnt, err_flag=err, **kw)
+    t.cuda.synchronize()
+    return host(idx), host(cnt), int(host(err)[0])
+
+
+def oracle_select(scores_np, **kw):
+    ratio = kw.get("ratio")
+    return oracle.select_rows(scores_np.astype(np.float64), causal=kw.get("causal", False),
+                              period=kw.get("causal_period", 1), offset=kw.get("causal_offset", 0),
+                              n_sink=kw.get("n_sink", 0), n_local=kw.get("n_local", 0),
+                              k=None if ratio else kw.get("k", 0), ratio=ratio)
+
+
+SELECT_CASES = [
+    # (rows, ncand, kind, kwargs, kmax)
+    (16, 16, "normal", dict(k=2, n_sink=1, n_local=1, causal=True, causal_period=16), 4),
+    (64, 512, "normal", dict(ratio=(10, 100), n_sink=1, n_local=4, causal=True, causal_period=512), 57),
+    (48, 2048, "ties", dict(ratio=(5, 100), n_sink=1, n_local=4, causal=True, causal_period=2048), 108),
+    (40, 256, "ties", dict(k=64), 64),
+    (8, 300, "normal", dict(k=0, n_sink=3), 3),
+    (8, 300, "normal", dict(k=500, n_local=7), 300),
+    (5, 4096, "ties", dict(k=1000), 1000),
+]
+
+
+@pytest.mark.parametrize("case", range(len(SELECT_CASES)))
+def test_select_bit_exact_lds_rows(sa, case):
+    R, n, kind, kw, kmax = SELECT_CASES[case]
+    print(f"select case {case}: rows {R} ncand {n} {kind} {kw}", flush=True)
+    s = W.score_rows(7, R, n, kind, case)
+    idx, cnt, err = gpu_select(sa, s, kmax, **kw)
+    want = oracle_select(s, **kw)
+    assert err == 0
+    for r in range(R):
+        assert cnt[r] == len(want[r]), r
+        assert np.array_equal(idx[r, :cnt[r]], want[r]), r
+        assert np.all(idx[r, cnt[r]:] == -1)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_select_bit_exact_long_rows(sa, kind):
+    # indexer-like causal rows (ragged lengths) and vertical/slash-like full rows
+    R, n = 6, 131072
+    print(f"long select {kind}", flush=True)
+    s = W.score_rows(8, R, n, kind)
+    for kw, kmax in [(dict(k=2048, causal=True, causal_period=R, causal_offset=n - R), 2048),
+                     (dict(k=1000), 1000), (dict(k=64, n_sink=2, n_local=2), 68)]:
+        idx, cnt, err = gpu_select(sa, s, kmax, **kw)
+        want = oracle_select(s, **kw)
+        assert err == 0
+        for r in range(R):
+            assert cnt[r] == len(want[r])
+            assert np.array_equal(idx[r, :cnt[r]], want[r])
+
+
+def test_select_ragged_long_rows_and_nan_flag(sa):
+    s = W.score_rows(9, 3, 5000, "normal")
+    idx, cnt, err = gpu_select(sa, s, 300, k=300)
+    want = oracle_select(s, k=300)
+    assert err == 0 and all(np.array_equal(idx[r, :cnt[r]], want[r]) for r in range(3))
+    s[1, 17] = np.nan
+    _, _, err = gpu_select(sa, s, 300, k=300)
+    assert err == 1
+
+
+def run_block_estimate(sa, q, k, scale):
+    t = torch()
+    B, Hq, N, d = q.shape
+    nb = N // 64
+    scores = t.empty((B, Hq, nb, nb), dtype=t.float32, device=q.device)
+    pq = t.empty((B, Hq, nb, d), dtype=t.float32, device=q.device)
+    pk = t.empty((B, k.shape[1], nb, d), dtype=t.float32, device=q.device)
+    sa.sa_estimate(sa.BLOCK_MEANPOOL, q, k, scores, scale=scale, pooled_q=pq, pooled_k=pk)
+    t.cuda.synchronize()
+    return host(scores), host(pq), host(pk)
+
+
+def test_block_estimate_exact_integer_inputs(sa):
+    """bf16 integers in [-2,2] with scale 1: block sums, /64 and the 128-term
+    dot products are exact in fp32, so the GPU equals the fp64 oracle bit for bit."""
+    B, Hq, Hkv, N, d = 1, 4, 2, 640, 128
+    q = W.integer_bf16(11, (B, Hq, N, d), -2, 2, 0)
+    k = W.integer_bf16(11, (B, Hkv, N, d), -2, 2, 1)
+    s, pq, pk = run_block_estimate(sa, dev_bf16(q), dev_bf16(k), 1.0)
+    want = oracle.block_scores(W.bf16_to_f32(q), W.bf16_to_f32(k), 64, 1.0)
+    assert np.array_equal(s, want)
+    assert np.array_equal(pq[0, 1], oracle.mean_pool(W.bf16_to_f32(q)[0, 1], 64))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_block_estimate_random(sa, dtype):
+    if dtype == "f32":
+        inp = W.prefill_fp32(12, 1, 2, 1024, 64)
+        q, k = dev_f32(inp.q), dev_f32(inp.k)
+        d = 64
+    else:
+        inp = W.prefill_bf16(12, 2, 4, 2, 1024, 128)
+        q, k = dev_bf16(inp.q), dev_bf16(inp.k)
+        d = 128
+    scale = 1 / math.sqrt(d)
+    s, _, _ = run_block_estimate(sa, q, k, scale)
+    want = oracle.block_scores(inp.f32("q"), inp.f32("k"), 64, scale)
+    assert_scores_close(s, want, f"block scores {dtype}")
+
+
+def run_fwd(sa, q, k, v, kept_lists, kmax, out_bf16=False, scale=None):
+    t = torch()
+    B, Hq, N, d = q.shape
+    nb = N // 64
+    flat = [kept_lists[b][h][i] for b in range(B) for h in range(Hq) for i in range(nb)]
+    idx, cnt = pad_table(flat, kmax)
+    out = t.empty((B, Hq, N, d), dtype=t.bfloat16 if out_bf16 else t.float32, device=q.device)
+    lse = t.empty((B, Hq, N), dtype=t.float32, device=q.device)
+    sa.sa_block_sparse_fwd(q, k, v, out, block_idx=dev_i32(idx.reshape(B, Hq, nb, kmax)),
+                           block_cnt=dev_i32(cnt.reshape(B, Hq, nb)), lse=lse, scale=scale)
+    t.cuda.synchronize()
+    return host(out), host(lse)
+
+
+def test_fwd_fp32_sink_diag_top2_on_oracle_sets(sa):
+    inp = W.prefill_fp32(W.CONFIG_SEEDS[1], 1, 1, 1024, 64)
+    scale = 1 / 8.0
+    S = oracle.block_scores(inp.q, inp.k, 64, scale)
+    kept = oracle.block_select(S, n_sink=1, n_local=1, k=2)
+    o, l = run_fwd(sa, dev_f32(inp.q), dev_f32(inp.k), dev_f32(inp.v), kept, 4, scale=scale)
+    wo, wl = oracle.block_sparse_attention(inp.q, inp.k, inp.v, kept, 64, scale)
+    assert_attention_close(o, wo, bf16=False, what="fp32 fwd")
+    assert np.max(np.abs(l - wl)) < 1e-5
+
+
+@pytest.mark.parametrize("d,out_bf16", [(128, False), (128, True), (64, False)])
+def test_fwd_bf16_on_oracle_sets(sa, d, out_bf16):
+    B, Hq, Hkv, N = 1, 4, 2, 1024
+    inp = W.prefill_bf16(13, B, Hq, Hkv, N, d)
+    scale = 1 / math.sqrt(d)
+    S = oracle.block_scores(inp.f32("q"), inp.f32("k"), 64, scale)
+    kept = oracle.block_select(S, n_sink=1, n_local=4, ratio=(30, 100))
+    kept[0][1] = [np.arange(i + 1) for i in range(N // 64)]      # head 1 dense causal
+    o, l = run_fwd(sa, dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), kept, N // 64, out_bf16=out_bf16)
+    wo, wl = oracle.block_sparse_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), kept, 64, scale)
+    assert_attention_close(o, wo, bf16=True, what=f"bf16 fwd d{d}")
+    assert np.max(np.abs(l - wl)) < 1e-3
+
+
+def test_fwd_bf16_empty_and_single_block_rows(sa):
+    B, Hq, Hkv, N, d = 1, 2, 1, 512, 128
+    inp = W.prefill_bf16(14, B, Hq, Hkv, N, d)
+    nb = N // 64
+    kept = [[[np.zeros(0, np.int64) if i % 3 == 0 else np.array([i // 2]) for i in range(nb)] for _ in range(Hq)]]
+    o, l = run_fwd(sa, dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), kept, 2)
+    wo, wl = oracle.block_sparse_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), kept, 64, 1 / math.sqrt(d))
+    assert_attention_close(o, wo, bf16=True, what="empty/single rows")
+    assert np.array_equal(np.isneginf(l), np.isneginf(wl))
+    assert np.all(o[:, :, 0:64] == 0)
+
+
+def run_block_layer(sa, q, k, v, n_sink, n_local, kmax, k_fixed=None, ratio=None, out_bf16=False, scale=None):
+    """estimate -> select -> forward, as the benchmark chains them."""
+    t = torch()
+    B, Hq, N, d = q.shape
+    nb = N // 64
+    scale = 1 / math.sqrt(d) if scale is None else scale
+    scores = t.empty((B, Hq, nb, nb), dtype=t.float32, device=q.device)
+    sa.sa_estimate(sa.BLOCK_MEANPOOL, q, k, scores, scale=scale)
+    idx = t.empty((B * Hq * nb, kmax), dtype=t.int32, device=q.device)
+    cnt = t.empty(B * Hq * nb, dtype=t.int32, device=q.device)
+    sel = dict(n_sink=n_sink, n_local=n_local, causal=True, causal_period=nb)
+    if ratio:
+        sel["ratio"] = ratio
+    else:
+        sel["k"] = k_fixed
+    sa.sa_select_topk(scores.view(B * Hq * nb, nb), idx, cnt, **sel)
+    out = t.empty((B, Hq, N, d), dtype=t.bfloat16 if out_bf16 else t.float32, device=q.device)
+    sa.sa_block_sparse_fwd(q, k, v, out, block_idx=idx.view(B, Hq, nb, kmax), block_cnt=cnt.view(B, Hq, nb),
+                           scale=scale)
+    t.cuda.synchronize()
+    return host(scores), host(idx).reshape(B, Hq, nb, kmax), host(cnt).reshape(B, Hq, nb), host(out)
+
+
+def test_end_to_end_sink_diag_top2_fp32(sa):
+    seed = W.CONFIG_SEEDS[1]
+    inp = W.prefill_fp32(seed, 1, 1, 1024, 64)
+    certify_prefill(inp, seed, 64, 1 / 8.0, 1, 1, k=2)
+    S, idx, cnt, o = run_block_layer(sa, dev_f32(inp.q), dev_f32(inp.k), dev_f32(inp.v), 1, 1, 4, k_fixed=2)
+    Sw = oracle.block_scores(inp.q, inp.k, 64, 1 / 8.0)
+    kept = oracle.block_select(Sw, n_sink=1, n_local=1, k=2)
+    assert_scores_close(S, Sw)
+    for i in range(16):
+        assert np.array_equal(idx[0, 0, i, :cnt[0, 0, i]], kept[0][0][i])
+    assert int(cnt.sum()) == 58
+    wo, _ = oracle.block_sparse_attention(inp.q, inp.k, inp.v, kept, 64, 1 / 8.0)
+    assert_attention_close(o, wo, bf16=False, what="config-1 end to end")
+
+
+def test_end_to_end_shifted_gqa_prefill_certified(sa):
+    """GQA 8/2, d128, N 4096, 1% shifted keys, sink + 4 local + ceil(10%):
+    certified rows -> identical kept sets; outputs within the bf16 bounds."""
+    seed = 21
+    B, Hq, Hkv, N, d = 1, 8, 2, 4096, 128
+    inp = W.prefill_bf16(seed, B, Hq, Hkv, N, d)
+    scale = 1 / math.sqrt(d)
+    nre = certify_prefill(inp, seed, 64, scale, 1, 4, ratio=(10, 100))
+    print(f"redrawn blocks: {nre}", flush=True)
+    nb = N // 64
+    kmax = 5 + math.ceil(0.1 * nb)
+    S, idx, cnt, o = run_block_layer(sa, dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), 1, 4, kmax,
+                                     ratio=(10, 100))
+    Sw = oracle.block_scores(inp.f32("q"), inp.f32("k"), 64, scale)
+    assert_scores_close(S, Sw)
+    kept = oracle.block_select(Sw, n_sink=1, n_local=4, ratio=(10, 100))
+    for h in range(Hq):
+        for i in range(nb):
+            assert np.array_equal(idx[0, h, i, :cnt[0, h, i]], kept[0][h][i]), (h, i)
+    wo, _ = oracle.block_sparse_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), kept, 64, scale)
+    assert_attention_close(o, wo, bf16=True, what="shifted GQA prefill")
+
+
+def test_determinism_bitwise(sa):
+    inp = W.prefill_bf16(22, 1, 4, 2, 2048, 128)
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    a = run_block_layer(sa, q, k, v, 1, 4, 12, ratio=(10, 100))
+    b = run_block_layer(sa, q, k, v, 1, 4, 12, ratio=(10, 100))
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
