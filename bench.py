@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark of the dynamic sparse attention path on one MI355X.
+
+Step (timed): one block-sparse prefill layer at 131072 tokens — pooled
+estimate, top-k with sink + 4 local blocks + ceil(5%) per query-block row, and
+the bf16 matrix-core forward — for batch 1, 32 query heads / 8 KV heads,
+head_dim 128, synthetic seeded inputs resident in HBM.
+
+value = kept-block FLOP (4*64*64*128 per kept 64x64 block, counted from the
+selected tables) / whole-step time.  ms_per_step = ms per layer at 128K.
+The same run also reports the clustered decode (KV GB/s, us per token), the
+token-indexer prefill with index reuse, and the vertical-slash layer as
+extras, the roofline of the dominant kernel (the forward), and the CPU oracle
+timed on a bounded sample of the same workload.
+
+python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+FLOP_PER_BLOCK = 4 * 64 * 64 * 128
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_128k.json")
+FWD_SOURCE = os.path.join(ROOT, "dynamic_sparse_attention_pool_amd", "csrc", "k_fwd.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev_bf16(bits):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to("cuda:0")
+
+
+def dev_t(x):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(x)).to("cuda:0")
+
+
+class Timer:
+    """HIP events on torch's current stream (the stream libsa launches on)."""
+
+    def __init__(self):
+        import torch
+        self.torch = torch
+        self.marks = {}
+
+    def span(self, name, fn):
+        t = self.torch
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        self.marks.setdefault(name, []).append((a, b))
+
+    def mean_ms(self, name):
+        return float(np.mean([a.elapsed_time(b) for a, b in self.marks[name]]))
+
+
+def source_hash(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def traffic_for(launch_flops_unused=None):
+    """HBM bytes per forward launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel source; else None."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("kernel_source_sha256_16") != source_hash(FWD_SOURCE):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+# ---------------------------------------------------------------- main workload
+def prefill_layer(N, ratio, steps, warmup, seed):
+    import torch
+    import workloads as W
+    from dynamic_sparse_attention_pool_amd.pipelines import BlockSparseLayer
+    t0 = time.time()
+    inp = W.prefill_bf16(seed, 1, 32, 8, N, 128)
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    log(f"[bench] inputs N={N} generated+uploaded in {time.time() - t0:.1f}s")
+    layer = BlockSparseLayer(q, k, v, n_sink=1, n_local=4, ratio=ratio, out_dtype=torch.bfloat16)
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    tm = Timer()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        tm.span("estimate", layer.estimate)
+        tm.span("select", layer.select)
+        tm.span("forward", layer.forward)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    kept = int(layer.cnt.sum().item())
+    assert int(layer.err.item()) == 0, "non-finite block score"
+    res = dict(N=N, ms_per_step=ms, kept_blocks=kept, flop=kept * FLOP_PER_BLOCK,
+               ms_estimate=tm.mean_ms("estimate"), ms_select=tm.mean_ms("select"),
+               ms_forward=tm.mean_ms("forward"), inputs=inp)
+    del layer, q, k, v
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------- extras
+def decode_extra(steps, warmup):
+    import torch
+    import workloads as W
+    from dynamic_sparse_attention_pool_amd.pipelines import ClusterDecode
+    T, Hq, Hkv, N, d, C, ksel = 8, 32, 8, 65536, 128, 256, 64
+    copies = []
+    for c in range(4):  # rotate over 4 contexts so no step finds the last one in the 256 MB MALL
+        inp = W.decode_clustered(W.CONFIG_SEEDS[4] + 100 * c, T, Hq, Hkv, N, d, C)
+        copies.append(ClusterDecode(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev_t(inp.labels),
+                                    dev_t(inp.centroids), n_sel=ksel))
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        copies[i % 4].step()
+    torch.cuda.synchronize()
+    tm = Timer()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        dc = copies[i % 4]
+        tm.span("estimate", dc.estimate)
+        tm.span("select", dc.select)
+        tm.span("forward", dc.forward)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    # algorithmic bytes: K+V rows of the union of selected clusters per KV head
+    kv_bytes = 0
+    for dc in copies:
+        sel = dc.sel.cpu().numpy()
+        ptr = dc.ptr.cpu().numpy().astype(np.int64)
+        for g in range(Hkv):
+            used = np.unique(sel[:, g * (Hq // Hkv):(g + 1) * (Hq // Hkv), :])
+            kv_bytes += int((ptr[g, used + 1] - ptr[g, used]).sum()) * 2 * d * 2
+    kv_bytes //= len(copies)
+    small = T * Hq * d * 2 + Hkv * C * d * 4 + T * Hq * d * 4
+    step_bytes = kv_bytes + small
+    fwd_ms = tm.mean_ms("forward")
+    return {"workload": "clustered decode: 8 queries x 32/8 heads, d128, 65536-key context, top 64 of 256 clusters",
+            "us_per_step": ms * 1e3, "us_per_token": ms * 1e3 / T,
+            "kv_bytes_per_step": kv_bytes, "GB_per_s_step": step_bytes / (ms * 1e-3) / 1e9,
+            "us_gather": fwd_ms * 1e3, "GB_per_s_gather": kv_bytes / (fwd_ms * 1e-3) / 1e9,
+            "frac_hbm_gather": kv_bytes / (fwd_ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "us_estimate": tm.mean_ms("estimate") * 1e3, "us_select": tm.mean_ms("select") * 1e3}
+
+
+def indexer_extra(steps, warmup):
+    import torch
+    import workloads as W
+    from dynamic_sparse_attention_pool_amd.pipelines import IndexerPrefill
+    seed = W.CONFIG_SEEDS[5]
+    T, N, Hi, di, k_sel = 4096, 131072, 64, 64, 2048
+    ind = W.indexer_random(seed, T, Hi, di, N)
+    layers = []
+    for l in range(4):
+        L = W.mqa_layer(seed, l, T, 16, 1, N, 128)
+        layers.append((dev_bf16(L.q), dev_bf16(L.k), dev_bf16(L.v)))
+    ip = IndexerPrefill(dev_bf16(ind.qi), dev_bf16(ind.ki), dev_t(ind.w), ind.pos0, layers, k_sel=k_sel,
+                        out_dtype=torch.bfloat16)
+    for _ in range(warmup):
+        ip.step(reuse=True)
+    torch.cuda.synchronize()
+    tm = Timer()
+    for _ in range(steps):
+        tm.span("total_reuse", lambda: ip.step(reuse=True))
+        tm.span("total_noreuse", lambda: ip.step(reuse=False))
+        tm.span("indexer", lambda: __import__("dynamic_sparse_attention_pool_amd").sa_estimate(
+            __import__("dynamic_sparse_attention_pool_amd").INDEXER, ip.qi, ip.ki, ip.scores, weights=ip.w,
+            q_pos0=ip.pos0))
+        tm.span("select", lambda: __import__("dynamic_sparse_attention_pool_amd").sa_select_topk(
+            ip.scores, ip.idx, ip.cnt, k=k_sel, causal=True, causal_period=T, causal_offset=ip.pos0))
+        tm.span("attend", lambda: ip.attend(1))
+    torch.cuda.synchronize()
+    pairs = sum(ind.pos0 + t + 1 for t in range(T))
+    idx_ms = tm.mean_ms("indexer")
+    return {"workload": "token top-2048 prefill chunk: 4096 queries at the end of 131072, 64x64 indexer, "
+                        "MQA 16/1 d128, 4 layers, layer 1 full / 2-4 shared",
+            "ms_4layers_with_reuse": tm.mean_ms("total_reuse"), "ms_4layers_without_reuse": tm.mean_ms("total_noreuse"),
+            "ms_indexer": idx_ms, "indexer_TFLOP_per_s": pairs * 8192 / (idx_ms * 1e-3) / 1e12,
+            "ms_select": tm.mean_ms("select"), "ms_attend_layer": tm.mean_ms("attend")}
+
+
+def vs_extra(steps, warmup, inp):
+    import torch
+    from dynamic_sparse_attention_pool_amd.pipelines import VerticalSlashLayer
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    layer = VerticalSlashLayer(q, k, v, n_vert=1000, n_slash=64, out_dtype=torch.bfloat16)
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    tm = Timer()
+    for _ in range(steps):
+        tm.span("estimate", layer.estimate)
+        tm.span("select", layer.select)
+        tm.span("forward", layer.forward)
+    torch.cuda.synchronize()
+    # kept keys per query block, counted from the built tables (diagonal tiles whole)
+    ivc = layer.iv.cpu().numpy()
+    ivn = layer.iv_cnt.cpu().numpy()
+    coln = layer.col_cnt.cpu().numpy().astype(np.int64)
+    keys = int(coln.sum())
+    B, Hq, nb = ivn.shape
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(nb):
+                n = ivn[b, h, i]
+                keys += int((ivc[b, h, i, :n, 1] - ivc[b, h, i, :n, 0]).sum())
+    flop = keys * 4 * 64 * 128
+    fwd = tm.mean_ms("forward")
+    return {"workload": "vertical-slash layer at 131072: last-64-query estimate, top 1000 columns + top 64 offsets",
+            "ms_layer": tm.mean_ms("estimate") + tm.mean_ms("select") + fwd, "ms_estimate": tm.mean_ms("estimate"),
+            "ms_select_build": tm.mean_ms("select"), "ms_forward": fwd, "kept_key_flop": flop,
+            "forward_TFLOP_per_s": flop / (fwd * 1e-3) / 1e12}
+
+
+# ---------------------------------------------------------------- CPU oracle baseline
+def cpu_baseline(inp, ratio, budget_s=20.0):
+    """The fp64 oracle on head 0 of the same layer: pooled estimate of head 0
+    and its KV head, selection of every query-block row, attention for a
+    strided subset of query blocks (as many as fit the time budget)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        cores = len(os.sched_getaffinity(0))
+    _, Hq, N, d = inp.q.shape
+    nb = N // 64
+    scale = 1 / math.sqrt(d)
+    import workloads as W
+    q0 = W.bf16_to_f32(inp.q[0:1, 0:1])
+    k0 = W.bf16_to_f32(inp.k[0:1, 0:1])
+    v0 = W.bf16_to_f32(inp.v[0:1, 0:1])
+    t0 = time.perf_counter()
+    S = oracle.block_scores(q0, k0, 64, scale)
+    kept = oracle.block_select(S, n_sink=1, n_local=4, ratio=ratio)
+    t_sel = time.perf_counter() - t0
+    blocks, flop = [], 0
+    t1 = time.perf_counter()
+    stride = 1
+    # longest rows first, strided, until the budget is used
+    order = list(range(nb - 1, -1, -1))
+    done = []
+    for i in order[::stride]:
+        oracle.block_sparse_attention(q0, k0, v0, kept, 64, scale, heads=[0], blocks=[i])
+        done.append(i)
+        flop += len(kept[0][0][i]) * FLOP_PER_BLOCK
+        if time.perf_counter() - t1 > budget_s:
+            break
+    t_att = time.perf_counter() - t1
+    # scale the estimate/select share to the sampled rows
+    frac_rows = len(done) / nb
+    t_total = t_att + t_sel * frac_rows
+    return {"value": flop / t_total / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"head 0 of the 128K layer: pooled estimate + selection (time pro-rated to the sampled rows) "
+                      f"and fp64 attention for the {len(done)} longest query-block rows of {nb}; "
+                      f"{flop / 1e9:.1f} GFLOP of kept blocks in {t_total:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-extras", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--only", default="", help="comma list of extras to run: decode,indexer,vs,prefill32k")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md for how it would "
+              "shard); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import dynamic_sparse_attention_pool_amd as sa
+    sa.load()
+    torch.cuda.init()
+
+    main = prefill_layer(131072, (5, 100), args.steps, args.warmup, seed=3)
+    ms = main["ms_per_step"]
+    value = main["flop"] / (ms * 1e-3) / 1e12
+    fwd_tflops = main["flop"] / (main["ms_forward"] * 1e-3) / 1e12
+    traffic = traffic_for()
+    line = {
+        "metric": "sparse-attn prefill TFLOP/s (kept blocks) & ms at 128K; decode KV GB/s",
+        "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "block-sparse prefill layer, 131072 tokens, batch 1, GQA 32/8, head_dim 128, "
+                               "1% keys +3u / queries +1u, sink + 4 local + ceil(5%) blocks of 64",
+                   "seq_len": 131072, "heads_q": 32, "heads_kv": 8, "head_dim": 128, "block": 64,
+                   "kept_blocks": main["kept_blocks"], "parallelism": "single GPU"},
+        "breakdown_ms": {"estimate": round(main["ms_estimate"], 4), "select": round(main["ms_select"], 4),
+                         "forward": round(main["ms_forward"], 4)},
+        "roofline": {"bound": "mfma", "kernel": "k_fwd_bf16<128,block>", "achieved": round(fwd_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+    }
+    extras = {}
+    only = set(x for x in args.only.split(",") if x)
+    if not args.no_extras:
+        for name, fn in [("decode", lambda: decode_extra(max(args.steps, 20), args.warmup)),
+                         ("indexer", lambda: indexer_extra(max(2, args.steps // 3), 1)),
+                         ("vs", lambda: vs_extra(max(2, args.steps // 3), 1, main["inputs"]))]:
+            if only and name not in only:
+                continue
+            try:
+                log(f"[bench] extra {name}")
+                extras[name] = fn()
+            except Exception as e:  # noqa: BLE001  (an extra that is not available is reported, not fatal)
+                extras[name] = {"error": f"{type(e).__name__}: {e}"}
+            torch.cuda.empty_cache()
+    if extras:
+        line["extras"] = extras
+    if not args.no_cpu:
+        log("[bench] cpu oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(main["inputs"], (5, 100))
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -396,7 +396,8 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
   for (int tt = 0; tt < ntile; ++tt) {
     const int base = tt * kBlk;
     const int len = min(kBlk, p.n_tok - base);
-    const int myid = lane < len ? ids[base + lane] : -1;
+    int myid = lane < len ? ids[base + lane] : -1;
+    if (myid >= N) myid = -1;  // out-of-range ids are treated as padding
     KEYS[w][lane] = myid;
     wave_sync();
     // rows to load (invalid slots read row 0 of a valid key; they are masked)

@@ -58,8 +58,9 @@ struct TileIter {
 
   __device__ bool next(TileRef& r) {
     if (MODE == 0) {
-      if (t >= cnt) return false;
-      const int j = bidx[t++];
+      int j = -1;
+      while (t < cnt && (j < 0 || j > iblk)) j = bidx[t++];  // entries outside 0..i are skipped
+      if (j < 0 || j > iblk) return false;
       r.base = j * kBlk;
       r.len = kBlk;
       r.gathered = 0;

@@ -1,0 +1,357 @@
+// Token indexer scores and the vertical-slash estimate (bf16 matrix cores).
+//
+// IndexCache article, §长文本的算力困境: a light indexer scores every causal
+// (query, key) pair, and its quadratic cost becomes the prefill bottleneck.
+// Score of the synthetic workload: I[t,s] = sum_h w_h * ReLU(q[t,h] . k[s]).
+// The contraction q[t,h] . k[s] is a dense GEMM per head; the ReLU sits
+// between it and the sum over heads, so each head's 64x32 tile is finished
+// in registers (max, then FMA with w_h) before the next head.  Eight waves
+// split the indexer heads and reduce their partial sums through LDS.
+//
+// "MInference 1.0" article, §方法介紹: vertical and slash indices come from
+// the attention of the last queries to every key.  Pass 1 gathers per-chunk
+// softmax statistics of the last 64 query rows; pass 2 recomputes the
+// probabilities tile by tile and reduces them along columns (vertical score)
+// and along diagonals (slash score, offset = query position - key).  The
+// diagonal sums of each 64-key tile are written as partials and merged in a
+// fixed order by a last kernel, so the result is deterministic.
+//
+// Both kernels feed K rows straight from memory into the A operand of
+// v_mfma_f32_32x32x16_bf16 (S^T = K . Q^T): lane half hf reads the contiguous
+// half [hf*D/2, (hf+1)*D/2) of a row over the k-steps, and the Q^T operand
+// walks the head dimension in the same order.
+#include <algorithm>
+
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+namespace {
+
+// ================================================================ indexer
+constexpr int kIdxWaves = 8;
+constexpr int kIdxD = 64;
+constexpr int kIdxChunk = 8192;  // keys per workgroup
+
+template <int HPW>
+__global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                            const float* __restrict__ w, int T, int Hi, int64_t Nk,
+                                                            int64_t pos0, float* __restrict__ out) {
+  __shared__ float red[kIdxWaves][64 * 33];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int nchunk = (int)((Nk + kIdxChunk - 1) / kIdxChunk);
+  const int tq = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
+  const int t0 = tq * 32;
+  const int64_t c0 = (int64_t)ck * kIdxChunk, c1 = std::min(Nk, c0 + kIdxChunk);
+  const int tl = std::min(t0 + l32, T - 1);
+  // Q^T for this wave's heads: query tl, dims 32hf + 8s .. +7 at step s
+  bf16x8 qv[HPW][4];
+  float wh[HPW];
+#pragma unroll
+  for (int j = 0; j < HPW; ++j) {
+    const int h = wv * HPW + j;
+    wh[j] = w[h];
+    const uint16_t* qr = q + ((int64_t)tl * Hi + h) * kIdxD + 32 * hf;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) qv[j][s] = as_bf16x8(ldg16(qr + 8 * s));
+  }
+  const int64_t lim_max = pos0 + std::min(t0 + 31, T - 1);  // largest causal key of the tile's queries
+  const int tid = threadIdx.x;
+  for (int64_t s0 = c0; s0 < c1; s0 += 64) {
+    const bool live = s0 <= lim_max;
+    if (live) {
+      bf16x8 ka[2][4];
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int64_t row = std::min(s0 + 32 * mt + l32, Nk - 1);
+        const uint16_t* kr = k + row * kIdxD + 32 * hf;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) ka[mt][s] = as_bf16x8(ldg16(kr + 8 * s));
+      }
+      float sum[32];
+#pragma unroll
+      for (int r = 0; r < 32; ++r) sum[r] = 0.f;
+#pragma unroll
+      for (int j = 0; j < HPW; ++j) {
+        f32x16 a0, a1;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          a0[r] = 0.f;
+          a1[r] = 0.f;
+        }
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          a0 = mfma32x32x16(ka[0][s], qv[j][s], a0);
+          a1 = mfma32x32x16(ka[1][s], qv[j][s], a1);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          sum[r] = fmaf(wh[j], fmaxf(a0[r], 0.f), sum[r]);
+          sum[16 + r] = fmaf(wh[j], fmaxf(a1[r], 0.f), sum[16 + r]);
+        }
+      }
+      // element (mt, r) is key 32mt + 8(r/4) + 4hf + r%4 of the tile, query l32
+#pragma unroll
+      for (int r = 0; r < 32; ++r) {
+        const int key = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
+        red[wv][key * 33 + l32] = sum[r];
+      }
+    }
+    __syncthreads();
+    // fixed-order sum over the waves; thread -> (query, 4 consecutive keys)
+    for (int e = tid; e < 32 * 16; e += 64 * kIdxWaves) {
+      const int qq = e / 16, kq = e % 16;
+      const int t = t0 + qq;
+      if (t < T) {
+        const int64_t lim = pos0 + t;
+        f32x4 v4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = 4 * kq + i;
+          float acc = 0.f;
+          if (live) {
+#pragma unroll
+            for (int ww = 0; ww < kIdxWaves; ++ww) acc += red[ww][key * 33 + qq];
+          }
+          v4[i] = (s0 + key > lim) ? -INFINITY : acc;
+        }
+        const int64_t s = s0 + 4 * kq;
+        float* op = out + (int64_t)t * Nk + s;
+        if (s + 3 < c1) {
+          *reinterpret_cast<f32x4*>(op) = v4;
+        } else {
+          for (int i = 0; i < 4 && s + i < c1; ++i) op[i] = v4[i];
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ================================================================ vertical-slash estimate
+constexpr int kVsLast = 64;
+constexpr int kVsTilesPerWg = 16;
+
+template <int D>
+struct VsOps {
+  static constexpr int NS = D / 16;  // k-steps
+  // A operand: K rows s0+32mt+l32, dims (D/2)hf + 8s .. +7
+  __device__ static void load_k(bf16x8 (&ka)[2][NS], const uint16_t* kb, int64_t s0, int64_t N, int l32, int hf) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const int64_t row = std::min(s0 + 32 * mt + l32, N - 1);
+      const uint16_t* kr = kb + row * D + (D / 2) * hf;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) ka[mt][s] = as_bf16x8(ldg16(kr + 8 * s));
+    }
+  }
+  __device__ static void scores(float (&x)[32], const bf16x8 (&ka)[2][NS], const bf16x8 (&qv)[NS], float sl2,
+                                int64_t s0, int64_t qpos, int64_t N, int hf) {
+    f32x16 a0, a1;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      a0[r] = 0.f;
+      a1[r] = 0.f;
+    }
+#pragma unroll
+    for (int s = 0; s < NS; ++s) {
+      a0 = mfma32x32x16(ka[0][s], qv[s], a0);
+      a1 = mfma32x32x16(ka[1][s], qv[s], a1);
+    }
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      const int key = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
+      const float v = (r < 16 ? a0[r] : a1[r - 16]) * sl2;
+      x[r] = (s0 + key > qpos || s0 + key >= N) ? -INFINITY : v;
+    }
+  }
+};
+
+// pass 1: per (head row, chunk of tiles, query) running max / sum (log2 domain)
+template <int D>
+__global__ __launch_bounds__(128) void k_vs_stats(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                  int hq, int hkv, int64_t N, float sl2, int nchunk,
+                                                  float* __restrict__ stats) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
+  const int b = bh / hq, h = bh % hq, g = h * hkv / hq;
+  const int r = 32 * wv + l32;  // query row among the last 64
+  const int64_t qpos = N - kVsLast + r;
+  const uint16_t* kb = k + ((int64_t)b * hkv + g) * N * D;
+  bf16x8 qv[D / 16];
+  {
+    const uint16_t* qr = q + ((int64_t)bh * N + qpos) * D + (D / 2) * hf;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qv[s] = as_bf16x8(ldg16(qr + 8 * s));
+  }
+  const int64_t ntile = (N + 63) / 64;
+  const int64_t tb = (int64_t)ck * kVsTilesPerWg, te = std::min(ntile, tb + kVsTilesPerWg);
+  float m = -INFINITY, l = 0.f;
+  for (int64_t t = tb; t < te; ++t) {
+    const int64_t s0 = t * 64;
+    if (s0 > N - 1) break;
+    bf16x8 ka[2][D / 16];
+    VsOps<D>::load_k(ka, kb, s0, N, l32, hf);
+    float x[32];
+    VsOps<D>::scores(x, ka, qv, sl2, s0, qpos, N, hf);
+    float mx = x[0];
+#pragma unroll
+    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mnew = fmaxf(m, mx);
+    const float muse = mnew == -INFINITY ? 0.f : mnew;
+    float ps = 0.f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) ps += fast_exp2(x[i] - muse);
+    ps += __shfl_xor(ps, 32);
+    l = l * fast_exp2(m - muse) + ps;
+    m = mnew;
+  }
+  if (hf == 0) {
+    float* sp = stats + (((int64_t)bh * nchunk + ck) * kVsLast + r) * 2;
+    sp[0] = m;
+    sp[1] = l;
+  }
+}
+
+__global__ __launch_bounds__(64) void k_vs_stats_merge(const float* __restrict__ stats, int nchunk, float* __restrict__ ml) {
+  const int bh = blockIdx.x, r = threadIdx.x;
+  float M = -INFINITY;
+  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, stats[(((int64_t)bh * nchunk + c) * kVsLast + r) * 2]);
+  const float Mu = M == -INFINITY ? 0.f : M;
+  float L = 0.f;
+  for (int c = 0; c < nchunk; ++c) {
+    const float* sp = stats + (((int64_t)bh * nchunk + c) * kVsLast + r) * 2;
+    L += sp[1] * fast_exp2(sp[0] - Mu);
+  }
+  ml[((int64_t)bh * kVsLast + r) * 2] = Mu;
+  ml[((int64_t)bh * kVsLast + r) * 2 + 1] = L > 0.f ? 1.f / L : 0.f;
+}
+
+// pass 2: probabilities per tile -> column sums (final) and diagonal partials
+template <int D>
+__global__ __launch_bounds__(128) void k_vs_accum(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                  int hq, int hkv, int64_t N, float sl2, int nchunk,
+                                                  const float* __restrict__ ml, float* __restrict__ a_v,
+                                                  float* __restrict__ dpart) {
+  __shared__ float P[64][kVsLast + 1];  // [key][query row]
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int bh = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
+  const int b = bh / hq, h = bh % hq, g = h * hkv / hq;
+  const int r = 32 * wv + l32;
+  const int64_t qpos = N - kVsLast + r;
+  const uint16_t* kb = k + ((int64_t)b * hkv + g) * N * D;
+  bf16x8 qv[D / 16];
+  {
+    const uint16_t* qr = q + ((int64_t)bh * N + qpos) * D + (D / 2) * hf;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) qv[s] = as_bf16x8(ldg16(qr + 8 * s));
+  }
+  const float M = ml[((int64_t)bh * kVsLast + r) * 2], invL = ml[((int64_t)bh * kVsLast + r) * 2 + 1];
+  const int64_t ntile = (N + 63) / 64;
+  const int64_t tb = (int64_t)ck * kVsTilesPerWg, te = std::min(ntile, tb + kVsTilesPerWg);
+  for (int64_t t = tb; t < te; ++t) {
+    const int64_t s0 = t * 64;
+    bf16x8 ka[2][D / 16];
+    VsOps<D>::load_k(ka, kb, s0, N, l32, hf);
+    float x[32];
+    VsOps<D>::scores(x, ka, qv, sl2, s0, qpos, N, hf);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const int key = 32 * (i / 16) + 8 * ((i % 16) / 4) + 4 * hf + (i % 4);
+      P[key][r] = fast_exp2(x[i] - M) * invL;
+    }
+    __syncthreads();
+    if (tid < 64) {  // column sum over the 64 query rows
+      float s = 0.f;
+      for (int rr = 0; rr < kVsLast; ++rr) s += P[tid][rr];
+      if (s0 + tid < N) a_v[(int64_t)bh * N + s0 + tid] = s;
+    }
+    // diagonal d = row - key in [-63, 63]
+    for (int dg = tid; dg < 127; dg += 128) {
+      const int delta = dg - 63;
+      float s = 0.f;
+      for (int key = std::max(0, -delta); key < 64 && key + delta < kVsLast; ++key) s += P[key][key + delta];
+      dpart[((int64_t)bh * ntile + t) * 128 + dg] = s;
+    }
+  }
+}
+
+// a_s[o] = sum over the (at most two) tiles whose diagonals reach offset o
+__global__ __launch_bounds__(256) void k_vs_slash(const float* __restrict__ dpart, int64_t N, int rows,
+                                                  float* __restrict__ a_s) {
+  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (e >= (int64_t)rows * N) return;
+  const int64_t bh = e / N, o = e % N;
+  const int64_t ntile = (N + 63) / 64;
+  const int64_t base = N - kVsLast - o;  // delta = o - (N - 64 - 64 tau) = 64 tau - base
+  int64_t tlo = (base - 63 + 63) / 64;   // ceil((base-63)/64) for base-63 >= 0
+  if (base - 63 < 0) tlo = -((63 - base) / 64);
+  const int64_t thi = (base + 63) >= 0 ? (base + 63) / 64 : -1;
+  float s = 0.f;
+  for (int64_t tau = std::max<int64_t>(0, tlo); tau <= std::min(ntile - 1, thi); ++tau) {
+    const int64_t delta = 64 * tau - base;
+    if (delta >= -63 && delta <= 63) s += dpart[(bh * ntile + tau) * 128 + delta + 63];
+  }
+  a_s[e] = s;
+}
+
+size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
+                          int64_t pos0, float* out, hipStream_t stream) {
+  const int nchunk = (int)((nk + kIdxChunk - 1) / kIdxChunk);
+  const dim3 grid((unsigned)(((T + 31) / 32) * nchunk));
+  const int hpw = hi / kIdxWaves;
+  switch (hpw) {
+    case 1: hipLaunchKernelGGL((k_indexer<1>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
+    case 2: hipLaunchKernelGGL((k_indexer<2>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
+    case 4: hipLaunchKernelGGL((k_indexer<4>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
+    case 8: hipLaunchKernelGGL((k_indexer<8>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+size_t vs_workspace_bytes(int64_t rows, int64_t seq) {
+  const int64_t ntile = (seq + 63) / 64;
+  const int64_t nchunk = (ntile + kVsTilesPerWg - 1) / kVsTilesPerWg;
+  return a256((size_t)(rows * nchunk * kVsLast * 2) * 4) + a256((size_t)(rows * kVsLast * 2) * 4) +
+         a256((size_t)(rows * ntile * 128) * 4);
+}
+
+hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv, int64_t seq,
+                              int head_dim, int last_q, float scale, float* a_v, float* a_s, void* ws,
+                              hipStream_t stream) {
+  if (last_q != kVsLast) return hipErrorInvalidValue;
+  const int rows = batch * hq;
+  const int64_t ntile = (seq + 63) / 64;
+  const int nchunk = (int)((ntile + kVsTilesPerWg - 1) / kVsTilesPerWg);
+  char* p = static_cast<char*>(ws);
+  float* stats = reinterpret_cast<float*>(p);
+  p += a256((size_t)((int64_t)rows * nchunk * kVsLast * 2) * 4);
+  float* ml = reinterpret_cast<float*>(p);
+  p += a256((size_t)((int64_t)rows * kVsLast * 2) * 4);
+  float* dpart = reinterpret_cast<float*>(p);
+  const float sl2 = scale * kLog2e;
+  const dim3 grid((unsigned)((int64_t)rows * nchunk));
+  if (head_dim == 128) {
+    hipLaunchKernelGGL((k_vs_stats<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, stats);
+    hipLaunchKernelGGL(k_vs_stats_merge, dim3(rows), dim3(64), 0, stream, stats, nchunk, ml);
+    hipLaunchKernelGGL((k_vs_accum<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, ml, a_v, dpart);
+  } else if (head_dim == 64) {
+    hipLaunchKernelGGL((k_vs_stats<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, stats);
+    hipLaunchKernelGGL(k_vs_stats_merge, dim3(rows), dim3(64), 0, stream, stats, nchunk, ml);
+    hipLaunchKernelGGL((k_vs_accum<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, ml, a_v, dpart);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  const int64_t n = (int64_t)rows * seq;
+  hipLaunchKernelGGL(k_vs_slash, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dpart, seq, rows, a_s);
+  return hipGetLastError();
+}
+
+}  // namespace sa

@@ -103,6 +103,8 @@ int check_estimate(const sa_estimate_args* a, size_t* ws) {
       if (a->heads_kv != 1) return fail(SA_ERR_SHAPE, "sa_estimate(INDEXER): one indexer key head");
       if (a->q_pos0 < 0) return fail(SA_ERR_VALUE, "sa_estimate(INDEXER): q_pos0 must be >= 0");
       if (a->seq_k > ((int64_t)1 << 31) - 64) return fail(SA_ERR_SHAPE, "sa_estimate(INDEXER): seq_k too large");
+      if (a->seq_k % 4) return fail(SA_ERR_SHAPE, "sa_estimate(INDEXER): seq_k must be a multiple of 4");
+      if (!aligned16(a->scores)) return fail(SA_ERR_ALIGN, "sa_estimate(INDEXER): scores must be 16-byte aligned");
       return ok();
     }
     default:

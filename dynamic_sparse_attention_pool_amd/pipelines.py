@@ -1,0 +1,202 @@
+"""Chained calls of the libsa entry points for the four workload families.
+
+Each class allocates its device buffers once (torch is the allocator) and
+exposes the steps of its path as methods that only enqueue libsa calls on
+torch's current stream.  No arithmetic happens here.
+"""
+from __future__ import annotations
+
+import math
+
+from . import (BLOCK_MEANPOOL, CENTROID, INDEXER, VSLASH, sa_block_sparse_fwd, sa_cluster_pack, sa_estimate,
+               sa_gather_decode, sa_select_topk, sa_vs_build)
+
+
+def _t():
+    import torch
+    return torch
+
+
+def max_kept_blocks(nb: int, n_sink: int, n_local: int, k=None, ratio=None) -> int:
+    """Capacity of a block table row: forced members plus the largest budget."""
+    best = 0
+    for i in range(nb):
+        n = i + 1
+        forced = len(set(range(min(n_sink, n))) | set(range(max(0, n - n_local), n)))
+        kb = k if ratio is None else -((-ratio[0] * n) // ratio[1])
+        best = max(best, forced + max(0, min(kb, n - forced)))
+    return best
+
+
+class BlockSparseLayer:
+    """Block-sparse prefill: pooled estimate -> top-k with sink/local -> forward."""
+
+    def __init__(self, q, k, v, *, n_sink: int, n_local: int, ratio=None, k_fixed=None, out_dtype=None,
+                 scale=None, with_lse=False):
+        torch = _t()
+        self.q, self.k, self.v = q, k, v
+        B, Hq, N, d = q.shape
+        self.nb = N // 64
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        self.n_sink, self.n_local, self.ratio, self.k_fixed = n_sink, n_local, ratio, k_fixed
+        self.kmax = max_kept_blocks(self.nb, n_sink, n_local, k_fixed, ratio)
+        dev = q.device
+        self.scores = torch.empty((B, Hq, self.nb, self.nb), dtype=torch.float32, device=dev)
+        self.pooled_q = torch.empty((B, Hq, self.nb, d), dtype=torch.float32, device=dev)
+        self.pooled_k = torch.empty((B, k.shape[1], self.nb, d), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((B, Hq, self.nb, self.kmax), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, Hq, self.nb), dtype=torch.int32, device=dev)
+        self.out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if with_lse else None
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+
+    def estimate(self):
+        sa_estimate(BLOCK_MEANPOOL, self.q, self.k, self.scores, scale=self.scale, pooled_q=self.pooled_q,
+                    pooled_k=self.pooled_k)
+
+    def select(self):
+        kw = dict(n_sink=self.n_sink, n_local=self.n_local, causal=True, causal_period=self.nb,
+                  err_flag=self.err)
+        if self.ratio is not None:
+            kw["ratio"] = self.ratio
+        else:
+            kw["k"] = self.k_fixed
+        sa_select_topk(self.scores.view(-1, self.nb), self.idx.view(-1, self.kmax), self.cnt.view(-1), **kw)
+
+    def forward(self):
+        sa_block_sparse_fwd(self.q, self.k, self.v, self.out, block_idx=self.idx, block_cnt=self.cnt,
+                            lse=self.lse, scale=self.scale)
+
+    def step(self):
+        self.estimate()
+        self.select()
+        self.forward()
+
+
+class VerticalSlashLayer:
+    """Vertical-slash prefill: last-64-query estimate -> top columns and top
+    offsets -> per-block tables -> forward."""
+
+    def __init__(self, q, k, v, *, n_vert: int, n_slash: int, out_dtype=None, scale=None, with_lse=False):
+        torch = _t()
+        self.q, self.k, self.v = q, k, v
+        B, Hq, N, d = q.shape
+        self.N, self.R = N, B * Hq
+        self.nb = N // 64
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        self.n_vert, self.n_slash = min(n_vert, N), min(n_slash, N)
+        dev = q.device
+        self.a_v = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        self.a_s = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        self.vert = torch.empty((self.R, self.n_vert), dtype=torch.int32, device=dev)
+        self.vert_cnt = torch.empty(self.R, dtype=torch.int32, device=dev)
+        self.slash = torch.empty((self.R, self.n_slash), dtype=torch.int32, device=dev)
+        self.slash_cnt = torch.empty(self.R, dtype=torch.int32, device=dev)
+        self.iv = torch.empty((B, Hq, self.nb, self.n_slash, 2), dtype=torch.int32, device=dev)
+        self.iv_cnt = torch.empty((B, Hq, self.nb), dtype=torch.int32, device=dev)
+        self.col = torch.empty((B, Hq, self.nb, self.n_vert), dtype=torch.int32, device=dev)
+        self.col_cnt = torch.empty((B, Hq, self.nb), dtype=torch.int32, device=dev)
+        self.out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
+        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if with_lse else None
+        self.ws = None
+
+    def estimate(self):
+        self.ws = sa_estimate(VSLASH, self.q, self.k, self.a_v, scores2=self.a_s, scale=self.scale)
+
+    def select(self):
+        sa_select_topk(self.a_v.view(self.R, self.N), self.vert, self.vert_cnt, k=self.n_vert)
+        sa_select_topk(self.a_s.view(self.R, self.N), self.slash, self.slash_cnt, k=self.n_slash)
+        sa_vs_build(self.vert, self.vert_cnt, self.slash, self.slash_cnt, self.iv.view(self.R, -1),
+                    self.iv_cnt.view(self.R, -1), self.col.view(self.R, -1), self.col_cnt.view(self.R, -1),
+                    seq=self.N)
+
+    def forward(self):
+        sa_block_sparse_fwd(self.q, self.k, self.v, self.out, iv=self.iv, iv_cnt=self.iv_cnt, col=self.col,
+                            col_cnt=self.col_cnt, lse=self.lse, scale=self.scale)
+
+    def step(self):
+        self.estimate()
+        self.select()
+        self.forward()
+
+
+class ClusterDecode:
+    """Clustered fixed-context decode: offline pack, then per step
+    centroid scores -> top clusters -> gathered attention."""
+
+    def __init__(self, q, k, v, labels, centroids, *, n_sel: int, out_dtype=None, scale=None, with_lse=False):
+        torch = _t()
+        T, Hq, d = q.shape
+        Hkv, N, _ = k.shape
+        C = centroids.shape[1]
+        dev = q.device
+        self.q, self.centroids, self.C, self.n_sel = q, centroids, C, n_sel
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        self.ptr = torch.empty((Hkv, C + 1), dtype=torch.int32, device=dev)
+        self.perm = torch.empty((Hkv, N), dtype=torch.int32, device=dev)
+        self.k = torch.empty_like(k)
+        self.v = torch.empty_like(v)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        sa_cluster_pack(labels, self.ptr, self.perm, C, k=k, v=v, k_packed=self.k, v_packed=self.v,
+                        err_flag=self.err)
+        self.scores = torch.empty((T, Hq, C), dtype=torch.float32, device=dev)
+        self.sel = torch.empty((T, Hq, n_sel), dtype=torch.int32, device=dev)
+        self.sel_cnt = torch.empty(T * Hq, dtype=torch.int32, device=dev)
+        self.out = torch.empty((T, Hq, d), dtype=out_dtype or torch.float32, device=dev)
+        self.lse = torch.empty((T, Hq), dtype=torch.float32, device=dev) if with_lse else None
+        self.ws = None
+
+    def estimate(self):
+        sa_estimate(CENTROID, self.q, self.k, self.scores, centroids=self.centroids, scale=self.scale)
+
+    def select(self):
+        sa_select_topk(self.scores.view(-1, self.C), self.sel.view(-1, self.n_sel), self.sel_cnt, k=self.n_sel)
+
+    def forward(self):
+        self.ws = sa_gather_decode(self.q, self.k, self.v, self.out, cluster_ptr=self.ptr, sel=self.sel,
+                                   lse=self.lse, scale=self.scale, workspace=self.ws)
+
+    def step(self):
+        self.estimate()
+        self.select()
+        self.forward()
+
+
+class IndexerPrefill:
+    """Token-level sparse prefill with a shared-layer index cache: the full
+    layer runs the indexer and top-k and stores the indices; the shared layers
+    attend through the same index buffer."""
+
+    def __init__(self, qi, ki, w, pos0: int, layers, *, k_sel: int, full_layers=(0,), out_dtype=None,
+                 scale=None):
+        torch = _t()
+        T = qi.shape[0]
+        N = ki.shape[0]
+        dev = qi.device
+        self.qi, self.ki, self.w, self.pos0, self.T, self.N = qi, ki, w, pos0, T, N
+        self.layers = layers                      # list of (q [T,Hq,d], k [Hkv,N,d], v)
+        self.full = set(full_layers)
+        self.k_sel = k_sel
+        d = layers[0][0].shape[-1]
+        self.scale = 1.0 / math.sqrt(d) if scale is None else scale
+        self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((T, k_sel), dtype=torch.int32, device=dev)   # the index cache
+        self.cnt = torch.empty(T, dtype=torch.int32, device=dev)
+        self.outs = [torch.empty(L[0].shape, dtype=out_dtype or torch.float32, device=dev) for L in layers]
+        self.ws = None
+
+    def index(self):
+        sa_estimate(INDEXER, self.qi, self.ki, self.scores, weights=self.w, q_pos0=self.pos0)
+        sa_select_topk(self.scores, self.idx, self.cnt, k=self.k_sel, causal=True, causal_period=self.T,
+                       causal_offset=self.pos0)
+
+    def attend(self, layer: int):
+        q, k, v = self.layers[layer]
+        self.ws = sa_gather_decode(q, k, v, self.outs[layer], tok_idx=self.idx, scale=self.scale,
+                                   workspace=self.ws)
+
+    def step(self, reuse: bool = True):
+        for layer in range(len(self.layers)):
+            if layer in self.full or not reuse:
+                self.index()
+            self.attend(layer)
