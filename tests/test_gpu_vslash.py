@@ -1,0 +1,173 @@
+"""GPU parity of the vertical-slash path: last-query estimate, top columns /
+offsets, per-block tables and the forward in tile-list mode."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as W
+from gpu_helpers import (assert_attention_close, assert_scores_close, dev_bf16, dev_i32, host,
+                         tie_tolerant_valid, torch)
+
+pytestmark = pytest.mark.gpu
+
+NONE = np.zeros(0, np.int64)
+
+
+@pytest.fixture(scope="module")
+def sa():
+    import dynamic_sparse_attention_pool_amd as m
+    m.load()
+    return m
+
+
+def oracle_vs_scores(inp, h, scale):
+    B, Hq, N, d = inp.q.shape
+    g = oracle.gqa_group(h, Hq, inp.k.shape[1])
+    return oracle.vs_estimate(inp.f32("q")[0, h, N - 64:], inp.f32("k")[0, g], np.arange(N - 64, N), scale)
+
+
+@pytest.mark.parametrize("N,d", [(2048, 128), (1024, 64)])
+def test_vs_estimate(sa, N, d):
+    inp = W.prefill_bf16(51, 1, 4, 2, N, d)
+    t = torch()
+    av = t.empty((1, 4, N), dtype=t.float32, device="cuda:0")
+    as_ = t.empty((1, 4, N), dtype=t.float32, device="cuda:0")
+    scale = 1 / math.sqrt(d)
+    sa.sa_estimate(sa.VSLASH, dev_bf16(inp.q), dev_bf16(inp.k), av, scores2=as_, scale=scale)
+    t.cuda.synchronize()
+    for h in range(4):
+        wv, ws = oracle_vs_scores(inp, h, scale)
+        assert_scores_close(host(av)[0, h][None], wv[None], "vertical")
+        assert_scores_close(host(as_)[0, h][None], ws[None], "slash")
+        assert abs(host(av)[0, h].sum() - 64) < 1e-3 and abs(host(as_)[0, h].sum() - 64) < 1e-3
+
+
+def test_vs_build_tables_exact(sa):
+    N, R, nv, ns = 4096, 5, 300, 40
+    r = np.random.default_rng(52)
+    cols = [np.sort(r.choice(N, size=nv, replace=False)) for _ in range(R)]
+    offs = [np.sort(r.choice(N, size=ns, replace=False)) for _ in range(R)]
+    offs[1][:3] = [0, 1, 2]
+    offs[1] = np.sort(offs[1])
+    vert = np.array(cols, np.int32)
+    slash = np.array(offs, np.int32)
+    t = torch()
+    nb = N // 64
+    iv = t.empty((R, nb, ns, 2), dtype=t.int32, device="cuda:0")
+    ivc = t.empty((R, nb), dtype=t.int32, device="cuda:0")
+    col = t.empty((R, nb, nv), dtype=t.int32, device="cuda:0")
+    colc = t.empty((R, nb), dtype=t.int32, device="cuda:0")
+    cnt_v = np.full(R, nv, np.int32)
+    cnt_v[2] = 17                                    # a short selection row
+    sa.sa_vs_build(dev_i32(vert), dev_i32(cnt_v), dev_i32(slash), dev_i32(np.full(R, ns, np.int32)),
+                   iv.view(R, -1), ivc, col.view(R, -1), colc, seq=N)
+    t.cuda.synchronize()
+    ivh, ivch, colh, colch = host(iv), host(ivc), host(col), host(colc)
+    for rr in range(R):
+        tables = oracle.vs_block_tables(cols[rr][:cnt_v[rr]], offs[rr], N, 64)
+        for i, (ivs, vert_i) in enumerate(tables):
+            assert ivch[rr, i] == len(ivs)
+            assert [tuple(x) for x in ivh[rr, i, :len(ivs)]] == ivs
+            assert np.array_equal(colh[rr, i, :colch[rr, i]], vert_i)
+
+
+def run_vs_fwd(sa, inp, sel, N):
+    """forward in tile-list mode on tables built by the library from sel."""
+    t = torch()
+    B, Hq = inp.q.shape[:2]
+    nv = max(len(c) for c, _ in sel[0])
+    ns = max(len(o) for _, o in sel[0])
+    vert = np.zeros((Hq, nv), np.int32)
+    slash = np.zeros((Hq, ns), np.int32)
+    cv = np.zeros(Hq, np.int32)
+    cs = np.zeros(Hq, np.int32)
+    for h, (c, o) in enumerate(sel[0]):
+        vert[h, :len(c)], cv[h] = c, len(c)
+        slash[h, :len(o)], cs[h] = o, len(o)
+    nb = N // 64
+    iv = t.empty((B, Hq, nb, ns, 2), dtype=t.int32, device="cuda:0")
+    ivc = t.empty((B, Hq, nb), dtype=t.int32, device="cuda:0")
+    col = t.empty((B, Hq, nb, nv), dtype=t.int32, device="cuda:0")
+    colc = t.empty((B, Hq, nb), dtype=t.int32, device="cuda:0")
+    sa.sa_vs_build(dev_i32(vert), dev_i32(cv), dev_i32(slash), dev_i32(cs), iv.view(Hq, -1), ivc.view(Hq, -1),
+                   col.view(Hq, -1), colc.view(Hq, -1), seq=N)
+    out = t.empty(inp.q.shape, dtype=t.float32, device="cuda:0")
+    lse = t.empty((B, Hq, N), dtype=t.float32, device="cuda:0")
+    sa.sa_block_sparse_fwd(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), out, iv=iv, iv_cnt=ivc, col=col,
+                           col_cnt=colc, lse=lse)
+    t.cuda.synchronize()
+    return host(out), host(lse)
+
+
+def test_vs_forward_on_oracle_selection(sa):
+    N, d = 2048, 128
+    inp = W.prefill_bf16(53, 1, 4, 2, N, d)
+    r = np.random.default_rng(53)
+    sel = [[(np.sort(r.choice(N, size=150, replace=False)), np.sort(r.choice(N, size=12, replace=False)))
+            for _ in range(4)]]
+    sel[0][2] = (np.arange(N), np.arange(N))          # everything: dense causal
+    sel[0][3] = (np.sort(r.choice(N, size=5, replace=False)), np.array([1000, 1500]))   # many empty rows
+    o, l = run_vs_fwd(sa, inp, sel, N)
+    wo, wl = oracle.vs_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), sel, 64, 1 / math.sqrt(d))
+    assert_attention_close(o, wo, bf16=True, what="vs forward")
+    assert np.array_equal(np.isneginf(l), np.isneginf(wl))
+    fin = np.isfinite(wl)
+    assert np.max(np.abs(l[fin] - wl[fin])) < 1e-3
+
+
+def test_vs_end_to_end_planted_certified(sa):
+    from dynamic_sparse_attention_pool_amd.pipelines import VerticalSlashLayer
+    N, d, nv, ns = 4096, 128, 100, 16
+    base = W.prefill_bf16(54, 1, 4, 2, N, d)
+    scale = 1 / math.sqrt(d)
+    for bv, bs in [(80, 3), (100, 3), (120, 4)]:    # fixed planting schedule
+        inp, _, _ = W.plant_vertical_slash(base, 54, nv, ns, bv, bs)
+        sc = [oracle_vs_scores(inp, h, scale) for h in range(4)]
+        if all(oracle.certified_row(a, nv, NONE) and oracle.certified_row(s, ns, NONE) for a, s in sc):
+            break
+    else:
+        pytest.fail("planting schedule did not certify")
+    layer = VerticalSlashLayer(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), n_vert=nv, n_slash=ns,
+                               out_dtype=torch().float32)
+    layer.step()
+    torch().cuda.synchronize()
+    sel = [[oracle.vs_select(a, s, nv, ns) for a, s in sc]]
+    vh, sh = host(layer.vert), host(layer.slash)
+    for h in range(4):
+        assert np.array_equal(vh[h], sel[0][h][0]) and np.array_equal(sh[h], sel[0][h][1])
+    wo, _ = oracle.vs_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), sel, 64, scale)
+    assert_attention_close(host(layer.out), wo, bf16=True, what="planted vs end to end")
+
+
+def test_vs_full_size_sampled(sa):
+    """The 131072-token vertical-slash layer as the benchmark runs it; sampled
+    heads and query blocks against the oracle."""
+    from dynamic_sparse_attention_pool_amd.pipelines import VerticalSlashLayer
+    N, d = 131072, 128
+    inp = W.prefill_bf16(W.CONFIG_SEEDS[3], 1, 32, 8, N, d)
+    layer = VerticalSlashLayer(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), n_vert=1000, n_slash=64,
+                               out_dtype=torch().float32)
+    layer.step()
+    torch().cuda.synchronize()
+    scale = 1 / math.sqrt(d)
+    vh, sh = host(layer.vert), host(layer.slash)
+    av_all, as_all = host(layer.a_v), host(layer.a_s)
+    for h in [0, 13, 31]:
+        wv, ws = oracle_vs_scores(inp, h, scale)
+        assert_scores_close(av_all[0, h][None], wv[None], f"vertical h{h}")
+        assert_scores_close(as_all[0, h][None], ws[None], f"slash h{h}")
+        for got, sc, kk in [(vh[h], wv, 1000), (sh[h], ws, 64)]:
+            if oracle.certified_row(sc, kk, NONE):
+                assert np.array_equal(got, oracle.topk_row(sc, kk, NONE))
+            else:
+                assert tie_tolerant_valid(got, sc, kk, NONE)
+        sel = [[None] * 32]
+        sel[0][h] = (vh[h], sh[h])
+        blocks = [0, 1, 1000, 2047]
+        wo, _ = oracle.vs_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), sel, 64, scale, heads=[h], blocks=blocks)
+        o = host(layer.out[0, h])
+        for i in blocks:
+            rows = slice(64 * i, 64 * i + 64)
+            assert_attention_close(o[rows], wo[0, h, rows], bf16=True, what=f"h{h} block {i}")
