@@ -25,7 +25,15 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
   return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) { return f2bf(lo) | (f2bf(hi) << 16); }
+// Two floats -> packed bf16 pair with the hardware conversion (v_cvt_pk_bf16_f32,
+// round to nearest even).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
@@ -61,6 +69,46 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 __device__ __forceinline__ bool is_nan(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight.
+// Inline assembly, because the compiler's wait-count pass does not see the
+// inline-assembly copies below and would drop a builtin wait as redundant.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xc07f); }
+// Drain every vector-memory load the compiler issued (visible to its
+// wait-count pass, so it also stops guarding those loads later on).
+__device__ __forceinline__ void drain_vmem() { __builtin_amdgcn_s_waitcnt(0x0f70); }
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// One 16-byte direct global->LDS copy per lane: lane L of the wave writes LDS
+// bytes [lds_off + 16L, +16).  Written as inline assembly so that the compiler
+// does not guard every later LDS read with a wait for all copies in flight.
+// A kernel that uses it waits on the vector-memory counter itself
+// (wait_vmcnt) and issues no other vector-memory loads while copies are in
+// flight, so its counts are exact.
+__device__ __forceinline__ void dma16(uint32_t lds_off, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds_off), "v"(gptr)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane j
+// points at 4 consecutive 16-bit values; lane j receives element j%4 of the
+// values pointed at by lanes 4e + j/4 of its group, e = 0..3.
+__device__ __forceinline__ v4i16 lds_read_tr16(const uint16_t* lds_elem) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(const __attribute__((address_space(3))) uint16_t*)lds_elem);
 }
 
 }  // namespace sa

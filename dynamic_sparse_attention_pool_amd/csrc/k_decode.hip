@@ -181,40 +181,69 @@ __global__ void k_decode_mask(const int32_t* __restrict__ sel, int T, int hq, in
   atomicOr(reinterpret_cast<unsigned long long*>(&mask[(int64_t)g * C + c]), 1ull << (t * grp + (h - g * grp)));
 }
 
-struct DecLds {
-  uint16_t vt[kD * kVS];
-  uint64_t rmask[kBlk];
+constexpr int kDecRows = 32;      // rows per tile
+constexpr int kDecMaxC = 1024;    // clusters whose tables are staged in LDS
+
+struct DecWaveLds {
+  uint16_t k[2][kDecRows * kD];   // double-buffered, row-major, chunk-swizzled
+  uint16_t v[2][kDecRows * kD];
+  uint64_t rmask[2][kDecRows];    // per row: which queries selected its cluster
 };
 
-// One workgroup per (KV head, packed-row range); NQT = query tiles of 32.
+// rows -> LDS: 32 rows x 256 B, chunk c of row r at position c ^ (r % 16);
+// 8 copies of 1 KB per tensor.
+__device__ __forceinline__ void dec_dma(uint16_t* kl, uint16_t* vl, const uint16_t* kb, const uint16_t* vb,
+                                        int64_t base, int len, int lane) {
+  const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds_addr(kl));
+  const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_addr(vl));
+#pragma unroll
+  for (int n = 0; n < 8; ++n) {
+    const int r = 4 * n + lane / 16;
+    const int c = (lane % 16) ^ (r % 16);
+    const int64_t row = base + min(r, len - 1);
+    dma16(kbase + n * 1024u, kb + row * kD + 8 * c);
+    dma16(vbase + n * 1024u, vb + row * kD + 8 * c);
+  }
+}
+
+// One workgroup per (KV head, packed-row range).  Its waves stream disjoint
+// 32-row tiles independently: each wave double-buffers its tiles in its own
+// LDS region through direct global->LDS copies, so the next tile is in flight
+// while the current one is computed.  NQT = query tiles of 32.
 template <int NQT>
 __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p, const uint64_t* __restrict__ mask,
                                                                  float* __restrict__ part, int nsplit) {
-  __shared__ DecLds L[kDecWaves];
+  __shared__ __attribute__((aligned(1024))) DecWaveLds L[kDecWaves];
+  __shared__ int32_t ptr_s[kDecMaxC + 1];
+  __shared__ uint64_t mask_s[kDecMaxC];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int g = blockIdx.x / nsplit, split = blockIdx.x % nsplit;
   const int grp = p.hq / p.hkv;
   const int nq = p.T * grp;
   const int64_t N = p.n_ctx;
-  const int* ptr = p.cluster_ptr + (int64_t)g * (p.C + 1);
-  const uint64_t* gm = mask + (int64_t)g * p.C;
+  const int C = p.C;
+  for (int c = threadIdx.x; c <= C; c += blockDim.x) ptr_s[c] = p.cluster_ptr[(int64_t)g * (C + 1) + c];
+  for (int c = threadIdx.x; c < C; c += blockDim.x) mask_s[c] = mask[(int64_t)g * C + c];
   const uint16_t* kb = p.k + (int64_t)g * N * kD;
   const uint16_t* vb = p.v + (int64_t)g * N * kD;
   const int64_t p0 = (int64_t)split * kRowsPerSplit;
   const int64_t p1 = min(N, p0 + kRowsPerSplit);
-  const int ntile = (int)((p1 - p0 + kBlk - 1) / kBlk);
+  const int ntile = (int)((p1 - p0 + kDecRows - 1) / kDecRows);
   const float sl2 = p.scale * kLog2e;
 
-  // Q^T: lane holds query 32nt+l32, dims 64hf + 8s .. +7 at step s
+  // Q^T: lane holds query 32nt+l32, dims 16s + 8hf .. +7 at step s
   bf16x8 qv[NQT][8];
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
     const int qi = min(32 * nt + l32, nq - 1);
     const int t = qi / grp, h = g * grp + qi % grp;
-    const uint16_t* qr = p.q + ((int64_t)t * p.hq + h) * kD + 64 * hf;
+    const uint16_t* qr = p.q + ((int64_t)t * p.hq + h) * kD + 8 * hf;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) qv[nt][s] = as_bf16x8(ldg16(qr + 8 * s));
+    for (int s = 0; s < 8; ++s) qv[nt][s] = as_bf16x8(ldg16(qr + 16 * s));
   }
+  drain_vmem();
+  __syncthreads();
+
   f32x16 o[NQT][4];
   float m[NQT], l[NQT];
 #pragma unroll
@@ -226,97 +255,109 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[nt][dt][r] = 0.f;
   }
+  DecWaveLds& W = L[w];
 
-  for (int t = w; t < ntile; t += kDecWaves) {
-    const int64_t base = p0 + (int64_t)t * kBlk;
-    const int len = (int)min((int64_t)kBlk, p1 - base);
-    // cluster of this lane's row: last c with ptr[c] <= row
-    const int64_t myrow = base + min(lane, len - 1);
-    int lo = 0, hi = p.C - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (ptr[mid] <= myrow) lo = mid;
-      else hi = mid - 1;
+  // next selected tile at or after index t (stride kDecWaves); writes its row masks
+  auto find = [&](int t, int buf) -> int {
+    for (; t < ntile; t += kDecWaves) {
+      const int64_t base = p0 + (int64_t)t * kDecRows;
+      const int len = (int)min((int64_t)kDecRows, p1 - base);
+      const int64_t row = base + min(l32, len - 1);
+      int lo = 0, hi = C - 1;  // last cluster c with ptr[c] <= row
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (ptr_s[mid] <= row) lo = mid;
+        else hi = mid - 1;
+      }
+      const uint64_t rm = l32 < len ? mask_s[lo] : 0ull;
+      if (__any(rm != 0ull)) {
+        if (hf == 0) W.rmask[buf][l32] = rm;
+        return t;
+      }
     }
-    const uint64_t rm = lane < len ? gm[lo] : 0ull;
-    if (!__any(rm != 0ull)) continue;  // nobody selected any row of this tile
-    L[w].rmask[lane] = rm;
-    // V rows -> LDS (transposed), K rows -> A operand registers
-    int rows[16];
+    return ntile;
+  };
+  auto issue = [&](int t, int buf) {
+    const int64_t base = p0 + (int64_t)t * kDecRows;
+    dec_dma(W.k[buf], W.v[buf], kb, vb, base, (int)min((int64_t)kDecRows, p1 - base), lane);
+  };
+
+  int cur = find(w, 0), buf = 0;
+  if (cur < ntile) issue(cur, 0);
+  int nxt = cur < ntile ? find(cur + kDecWaves, 1) : ntile;
+  if (nxt < ntile) issue(nxt, 1);
+  while (cur < ntile) {
+    if (nxt < ntile) wait_vmcnt<16>();
+    else wait_vmcnt<0>();
+    const uint16_t* kl = W.k[buf];
+    const uint16_t* vl = W.v[buf];
+    // row masks of the 16 rows this lane's accumulators cover: rows 8j + 4hf + i
+    uint64_t rmv[16];
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) rows[4 * n + e] = (int)(base + min(v_slot(lane, n, e), len - 1));
-    VRegs VR;
-    v_fetch(VR, vb, rows, lane);
-    bf16x8 ka[2][8];
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int64_t row = base + min(32 * mt + l32, len - 1);
-      const uint16_t* kr = kb + row * kD + 64 * hf;
-#pragma unroll
-      for (int s = 0; s < 8; ++s) ka[mt][s] = as_bf16x8(ldg16(kr + 8 * s));
-    }
-    v_store<32>(L[w].vt, VR, lane);
-    wave_sync();
+      for (int i = 0; i < 4; ++i) rmv[4 * j + i] = W.rmask[buf][8 * j + 4 * hf + i];
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-      f32x16 s0, s1;
+      f32x16 s0;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        s0[r] = 0.f;
-        s1[r] = 0.f;
-      }
+      for (int r = 0; r < 16; ++r) s0[r] = 0.f;
 #pragma unroll
-      for (int s = 0; s < 8; ++s) {
-        s0 = mfma32x32x16(ka[0][s], qv[nt][s], s0);
-        s1 = mfma32x32x16(ka[1][s], qv[nt][s], s1);
+      for (int st = 0; st < 8; ++st) {
+        const int c = 2 * st + hf;
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&kl[l32 * kD + 8 * (c ^ (l32 % 16))]));
+        s0 = mfma32x32x16(a, qv[nt][st], s0);
       }
       const int qi = 32 * nt + l32;
-      float x[32];
+      float x[16];
+      float mx = -INFINITY;
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const int slot = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
-        const float sv = (r < 16 ? s0[r] : s1[r - 16]) * sl2;
-        const bool keep = qi < nq && ((L[w].rmask[slot] >> qi) & 1ull);
-        x[r] = keep ? sv : -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const bool keep = qi < nq && ((rmv[r] >> qi) & 1ull);
+        x[r] = keep ? s0[r] : -INFINITY;
+        mx = fmaxf(mx, x[r]);
       }
-      float mx = x[0];
-#pragma unroll
-      for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
       const float mnew = fmaxf(m[nt], mx);
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-      const float alpha = fast_exp2(m[nt] - muse);
       float ps = 0.f;
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        x[r] = fast_exp2(x[r] - muse);
+      for (int r = 0; r < 16; ++r) {
+        x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
         ps += x[r];
       }
       ps += __shfl_xor(ps, 32);
+      const float alpha = fast_exp2(m[nt] - muse);
       l[nt] = l[nt] * alpha + ps;
       m[nt] = mnew;
-      bf16x8 pv[4];
+      bf16x8 pv[2];
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        u32x4 u;
+      for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
-        pv[ks] = as_bf16x8(u);
-      }
+        for (int e = 0; e < 8; ++e) pv[ks][e] = (__bf16)x[8 * ks + e];
+      const int gl = lane & 15, gsub = (lane >> 4) & 1;
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[nt][dt][r] *= alpha;
+        const int dim = 32 * dt + 16 * gsub + 4 * (gl & 3);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-          const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&L[w].vt[(32 * dt + l32) * kVS + 16 * ks + 8 * hf]));
-          o[nt][dt] = mfma32x32x16(a, pv[ks], o[nt][dt]);
+        for (int ks = 0; ks < 2; ++ks) {
+          const int k0 = 16 * ks + 4 * hf + (gl >> 2), k1 = k0 + 8;
+          const v4i16 lo = lds_read_tr16(vl + k0 * kD + 8 * ((dim >> 3) ^ (k0 % 16)) + (dim & 7));
+          const v4i16 hi = lds_read_tr16(vl + k1 * kD + 8 * ((dim >> 3) ^ (k1 % 16)) + (dim & 7));
+          const short __attribute__((ext_vector_type(8))) ab = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[nt][dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ab), pv[ks], o[nt][dt]);
         }
       }
     }
-    wave_sync();
+    wait_lgkm0();  // done reading this buffer before it is refilled
+    cur = nxt;
+    buf ^= 1;
+    if (cur < ntile) {
+      nxt = find(cur + kDecWaves, buf ^ 1);
+      if (nxt < ntile) issue(nxt, buf ^ 1);
+    }
   }
 
   // ---- this wave's partial (max, sum, unnormalised output) for its queries

@@ -9,15 +9,19 @@
 //
 // bf16 kernel — one workgroup (2 waves) per (batch, head, query block); each
 // wave owns 32 query rows.  Per tile:
+//   K and V rows are copied straight from memory into LDS by the direct
+//   global->LDS path (global_load_lds_dwordx4), row-major with the 16-byte
+//   chunks of row r XOR-swizzled by r, so no VGPR staging and no VALU work;
 //   S^T[key][query] = K_tile . Q^T          (v_mfma_f32_32x32x16_bf16, K from LDS,
 //                                            Q^T resident in VGPRs)
 //   online softmax along keys: every lane holds one query column, so the row
 //   statistics need a single exchange with lane^32
-//   O^T[d][query] += V^T . P^T               (V^T from LDS, P^T straight from the
-//                                            S^T accumulators, no shuffles)
-// The V tile is written to LDS transposed and with its keys permuted inside
-// each 16-key group so that the P^T register order lines up with it.
-// The next tile is fetched into VGPRs while the current one is computed.
+//   O^T[d][query] += V^T . P^T               (V^T read with ds_read_b64_tr_b16, which
+//                                            transposes 4-key x 16-dim blocks on the
+//                                            way out of LDS; P^T comes straight from
+//                                            the S^T accumulators, no shuffles)
+// K(t+1) is fetched while the softmax and P.V of tile t run, V(t+1) while the
+// next S^T runs: one LDS buffer each, four barriers per tile.
 #include <climits>
 
 #include "common.h"
@@ -28,22 +32,14 @@ namespace {
 
 constexpr int kBlk = 64;
 constexpr int kThreads = 128;
-
-template <int D>
-struct FwdLds {
-  static constexpr int KS = D + 8;      // K row stride (elements): 16 B pad against bank conflicts
-  static constexpr int VS = kBlk + 8;   // V^T row stride (elements)
-  uint16_t k[kBlk * KS];
-  uint16_t vt[D * VS];
-  int32_t key[kBlk];
-};
+constexpr int kMetaMax = 2048 + 128;  // staged block list, or column list + intervals
 
 // Tile source: either a contiguous key range or a gathered list of columns.
 struct TileRef {
   int base;      // first key (contiguous) or offset into the column list (gathered)
   int len;       // valid keys, 1..64
   int gathered;  // 0 / 1
-  int diag;      // block mode: tile is the query block's own diagonal block
+  int diag;      // tile may hold keys beyond some query row of the block
 };
 
 template <int MODE>
@@ -92,80 +88,40 @@ struct TileIter {
   }
 };
 
-template <int D>
-struct TileRegs {
-  static constexpr int NK = D / 16;   // 16-byte K chunks per thread
-  static constexpr int NV = D / 64;   // (4 keys x 8 dims) V groups per thread
-  u32x4 k[NK];
-  u32x4 v[NV][4];
-  int32_t key;                        // absolute key of slot tid (tid < 64)
-};
-
-template <int D>
 __device__ __forceinline__ int tile_row(const TileRef& r, const int32_t* cols, int slot) {
   const int s = min(slot, r.len - 1);
   return r.gathered ? cols[r.base + s] : r.base + s;
 }
 
+// One 64-row tile (K or V) -> LDS, row-major, chunk c of row r at position
+// c ^ (r % CPR).  Each wave issues NI copies of 1 KB.
 template <int D>
-__device__ __forceinline__ void tile_fetch(TileRegs<D>& R, const TileRef& r, const uint16_t* kb,
-                                           const uint16_t* vb, const int32_t* cols, int tid) {
-  constexpr int CPR = D / 8;  // chunks per row
+__device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* gbase, const TileRef& r,
+                                         const int32_t* cols, int w, int lane) {
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;       // rows per 1 KB copy
+  constexpr int NI = kBlk / RPI / 2;  // copies per wave
+  const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)(w * NI) * 1024u);
 #pragma unroll
-  for (int n = 0; n < TileRegs<D>::NK; ++n) {
-    const int c = tid + kThreads * n;
-    const int slot = c / CPR, dc = c % CPR;
-    const int row = tile_row<D>(r, cols, slot);
-    R.k[n] = ldg16(kb + (int64_t)row * D + 8 * dc);
-  }
-#pragma unroll
-  for (int n = 0; n < TileRegs<D>::NV; ++n) {
-    const int gidx = tid + kThreads * n;
-    const int kg = gidx % 16, dc = gidx / 16;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int row = tile_row<D>(r, cols, 4 * kg + e);
-      R.v[n][e] = ldg16(vb + (int64_t)row * D + 8 * dc);
-    }
-  }
-  if (tid < kBlk) {
-    R.key = tid < r.len ? (r.gathered ? cols[r.base + tid] : r.base + tid) : INT_MAX;
+  for (int n = 0; n < NI; ++n) {
+    const int row = (w * NI + n) * RPI + lane / CPR;
+    const int c = (lane % CPR) ^ (row % CPR);
+    const uint16_t* src = gbase + (int64_t)tile_row(r, cols, row) * D + 8 * c;
+    dma16(base + (uint32_t)n * 1024u, src);
   }
 }
 
 template <int D>
-__device__ __forceinline__ void tile_store(FwdLds<D>& L, const TileRegs<D>& R, int tid) {
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int n = 0; n < TileRegs<D>::NK; ++n) {
-    const int c = tid + kThreads * n;
-    const int slot = c / CPR, dc = c % CPR;
-    *reinterpret_cast<u32x4*>(&L.k[slot * FwdLds<D>::KS + 8 * dc]) = R.k[n];
-  }
-#pragma unroll
-  for (int n = 0; n < TileRegs<D>::NV; ++n) {
-    const int gidx = tid + kThreads * n;
-    const int kg = gidx % 16, dc = gidx / 16;
-    // keys 4kg..4kg+3 sit at positions 16*(kg/4) + 4*swap(kg%4), swap = {0,2,1,3}
-    const int q4 = kg & 3;
-    const int pos = 16 * (kg >> 2) + 4 * ((q4 == 1) ? 2 : (q4 == 2) ? 1 : q4);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, sh = (e & 1) * 16;
-      const uint32_t x0 = (R.v[n][0][w] >> sh) & 0xffffu, x1 = (R.v[n][1][w] >> sh) & 0xffffu;
-      const uint32_t x2 = (R.v[n][2][w] >> sh) & 0xffffu, x3 = (R.v[n][3][w] >> sh) & 0xffffu;
-      u32x2 pk;
-      pk[0] = x0 | (x1 << 16);
-      pk[1] = x2 | (x3 << 16);
-      *reinterpret_cast<u32x2*>(&L.vt[(8 * dc + e) * FwdLds<D>::VS + pos]) = pk;
-    }
-  }
-  if (tid < kBlk) L.key[tid] = R.key;
+__device__ __forceinline__ int swz(int row, int chunk) {
+  return row * D + 8 * (chunk ^ (row % (D / 8)));
 }
 
 template <int D, int MODE, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void k_fwd_bf16(FwdParams p) {
-  __shared__ FwdLds<D> L;
+__global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
+  __shared__ __attribute__((aligned(1024))) uint16_t Kl[kBlk * D];
+  __shared__ __attribute__((aligned(1024))) uint16_t Vl[kBlk * D];
+  __shared__ int32_t meta[MODE == 0 ? 2048 : kMetaMax];
+  constexpr int NDMA = D / 16;  // direct-to-LDS copies per wave per tile (K or V)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
   const int n_items = gridDim.x;
   const int item = xcd_remap(blockIdx.x, n_items);
@@ -186,17 +142,27 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(FwdParams p) {
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + ((int64_t)b * p.heads_kv + g) * N * D;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + ((int64_t)b * p.heads_kv + g) * N * D;
 
+  // ---- stage this row's tile list in LDS (no vector-memory reads inside the pipeline)
   TileIter<MODE> it;
   const int32_t* cols = nullptr;
   if (MODE == 0) {
-    it.bidx = p.block_idx + row_id * p.kmax;
-    it.cnt = p.block_cnt[row_id];
+    const int cnt = min(p.block_cnt[row_id], 2048);
+    const int32_t* src = p.block_idx + row_id * p.kmax;
+    for (int e = tid; e < cnt; e += kThreads) meta[e] = src[e];
+    it.bidx = meta;
+    it.cnt = cnt;
     it.iblk = iblk;
   } else {
-    it.iv = p.iv + row_id * p.max_iv * 2;
-    it.n_iv = p.iv_cnt[row_id];
-    it.n_col = p.col_cnt[row_id];
-    cols = p.col + row_id * p.max_col;
+    const int niv = min(p.iv_cnt[row_id], 64);
+    const int ncol = min(p.col_cnt[row_id], kMetaMax - 128);
+    const int32_t* isrc = p.iv + row_id * p.max_iv * 2;
+    const int32_t* csrc = p.col + row_id * p.max_col;
+    for (int e = tid; e < 2 * niv; e += kThreads) meta[e] = isrc[e];
+    for (int e = tid; e < ncol; e += kThreads) meta[128 + e] = csrc[e];
+    it.iv = meta;
+    it.n_iv = niv;
+    it.n_col = ncol;
+    cols = meta + 128;
   }
 
   // Q^T operand: lane holds query row 32w+l32, dims 16s+8hf .. +7 of step s
@@ -208,6 +174,8 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(FwdParams p) {
   }
   const int qpos = iblk * kBlk + 32 * w + l32;  // absolute query row of this lane
   const float sl2 = p.scale * kLog2e;
+  drain_vmem();  // Q^T resident: from here on the only vector-memory ops are the tile copies
+  __syncthreads();
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -216,18 +184,16 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(FwdParams p) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
   float m = -INFINITY, lsum = 0.f;
 
-  TileRegs<D> R;
   TileRef cur, nxt;
   bool have = it.next(cur);
-  if (have) tile_fetch<D>(R, cur, kb, vb, cols, tid);
+  if (have) {
+    dma_tile<D>(Kl, kb, cur, cols, w, lane);
+    dma_tile<D>(Vl, vb, cur, cols, w, lane);
+  }
   while (have) {
-    __syncthreads();
-    tile_store<D>(L, R, tid);
-    __syncthreads();
-    const bool more = it.next(nxt);
-    if (more) tile_fetch<D>(R, nxt, kb, vb, cols, tid);
-
-    // ---- S^T = K . Q^T for the 64 keys of the tile (two 32-key M tiles)
+    // ---- K(t) in LDS
+    wait_vmcnt<NDMA>();
+    __builtin_amdgcn_s_barrier();
     f32x16 s0, s1;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
@@ -236,19 +202,23 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(FwdParams p) {
     }
 #pragma unroll
     for (int st = 0; st < D / 16; ++st) {
-      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&L.k[l32 * FwdLds<D>::KS + 16 * st + 8 * hf]));
-      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&L.k[(32 + l32) * FwdLds<D>::KS + 16 * st + 8 * hf]));
+      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(l32, 2 * st + hf)]));
+      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 + l32, 2 * st + hf)]));
       s0 = mfma32x32x16(a0, qv[st], s0);
       s1 = mfma32x32x16(a1, qv[st], s1);
     }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();  // both waves are done with K(t)
+    const bool more = it.next(nxt);
+    if (more) dma_tile<D>(Kl, kb, nxt, cols, w, lane);
 
     // ---- online softmax (log2 domain); element r of M tile mt is key slot
     //      32*mt + 8*(r/4) + 4*hf + r%4
     float x[32];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      x[r] = s0[r] * sl2;
-      x[16 + r] = s1[r] * sl2;
+      x[r] = s0[r];
+      x[16 + r] = s1[r];
     }
     if (cur.diag) {
       if (MODE == 0) {
@@ -262,50 +232,68 @@ __global__ __launch_bounds__(kThreads) void k_fwd_bf16(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 32; ++r) {
           const int slot = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
-          const int key = L.key[slot];
-          if (key > qpos) x[r] = -INFINITY;  // empty slots hold INT_MAX
+          const int key = slot >= cur.len ? INT_MAX : (cur.gathered ? cols[cur.base + slot] : cur.base + slot);
+          if (key > qpos) x[r] = -INFINITY;
         }
       }
     }
     float mx = x[0];
 #pragma unroll
     for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
     const float mnew = fmaxf(m, mx);
     const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = fast_exp2(m - muse);
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
-      x[r] = fast_exp2(x[r] - muse);
+      x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
       ps += x[r];
     }
     ps += __shfl_xor(ps, 32);
-    lsum = lsum * alpha + ps;
+    if (__any(mnew > m)) {  // rescale only when some row maximum grew
+      const float alpha = fast_exp2(m - muse);
+      lsum *= alpha;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+    }
+    lsum += ps;
     m = mnew;
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 
     // ---- P^T operand for k-step ks = the 8 consecutive registers x[8ks .. 8ks+7]
     bf16x8 pv[4];
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      u32x4 u;
+    for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[e] = pack_bf16x2(x[8 * ks + 2 * e], x[8 * ks + 2 * e + 1]);
-      pv[ks] = as_bf16x8(u);
-    }
-    // ---- O^T += V^T . P^T
+      for (int e = 0; e < 8; ++e) pv[ks][e] = (__bf16)x[8 * ks + e];
+
+    // ---- V(t) in LDS
+    if (more) wait_vmcnt<NDMA>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    // O^T += V^T . P^T; the A operand (dims 32dt + l32, keys 16ks + 4hf + e and
+    // 16ks + 8 + 4hf + e) comes from two transposing reads: in each 16-lane group,
+    // lane j points at V[key0 + j/4][dim0 + 4(j%4) .. +3]
+    const int gl = lane & 15, gsub = (lane >> 4) & 1;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
+      const int dim = 32 * dt + 16 * gsub + 4 * (gl & 3);
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&L.vt[(32 * dt + l32) * FwdLds<D>::VS + 16 * ks + 8 * hf]));
-        o[dt] = mfma32x32x16(a, pv[ks], o[dt]);
+        const int k0 = 16 * ks + 4 * hf + (gl >> 2);
+        const int a0 = k0 * D + 8 * ((dim >> 3) ^ (k0 % (D / 8))) + (dim & 7);
+        const int k1 = k0 + 8;
+        const int a1 = k1 * D + 8 * ((dim >> 3) ^ (k1 % (D / 8))) + (dim & 7);
+        const v4i16 lo = lds_read_tr16(Vl + a0);
+        const v4i16 hi = lds_read_tr16(Vl + a1);
+        const short __attribute__((ext_vector_type(8))) ab = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ab), pv[ks], o[dt]);
       }
     }
+    wait_lgkm0();
+    __builtin_amdgcn_s_barrier();  // both waves are done with V(t)
+    if (more) dma_tile<D>(Vl, vb, nxt, cols, w, lane);
     cur = nxt;
     have = more;
   }
@@ -386,7 +374,7 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
   TileRef r;
   while (it.next(r)) {
     __syncthreads();
-    const int row = tile_row<D>(r, cols, tid);
+    const int row = tile_row(r, cols, tid);
     for (int d = 0; d < D; d += 4) {
       *reinterpret_cast<f32x4*>(&Ks[tid][d]) = *reinterpret_cast<const f32x4*>(kb + (int64_t)row * D + d);
       *reinterpret_cast<f32x4*>(&Vs[tid][d]) = *reinterpret_cast<const f32x4*>(vb + (int64_t)row * D + d);

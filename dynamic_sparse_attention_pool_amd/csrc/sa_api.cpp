@@ -307,9 +307,13 @@ static int check_fwd(const sa_fwd_args* a) {
   if (a->mode == SA_FWD_BLOCK) {
     if (!a->block_idx || !a->block_cnt) return fail(SA_ERR_NULL, "sa_block_sparse_fwd(BLOCK): block_idx and block_cnt required");
     if (a->kmax <= 0) return fail(SA_ERR_SHAPE, "sa_block_sparse_fwd(BLOCK): kmax must be positive");
+    if (a->dtype == SA_BF16 && a->kmax > 2048)
+      return fail(SA_ERR_UNSUPPORTED, "sa_block_sparse_fwd(BLOCK): bf16 path stages at most 2048 blocks per row (kmax)");
   } else if (a->mode == SA_FWD_VSLASH) {
     if (!a->iv || !a->iv_cnt || !a->col || !a->col_cnt) return fail(SA_ERR_NULL, "sa_block_sparse_fwd(VSLASH): tables required");
     if (a->max_iv <= 0 || a->max_col <= 0) return fail(SA_ERR_SHAPE, "sa_block_sparse_fwd(VSLASH): capacities must be positive");
+    if (a->dtype == SA_BF16 && (a->max_iv > 64 || a->max_col > 2048))
+      return fail(SA_ERR_UNSUPPORTED, "sa_block_sparse_fwd(VSLASH): bf16 path stages at most 64 intervals and 2048 columns per row");
   } else {
     return fail(SA_ERR_VALUE, "sa_block_sparse_fwd: unknown mode %d", a->mode);
   }
@@ -374,6 +378,7 @@ static int check_gather(const sa_gather_args* a, size_t* ws) {
     if (a->n_clusters <= 0 || a->n_sel <= 0) return fail(SA_ERR_SHAPE, "sa_gather_decode(CLUSTER): n_clusters and n_sel must be positive");
     if (a->n_q * (a->heads_q / a->heads_kv) > 64)
       return fail(SA_ERR_UNSUPPORTED, "sa_gather_decode(CLUSTER): at most 64 queries per KV head");
+    if (a->n_clusters > 1024) return fail(SA_ERR_UNSUPPORTED, "sa_gather_decode(CLUSTER): at most 1024 clusters");
     *ws = sa::cluster_decode_workspace_bytes((int)a->n_q, (int)a->heads_q, (int)a->heads_kv, a->n_clusters, a->n_ctx);
   } else if (a->mode == SA_GATHER_TOKEN) {
     if (!a->tok_idx) return fail(SA_ERR_NULL, "sa_gather_decode(TOKEN): tok_idx required");
