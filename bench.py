@@ -34,7 +34,7 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 FLOP_PER_BLOCK = 4 * 64 * 64 * 128
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fwd_bf16_128k.json")
-FWD_SOURCE = os.path.join(ROOT, "dynamic_sparse_attention_pool_amd", "csrc", "k_fwd.hip")
+FWD_SOURCES = [os.path.join(ROOT, "dynamic_sparse_attention_pool_amd", "csrc", f) for f in ("k_fwd.hip", "common.h")]
 
 
 def log(*a):
@@ -71,9 +71,12 @@ class Timer:
         return float(np.mean([a.elapsed_time(b) for a, b in self.marks[name]]))
 
 
-def source_hash(path):
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_for(launch_flops_unused=None):
@@ -83,7 +86,7 @@ def traffic_for(launch_flops_unused=None):
         return None
     with open(TRAFFIC_FILE) as f:
         t = json.load(f)
-    if t.get("kernel_source_sha256_16") != source_hash(FWD_SOURCE):
+    if t.get("kernel_source_sha256_16") != source_hash(FWD_SOURCES):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -133,17 +136,32 @@ def decode_extra(steps, warmup):
         copies.append(ClusterDecode(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev_t(inp.labels),
                                     dev_t(inp.centroids), n_sel=ksel))
     torch.cuda.synchronize()
-    for i in range(warmup):
+    for i in range(max(warmup, 4)):
         copies[i % 4].step()
     torch.cuda.synchronize()
+    # a decode step is a handful of short launches: replay each as one HIP graph so
+    # the host's launch overhead is not what gets timed
+    graphs = []
+    for dc in copies:
+        parts = []
+        for fn in (dc.estimate, dc.select, dc.forward, dc.step):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                fn()
+            parts.append(gr)
+        graphs.append(parts)
+    torch.cuda.synchronize()
     tm = Timer()
+    for i in range(steps):
+        ge, gs, gf, _ = graphs[i % 4]
+        tm.span("estimate", ge.replay)
+        tm.span("select", gs.replay)
+        tm.span("forward", gf.replay)
+    torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
     for i in range(steps):
-        dc = copies[i % 4]
-        tm.span("estimate", dc.estimate)
-        tm.span("select", dc.select)
-        tm.span("forward", dc.forward)
+        graphs[i % 4][3].replay()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
@@ -159,7 +177,8 @@ def decode_extra(steps, warmup):
     small = T * Hq * d * 2 + Hkv * C * d * 4 + T * Hq * d * 4
     step_bytes = kv_bytes + small
     fwd_ms = tm.mean_ms("forward")
-    return {"workload": "clustered decode: 8 queries x 32/8 heads, d128, 65536-key context, top 64 of 256 clusters",
+    return {"workload": "clustered decode: 8 queries x 32/8 heads, d128, 65536-key context, top 64 of 256 clusters; "
+                        "each step replayed as a HIP graph, rotating 4 contexts",
             "us_per_step": ms * 1e3, "us_per_token": ms * 1e3 / T,
             "kv_bytes_per_step": kv_bytes, "GB_per_s_step": step_bytes / (ms * 1e-3) / 1e9,
             "us_gather": fwd_ms * 1e3, "GB_per_s_gather": kv_bytes / (fwd_ms * 1e-3) / 1e9,
@@ -287,17 +306,27 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extras to run: decode,indexer,vs,prefill32k")
+    ap.add_argument("--only", default="", help="comma list of extras to run: decode,indexer,vs")
+    ap.add_argument("--pmc-copy", action="store_true",
+                    help="first run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (see DESIGN.md for how it would "
-              "shard); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path (each GPU would run "
+              "the same kernels on its own share of heads); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
     import torch
     import dynamic_sparse_attention_pool_amd as sa
     sa.load()
     torch.cuda.init()
 
+    if args.pmc_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] reference copy: 1073741824 bytes read, 1073741824 bytes written")
+        del src, dst
     main = prefill_layer(131072, (5, 100), args.steps, args.warmup, seed=3)
     ms = main["ms_per_step"]
     value = main["flop"] / (ms * 1e-3) / 1e12

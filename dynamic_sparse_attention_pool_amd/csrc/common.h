@@ -100,9 +100,24 @@ __device__ __forceinline__ void dma16(uint32_t lds_off, const void* gptr) {
                : "memory", "m0");
 }
 
+// Same copy with a wave-uniform 64-bit base (SGPR pair) and a 32-bit per-lane
+// byte offset, which saves the 64-bit address arithmetic per lane.
+__device__ __forceinline__ void dma16_sb(uint32_t lds_off, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_off), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
+
+// XOR key of row r for tiles of 256-byte rows (16 chunks of 16 bytes): chunk c
+// of row r is stored at position c ^ key(r).  Sixteen consecutive rows get
+// distinct keys, and 4 consecutive rows (a multiple of 4 apart from 0) x 4
+// consecutive chunks (starting at a multiple of 4) map to 16 distinct positions.
+__device__ __forceinline__ int swz_key128(int row) { return 4 * (row & 3) + ((row >> 2) & 3); }
 
 // Transposing LDS read (ds_read_b64_tr_b16): in each 16-lane group, lane j
 // points at 4 consecutive 16-bit values; lane j receives element j%4 of the

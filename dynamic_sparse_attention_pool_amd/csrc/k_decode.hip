@@ -158,28 +158,10 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // ================================================================ cluster decode
-constexpr int kDecWaves = 4;
-constexpr int kRowsPerSplit = 2048;
+constexpr int kDecWaves = 2;
+constexpr int kRowsPerSplit = 1024;
 
 int decode_splits(int64_t n_ctx) { return (int)((n_ctx + kRowsPerSplit - 1) / kRowsPerSplit); }
-
-__global__ void k_fill_u64(uint64_t* p, int64_t n) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) p[i] = 0ull;
-}
-
-// mask[g][c] bit j <=> query j of KV head g (j = t*grp + head-in-group) selected cluster c
-__global__ void k_decode_mask(const int32_t* __restrict__ sel, int T, int hq, int hkv, int C, int n_sel,
-                              uint64_t* __restrict__ mask) {
-  const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (e >= (int64_t)T * hq * n_sel) return;
-  const int th = (int)(e / n_sel);
-  const int t = th / hq, h = th % hq;
-  const int grp = hq / hkv;
-  const int g = h / grp;
-  const int c = sel[e];
-  if (c < 0 || c >= C) return;
-  atomicOr(reinterpret_cast<unsigned long long*>(&mask[(int64_t)g * C + c]), 1ull << (t * grp + (h - g * grp)));
-}
 
 constexpr int kDecRows = 32;      // rows per tile
 constexpr int kDecMaxC = 1024;    // clusters whose tables are staged in LDS
@@ -190,7 +172,7 @@ struct DecWaveLds {
   uint64_t rmask[2][kDecRows];    // per row: which queries selected its cluster
 };
 
-// rows -> LDS: 32 rows x 256 B, chunk c of row r at position c ^ (r % 16);
+// rows -> LDS: 32 rows x 256 B, chunk c of row r at position c ^ key(r);
 // 8 copies of 1 KB per tensor.
 __device__ __forceinline__ void dec_dma(uint16_t* kl, uint16_t* vl, const uint16_t* kb, const uint16_t* vb,
                                         int64_t base, int len, int lane) {
@@ -199,7 +181,7 @@ __device__ __forceinline__ void dec_dma(uint16_t* kl, uint16_t* vl, const uint16
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int r = 4 * n + lane / 16;
-    const int c = (lane % 16) ^ (r % 16);
+    const int c = (lane % 16) ^ swz_key128(r);
     const int64_t row = base + min(r, len - 1);
     dma16(kbase + n * 1024u, kb + row * kD + 8 * c);
     dma16(vbase + n * 1024u, vb + row * kD + 8 * c);
@@ -211,8 +193,7 @@ __device__ __forceinline__ void dec_dma(uint16_t* kl, uint16_t* vl, const uint16
 // LDS region through direct global->LDS copies, so the next tile is in flight
 // while the current one is computed.  NQT = query tiles of 32.
 template <int NQT>
-__global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p, const uint64_t* __restrict__ mask,
-                                                                 float* __restrict__ part, int nsplit) {
+__global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p, float* __restrict__ part, int nsplit) {
   __shared__ __attribute__((aligned(1024))) DecWaveLds L[kDecWaves];
   __shared__ int32_t ptr_s[kDecMaxC + 1];
   __shared__ uint64_t mask_s[kDecMaxC];
@@ -223,7 +204,16 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
   const int64_t N = p.n_ctx;
   const int C = p.C;
   for (int c = threadIdx.x; c <= C; c += blockDim.x) ptr_s[c] = p.cluster_ptr[(int64_t)g * (C + 1) + c];
-  for (int c = threadIdx.x; c < C; c += blockDim.x) mask_s[c] = mask[(int64_t)g * C + c];
+  for (int c = threadIdx.x; c < C; c += blockDim.x) mask_s[c] = 0ull;
+  __syncthreads();
+  // mask_s[c] bit j <=> query j of this KV head (token t, head-in-group hh: j = t*grp + hh)
+  // selected cluster c; duplicate and out-of-range ids fall out naturally
+  for (int e = threadIdx.x; e < nq * p.n_sel; e += blockDim.x) {
+    const int qi = e / p.n_sel, sidx = e % p.n_sel;
+    const int t = qi / grp, hh = qi % grp;
+    const int c = p.sel[((int64_t)t * p.hq + g * grp + hh) * p.n_sel + sidx];
+    if (c >= 0 && c < C) atomicOr(reinterpret_cast<unsigned long long*>(&mask_s[c]), 1ull << qi);
+  }
   const uint16_t* kb = p.k + (int64_t)g * N * kD;
   const uint16_t* vb = p.v + (int64_t)g * N * kD;
   const int64_t p0 = (int64_t)split * kRowsPerSplit;
@@ -258,18 +248,27 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
   DecWaveLds& W = L[w];
 
   // next selected tile at or after index t (stride kDecWaves); writes its row masks
+  // cluster of this lane's row: last c with ptr[c] <= row.  Rows only grow
+  // along a wave's tiles, so after one binary search the cluster index
+  // advances incrementally.
+  int cl = 0;
+  {
+    const int64_t row0 = p0 + (int64_t)w * kDecRows + l32;
+    int lo = 0, hi = C - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (ptr_s[mid] <= row0) lo = mid;
+      else hi = mid - 1;
+    }
+    cl = lo;
+  }
   auto find = [&](int t, int buf) -> int {
     for (; t < ntile; t += kDecWaves) {
       const int64_t base = p0 + (int64_t)t * kDecRows;
       const int len = (int)min((int64_t)kDecRows, p1 - base);
       const int64_t row = base + min(l32, len - 1);
-      int lo = 0, hi = C - 1;  // last cluster c with ptr[c] <= row
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (ptr_s[mid] <= row) lo = mid;
-        else hi = mid - 1;
-      }
-      const uint64_t rm = l32 < len ? mask_s[lo] : 0ull;
+      while (cl + 1 < C && ptr_s[cl + 1] <= row) ++cl;
+      const uint64_t rm = l32 < len ? mask_s[cl] : 0ull;
       if (__any(rm != 0ull)) {
         if (hf == 0) W.rmask[buf][l32] = rm;
         return t;
@@ -305,7 +304,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
 #pragma unroll
       for (int st = 0; st < 8; ++st) {
         const int c = 2 * st + hf;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&kl[l32 * kD + 8 * (c ^ (l32 % 16))]));
+        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&kl[l32 * kD + 8 * (c ^ swz_key128(l32))]));
         s0 = mfma32x32x16(a, qv[nt][st], s0);
       }
       const int qi = 32 * nt + l32;
@@ -344,8 +343,8 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           const int k0 = 16 * ks + 4 * hf + (gl >> 2), k1 = k0 + 8;
-          const v4i16 lo = lds_read_tr16(vl + k0 * kD + 8 * ((dim >> 3) ^ (k0 % 16)) + (dim & 7));
-          const v4i16 hi = lds_read_tr16(vl + k1 * kD + 8 * ((dim >> 3) ^ (k1 % 16)) + (dim & 7));
+          const v4i16 lo = lds_read_tr16(vl + k0 * kD + 8 * ((dim >> 3) ^ swz_key128(k0)) + (dim & 7));
+          const v4i16 hi = lds_read_tr16(vl + k1 * kD + 8 * ((dim >> 3) ^ swz_key128(k1)) + (dim & 7));
           const short __attribute__((ext_vector_type(8))) ab = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           o[nt][dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ab), pv[ks], o[nt][dt]);
         }
@@ -360,26 +359,51 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
     }
   }
 
-  // ---- this wave's partial (max, sum, unnormalised output) for its queries
-  float* pw = part + (((int64_t)g * nsplit + split) * kDecWaves + w) * 64 * (kD + 2);
+  // ---- merge the waves of this workgroup through LDS (tile buffers are free now),
+  //      then write the range's partial (max, sum, unnormalised output)
+  __syncthreads();
+  float* red_o = reinterpret_cast<float*>(&L[0]);       // [wave][query 64][kD]
+  float* red_ml = reinterpret_cast<float*>(&mask_s[0]);  // [wave][query 64][2]
+  static_assert(sizeof(L) >= kDecWaves * 64 * kD * sizeof(float), "LDS reuse");
+  static_assert(sizeof(mask_s) >= kDecWaves * 64 * 2 * sizeof(float), "LDS reuse");
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
     const int qi = 32 * nt + l32;
     if (qi < nq) {
-      float* pp = pw + qi * (kD + 2);
       if (hf == 0) {
-        pp[0] = m[nt];
-        pp[1] = l[nt];
+        red_ml[(w * 64 + qi) * 2] = m[nt];
+        red_ml[(w * 64 + qi) * 2 + 1] = l[nt];
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) pp[2 + 32 * dt + 8 * (r / 4) + 4 * hf + (r % 4)] = o[nt][dt][r];
+        for (int r = 0; r < 16; ++r) red_o[(w * 64 + qi) * kD + 32 * dt + 8 * (r / 4) + 4 * hf + (r % 4)] = o[nt][dt][r];
+    }
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < nq * kD; e += blockDim.x) {
+    const int qi = e / kD, d = e % kD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, red_ml[(ww * 64 + qi) * 2]);
+    const float Mu = M == -INFINITY ? 0.f : M;
+    float Ls = 0.f, Os = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < kDecWaves; ++ww) {
+      const float f = fast_exp2(red_ml[(ww * 64 + qi) * 2] - Mu);
+      Ls += red_ml[(ww * 64 + qi) * 2 + 1] * f;
+      Os += red_o[(ww * 64 + qi) * kD + d] * f;
+    }
+    float* pp = part + (((int64_t)g * nsplit + split) * 64 + qi) * (kD + 2);
+    pp[2 + d] = Os;
+    if (d == 0) {
+      pp[0] = M;
+      pp[1] = Ls;
     }
   }
 }
 
-// Fixed-order merge of the partials of every (range, wave) slot.
+// Fixed-order merge of the partials of every packed-row range.
 __global__ __launch_bounds__(128) void k_decode_combine(GatherParams p, const float* __restrict__ part, int nslot) {
   const int grp = p.hq / p.hkv;
   const int th = blockIdx.x;  // (t, h)
@@ -388,9 +412,11 @@ __global__ __launch_bounds__(128) void k_decode_combine(GatherParams p, const fl
   const int qi = t * grp + (h - g * grp);
   const int d = threadIdx.x;
   float M = -INFINITY;
+#pragma unroll 8
   for (int s = 0; s < nslot; ++s) M = fmaxf(M, part[(((int64_t)g * nslot + s) * 64 + qi) * (kD + 2)]);
   const float Mu = M == -INFINITY ? 0.f : M;
   float Ls = 0.f, Os = 0.f;
+#pragma unroll 8
   for (int s = 0; s < nslot; ++s) {
     const float* pp = part + (((int64_t)g * nslot + s) * 64 + qi) * (kD + 2);
     const float f = fast_exp2(pp[0] - Mu);
@@ -573,25 +599,20 @@ hipError_t launch_cluster_pack(const int32_t* labels, int64_t hkv, int64_t n, in
 size_t cluster_decode_workspace_bytes(int T, int hq, int hkv, int C, int64_t n_ctx) {
   (void)T;
   (void)hq;
-  return a256((size_t)hkv * C * 8) + a256((size_t)hkv * decode_splits(n_ctx) * kDecWaves * 64 * (kD + 2) * 4);
+  (void)C;
+  return a256((size_t)hkv * decode_splits(n_ctx) * 64 * (kD + 2) * 4);
 }
 
 hipError_t launch_cluster_decode(const GatherParams& p, void* ws, hipStream_t stream) {
   const int nsplit = decode_splits(p.n_ctx);
-  uint64_t* mask = reinterpret_cast<uint64_t*>(ws);
-  float* part = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + a256((size_t)p.hkv * p.C * 8));
-  const int64_t nm = (int64_t)p.hkv * p.C;
-  hipLaunchKernelGGL(k_fill_u64, dim3((unsigned)std::min<int64_t>(1024, (nm + 255) / 256)), dim3(256), 0, stream, mask, nm);
-  const int64_t ns = (int64_t)p.T * p.hq * p.n_sel;
-  hipLaunchKernelGGL(k_decode_mask, dim3((unsigned)((ns + 255) / 256)), dim3(256), 0, stream, p.sel, p.T, p.hq, p.hkv,
-                     p.C, p.n_sel, mask);
+  float* part = reinterpret_cast<float*>(ws);
   const int nq = p.T * (p.hq / p.hkv);
   const dim3 grid(p.hkv * nsplit);
   if (nq <= 32)
-    hipLaunchKernelGGL((k_decode_split<1>), grid, dim3(64 * kDecWaves), 0, stream, p, mask, part, nsplit);
+    hipLaunchKernelGGL((k_decode_split<1>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
   else
-    hipLaunchKernelGGL((k_decode_split<2>), grid, dim3(64 * kDecWaves), 0, stream, p, mask, part, nsplit);
-  hipLaunchKernelGGL(k_decode_combine, dim3(p.T * p.hq), dim3(kD), 0, stream, p, part, nsplit * kDecWaves);
+    hipLaunchKernelGGL((k_decode_split<2>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
+  hipLaunchKernelGGL(k_decode_combine, dim3(p.T * p.hq), dim3(kD), 0, stream, p, part, nsplit);
   return hipGetLastError();
 }
 

@@ -118,9 +118,11 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
 }
 
 // ---------------------------------------------------------------- k_centroid_score
-// One workgroup per (KV head, chunk of 32 centroids).  The chunk's centroids
-// and all queries of the KV head's group sit in LDS; each thread computes
-// (query, centroid) dot products in fp32.
+// One workgroup per (KV head, chunk of 8 centroids), 256 of them at the decode
+// size.  The chunk's centroids and all queries of the KV head's group sit in
+// LDS; each thread computes (query, centroid) dot products in fp32.
+constexpr int kCentChunk = 8;
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q, const float* __restrict__ cent,
                                                         int T_, int hq, int hkv, int C, int D, float scale,
@@ -128,11 +130,11 @@ __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q,
   extern __shared__ float sm[];
   const int grp = hq / hkv;
   const int nq = T_ * grp;
-  const int nchunk = (C + 31) / 32;
-  const int g = blockIdx.x / nchunk, c0 = (blockIdx.x % nchunk) * 32;
-  float* Cs = sm;                 // [32][D+1]
-  float* Qs = sm + 32 * (D + 1);  // [nq][D+1]
-  for (int e = threadIdx.x; e < 32 * D; e += blockDim.x) {
+  const int nchunk = (C + kCentChunk - 1) / kCentChunk;
+  const int g = blockIdx.x / nchunk, c0 = (blockIdx.x % nchunk) * kCentChunk;
+  float* Cs = sm;                         // [kCentChunk][D+1]
+  float* Qs = sm + kCentChunk * (D + 1);  // [nq][D+1]
+  for (int e = threadIdx.x; e < kCentChunk * D; e += blockDim.x) {
     const int c = e / D, d = e % D;
     Cs[c * (D + 1) + d] = (c0 + c < C) ? cent[((int64_t)g * C + c0 + c) * D + d] : 0.f;
   }
@@ -146,11 +148,19 @@ __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q,
     Qs[qi * (D + 1) + d] = v;
   }
   __syncthreads();
-  for (int e = threadIdx.x; e < nq * 32; e += blockDim.x) {
-    const int qi = e / 32, c = e % 32;
+  for (int e = threadIdx.x; e < nq * kCentChunk; e += blockDim.x) {
+    const int qi = e / kCentChunk, c = e % kCentChunk;
     if (c0 + c >= C) continue;
+    const float* qr = Qs + qi * (D + 1);
+    const float* cr = Cs + c * (D + 1);
     float acc = 0.f;
-    for (int d = 0; d < D; ++d) acc = fmaf(Qs[qi * (D + 1) + d], Cs[c * (D + 1) + d], acc);
+    if (D == 128) {
+#pragma unroll
+      for (int d = 0; d < 128; ++d) acc = fmaf(qr[d], cr[d], acc);
+    } else {
+#pragma unroll 8
+      for (int d = 0; d < D; ++d) acc = fmaf(qr[d], cr[d], acc);
+    }
     const int t = qi / grp, h = g * grp + qi % grp;
     out[((int64_t)t * hq + h) * C + c0 + c] = acc * scale;
   }
@@ -191,9 +201,9 @@ hipError_t launch_block_score(const float* pq, const float* pk, int batch, int h
 hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,
                                  int C, int head_dim, float scale, float* out, hipStream_t stream) {
   const int grp = hq / hkv;
-  const size_t lds = (size_t)(32 + T * grp) * (head_dim + 1) * sizeof(float);
+  const size_t lds = (size_t)(kCentChunk + T * grp) * (head_dim + 1) * sizeof(float);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
-  const int nchunk = (C + 31) / 32;
+  const int nchunk = (C + kCentChunk - 1) / kCentChunk;
   const dim3 grid(hkv * nchunk);
   if (q_bf16)
     hipLaunchKernelGGL((k_centroid_score<uint16_t>), grid, dim3(256), lds, stream, (const uint16_t*)q, cent, T,

@@ -33,6 +33,7 @@ namespace {
 constexpr int kBlk = 64;
 constexpr int kThreads = 128;
 constexpr int kMetaMax = 2048 + 128;  // staged block list, or column list + intervals
+constexpr float kSlack = 8.f;         // lazy-rescale threshold, log2 units
 
 // Tile source: either a contiguous key range or a gathered list of columns.
 struct TileRef {
@@ -93,8 +94,19 @@ __device__ __forceinline__ int tile_row(const TileRef& r, const int32_t* cols, i
   return r.gathered ? cols[r.base + s] : r.base + s;
 }
 
+// XOR key of row r: chunk c of row r sits at position c ^ key(r).  For d = 128
+// the key is 4*(r%4) + (r/4)%4: sixteen consecutive rows get distinct keys (a
+// 16-lane K read of one chunk hits 16 different bank groups) and the 4 rows x
+// 4 chunks read by a half-wave of transposing V reads land on 16 different
+// positions.  For d = 64 the key is r % 8.
+template <int D>
+__device__ __forceinline__ int swz_key(int row) {
+  if (D == 128) return swz_key128(row);
+  return row % (D / 8);
+}
+
 // One 64-row tile (K or V) -> LDS, row-major, chunk c of row r at position
-// c ^ (r % CPR).  Each wave issues NI copies of 1 KB.
+// c ^ key(r).  Each wave issues NI copies of 1 KB.
 template <int D>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* gbase, const TileRef& r,
                                          const int32_t* cols, int w, int lane) {
@@ -105,15 +117,48 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* gbase, c
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
     const int row = (w * NI + n) * RPI + lane / CPR;
-    const int c = (lane % CPR) ^ (row % CPR);
-    const uint16_t* src = gbase + (int64_t)tile_row(r, cols, row) * D + 8 * c;
-    dma16(base + (uint32_t)n * 1024u, src);
+    const int c = (lane % CPR) ^ swz_key<D>(row);
+    const uint32_t off = (uint32_t)tile_row(r, cols, row) * (uint32_t)(D * 2) + (uint32_t)(16 * c);
+    dma16_sb(base + (uint32_t)n * 1024u, gbase, off);
   }
 }
 
+// Workgroup -> (head in group, query-block rank, batch x KV head).
+// ORDER 0: each XCD takes one contiguous range of items (a KV head per XCD
+//          when batch x KV heads == 8).
+// ORDER 1: every XCD works on the same KV head at the same time (its K/V then
+//          stays in the 256 MB Infinity Cache), each XCD taking runs of 8
+//          consecutive query blocks so neighbouring rows share their local
+//          blocks in that XCD's L2; needs nqb % 64 == 0.
+#ifndef SA_FWD_ORDER
+#define SA_FWD_ORDER 0
+#endif
+constexpr int kOrder = SA_FWD_ORDER;
+
+template <int ORDER>
+__device__ __forceinline__ void item_of(int bid, int n_items, int grp, int nqb, int& hh, int& ii, int& bg) {
+  if (ORDER == 1 && (nqb % 64) == 0) {
+    const int x = bid % kXcds, slot = bid / kXcds;
+    const int per_bg = (nqb / kXcds) * grp;  // items of one KV head on one XCD
+    bg = slot / per_bg;
+    const int rem = slot % per_bg;
+    hh = rem % grp;
+    const int r8 = (rem / grp) % 8;
+    const int cidx = rem / (8 * grp);
+    ii = (cidx * kXcds + x) * 8 + r8;
+    return;
+  }
+  int rest = xcd_remap(bid, n_items);
+  hh = rest % grp;
+  rest /= grp;
+  ii = rest % nqb;
+  bg = rest / nqb;
+}
+
+// Element offset of 16-byte chunk `chunk` of row `row` in a swizzled tile.
 template <int D>
 __device__ __forceinline__ int swz(int row, int chunk) {
-  return row * D + 8 * (chunk ^ (row % (D / 8)));
+  return row * D + 8 * (chunk ^ swz_key<D>(row));
 }
 
 template <int D, int MODE, bool OUT_BF16>
@@ -123,16 +168,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   __shared__ int32_t meta[MODE == 0 ? 2048 : kMetaMax];
   constexpr int NDMA = D / 16;  // direct-to-LDS copies per wave per tile (K or V)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int n_items = gridDim.x;
-  const int item = xcd_remap(blockIdx.x, n_items);
   const int grp = p.heads_q / p.heads_kv;
-  int rest = item;
-  const int hh = rest % grp;
-  rest /= grp;
-  const int ii = rest % p.nqb;
-  rest /= p.nqb;
-  const int g = rest % p.heads_kv;
-  const int b = rest / p.heads_kv;
+  int hh, ii, bg;
+  item_of<kOrder>(blockIdx.x, gridDim.x, grp, p.nqb, hh, ii, bg);
+  const int g = bg % p.heads_kv;
+  const int b = bg / p.heads_kv;
   const int iblk = p.nqb - 1 - ii;  // long rows first
   const int h = g * grp + hh;
   const int64_t N = p.seq;
@@ -200,12 +240,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
       s0[r] = 0.f;
       s1[r] = 0.f;
     }
+    {
+      // operands of step st+1 are read while step st runs on the matrix core
+      bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(l32, hf)]));
+      bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 + l32, hf)]));
 #pragma unroll
-    for (int st = 0; st < D / 16; ++st) {
-      const bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(l32, 2 * st + hf)]));
-      const bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 + l32, 2 * st + hf)]));
-      s0 = mfma32x32x16(a0, qv[st], s0);
-      s1 = mfma32x32x16(a1, qv[st], s1);
+      for (int st = 0; st < D / 16; ++st) {
+        bf16x8 n0 = a0, n1 = a1;
+        if (st + 1 < D / 16) {
+          n0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(l32, 2 * (st + 1) + hf)]));
+          n1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 + l32, 2 * (st + 1) + hf)]));
+        }
+        s0 = mfma32x32x16(a0, qv[st], s0);
+        s1 = mfma32x32x16(a1, qv[st], s1);
+        a0 = n0;
+        a1 = n1;
+      }
     }
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();  // both waves are done with K(t)
@@ -241,25 +291,32 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
 #pragma unroll
     for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
-    const float mnew = fmaxf(m, mx);
-    const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-    float ps = 0.f;
+    // Lazy rescaling: the reference maximum m only moves when the tile's
+    // maximum exceeds it by more than kSlack (log2 units), so probabilities
+    // stay below 2^kSlack and O / l are rescaled only on such jumps.  The
+    // final O / l and lse use the same m, so the result is exact up to rounding.
+    if (__any(mx > m + kSlack)) {
+      const float mnew = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.f : fast_exp2(m - mnew);
+      if (__any(m != -INFINITY)) {
+        lsum *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
+      m = mnew;
+    }
+    const float muse = (m == -INFINITY) ? 0.f : m;
+    float pp[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
       x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
-      ps += x[r];
+      pp[r & 3] += x[r];
     }
+    float ps = (pp[0] + pp[1]) + (pp[2] + pp[3]);
     ps += __shfl_xor(ps, 32);
-    if (__any(mnew > m)) {  // rescale only when some row maximum grew
-      const float alpha = fast_exp2(m - muse);
-      lsum *= alpha;
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
-    }
     lsum += ps;
-    m = mnew;
 
     // ---- P^T operand for k-step ks = the 8 consecutive registers x[8ks .. 8ks+7]
     bf16x8 pv[4];
@@ -277,14 +334,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
     // lane j points at V[key0 + j/4][dim0 + 4(j%4) .. +3]
     const int gl = lane & 15, gsub = (lane >> 4) & 1;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const int dim = 32 * dt + 16 * gsub + 4 * (gl & 3);
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int dt = 0; dt < D / 32; ++dt) {  // independent accumulators back to back
+        const int dim = 32 * dt + 16 * gsub + 4 * (gl & 3);
         const int k0 = 16 * ks + 4 * hf + (gl >> 2);
-        const int a0 = k0 * D + 8 * ((dim >> 3) ^ (k0 % (D / 8))) + (dim & 7);
+        const int a0 = k0 * D + 8 * ((dim >> 3) ^ swz_key<D>(k0)) + (dim & 7);
         const int k1 = k0 + 8;
-        const int a1 = k1 * D + 8 * ((dim >> 3) ^ (k1 % (D / 8))) + (dim & 7);
+        const int a1 = k1 * D + 8 * ((dim >> 3) ^ swz_key<D>(k1)) + (dim & 7);
         const v4i16 lo = lds_read_tr16(Vl + a0);
         const v4i16 hi = lds_read_tr16(Vl + a1);
         const short __attribute__((ext_vector_type(8))) ab = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};

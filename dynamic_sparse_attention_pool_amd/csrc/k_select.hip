@@ -7,13 +7,13 @@
 // members are a prefix and a suffix of the causal range, the ranked pool is one
 // contiguous range [pb, pe).
 //
-// Method: scores become order-preserving 32-bit keys; an MSB-first radix
-// select (4 passes of 8 bits, LDS histograms) finds the k-th largest key T and
-// how many keys equal to T must be taken; one more pass emits, in index order,
-// the forced members, every pool key > T and the lowest-index keys == T.  The
-// emission order makes the output ascending and breaks ties toward the lower
-// index, which is the required total order.  Rows of up to 4096 candidates are
-// staged in LDS once; longer rows are re-read from memory on every pass.
+// Method: scores become order-preserving 32-bit keys; a radix select finds the
+// k-th largest key T and how many keys equal to T must be taken; one more pass
+// emits, in index order, the forced members, every pool key > T and the
+// lowest-index keys == T.  The emission order makes the output ascending and
+// breaks ties toward the lower index, which is the required total order.
+// Rows of up to 4096 candidates are staged in LDS once; longer rows are read
+// twice (bracketing pass + emission) when the sampled bracket holds.
 #include "common.h"
 #include "launch.h"
 
@@ -37,13 +37,68 @@ __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, u
   return incl - v;
 }
 
+// k-th largest key (1 <= k <= e-b) of key_at(b..e-1): MSB-first radix select
+// with 8-bit digits and LDS histograms.  Returns T and how many keys equal to
+// T belong to the top k.  Called by every thread of the workgroup.
+template <int NT, class KeyAt>
+__device__ void radix_kth(KeyAt key_at, int64_t b, int64_t e, int64_t k, uint32_t* hist, uint32_t* tmp,
+                          uint32_t* shv, uint32_t& T, int64_t& need) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u, pmask = 0u;
+  int64_t remaining = k;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int d = tid; d < 256; d += NT) hist[d] = 0u;
+    __syncthreads();
+    for (int64_t i = b + tid; i < e; i += NT) {
+      const uint32_t kk = key_at(i);
+      if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    // suffix sums over the 256 digits: tmp[t] = keys with digit >= 255-t
+    if (tid < 256) tmp[tid] = hist[255 - tid];
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      uint32_t a = 0u;
+      if (tid < 256 && tid >= off) a = tmp[tid - off];
+      __syncthreads();
+      if (tid < 256) tmp[tid] += a;
+      __syncthreads();
+    }
+    if (tid < 256) {
+      const uint32_t ge = tmp[tid];
+      const uint32_t gt = tid > 0 ? tmp[tid - 1] : 0u;
+      if (gt < (uint32_t)remaining && (uint32_t)remaining <= ge) {
+        shv[0] = 255u - tid;
+        shv[1] = gt;
+      }
+    }
+    __syncthreads();
+    remaining -= shv[1];
+    prefix |= shv[0] << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  T = prefix;
+  need = remaining;
+}
+
+// Row-wise selection.  IN_LDS: the row (<= 4096 candidates) is staged in LDS
+// and ranked there.  Otherwise the threshold comes from a sample: 4096 evenly
+// spaced pool keys bracket the k-th key between two sample ranks, one pass
+// over the row counts the keys above the bracket and gathers the keys inside
+// it into LDS, and the exact threshold is ranked among those.  When the
+// bracket misses (or holds too many keys) a full radix select over the row
+// runs instead, so the result never depends on the sample.
 template <int NT, bool IN_LDS>
 __global__ __launch_bounds__(NT) void k_select(SelectParams p) {
   constexpr int kLdsMax = 4096;
-  __shared__ uint32_t keys[IN_LDS ? kLdsMax : 1];
+  constexpr int kSample = 4096;
+  constexpr int kBand = 8192;
+  __shared__ uint32_t keys[IN_LDS ? kLdsMax : kSample];
+  __shared__ uint32_t band[IN_LDS ? 1 : kBand];
   __shared__ uint32_t hist[256];
   __shared__ uint32_t tmp[NT];
-  __shared__ uint32_t sh_digit, sh_above, sh_nan;
+  __shared__ uint32_t shv[4];
 
   const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
@@ -54,68 +109,75 @@ __global__ __launch_bounds__(NT) void k_select(SelectParams p) {
   const int64_t npool = pe - pb;
   int64_t kr = p.rden > 0 ? ((int64_t)p.rnum * n + p.rden - 1) / p.rden : (int64_t)p.k;
   kr = max((int64_t)0, min(kr, npool));
+  const bool take_all = (kr == npool);
 
-  if (tid == 0) sh_nan = 0u;
+  if (tid < 4) shv[tid] = 0u;
   __syncthreads();
-  bool nan_seen = false;
+  uint32_t T = 0xffffffffu;
+  int64_t need = 0;  // keys equal to T that are taken
   if (IN_LDS) {
+    bool nan_seen = false;
     for (int64_t i = tid; i < n; i += NT) {
       const float f = row[i];
       nan_seen |= is_nan(f);
       keys[i] = order_key(f);
     }
+    if (nan_seen) atomicOr(&shv[2], 1u);
+    __syncthreads();
+    if (kr > 0 && !take_all)
+      radix_kth<NT>([&](int64_t i) { return keys[i]; }, pb, pe, kr, hist, tmp, shv, T, need);
   } else {
-    for (int64_t i = tid; i < n; i += NT) nan_seen |= is_nan(row[i]);
-  }
-  if (nan_seen) atomicOr(&sh_nan, 1u);
-  __syncthreads();
-  if (sh_nan && tid == 0 && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
-
-  auto key_at = [&](int64_t i) -> uint32_t { return IN_LDS ? keys[i] : order_key(row[i]); };
-
-  // ---- threshold: the kr-th largest key of the pool
-  uint32_t T = 0xffffffffu;
-  int64_t need = 0;  // keys equal to T that are taken
-  bool take_all = (kr == npool);
-  if (kr > 0 && !take_all) {
-    uint32_t prefix = 0u, pmask = 0u;
-    int64_t remaining = kr;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int d = tid; d < 256; d += NT) hist[d] = 0u;
+    bool nan_seen = false;
+    if (kr > 0 && !take_all) {
+      // ---- bracket the threshold with a sample of the pool
+      const int ns = (int)min((int64_t)kSample, npool);
+      for (int s = tid; s < ns; s += NT) keys[s] = order_key(row[pb + ((int64_t)s * npool) / ns]);
       __syncthreads();
+      const double frac = (double)kr * ns / (double)npool;
+      const int margin = (int)(3.0 * sqrt(frac)) + 8;
+      const int64_t rk_hi = max((int64_t)1, (int64_t)frac - margin);
+      const int64_t rk_lo = min((int64_t)ns, (int64_t)ceil(frac) + margin);
+      uint32_t hi, lo;
+      int64_t dummy;
+      radix_kth<NT>([&](int64_t i) { return keys[i]; }, 0, ns, rk_hi, hist, tmp, shv, hi, dummy);
+      radix_kth<NT>([&](int64_t i) { return keys[i]; }, 0, ns, rk_lo, hist, tmp, shv, lo, dummy);
+      // ---- one pass: keys above the bracket are counted, keys inside are gathered
+      if (tid == 0) {
+        shv[0] = 0u;  // keys > hi
+        shv[1] = 0u;  // keys in [lo, hi]
+      }
+      __syncthreads();
+      uint32_t above = 0u;
       for (int64_t i = pb + tid; i < pe; i += NT) {
-        const uint32_t kk = key_at(i);
-        if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
-      }
-      __syncthreads();
-      // suffix sums over the 256 digits (counts of keys with digit >= d)
-      if (tid < 256) tmp[tid] = hist[255 - tid];
-      __syncthreads();
-      for (int off = 1; off < 256; off <<= 1) {
-        uint32_t a = 0u;
-        if (tid < 256 && tid >= off) a = tmp[tid - off];
-        __syncthreads();
-        if (tid < 256) tmp[tid] += a;
-        __syncthreads();
-      }
-      // tmp[t] = number of keys with digit >= 255-t
-      if (tid < 256) {
-        const uint32_t ge = tmp[tid];
-        const uint32_t gt = tid > 0 ? tmp[tid - 1] : 0u;
-        if (gt < (uint32_t)remaining && (uint32_t)remaining <= ge) {
-          sh_digit = 255u - tid;
-          sh_above = gt;
+        const float f = row[i];
+        nan_seen |= is_nan(f);
+        const uint32_t kk = order_key(f);
+        if (kk > hi) ++above;
+        else if (kk >= lo) {
+          const uint32_t pos = atomicAdd(&shv[1], 1u);
+          if (pos < (uint32_t)kBand) band[pos] = kk;
         }
       }
+      atomicAdd(&shv[0], above);
       __syncthreads();
-      remaining -= sh_above;
-      prefix |= sh_digit << shift;
-      pmask |= 255u << shift;
+      const int64_t c_hi = shv[0], c_mid = shv[1];
       __syncthreads();
+      if (c_hi < kr && kr <= c_hi + c_mid && c_mid <= kBand) {
+        radix_kth<NT>([&](int64_t i) { return band[i]; }, 0, c_mid, kr - c_hi, hist, tmp, shv, T, need);
+      } else {
+        radix_kth<NT>([&](int64_t i) { return order_key(row[i]); }, pb, pe, kr, hist, tmp, shv, T, need);
+      }
     }
-    T = prefix;
-    need = remaining;
+    // NaN check over the forced members (and over the pool when it was not read)
+    const bool pool_read = kr > 0 && !take_all;
+    for (int64_t i = tid; i < n; i += NT)
+      if (!pool_read || i < pb || i >= pe) nan_seen |= is_nan(row[i]);
+    if (nan_seen) atomicOr(&shv[2], 1u);
+    __syncthreads();
   }
+  if (shv[2] && tid == 0 && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
+
+  auto key_at = [&](int64_t i) -> uint32_t { return IN_LDS ? keys[i] : order_key(row[i]); };
 
   // ---- emission in index order, tiles of NT*4 candidates
   int32_t* out = p.idx + r * p.kmax;
@@ -169,6 +231,60 @@ __global__ __launch_bounds__(NT) void k_select(SelectParams p) {
   if (tid == 0) p.cnt[r] = (int32_t)total;
 }
 
+// Rows of at most 256 candidates (cluster selection): one thread per
+// candidate computes its rank under the total order (higher score first, lower
+// index first on ties) by sweeping the row in LDS; candidates with rank < k are
+// kept and written in index order through a wave-ballot prefix count.
+__global__ __launch_bounds__(256) void k_select_small(SelectParams p) {
+  __shared__ uint32_t keys[256];
+  __shared__ uint32_t wave_cnt[4];
+  __shared__ uint32_t shnan;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float* row = p.scores + r * p.ld;
+  const int n = (int)(p.causal ? min(p.ncand, (r % p.period) + p.offset + 1) : p.ncand);
+  const int pb = min(p.n_sink, n);
+  const int pe = max(pb, n - p.n_local);
+  const int npool = pe - pb;
+  int64_t kr = p.rden > 0 ? ((int64_t)p.rnum * n + p.rden - 1) / p.rden : (int64_t)p.k;
+  kr = max((int64_t)0, min(kr, (int64_t)npool));
+  if (tid == 0) shnan = 0u;
+  float f = 0.f;
+  if (tid < n) {
+    f = row[tid];
+    keys[tid] = order_key(f);
+  }
+  __syncthreads();
+  if (tid < n && is_nan(f)) atomicOr(&shnan, 1u);
+  bool take = false;
+  if (tid < n) {
+    if (tid < pb || tid >= pe) {
+      take = true;
+    } else if (kr > 0) {
+      const uint32_t mine = keys[tid];
+      int rank = 0;
+      for (int j = pb; j < pe; ++j) {
+        const uint32_t kj = keys[j];
+        rank += (kj > mine) | ((kj == mine) & (j < tid));
+      }
+      take = rank < kr;
+    }
+  }
+  const uint64_t bal = __ballot(take);
+  if (lane == 0) wave_cnt[wv] = (uint32_t)__popcll(bal);
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wv; ++w) base += wave_cnt[w];
+  const uint32_t total = wave_cnt[0] + wave_cnt[1] + wave_cnt[2] + wave_cnt[3];
+  int32_t* out = p.idx + r * p.kmax;
+  if (take) out[base + __popcll(bal & ((1ull << lane) - 1ull))] = tid;
+  for (int j = (int)total + tid; j < p.kmax; j += 256) out[j] = -1;
+  if (tid == 0) {
+    p.cnt[r] = (int32_t)total;
+    if (shnan && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
+  }
+}
+
 // ---------------------------------------------------------------- vertical-slash tables
 // One thread per (row, query block).  Offsets arrive ascending, so walking
 // them backwards yields tile starts 64i-o in ascending order; overlapping or
@@ -218,7 +334,9 @@ __global__ __launch_bounds__(64) void k_vs_build(VsBuildParams p) {
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   if (p.rows == 0) return hipSuccess;
   const dim3 grid((unsigned)p.rows);
-  if (p.ncand <= 4096)
+  if (p.ncand <= 256)
+    hipLaunchKernelGGL(k_select_small, grid, dim3(256), 0, stream, p);
+  else if (p.ncand <= 4096)
     hipLaunchKernelGGL((k_select<256, true>), grid, dim3(256), 0, stream, p);
   else
     hipLaunchKernelGGL((k_select<1024, false>), grid, dim3(1024), 0, stream, p);

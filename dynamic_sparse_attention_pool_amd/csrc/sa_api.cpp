@@ -1,7 +1,7 @@
 // C-ABI layer of libsa: argument validation, workspace sizing and dispatch.
 // Every check runs on the host before any launch; see include/sa.h for the
 // contract of each entry point.
-#include "../../include/sa.h"
+#include "sa.h"
 
 #include <hip/hip_runtime.h>
 
