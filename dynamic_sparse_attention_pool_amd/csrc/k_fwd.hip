@@ -50,6 +50,7 @@ struct TileIter {
   int cnt = 0, t = 0, iblk = 0;
   // vertical-slash mode
   const int32_t* iv = nullptr;
+  const int32_t* col = nullptr;  // ascending column list (optional: without it every column tile is masked)
   int n_iv = 0, cur_iv = 0, cur_off = 0;
   int n_col = 0, col_off = 0;
 
@@ -69,7 +70,8 @@ struct TileIter {
       r.base = s + cur_off;
       r.len = min(kBlk, e - r.base);
       r.gathered = 0;
-      r.diag = 1;
+      // masking only for a short tile or one reaching past the block's first query row
+      r.diag = (r.len < kBlk) || (r.base + r.len - 1 > iblk * kBlk);
       cur_off += kBlk;
       if (s + cur_off >= e) {
         ++cur_iv;
@@ -81,7 +83,7 @@ struct TileIter {
       r.base = col_off;
       r.len = min(kBlk, n_col - col_off);
       r.gathered = 1;
-      r.diag = 1;
+      r.diag = (r.len < kBlk) || col == nullptr || (col[r.base + r.len - 1] > iblk * kBlk);
       col_off += kBlk;
       return true;
     }
@@ -124,20 +126,16 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* gbase, c
 }
 
 // Workgroup -> (head in group, query-block rank, batch x KV head).
-// ORDER 0: each XCD takes one contiguous range of items (a KV head per XCD
+// order 0: each XCD takes one contiguous range of items (a KV head per XCD
 //          when batch x KV heads == 8).
-// ORDER 1: every XCD works on the same KV head at the same time (its K/V then
-//          stays in the 256 MB Infinity Cache), each XCD taking runs of 8
-//          consecutive query blocks so neighbouring rows share their local
-//          blocks in that XCD's L2; needs nqb % 64 == 0.
-#ifndef SA_FWD_ORDER
-#define SA_FWD_ORDER 0
-#endif
-constexpr int kOrder = SA_FWD_ORDER;
-
-template <int ORDER>
-__device__ __forceinline__ void item_of(int bid, int n_items, int grp, int nqb, int& hh, int& ii, int& bg) {
-  if (ORDER == 1 && (nqb % 64) == 0) {
+// order 1: every XCD works on the same KV head at the same time, so the K/V
+//          being read stays in the 256 MB Infinity Cache even when all heads'
+//          K/V do not fit; each XCD takes runs of 8 consecutive query blocks
+//          (neighbouring rows share their local blocks in that XCD's L2).
+//          Needs nqb % 64 == 0 and the item count a multiple of 8.
+__device__ __forceinline__ void item_of(int bid, int n_items, int grp, int nqb, int order, int& hh, int& ii,
+                                        int& bg) {
+  if (order == 1) {
     const int x = bid % kXcds, slot = bid / kXcds;
     const int per_bg = (nqb / kXcds) * grp;  // items of one KV head on one XCD
     bg = slot / per_bg;
@@ -170,7 +168,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
   const int grp = p.heads_q / p.heads_kv;
   int hh, ii, bg;
-  item_of<kOrder>(blockIdx.x, gridDim.x, grp, p.nqb, hh, ii, bg);
+  item_of(blockIdx.x, gridDim.x, grp, p.nqb, p.order, hh, ii, bg);
   const int g = bg % p.heads_kv;
   const int b = bg / p.heads_kv;
   const int iblk = p.nqb - 1 - ii;  // long rows first
@@ -202,7 +200,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
     it.iv = meta;
     it.n_iv = niv;
     it.n_col = ncol;
+    it.iblk = iblk;
     cols = meta + 128;
+    it.col = cols;
   }
 
   // Q^T operand: lane holds query row 32w+l32, dims 16s+8hf .. +7 of step s
@@ -475,10 +475,15 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, 
   const int n_items = p.batch * p.heads_q * p.nqb;
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items);
+  // KV-head-major order once the K/V of all heads (bf16) outgrows ~192 MB,
+  // i.e. no longer fits the Infinity Cache beside everything else.
+  const double kv_bytes = 4.0 * p.batch * p.heads_kv * (double)p.seq * head_dim;
+  FwdParams pp = p;
+  pp.order = (in_bf16 && p.nqb % 64 == 0 && n_items % kXcds == 0 && kv_bytes > 192.0 * (1 << 20)) ? 1 : 0;
   if (in_bf16) {
 #define SA_FWD_CASE(D_, M_, OB_)                                                   \
   if (head_dim == D_ && mode == M_ && out_bf16 == OB_) {                           \
-    hipLaunchKernelGGL((k_fwd_bf16<D_, M_, OB_>), grid, dim3(kThreads), 0, stream, p); \
+    hipLaunchKernelGGL((k_fwd_bf16<D_, M_, OB_>), grid, dim3(kThreads), 0, stream, pp); \
     return hipGetLastError();                                                      \
   }
     SA_FWD_CASE(128, 0, true)

@@ -24,6 +24,7 @@ struct FwdParams {
   int32_t batch, heads_q, heads_kv, nqb;
   int32_t kmax, max_iv, max_col;
   float scale;
+  int32_t order;  // workgroup order of the bf16 kernel, chosen by launch_fwd
 };
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, bool out_bf16,
                       hipStream_t stream);

@@ -354,6 +354,7 @@ int sa_block_sparse_fwd(const sa_fwd_args* a, void* workspace, size_t workspace_
   p.max_iv = a->max_iv;
   p.max_col = a->max_col;
   p.scale = a->scale;
+  p.order = 0;
   return launched(sa::launch_fwd(p, (int)a->head_dim, a->mode, a->dtype == SA_BF16, a->out_dtype == SA_BF16,
                                  as_stream(stream)),
                   "sa_block_sparse_fwd");
