@@ -20,33 +20,51 @@
 namespace sa {
 namespace {
 
+// Inclusive prefix sum within a wave (64 lanes, all active).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t x = __shfl_up(v, off);
+    if (lane >= off) v += x;
+  }
+  return v;
+}
+
+// Exclusive prefix sum over the workgroup (wave scans, then the wave totals).
 template <int NT>
 __device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* tmp, uint32_t& total) {
-  const int tid = threadIdx.x;
-  tmp[tid] = v;
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const uint32_t incl = wave_incl_scan(v);
+  if ((tid & 63) == 63) tmp[wv] = incl;
   __syncthreads();
-  for (int off = 1; off < NT; off <<= 1) {
-    const uint32_t a = tid >= off ? tmp[tid - off] : 0u;
-    __syncthreads();
-    tmp[tid] += a;
-    __syncthreads();
+  uint32_t before = 0u, all = 0u;
+#pragma unroll
+  for (int j = 0; j < NW; ++j) {
+    const uint32_t x = tmp[j];
+    before += j < wv ? x : 0u;
+    all += x;
   }
-  const uint32_t incl = tmp[tid];
-  total = tmp[NT - 1];
+  total = all;
   __syncthreads();
-  return incl - v;
+  return before + incl - v;
 }
 
 // k-th largest key (1 <= k <= e-b) of key_at(b..e-1): MSB-first radix select
 // with 8-bit digits and LDS histograms.  Returns T and how many keys equal to
 // T belong to the top k.  Called by every thread of the workgroup.
+// With top_shift < 24 the caller guarantees that all keys share their bits
+// above top_shift + 8 with `known` (e.g. keys inside a bracket [lo, hi]); those
+// digits are not counted again.
 template <int NT, class KeyAt>
 __device__ void radix_kth(KeyAt key_at, int64_t b, int64_t e, int64_t k, uint32_t* hist, uint32_t* tmp,
-                          uint32_t* shv, uint32_t& T, int64_t& need) {
+                          uint32_t* shv, uint32_t& T, int64_t& need, int top_shift = 24, uint32_t known = 0u) {
   const int tid = threadIdx.x;
-  uint32_t prefix = 0u, pmask = 0u;
+  uint32_t pmask = top_shift >= 24 ? 0u : ~((1u << (top_shift + 8)) - 1u);
+  uint32_t prefix = known & pmask;
   int64_t remaining = k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  for (int shift = top_shift; shift >= 0; shift -= 8) {
     for (int d = tid; d < 256; d += NT) hist[d] = 0u;
     __syncthreads();
     for (int64_t i = b + tid; i < e; i += NT) {
@@ -54,19 +72,20 @@ __device__ void radix_kth(KeyAt key_at, int64_t b, int64_t e, int64_t k, uint32_
       if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
     }
     __syncthreads();
-    // suffix sums over the 256 digits: tmp[t] = keys with digit >= 255-t
-    if (tid < 256) tmp[tid] = hist[255 - tid];
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-      uint32_t a = 0u;
-      if (tid < 256 && tid >= off) a = tmp[tid - off];
-      __syncthreads();
-      if (tid < 256) tmp[tid] += a;
-      __syncthreads();
-    }
+    // suffix sums over the 256 digits (thread t: keys with digit >= 255-t),
+    // by the first four waves
+    uint32_t v = 0u, incl = 0u;
     if (tid < 256) {
-      const uint32_t ge = tmp[tid];
-      const uint32_t gt = tid > 0 ? tmp[tid - 1] : 0u;
+      v = hist[255 - tid];
+      incl = wave_incl_scan(v);
+      if ((tid & 63) == 63) tmp[tid >> 6] = incl;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      uint32_t before = 0u;
+      for (int j = 0; j < (tid >> 6); ++j) before += tmp[j];
+      const uint32_t ge = before + incl;
+      const uint32_t gt = ge - v;
       if (gt < (uint32_t)remaining && (uint32_t)remaining <= ge) {
         shv[0] = 255u - tid;
         shv[1] = gt;
@@ -231,6 +250,271 @@ __global__ __launch_bounds__(NT) void k_select(SelectParams p) {
   if (tid == 0) p.cnt[r] = (int32_t)total;
 }
 
+// Exclusive prefix sums of two counters over the workgroup: wave scans by
+// lane shuffles, then one pass over the wave totals.
+template <int NT>
+__device__ __forceinline__ void block_excl_scan2(uint32_t a, uint32_t b, uint32_t* wsum, uint32_t& ea, uint32_t& eb,
+                                                 uint32_t& ta, uint32_t& tb) {
+  constexpr int NW = NT / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  uint32_t ia = a, ib = b;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint32_t xa = __shfl_up(ia, off), xb = __shfl_up(ib, off);
+    if (lane >= off) {
+      ia += xa;
+      ib += xb;
+    }
+  }
+  if (lane == 63) {
+    wsum[2 * wv] = ia;
+    wsum[2 * wv + 1] = ib;
+  }
+  __syncthreads();
+  uint32_t pa = 0u, pb = 0u, sa = 0u, sb = 0u;
+  for (int j = 0; j < NW; ++j) {
+    const uint32_t va = wsum[2 * j], vb = wsum[2 * j + 1];
+    if (j < wv) {
+      pa += va;
+      pb += vb;
+    }
+    sa += va;
+    sb += vb;
+  }
+  ea = pa + ia - a;
+  eb = pb + ib - b;
+  ta = sa;
+  tb = sb;
+  __syncthreads();
+}
+
+// Long rows (4096 < candidates <= kBmMax), read once.  A sample of 256 runs of
+// 16 consecutive pool keys (a few cache lines, not the whole row) brackets the
+// k-th key; one pass over the row marks the keys above the bracket in an LDS
+// bitmap and gathers (key, index) of the keys inside it; the exact threshold T
+// is ranked among those, keys > T join the bitmap and keys == T go to a tie
+// bitmap.  Emission walks the bitmaps in index order with one prefix sum, so
+// the row is not read again.  When the bracket misses, the threshold comes
+// from a radix select over the row and one more pass fills the bitmaps.
+constexpr int kBmMax = 131072;
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_select_long(SelectParams p) {
+  constexpr int kSample = 4096, kRun = 16, kBand = 4096, kWords = kBmMax / 32;
+  // ~69 KB of LDS: two workgroups per CU, so one's ranking overlaps the other's pass
+  __shared__ uint32_t keys[kSample];  // the sample, then the band's keys
+  uint32_t* bk = keys;
+  __shared__ int32_t bi[kBand];
+  __shared__ uint32_t selbm[kWords];
+  __shared__ uint32_t tiebm[kWords];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t tmp[NT];
+  __shared__ uint32_t shv[4];
+
+  const int tid = threadIdx.x;
+  const int64_t r = blockIdx.x;
+  const float* row = p.scores + r * p.ld;
+  const int n = (int)(p.causal ? min(p.ncand, (r % p.period) + p.offset + 1) : p.ncand);
+  const int pb = min(p.n_sink, n);
+  const int pe = max(pb, n - p.n_local);
+  const int npool = pe - pb;
+  int64_t kr = p.rden > 0 ? ((int64_t)p.rnum * n + p.rden - 1) / p.rden : (int64_t)p.k;
+  kr = max((int64_t)0, min(kr, (int64_t)npool));
+  const bool take_all = (kr == npool);
+  const int nw = (n + 31) / 32;
+  const bool aligned = (p.ld % 4) == 0 && (reinterpret_cast<uintptr_t>(p.scores) & 15) == 0;
+
+  for (int w = tid; w < nw; w += NT) {
+    selbm[w] = 0u;
+    tiebm[w] = 0u;
+  }
+  if (tid < 4) shv[tid] = 0u;
+  __syncthreads();
+
+  bool nan_seen = false;
+  uint32_t T = 0xffffffffu;
+  int64_t need = 0;  // keys equal to T that are taken
+  if (kr > 0 && !take_all) {
+    // ---- bracket the threshold with a sample of the pool
+    int ns;
+    if (npool >= 2 * kSample) {
+      ns = kSample;
+      constexpr int nrun = kSample / kRun;
+      for (int s = tid; s < ns; s += NT) {
+        const int c = s / kRun;
+        const int at = pb + (int)(((int64_t)c * (npool - kRun)) / (nrun - 1)) + s % kRun;
+        keys[s] = order_key(row[at]);
+      }
+    } else {
+      ns = min(kSample, npool);
+      for (int s = tid; s < ns; s += NT) keys[s] = order_key(row[pb + ((int64_t)s * npool) / ns]);
+    }
+    __syncthreads();
+    const double frac = (double)kr * ns / (double)npool;
+    const int margin = (int)(3.0 * sqrt(frac)) + 8;
+    const int64_t rk_hi = max((int64_t)1, (int64_t)frac - margin);
+    const int64_t rk_lo = min((int64_t)ns, (int64_t)ceil(frac) + margin);
+    uint32_t hi, lo;
+    int64_t dummy;
+    radix_kth<NT>([&](int64_t i) { return keys[i]; }, 0, ns, rk_hi, hist, tmp, shv, hi, dummy);
+    radix_kth<NT>([&](int64_t i) { return keys[i]; }, 0, ns, rk_lo, hist, tmp, shv, lo, dummy);
+    if (tid == 0) {
+      shv[0] = 0u;  // keys > hi
+      shv[1] = 0u;  // keys in [lo, hi]
+    }
+    __syncthreads();
+    // ---- the one pass over the pool.  Per key: its order key, a running
+    // min / max of the keys (a NaN maps outside [key(-inf), key(+inf)]) and one
+    // compare; only keys >= lo (a few percent) take the slow branch.
+    uint32_t above = 0u, kmin = 0xffffffffu, kmax_ = 0u;
+    auto slow = [&](int i, uint32_t kk) {
+      if (kk > hi) {
+        ++above;
+        atomicOr(&selbm[i >> 5], 1u << (i & 31));
+      } else {
+        const uint32_t pos = atomicAdd(&shv[1], 1u);
+        if (pos < (uint32_t)kBand) {
+          bk[pos] = kk;
+          bi[pos] = i;
+        }
+      }
+    };
+    if (aligned) {
+      // 16-byte loads, 4 per thread in flight; the 4-aligned chunks covering
+      // [pb, pe) stay inside the row's ld (a multiple of 4)
+      const int c0 = pb >> 2, c1 = (pe + 3) >> 2;
+      const f32x4* row4 = reinterpret_cast<const f32x4*>(row);
+      for (int cb = c0 + tid; cb < c1; cb += 4 * NT) {
+        f32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = cb + u * NT;
+          if (c < c1) v[u] = row4[c];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int c = cb + u * NT;
+          if (c < c1) {
+            const bool inner = 4 * c >= pb && 4 * c + 3 < pe;
+            uint32_t kk[4];
+            bool hit = false;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              kk[e] = order_key(v[u][e]);
+              const bool in = inner || (4 * c + e >= pb && 4 * c + e < pe);
+              if (in) {
+                kmin = min(kmin, kk[e]);
+                kmax_ = max(kmax_, kk[e]);
+                hit |= kk[e] >= lo;
+              }
+            }
+            if (hit) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const int i = 4 * c + e;
+                if (kk[e] >= lo && i >= pb && i < pe) slow(i, kk[e]);
+              }
+            }
+          }
+        }
+      }
+    } else {
+      for (int ib = pb + tid; ib < pe; ib += 8 * NT) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = ib + u * NT;
+          if (i < pe) v[u] = row[i];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = ib + u * NT;
+          if (i < pe) {
+            const uint32_t kk = order_key(v[u]);
+            kmin = min(kmin, kk);
+            kmax_ = max(kmax_, kk);
+            if (kk >= lo) slow(i, kk);
+          }
+        }
+      }
+    }
+    // order keys of -inf and +inf: anything outside is a NaN
+    nan_seen |= kmin < 0x007fffffu || kmax_ > 0xff800000u;
+    atomicAdd(&shv[0], above);
+    __syncthreads();
+    const int64_t c_hi = shv[0], c_mid = shv[1];
+    __syncthreads();
+    if (c_hi < kr && kr <= c_hi + c_mid && c_mid <= kBand) {
+      // band keys lie in [lo, hi]: they share every bit above the first one where lo and hi differ
+      const int top = lo == hi ? 0 : ((31 - __builtin_clz(lo ^ hi)) / 8) * 8;
+      radix_kth<NT>([&](int64_t i) { return bk[i]; }, 0, c_mid, kr - c_hi, hist, tmp, shv, T, need, top, lo);
+      for (int j = tid; j < (int)c_mid; j += NT) {
+        const int i = bi[j];
+        if (bk[j] > T) atomicOr(&selbm[i >> 5], 1u << (i & 31));
+        else if (bk[j] == T) atomicOr(&tiebm[i >> 5], 1u << (i & 31));
+      }
+    } else {
+      // bracket missed: exact threshold over the whole pool, then the bitmaps afresh
+      radix_kth<NT>([&](int64_t i) { return order_key(row[i]); }, pb, pe, kr, hist, tmp, shv, T, need);
+      for (int w = tid; w < nw; w += NT) selbm[w] = 0u;
+      __syncthreads();
+      for (int i = pb + tid; i < pe; i += NT) {
+        const uint32_t kk = order_key(row[i]);
+        if (kk > T) atomicOr(&selbm[i >> 5], 1u << (i & 31));
+        else if (kk == T) atomicOr(&tiebm[i >> 5], 1u << (i & 31));
+      }
+    }
+  } else if (take_all) {
+    for (int i = pb + tid; i < pe; i += NT) atomicOr(&selbm[i >> 5], 1u << (i & 31));
+  }
+  // forced members (and the NaN check over everything the pass did not read)
+  const bool pool_read = kr > 0 && !take_all;
+  for (int i = tid; i < pb; i += NT) {
+    atomicOr(&selbm[i >> 5], 1u << (i & 31));
+    nan_seen |= is_nan(row[i]);
+  }
+  for (int i = pe + tid; i < n; i += NT) {
+    atomicOr(&selbm[i >> 5], 1u << (i & 31));
+    nan_seen |= is_nan(row[i]);
+  }
+  if (!pool_read)
+    for (int i = pb + tid; i < pe; i += NT) nan_seen |= is_nan(row[i]);
+  if (nan_seen) atomicOr(&shv[2], 1u);
+  __syncthreads();
+  if (shv[2] && tid == 0 && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
+
+  // ---- emission in index order: thread t owns words [t*wpt, (t+1)*wpt)
+  const int wpt = (nw + NT - 1) / NT;
+  const int w0 = min(nw, tid * wpt), w1 = min(nw, w0 + wpt);
+  uint32_t cs = 0u, ce = 0u;
+  for (int w = w0; w < w1; ++w) {
+    cs += __popc(selbm[w]);
+    ce += __popc(tiebm[w]);
+  }
+  uint32_t g_before, e_before, tot_s, tot_e;
+  block_excl_scan2<NT>(cs, ce, tmp, g_before, e_before, tot_s, tot_e);
+  int32_t* out = p.idx + r * p.kmax;
+  for (int w = w0; w < w1; ++w) {
+    const uint32_t sw = selbm[w], tw = tiebm[w];
+    uint32_t mbits = sw | tw;
+    while (mbits) {
+      const int bit = __builtin_ctz(mbits);
+      mbits &= mbits - 1u;
+      const int i = 32 * w + bit;
+      if ((sw >> bit) & 1u) {
+        out[g_before + (uint32_t)min((int64_t)e_before, need)] = i;
+        ++g_before;
+      } else {
+        if ((int64_t)e_before < need) out[g_before + e_before] = i;
+        ++e_before;
+      }
+    }
+  }
+  const int64_t total = (int64_t)tot_s + min((int64_t)tot_e, need);
+  for (int64_t j = total + tid; j < p.kmax; j += NT) out[j] = -1;
+  if (tid == 0) p.cnt[r] = (int32_t)total;
+}
+
 // Rows of at most 256 candidates (cluster selection): one thread per
 // candidate computes its rank under the total order (higher score first, lower
 // index first on ties) by sweeping the row in LDS; candidates with rank < k are
@@ -338,6 +622,8 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
     hipLaunchKernelGGL(k_select_small, grid, dim3(256), 0, stream, p);
   else if (p.ncand <= 4096)
     hipLaunchKernelGGL((k_select<256, true>), grid, dim3(256), 0, stream, p);
+  else if (p.ncand <= kBmMax)
+    hipLaunchKernelGGL((k_select_long<1024>), grid, dim3(1024), 0, stream, p);
   else
     hipLaunchKernelGGL((k_select<1024, false>), grid, dim3(1024), 0, stream, p);
   return hipGetLastError();

@@ -125,7 +125,9 @@ int sa_estimate(const sa_estimate_args* args, void* workspace, size_t workspace_
  * article, §长文本的算力困境).  Local and global members are always attended
  * ("稀疏注意力机制解析" explainer, §1.2), which gives the forced sets.
  *
- * scores: [rows, ld] float, row r reads scores[r*ld + 0 .. n_r-1].
+ * scores: [rows, ld] float (the whole rows*ld buffer must be allocated), row r
+ *   uses scores[r*ld + 0 .. n_r-1]; rows longer than 4096 candidates may also
+ *   read, and ignore, up to 3 further entries of the same row.
  * Candidates of row r: 0 .. n_r-1 with
  *     n_r = causal ? min(ncand, (r % causal_period) + causal_offset + 1) : ncand
  * Forced (always kept, not counted in k): 0 .. min(n_sink,n_r)-1 and

@@ -65,7 +65,7 @@ def test_select_bit_exact_lds_rows(sa, case):
         assert np.all(idx[r, cnt[r]:] == -1)
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "coarse"])
 def test_select_bit_exact_long_rows(sa, kind):
     # indexer-like causal rows (ragged lengths) and vertical/slash-like full rows
     R, n = 6, 131072
@@ -79,6 +79,20 @@ def test_select_bit_exact_long_rows(sa, kind):
         for r in range(R):
             assert cnt[r] == len(want[r])
             assert np.array_equal(idx[r, :cnt[r]], want[r])
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties"])
+def test_select_rows_longer_than_one_bitmap(sa, kind):
+    # past 131072 candidates the two-pass kernel takes over
+    R, n = 3, 140000
+    print(f"select beyond bitmap {kind}", flush=True)
+    s = W.score_rows(10, R, n, kind)
+    for kw, kmax in [(dict(k=500), 500), (dict(k=2048, causal=True, causal_period=R, causal_offset=n - R), 2048)]:
+        idx, cnt, err = gpu_select(sa, s, kmax, **kw)
+        want = oracle_select(s, **kw)
+        assert err == 0
+        for r in range(R):
+            assert cnt[r] == len(want[r]) and np.array_equal(idx[r, :cnt[r]], want[r])
 
 
 def test_select_ragged_long_rows_and_nan_flag(sa):

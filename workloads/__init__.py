@@ -277,11 +277,14 @@ def mqa_layer(seed: int, layer: int, T: int, Hq: int, Hkv: int, Nctx: int, d: in
 # ---------------------------------------------------------------- raw score rows
 def score_rows(seed: int, R: int, n: int, kind: str = "normal", *path: int) -> np.ndarray:
     """float32 score rows for selection tests: 'normal' (continuous),
-    'ties' (few distinct values, many exact ties, signed zeros included)."""
+    'ties' (few distinct values, many exact ties, signed zeros included),
+    'coarse' (normal values rounded to multiples of 1/16)."""
     r = rng(seed, S_TOPK, *path)
     if kind == "normal":
         return r.standard_normal((R, n), dtype=np.float32)
     if kind == "ties":
         vals = np.array([-2.0, -1.0, -0.0, 0.0, 0.5, 1.0, 3.0], np.float32)
         return vals[r.integers(0, len(vals), size=(R, n))]
+    if kind == "coarse":  # normal values on a 1/16 grid: runs of equal keys around any threshold
+        return (np.round(r.standard_normal((R, n), dtype=np.float32) * 16) / 16).astype(np.float32)
     raise ValueError(kind)
