@@ -4,9 +4,10 @@
 // (query, key) pair, and its quadratic cost becomes the prefill bottleneck.
 // Score of the synthetic workload: I[t,s] = sum_h w_h * ReLU(q[t,h] . k[s]).
 // The contraction q[t,h] . k[s] is a dense GEMM per head; the ReLU sits
-// between it and the sum over heads, so each head's 64x32 tile is finished
-// in registers (max, then FMA with w_h) before the next head.  Eight waves
-// split the indexer heads and reduce their partial sums through LDS.
+// between it and the sum over heads, so each head's tile is finished in
+// registers (max, then FMA with w_h).  With 32 or 64 heads the heads lie on
+// the matrix rows (k_indexer2); other head counts split the heads over eight
+// waves that reduce their partial sums through LDS (k_indexer).
 //
 // "MInference 1.0" article, §方法介紹: vertical and slash indices come from
 // the attention of the last queries to every key.  Pass 1 gathers per-chunk
@@ -29,6 +30,10 @@ namespace sa {
 namespace {
 
 // ================================================================ indexer
+// max(x, 0) as one integer max on the bit pattern: every negative float
+// (including -0) is a negative int32; finite inputs only (products of bf16).
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 constexpr int kIdxWaves = 8;
 constexpr int kIdxD = 64;
 constexpr int kIdxChunk = 8192;  // keys per workgroup
@@ -86,8 +91,8 @@ __global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __re
         }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          sum[r] = fmaf(wh[j], fmaxf(a0[r], 0.f), sum[r]);
-          sum[16 + r] = fmaf(wh[j], fmaxf(a1[r], 0.f), sum[16 + r]);
+          sum[r] = fmaf(wh[j], relu_bits(a0[r]), sum[r]);
+          sum[16 + r] = fmaf(wh[j], relu_bits(a1[r]), sum[16 + r]);
         }
       }
       // element (mt, r) is key 32mt + 8(r/4) + 4hf + r%4 of the tile, query l32
@@ -126,6 +131,103 @@ __global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __re
     }
     __syncthreads();
   }
+}
+
+// Heads on the matrix rows.  For a query t the product Q_t . K^T puts the 32
+// heads of a head group on the rows of v_mfma_f32_32x32x16_bf16 and 32 keys on
+// its columns, so each lane holds 16 heads of one key: the ReLU and the
+// weighted sum over heads are 16 in-register FMAs and one exchange with the
+// lane holding the other 16 heads.  A workgroup (8 waves x 4 queries) walks
+// its key range in tiles of 64 keys copied once into LDS (double-buffered) and
+// shared by all waves; there is no cross-wave reduction.  Queries per wave:
+// 4 with one head group, 3 with two (the query operands then fill 96 registers).
+constexpr int kIdx2Waves = 8;
+template <int HG>
+constexpr int idx2_qpw() { return HG == 1 ? 4 : 3; }
+
+// chunk c of row r of a 64 x 128-byte K tile sits at position c ^ ((r >> 1) & 7)
+__device__ __forceinline__ int idx2_swz(int r, int c) { return r * 64 + 8 * (c ^ ((r >> 1) & 7)); }
+
+template <int HG>
+__global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __restrict__ q,
+                                                               const uint16_t* __restrict__ k,
+                                                               const float* __restrict__ w, int T, int Hi,
+                                                               int64_t Nk, int64_t pos0, float* __restrict__ out) {
+  constexpr int kIdx2Qpw = idx2_qpw<HG>(), kIdx2Q = kIdx2Waves * kIdx2Qpw;
+  __shared__ __attribute__((aligned(1024))) uint16_t Kt[2][64 * kIdxD];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int nchunk = (int)((Nk + kIdxChunk - 1) / kIdxChunk);
+  const int tq = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
+  const int t0 = tq * kIdx2Q;
+  const int64_t c0 = (int64_t)ck * kIdxChunk, c1 = std::min(Nk, c0 + kIdxChunk);
+  const int64_t lim_max = pos0 + std::min(t0 + kIdx2Q - 1, T - 1);  // largest causal key of the queries
+  // A operands: query t0 + 4wv + j, head 32g + l32, dims 16s + 8hf .. +7
+  bf16x8 qa[kIdx2Qpw][HG][4];
+#pragma unroll
+  for (int j = 0; j < kIdx2Qpw; ++j) {
+    const int t = std::min(t0 + kIdx2Qpw * wv + j, T - 1);
+#pragma unroll
+    for (int g = 0; g < HG; ++g) {
+      const uint16_t* qr = q + ((int64_t)t * Hi + 32 * g + l32) * kIdxD + 8 * hf;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) qa[j][g][s4] = as_bf16x8(ldg16(qr + 16 * s4));
+    }
+  }
+  // weight of the head on accumulator row r: 32g + 8(r/4) + 4hf + r%4
+  float wr[HG][16];
+#pragma unroll
+  for (int g = 0; g < HG; ++g)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) wr[g][r] = w[32 * g + 8 * (r / 4) + 4 * hf + (r % 4)];
+  drain_vmem();
+
+  const int64_t s_end = std::min(c1, lim_max + 1);  // keys past every query's limit are only written
+  const int ntile = s_end > c0 ? (int)((s_end - c0 + 63) / 64) : 0;
+  // one 1 KB copy per wave: rows 8wv .. 8wv+7 of the tile
+  auto copy = [&](int tl, int buf) {
+    const int r = 8 * wv + lane / 8, c = lane % 8;
+    const int64_t row = std::min(c0 + 64 * (int64_t)tl + r, Nk - 1);
+    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[buf][0]) + (uint32_t)wv * 1024u);
+    dma16(dst, k + row * kIdxD + 8 * (c ^ ((r >> 1) & 7)));
+  };
+  if (ntile > 0) copy(0, 0);
+  for (int tl = 0; tl < ntile; ++tl) {
+    const int buf = tl & 1;
+    wait_vmcnt<0>();
+    __syncthreads();  // tile tl landed for every wave; buffer buf^1 is free
+    if (tl + 1 < ntile) copy(tl + 1, buf ^ 1);
+    const int64_t s0 = c0 + 64 * (int64_t)tl;
+#pragma unroll
+    for (int hv = 0; hv < 2; ++hv) {
+      bf16x8 kb[4];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        kb[s4] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kt[buf][idx2_swz(32 * hv + l32, 2 * s4 + hf)]));
+      const int64_t key = s0 + 32 * hv + l32;
+#pragma unroll
+      for (int j = 0; j < kIdx2Qpw; ++j) {
+        float sum = 0.f;
+#pragma unroll
+        for (int g = 0; g < HG; ++g) {
+          f32x16 acc = mfma32x32x16(qa[j][g][0], kb[0], f32x16{});
+#pragma unroll
+          for (int s4 = 1; s4 < 4; ++s4) acc = mfma32x32x16(qa[j][g][s4], kb[s4], acc);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) sum = fmaf(wr[g][r], relu_bits(acc[r]), sum);
+        }
+        sum += __shfl_xor(sum, 32);
+        const int t = t0 + kIdx2Qpw * wv + j;
+        if (hf == 0 && t < T && key < c1) out[(int64_t)t * Nk + key] = key > pos0 + t ? -INFINITY : sum;
+      }
+    }
+  }
+  // keys of the chunk beyond every query's causal limit
+  for (int64_t sidx = std::max(c0, s_end) + lane; sidx < c1; sidx += 64)
+#pragma unroll
+    for (int j = 0; j < kIdx2Qpw; ++j) {
+      const int t = t0 + kIdx2Qpw * wv + j;
+      if (t < T) out[(int64_t)t * Nk + sidx] = -INFINITY;
+    }
 }
 
 // ================================================================ vertical-slash estimate
@@ -304,6 +406,18 @@ size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
                           int64_t pos0, float* out, hipStream_t stream) {
   const int nchunk = (int)((nk + kIdxChunk - 1) / kIdxChunk);
+  if (hi == 32) {
+    constexpr int nq = kIdx2Waves * idx2_qpw<1>();
+    const dim3 grid2((unsigned)(((T + nq - 1) / nq) * nchunk));
+    hipLaunchKernelGGL((k_indexer2<1>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, pos0, out);
+    return hipGetLastError();
+  }
+  if (hi == 64) {
+    constexpr int nq = kIdx2Waves * idx2_qpw<2>();
+    const dim3 grid2((unsigned)(((T + nq - 1) / nq) * nchunk));
+    hipLaunchKernelGGL((k_indexer2<2>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, pos0, out);
+    return hipGetLastError();
+  }
   const dim3 grid((unsigned)(((T + 31) / 32) * nchunk));
   const int hpw = hi / kIdxWaves;
   switch (hpw) {

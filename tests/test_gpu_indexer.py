@@ -42,7 +42,7 @@ def test_indexer_exact_integer_inputs(sa):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("T,Hi,N", [(80, 64, 20000), (32, 16, 8192), (7, 8, 4096)])
+@pytest.mark.parametrize("T,Hi,N", [(80, 64, 20000), (64, 32, 9000), (32, 16, 8192), (7, 8, 4096)])
 def test_indexer_random(sa, T, Hi, N):
     ind = W.indexer_random(42, T, Hi, 64, N)
     got = gpu_indexer(sa, ind.qi, ind.ki, ind.w, ind.pos0)
