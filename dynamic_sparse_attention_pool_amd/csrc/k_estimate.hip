@@ -117,6 +117,80 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
     }
 }
 
+// 128x128 tile of S per workgroup on the fp32 matrix cores
+// (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation).  The pooled Q
+// and K rows of the tile pass through LDS 32 dimensions at a time, row pitch
+// 34 floats, so the 32 rows x 2 columns read by one MFMA operand hit 64
+// different banks; wave (wi, wj) computes the 64x64 quarter (wi, wj) as 2x2
+// MFMA tiles.  Tiles above the diagonal only write -inf.
+template <int D>
+__global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restrict__ pq, const float* __restrict__ pk,
+                                                          int hq, int hkv, int nb, float scale,
+                                                          float* __restrict__ S) {
+  constexpr int T = 128, DC = 32, P = DC + 2;
+  __shared__ float Qs[T * P];
+  __shared__ float Ks[T * P];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int nbt = (nb + T - 1) / T;
+  const int bh = blockIdx.x / (nbt * nbt);
+  const int tile = blockIdx.x % (nbt * nbt);
+  const int ti = tile / nbt, tj = tile % nbt;
+  const int b = bh / hq, h = bh % hq;
+  const int g = (h * hkv) / hq;
+  float* Sb = S + (int64_t)bh * nb * nb;
+  if (tj > ti) {
+    for (int e = tid; e < T * T; e += 256) {
+      const int i = ti * T + e / T, j = tj * T + e % T;
+      if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = -INFINITY;
+    }
+    return;
+  }
+  const float* Qb = pq + (int64_t)bh * nb * D;
+  const float* Kb = pk + ((int64_t)b * hkv + g) * nb * D;
+  const int wi = wv >> 1, wj = wv & 1;
+  f32x16 acc[2][2] = {};
+  for (int d0 = 0; d0 < D; d0 += DC) {
+    for (int e = tid; e < T * (DC / 4); e += 256) {
+      const int rr = e / (DC / 4), c4 = e % (DC / 4);
+      const int qi = ti * T + rr, kj = tj * T + rr;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      const f32x4 vq = qi < nb ? *reinterpret_cast<const f32x4*>(Qb + (int64_t)qi * D + d0 + 4 * c4) : z;
+      const f32x4 vk = kj < nb ? *reinterpret_cast<const f32x4*>(Kb + (int64_t)kj * D + d0 + 4 * c4) : z;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        Qs[rr * P + 4 * c4 + x] = vq[x];
+        Ks[rr * P + 4 * c4 + x] = vk[x];
+      }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int kk = 0; kk < DC / 2; ++kk) {
+      float qa[2], kb[2];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        qa[m] = Qs[(64 * wi + 32 * m + l32) * P + 2 * kk + hf];  // A[i][k]: row i = l32, k = hf
+        kb[m] = Ks[(64 * wj + 32 * m + l32) * P + 2 * kk + hf];  // B[k][j] = K[j][k]: column j = l32
+      }
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[m], kb[n], acc[m][n], 0, 0, 0);
+    }
+    __syncthreads();
+  }
+  // element r of tile (m, n): row 64wi + 32m + 8(r/4) + 4hf + r%4, column 64wj + 32n + l32
+#pragma unroll
+  for (int m = 0; m < 2; ++m)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int i = ti * T + 64 * wi + 32 * m + 8 * (r / 4) + 4 * hf + (r % 4);
+        const int j = tj * T + 64 * wj + 32 * n + l32;
+        if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = (j <= i) ? acc[m][n][r] * scale : -INFINITY;
+      }
+}
+
 // ---------------------------------------------------------------- k_centroid_score
 // One workgroup per (KV head, chunk of 8 centroids), 256 of them at the decode
 // size.  The chunk's centroids and all queries of the KV head's group sit in
@@ -190,6 +264,18 @@ hipError_t launch_pool(const void* x, int64_t rows, int64_t seq, int head_dim, b
 
 hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, int nb,
                               int head_dim, float scale, float* scores, hipStream_t stream) {
+  if (head_dim == 128 || head_dim == 64) {
+    const int nbt2 = (nb + 127) / 128;
+    const int64_t n2 = (int64_t)batch * hq * nbt2 * nbt2;
+    if (n2 == 0) return hipSuccess;
+    if (head_dim == 128)
+      hipLaunchKernelGGL((k_block_score_mfma<128>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, nb,
+                         scale, scores);
+    else
+      hipLaunchKernelGGL((k_block_score_mfma<64>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, nb,
+                         scale, scores);
+    return hipGetLastError();
+  }
   const int nbt = (nb + 63) / 64;
   const int64_t n = (int64_t)batch * hq * nbt * nbt;
   if (n == 0) return hipSuccess;
