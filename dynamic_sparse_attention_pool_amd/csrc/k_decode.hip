@@ -158,7 +158,7 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 // ================================================================ cluster decode
-constexpr int kDecWaves = 2;
+constexpr int kDecWaves = 4;
 constexpr int kRowsPerSplit = 1024;
 
 int decode_splits(int64_t n_ctx) { return (int)((n_ctx + kRowsPerSplit - 1) / kRowsPerSplit); }
@@ -167,33 +167,33 @@ constexpr int kDecRows = 32;      // rows per tile
 constexpr int kDecMaxC = 1024;    // clusters whose tables are staged in LDS
 
 struct DecWaveLds {
-  uint16_t k[2][kDecRows * kD];   // double-buffered, row-major, chunk-swizzled
-  uint16_t v[2][kDecRows * kD];
+  uint16_t v[2][kDecRows * kD];   // double-buffered V tiles, row-major, chunk-swizzled
   uint64_t rmask[2][kDecRows];    // per row: which queries selected its cluster
 };
 
-// rows -> LDS: 32 rows x 256 B, chunk c of row r at position c ^ key(r);
-// 8 copies of 1 KB per tensor.
-__device__ __forceinline__ void dec_dma(uint16_t* kl, uint16_t* vl, const uint16_t* kb, const uint16_t* vb,
-                                        int64_t base, int len, int lane) {
-  const uint32_t kbase = __builtin_amdgcn_readfirstlane(lds_addr(kl));
+// V rows -> LDS: 32 rows x 256 B, chunk c of row r at position c ^ key(r);
+// 8 copies of 1 KB.
+__device__ __forceinline__ void dec_dma_v(uint16_t* vl, const uint16_t* vb, int64_t base, int len, int lane) {
   const uint32_t vbase = __builtin_amdgcn_readfirstlane(lds_addr(vl));
 #pragma unroll
   for (int n = 0; n < 8; ++n) {
     const int r = 4 * n + lane / 16;
     const int c = (lane % 16) ^ swz_key128(r);
     const int64_t row = base + min(r, len - 1);
-    dma16(kbase + n * 1024u, kb + row * kD + 8 * c);
     dma16(vbase + n * 1024u, vb + row * kD + 8 * c);
   }
 }
 
 // One workgroup per (KV head, packed-row range).  Its waves stream disjoint
-// 32-row tiles independently: each wave double-buffers its tiles in its own
-// LDS region through direct global->LDS copies, so the next tile is in flight
-// while the current one is computed.  NQT = query tiles of 32.
+// 32-row tiles independently.  K rows go straight from memory into the A
+// operand registers of the score product; V tiles go through a per-wave,
+// double-buffered LDS region by direct copies (the transposing LDS reads need
+// them there).  The next tile's K and V are requested right after the current
+// tile's scores, so they are in flight during its softmax and P.V; LDS per
+// wave is 16.5 KB, so two workgroups of four waves share a CU.
+// NQT = query tiles of 32.
 template <int NQT>
-__global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p, float* __restrict__ part, int nsplit) {
+__global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_split(GatherParams p, float* __restrict__ part, int nsplit) {
   __shared__ __attribute__((aligned(1024))) DecWaveLds L[kDecWaves];
   __shared__ int32_t ptr_s[kDecMaxC + 1];
   __shared__ uint64_t mask_s[kDecMaxC];
@@ -231,7 +231,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
 #pragma unroll
     for (int s = 0; s < 8; ++s) qv[nt][s] = as_bf16x8(ldg16(qr + 16 * s));
   }
-  drain_vmem();
   __syncthreads();
 
   f32x16 o[NQT][4];
@@ -247,7 +246,6 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
   }
   DecWaveLds& W = L[w];
 
-  // next selected tile at or after index t (stride kDecWaves); writes its row masks
   // cluster of this lane's row: last c with ptr[c] <= row.  Rows only grow
   // along a wave's tiles, so after one binary search the cluster index
   // advances incrementally.
@@ -262,6 +260,7 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
     }
     cl = lo;
   }
+  // next selected tile at or after index t (stride kDecWaves); writes its row masks
   auto find = [&](int t, int buf) -> int {
     for (; t < ntile; t += kDecWaves) {
       const int64_t base = p0 + (int64_t)t * kDecRows;
@@ -276,19 +275,31 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
     }
     return ntile;
   };
-  auto issue = [&](int t, int buf) {
+  // K operand of tile t: lane row l32, dims 16s + 8hf .. +7 of step s (ordinary
+  // loads: the compiler's wait for them also covers the older V copies)
+  bf16x8 kr[8];
+  auto fetch = [&](int t, int buf) {
     const int64_t base = p0 + (int64_t)t * kDecRows;
-    dec_dma(W.k[buf], W.v[buf], kb, vb, base, (int)min((int64_t)kDecRows, p1 - base), lane);
+    const int len = (int)min((int64_t)kDecRows, p1 - base);
+    dec_dma_v(W.v[buf], vb, base, len, lane);
+    const uint16_t* krow = kb + (base + min(l32, len - 1)) * kD + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kr[s] = as_bf16x8(ldg16(krow + 16 * s));
   };
 
   int cur = find(w, 0), buf = 0;
-  if (cur < ntile) issue(cur, 0);
-  int nxt = cur < ntile ? find(cur + kDecWaves, 1) : ntile;
-  if (nxt < ntile) issue(nxt, 1);
+  if (cur < ntile) fetch(cur, 0);
   while (cur < ntile) {
-    if (nxt < ntile) wait_vmcnt<16>();
-    else wait_vmcnt<0>();
-    const uint16_t* kl = W.k[buf];
+    f32x16 sc[NQT];
+#pragma unroll
+    for (int nt = 0; nt < NQT; ++nt) {
+      sc[nt] = mfma32x32x16(kr[0], qv[nt][0], f32x16{});
+#pragma unroll
+      for (int st = 1; st < 8; ++st) sc[nt] = mfma32x32x16(kr[st], qv[nt][st], sc[nt]);
+    }
+    // next tile: K into the (now free) registers, V into the other buffer
+    const int nxt = find(cur + kDecWaves, buf ^ 1);
+    if (nxt < ntile) fetch(nxt, buf ^ 1);
     const uint16_t* vl = W.v[buf];
     // row masks of the 16 rows this lane's accumulators cover: rows 8j + 4hf + i
     uint64_t rmv[16];
@@ -298,22 +309,13 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
       for (int i = 0; i < 4; ++i) rmv[4 * j + i] = W.rmask[buf][8 * j + 4 * hf + i];
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
-      f32x16 s0;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s0[r] = 0.f;
-#pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int c = 2 * st + hf;
-        const bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&kl[l32 * kD + 8 * (c ^ swz_key128(l32))]));
-        s0 = mfma32x32x16(a, qv[nt][st], s0);
-      }
       const int qi = 32 * nt + l32;
       float x[16];
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const bool keep = qi < nq && ((rmv[r] >> qi) & 1ull);
-        x[r] = keep ? s0[r] : -INFINITY;
+        x[r] = keep ? sc[nt][r] : -INFINITY;
         mx = fmaxf(mx, x[r]);
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
@@ -353,52 +355,51 @@ __global__ __launch_bounds__(64 * kDecWaves) void k_decode_split(GatherParams p,
     wait_lgkm0();  // done reading this buffer before it is refilled
     cur = nxt;
     buf ^= 1;
-    if (cur < ntile) {
-      nxt = find(cur + kDecWaves, buf ^ 1);
-      if (nxt < ntile) issue(nxt, buf ^ 1);
-    }
   }
+  wait_vmcnt<0>();  // every copy this wave issued was consumed; make it explicit before LDS reuse
 
   // ---- merge the waves of this workgroup through LDS (tile buffers are free now),
-  //      then write the range's partial (max, sum, unnormalised output)
-  __syncthreads();
-  float* red_o = reinterpret_cast<float*>(&L[0]);       // [wave][query 64][kD]
-  float* red_ml = reinterpret_cast<float*>(&mask_s[0]);  // [wave][query 64][2]
-  static_assert(sizeof(L) >= kDecWaves * 64 * kD * sizeof(float), "LDS reuse");
-  static_assert(sizeof(mask_s) >= kDecWaves * 64 * 2 * sizeof(float), "LDS reuse");
+  //      one query tile at a time, then write the range's partial
+  //      (max, sum, unnormalised output)
+  float* red_o = reinterpret_cast<float*>(&L[0]);       // [wave][query 32][kD]
+  float* red_ml = reinterpret_cast<float*>(&mask_s[0]);  // [wave][query 32][2]
+  static_assert(sizeof(L) >= kDecWaves * 32 * kD * sizeof(float), "LDS reuse");
+  static_assert(sizeof(mask_s) >= kDecWaves * 32 * 2 * sizeof(float), "LDS reuse");
 #pragma unroll
   for (int nt = 0; nt < NQT; ++nt) {
+    __syncthreads();
     const int qi = 32 * nt + l32;
     if (qi < nq) {
       if (hf == 0) {
-        red_ml[(w * 64 + qi) * 2] = m[nt];
-        red_ml[(w * 64 + qi) * 2 + 1] = l[nt];
+        red_ml[(w * 32 + l32) * 2] = m[nt];
+        red_ml[(w * 32 + l32) * 2 + 1] = l[nt];
       }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red_o[(w * 64 + qi) * kD + 32 * dt + 8 * (r / 4) + 4 * hf + (r % 4)] = o[nt][dt][r];
+        for (int r = 0; r < 16; ++r) red_o[(w * 32 + l32) * kD + 32 * dt + 8 * (r / 4) + 4 * hf + (r % 4)] = o[nt][dt][r];
     }
-  }
-  __syncthreads();
-  for (int e = threadIdx.x; e < nq * kD; e += blockDim.x) {
-    const int qi = e / kD, d = e % kD;
-    float M = -INFINITY;
+    __syncthreads();
+    const int nq_t = min(32, nq - 32 * nt);
+    for (int e = threadIdx.x; e < nq_t * kD; e += blockDim.x) {
+      const int q = e / kD, d = e % kD;
+      float M = -INFINITY;
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, red_ml[(ww * 64 + qi) * 2]);
-    const float Mu = M == -INFINITY ? 0.f : M;
-    float Ls = 0.f, Os = 0.f;
+      for (int ww = 0; ww < kDecWaves; ++ww) M = fmaxf(M, red_ml[(ww * 32 + q) * 2]);
+      const float Mu = M == -INFINITY ? 0.f : M;
+      float Ls = 0.f, Os = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < kDecWaves; ++ww) {
-      const float f = fast_exp2(red_ml[(ww * 64 + qi) * 2] - Mu);
-      Ls += red_ml[(ww * 64 + qi) * 2 + 1] * f;
-      Os += red_o[(ww * 64 + qi) * kD + d] * f;
-    }
-    float* pp = part + (((int64_t)g * nsplit + split) * 64 + qi) * (kD + 2);
-    pp[2 + d] = Os;
-    if (d == 0) {
-      pp[0] = M;
-      pp[1] = Ls;
+      for (int ww = 0; ww < kDecWaves; ++ww) {
+        const float f = fast_exp2(red_ml[(ww * 32 + q) * 2] - Mu);
+        Ls += red_ml[(ww * 32 + q) * 2 + 1] * f;
+        Os += red_o[(ww * 32 + q) * kD + d] * f;
+      }
+      float* pp = part + (((int64_t)g * nsplit + split) * 64 + 32 * nt + q) * (kD + 2);
+      pp[2 + d] = Os;
+      if (d == 0) {
+        pp[0] = M;
+        pp[1] = Ls;
+      }
     }
   }
 }
