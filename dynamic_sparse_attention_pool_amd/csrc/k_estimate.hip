@@ -139,9 +139,17 @@ __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restric
   const int g = (h * hkv) / hq;
   float* Sb = S + (int64_t)bh * nb * nb;
   if (tj > ti) {
-    for (int e = tid; e < T * T; e += 256) {
-      const int i = ti * T + e / T, j = tj * T + e % T;
-      if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = -INFINITY;
+    if ((nb & 3) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {  // 16-byte aligned rows
+      const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      for (int e = tid; e < T * T / 4; e += 256) {
+        const int i = ti * T + e / (T / 4), j = tj * T + 4 * (e % (T / 4));
+        if (i < nb && j < nb) *reinterpret_cast<f32x4*>(Sb + (int64_t)i * nb + j) = ninf;
+      }
+    } else {
+      for (int e = tid; e < T * T; e += 256) {
+        const int i = ti * T + e / T, j = tj * T + e % T;
+        if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = -INFINITY;
+      }
     }
     return;
   }
