@@ -14,6 +14,8 @@
 // breaks ties toward the lower index, which is the required total order.
 // Rows of up to 4096 candidates are staged in LDS once; longer rows are read
 // twice (bracketing pass + emission) when the sampled bracket holds.
+#include <climits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -613,6 +615,83 @@ __global__ __launch_bounds__(64) void k_vs_build(VsBuildParams p) {
   p.col_cnt[gid] = nc;
 }
 
+// The same tables with one wave per (row, query block), for n_slash <= 64.
+// Lane j takes offset index ns-1-j: tile ends 64i-o+64 then ascend with the
+// lane, so a tile starts a new interval exactly when it begins after the
+// previous lane's end; a ballot numbers the intervals.  Columns are taken 64
+// at a time: each lane finds the interval around its column by binary search
+// and a ballot compacts the kept ones in order.
+constexpr int kVbWaves = 4;
+
+__global__ __launch_bounds__(64 * kVbWaves) void k_vs_build_wave(VsBuildParams p) {
+  __shared__ int32_t sb[kVbWaves][64];
+  __shared__ int32_t se[kVbWaves][64];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t nqb = p.seq / p.bs;
+  const int64_t gid = (int64_t)blockIdx.x * kVbWaves + wv;
+  if (gid >= p.rows * nqb) return;  // whole waves only; no workgroup barrier below
+  const int64_t r = gid / nqb;
+  const int i = (int)(gid % nqb);
+  const int32_t* offs = p.slash + r * p.n_slash;
+  const int32_t* cols = p.vert + r * p.n_vert;
+  const int ns = min(p.slash_cnt[r], 64), nv = p.vert_cnt[r];
+  int32_t* iv = p.iv + gid * p.n_slash * 2;
+  int32_t* col = p.col + gid * p.n_vert;
+  const int q0 = i * p.bs;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  // ---- slash tiles -> disjoint intervals
+  int b = 0, e = 0;
+  bool valid = false;
+  if (lane < ns) {
+    const int o = offs[ns - 1 - lane];
+    e = q0 - o + p.bs;
+    valid = e > 0;
+    b = max(0, q0 - o);
+  }
+  const int prev_e = __shfl_up(e, 1);  // every lane takes part in the exchanges
+  const int prev_v = __shfl_up((int)valid, 1);
+  const bool prev_valid = lane > 0 && prev_v != 0;
+  const bool starts = valid && (!prev_valid || b > prev_e);
+  const uint64_t ms = __ballot(starts);
+  const int next_s = __shfl_down((int)starts, 1);
+  const bool next_starts = lane < 63 && next_s != 0;
+  const bool ends = valid && (lane == ns - 1 || next_starts);
+  const int k_here = (int)__popcll(ms & (lt | (1ull << lane))) - 1;  // interval of this lane
+  if (starts) {
+    iv[2 * k_here] = b;
+    sb[wv][k_here] = b;
+  }
+  if (ends) {
+    iv[2 * k_here + 1] = e;
+    se[wv][k_here] = e;
+  }
+  const int niv = (int)__popcll(ms);
+  __builtin_amdgcn_wave_barrier();
+  // ---- kept columns: <= the block's last row and outside every interval
+  const int last = q0 + p.bs - 1;
+  int nc = 0;
+  for (int c0 = 0; c0 < nv; c0 += 64) {
+    const int x = c0 + lane < nv ? cols[c0 + lane] : INT_MAX;
+    const bool in_range = x <= last;
+    int lo = 0, hi = niv;  // intervals with start <= x: [0, lo)
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sb[wv][mid] <= x) lo = mid + 1;
+      else hi = mid;
+    }
+    const bool inside = lo > 0 && x < se[wv][lo - 1];
+    const bool keep = in_range && !inside;
+    const uint64_t mk = __ballot(keep);
+    if (keep) col[nc + (int)__popcll(mk & lt)] = x;
+    nc += (int)__popcll(mk);
+    if (__any(!in_range)) break;  // columns ascend: nothing later is kept
+  }
+  if (lane == 0) {
+    p.iv_cnt[gid] = niv;
+    p.col_cnt[gid] = nc;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
@@ -632,7 +711,11 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
 hipError_t launch_vs_build(const VsBuildParams& p, hipStream_t stream) {
   const int64_t n = p.rows * (p.seq / p.bs);
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_vs_build, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream, p);
+  if (p.n_slash <= 64)
+    hipLaunchKernelGGL(k_vs_build_wave, dim3((unsigned)((n + kVbWaves - 1) / kVbWaves)), dim3(64 * kVbWaves), 0,
+                       stream, p);
+  else
+    hipLaunchKernelGGL(k_vs_build, dim3((unsigned)((n + 63) / 64)), dim3(64), 0, stream, p);
   return hipGetLastError();
 }
 

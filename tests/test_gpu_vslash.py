@@ -44,8 +44,9 @@ def test_vs_estimate(sa, N, d):
         assert abs(host(av)[0, h].sum() - 64) < 1e-3 and abs(host(as_)[0, h].sum() - 64) < 1e-3
 
 
-def test_vs_build_tables_exact(sa):
-    N, R, nv, ns = 4096, 5, 300, 40
+@pytest.mark.parametrize("ns", [40, 64, 100])  # up to 64 offsets: one wave per row; more: one thread per row
+def test_vs_build_tables_exact(sa, ns):
+    N, R, nv = 4096, 5, 300
     r = np.random.default_rng(52)
     cols = [np.sort(r.choice(N, size=nv, replace=False)) for _ in range(R)]
     offs = [np.sort(r.choice(N, size=ns, replace=False)) for _ in range(R)]
