@@ -204,20 +204,37 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
       for (int s4 = 0; s4 < 4; ++s4)
         kb[s4] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kt[buf][idx2_swz(32 * hv + l32, 2 * s4 + hf)]));
       const int64_t key = s0 + 32 * hv + l32;
+      // units u = (query j, head group g); the products of unit u+1 run on the
+      // matrix cores while the ReLU-weighted sum of unit u runs on the VALU
+      constexpr int U = kIdx2Qpw * HG;
+      f32x16 acc[2];
+      auto prod = [&](int u, f32x16& a) {
+        const int j = u / HG, g = u % HG;
+        a = mfma32x32x16(qa[j][g][0], kb[0], f32x16{});
 #pragma unroll
-      for (int j = 0; j < kIdx2Qpw; ++j) {
-        float sum = 0.f;
+        for (int s4 = 1; s4 < 4; ++s4) a = mfma32x32x16(qa[j][g][s4], kb[s4], a);
+      };
+      prod(0, acc[0]);
+      float sum = 0.f;
 #pragma unroll
-        for (int g = 0; g < HG; ++g) {
-          f32x16 acc = mfma32x32x16(qa[j][g][0], kb[0], f32x16{});
+      for (int u = 0; u < U; ++u) {
+        const int j = u / HG, g = u % HG;
+        if (u + 1 < U) prod(u + 1, acc[(u + 1) & 1]);
 #pragma unroll
-          for (int s4 = 1; s4 < 4; ++s4) acc = mfma32x32x16(qa[j][g][s4], kb[s4], acc);
+        for (int r = 0; r < 16; ++r) sum = fmaf(wr[g][r], relu_bits(acc[u & 1][r]), sum);
+        if (u + 1 < U) {
 #pragma unroll
-          for (int r = 0; r < 16; ++r) sum = fmaf(wr[g][r], relu_bits(acc[r]), sum);
+          for (int x = 0; x < 4; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+            __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);  // eight VALU
+          }
         }
-        sum += __shfl_xor(sum, 32);
-        const int t = t0 + kIdx2Qpw * wv + j;
-        if (hf == 0 && t < T && key < c1) out[(int64_t)t * Nk + key] = key > pos0 + t ? -INFINITY : sum;
+        if (g == HG - 1) {
+          const float tot = sum + __shfl_xor(sum, 32);
+          const int t = t0 + kIdx2Qpw * wv + j;
+          if (hf == 0 && t < T && key < c1) out[(int64_t)t * Nk + key] = key > pos0 + t ? -INFINITY : tot;
+          sum = 0.f;
+        }
       }
     }
   }
