@@ -347,6 +347,11 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
     }
+    if traffic is not None:
+        # the same launch seen from DRAM: measured HBM-side bytes over its duration
+        tbps = traffic / (main["ms_forward"] * 1e-3) / 1e12
+        line["roofline"]["traffic_TB_per_s"] = round(tbps, 3)
+        line["roofline"]["traffic_frac_hbm"] = round(tbps * 1e3 / PEAK_HBM_GBS, 4)
     extras = {}
     only = set(x for x in args.only.split(",") if x)
     if not args.no_extras:
