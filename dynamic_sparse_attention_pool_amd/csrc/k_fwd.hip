@@ -11,7 +11,8 @@
 // wave owns 32 query rows.  Per tile:
 //   K and V rows are copied straight from memory into LDS by the direct
 //   global->LDS path (global_load_lds_dwordx4), row-major with the 16-byte
-//   chunks of row r XOR-swizzled by r, so no VGPR staging and no VALU work;
+//   chunks of each row XOR-swizzled by a key of the row index, so no VGPR
+//   staging and no bank conflicts;
 //   S^T[key][query] = K_tile . Q^T          (v_mfma_f32_32x32x16_bf16, K from LDS,
 //                                            Q^T resident in VGPRs)
 //   online softmax along keys: every lane holds one query column, so the row
@@ -21,7 +22,10 @@
 //                                            way out of LDS; P^T comes straight from
 //                                            the S^T accumulators, no shuffles)
 // K(t+1) is fetched while the softmax and P.V of tile t run, V(t+1) while the
-// next S^T runs: one LDS buffer each, four barriers per tile.
+// next S^T runs: one LDS buffer each (40 KB per workgroup, four workgroups per
+// CU), four barriers per tile.  The tile fills, not the matrix cores, bound this
+// kernel: every kept (head, query block, key block) brings its own 32 KB of K
+// and V through L2.
 #include <climits>
 
 #include "common.h"

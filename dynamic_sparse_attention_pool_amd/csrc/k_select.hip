@@ -12,8 +12,10 @@
 // emits, in index order, the forced members, every pool key > T and the
 // lowest-index keys == T.  The emission order makes the output ascending and
 // breaks ties toward the lower index, which is the required total order.
-// Rows of up to 4096 candidates are staged in LDS once; longer rows are read
-// twice (bracketing pass + emission) when the sampled bracket holds.
+// Rows of up to 4096 candidates are staged in LDS once; rows of up to 131072
+// are read once (k_select_long: sampled bracket, selection bitmaps in LDS);
+// longer rows are read twice (bracketing pass + emission) when the sampled
+// bracket holds.
 #include <climits>
 
 #include "common.h"

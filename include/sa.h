@@ -140,8 +140,9 @@ int sa_estimate(const sa_estimate_args* args, void* workspace, size_t workspace_
  *     largest possible count fits kmax (SA_ERR_SHAPE otherwise).
  * err_flag: optional device int32; set to 1 when a candidate score is NaN
  *     (that row's output is then unspecified).  Never cleared by the library.
- * Rows with up to 4096 candidates are ranked in LDS; longer rows (up to 2^24)
- * with a multi-pass radix select that re-reads the row.
+ * Rows with up to 4096 candidates are ranked in LDS; rows with up to 131072
+ * are read once (sampled bracket, LDS bitmaps); longer rows (up to 2^24) are
+ * read twice, or more when the sample does not bracket the k-th score.
  * ====================================================================== */
 typedef struct sa_select_args {
   const float* scores;
