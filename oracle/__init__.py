@@ -12,7 +12,8 @@ Sources (cited by page title and section in each function):
     §延遲和內核中的稀疏模式, Fig. 4 (verticals in 1x64 pieces, slashes in
     64x64 blocks).
   * "Squeezed Attention：基于语义聚类的长上下文LLM推理加速" — §技术方案
-    (query-centroid similarity, top-K clusters, attention over their keys) and
+    (query-centroid similarity, top-K clusters, attention over their keys;
+    the number of clusters adapting to the similarity distribution) and
     §部署建议 (K = sqrt(N) clusters, select 1/4 to 1/2 of them).
   * IndexCache article — §长文本的算力困境 (lightning indexer keeps a token
     subset per layer) and §"偷懒"的艺术 (shared layers copy the nearest full
@@ -25,17 +26,18 @@ them.  Functions with no independent pin say "parity unpinned" in their
 docstring.
 """
 from .select import (candidate_count, forced_set, budget, topk_row, select_rows,
-                     certified_row, ratio_budget)
+                     certified_row, ratio_budget, mass_weights, mass_count, mass_row, mass_margin)
 from .attention import attend_rows, gqa_group
 from .blocksparse import mean_pool, block_scores, block_select, block_sparse_attention
 from .vslash import vs_estimate, vs_select, vs_block_keys, vs_block_tables, vs_attention
-from .cluster import centroid_scores, cluster_select, cluster_pack, cluster_decode
+from .cluster import centroid_scores, cluster_select, cluster_select_mass, cluster_pack, cluster_decode
 from .indexer import indexer_scores, indexer_select, gathered_attention, index_cache_forward
 
 __all__ = [
     "candidate_count", "forced_set", "budget", "topk_row", "select_rows", "certified_row",
-    "ratio_budget", "attend_rows", "gqa_group", "mean_pool", "block_scores", "block_select",
-    "block_sparse_attention", "vs_estimate", "vs_select", "vs_block_keys", "vs_block_tables",
-    "vs_attention", "centroid_scores", "cluster_select", "cluster_pack", "cluster_decode",
+    "ratio_budget", "mass_weights", "mass_count", "mass_row", "mass_margin", "attend_rows",
+    "gqa_group", "mean_pool", "block_scores", "block_select", "block_sparse_attention",
+    "vs_estimate", "vs_select", "vs_block_keys", "vs_block_tables", "vs_attention",
+    "centroid_scores", "cluster_select", "cluster_select_mass", "cluster_pack", "cluster_decode",
     "indexer_scores", "indexer_select", "gathered_attention", "index_cache_forward",
 ]

@@ -14,7 +14,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import attend_rows, gqa_group
-from .select import topk_row
+from .select import topk_row, mass_row
 
 
 def centroid_scores(q: np.ndarray, centroids: np.ndarray, scale: float) -> np.ndarray:
@@ -33,6 +33,13 @@ def cluster_select(s: np.ndarray, k: int):
     """Top-k cluster ids per (t, h), ascending: list[T][Hq]."""
     none = np.zeros(0, np.int64)
     return [[topk_row(s[t, h], k, none) for h in range(s.shape[1])] for t in range(s.shape[0])]
+
+
+def cluster_select_mass(s: np.ndarray, mass: float, k_min: int = 0, k_max: int | None = None):
+    """Adaptive cluster choice per (t, h), ascending: list[T][Hq].  The count
+    follows the softmax of the row's centroid scores (Squeezed Attention page,
+    §技术方案, adaptive cluster selection); the rule is mass_row's."""
+    return [[mass_row(s[t, h], mass, k_min, k_max) for h in range(s.shape[1])] for t in range(s.shape[0])]
 
 
 def cluster_pack(labels: np.ndarray, C: int):

@@ -88,3 +88,57 @@ def certified_row(scores: np.ndarray, k: int, forced: np.ndarray, rel: float = 1
     v = np.sort(s[pool])[::-1]
     scale = np.max(np.abs(s[pool]))
     return bool(v[k - 1] - v[k] > rel * scale)
+
+
+# ---------------------------------------------------------------------------
+# Adaptive budget (Squeezed Attention page, §技术方案, key technical points:
+# the number of clusters kept follows the distribution of the query's centroid
+# similarities).  The page gives no formula; the reading taken here:
+#   * a row's scores are logits; candidate j weighs w_j = exp(s_j - m) with m
+#     the row maximum, and an entry equal to m weighs exactly 1 (so +inf
+#     entries share all the mass and an all -inf row weighs uniformly);
+#   * in the order of topk_row (higher score first, lower index on ties) the
+#     row keeps the shortest prefix whose weight reaches mass * sum(w);
+#   * that count is clamped to [k_min, k_max] and to the row length.
+# ---------------------------------------------------------------------------
+def mass_weights(scores: np.ndarray) -> np.ndarray:
+    """w_j = exp(s_j - max s), with entries equal to the maximum weighing 1."""
+    s = np.asarray(scores, dtype=np.float64)
+    if np.isnan(s).any():
+        raise ValueError("NaN score")
+    m = s.max()
+    with np.errstate(invalid="ignore"):
+        return np.where(s == m, 1.0, np.exp(s - m))
+
+
+def mass_count(scores: np.ndarray, mass: float, k_min: int = 0, k_max: int | None = None) -> int:
+    """Shortest prefix (in selection order) holding at least ``mass`` of the
+    softmax weight, clamped to [k_min, k_max] and to the row length."""
+    s = np.asarray(scores, dtype=np.float64)
+    n = s.shape[0]
+    w = mass_weights(s)
+    order = np.lexsort((np.arange(n), -s))
+    ws = w[order]
+    before = np.concatenate([[0.0], np.cumsum(ws)[:-1]])   # weight ahead of each position
+    c = int(np.count_nonzero(before < mass * ws.sum()))
+    c = max(c, k_min)
+    if k_max is not None:
+        c = min(c, k_max)
+    return min(c, n)
+
+
+def mass_row(scores: np.ndarray, mass: float, k_min: int = 0, k_max: int | None = None) -> np.ndarray:
+    """Ascending indices of the adaptive selection of one row."""
+    c = mass_count(scores, mass, k_min, k_max)
+    return topk_row(scores, c, np.zeros(0, np.int64))
+
+
+def mass_margin(scores: np.ndarray, mass: float) -> float:
+    """Distance, relative to the total weight, between mass and the nearest
+    prefix share.  When it exceeds the arithmetic error of a caller's
+    summation, that caller must find the same count."""
+    s = np.asarray(scores, dtype=np.float64)
+    w = mass_weights(s)
+    order = np.lexsort((np.arange(s.shape[0]), -s))
+    cum = np.concatenate([[0.0], np.cumsum(w[order])])
+    return float(np.min(np.abs(cum / cum[-1] - mass)))

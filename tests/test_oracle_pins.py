@@ -278,6 +278,90 @@ def test_vs_slash_only_offset_zero_is_block_diagonal():
     assert np.max(np.abs(O - Ob)) < 1e-13
 
 
+
+# ------------------------------------------------------------------ adaptive budget
+def brute_mass_count(s, mass):
+    """Fewest candidates of ANY subset whose softmax share reaches ``mass``,
+    by enumerating subsets; shares are exactly rounded sums (math.fsum) of
+    math.exp over the row.  Returns (count, best share of that size)."""
+    n = len(s)
+    m = max(s)
+    e = [math.exp(x - m) for x in s]
+    tot = math.fsum(e)
+    for c in range(1, n + 1):
+        best = max(math.fsum(e[i] for i in comb) for comb in itertools.combinations(range(n), c))
+        if best >= mass * tot:
+            return c, best / tot
+    return n, 1.0
+
+
+def test_mass_count_equals_bruteforce_fewest_subset():
+    r = np.random.default_rng(41)
+    checked = 0
+    for trial in range(150):
+        n = int(r.integers(1, 11))
+        s = r.normal(0.0, float(r.choice([0.3, 1.0, 3.0])), n)
+        mass = float(r.uniform(0.05, 1.0))
+        if oracle.mass_margin(s, mass) < 1e-9:
+            continue
+        c = oracle.mass_count(s, mass)
+        bc, share = brute_mass_count(list(s), mass)
+        assert c == bc
+        sel = oracle.mass_row(s, mass)
+        assert list(sel) == list(oracle.topk_row(s, c, np.zeros(0, np.int64)))
+        w = np.exp(s - s.max())
+        assert abs(w[sel].sum() / w.sum() - share) < 1e-12    # the kept prefix is a best subset
+        checked += 1
+    assert checked > 120
+
+
+def test_mass_count_uniform_row_is_ceiling():
+    for n in range(1, 41):
+        for j in range(1, 9):
+            s = np.full(n, 0.7)
+            assert oracle.mass_count(s, j / 8) == math.ceil(j * n / 8)
+            assert list(oracle.mass_row(s, j / 8)) == list(range(math.ceil(j * n / 8)))
+
+
+def test_mass_count_geometric_closed_form():
+    # weights 2^-j (scores -j ln 2): the first c hold (1 - 2^-c)/(1 - 2^-n) of the mass
+    r = np.random.default_rng(42)
+    for n in (1, 2, 5, 17, 30):
+        for c in range(1, n + 1):
+            mass = (1.0 - 1.5 * 2.0 ** -c) / (1.0 - 2.0 ** -n)
+            perm = r.permutation(n)
+            s = np.empty(n)
+            s[perm] = -np.arange(n) * math.log(2.0)
+            assert oracle.mass_count(s, mass) == c
+            assert list(oracle.mass_row(s, mass)) == sorted(perm[:c])
+
+
+def test_mass_count_invariants_and_special_rows():
+    r = np.random.default_rng(43)
+    for trial in range(40):
+        n = int(r.integers(2, 200))
+        s = r.normal(0, 2, n)
+        prev = 0
+        for mass in (0.1, 0.3, 0.5, 0.7, 0.9, 1.0):
+            c = oracle.mass_count(s, mass)
+            assert prev <= c <= n                      # monotone in the mass
+            prev = c
+            if oracle.mass_margin(s, mass) > 1e-9:      # a common shift leaves the softmax alone
+                assert oracle.mass_count(s + 1000.25, mass) == c
+        assert oracle.mass_count(s, 1.0) == n          # moderate range: every weight is positive
+        assert oracle.mass_count(s, 0.9, k_min=n) == n
+        assert oracle.mass_count(s, 0.9, k_max=1) == 1
+    dom = np.zeros(16)
+    dom[5] = 60.0
+    assert list(oracle.mass_row(dom, 0.99)) == [5]
+    inf2 = np.array([0.0, np.inf, 3.0, np.inf])        # the +inf entries share everything
+    assert list(oracle.mass_row(inf2, 0.5)) == [1]
+    assert list(oracle.mass_row(inf2, 0.51)) == [1, 3]
+    assert list(oracle.mass_row(np.full(6, -np.inf), 0.5)) == [0, 1, 2]   # uniform
+    assert list(oracle.mass_row(np.array([1.0, -np.inf, 1.0]), 1.0)) == [0, 2]
+    with pytest.raises(ValueError):
+        oracle.mass_count(np.array([1.0, np.nan]), 0.5)
+
 # ------------------------------------------------------------------ clustered decode
 def test_cluster_rule_from_page():
     g = gold("page_facts.json")["squeezed_cluster_rule"]
