@@ -135,10 +135,12 @@ def mass_row(scores: np.ndarray, mass: float, k_min: int = 0, k_max: int | None 
 
 def mass_margin(scores: np.ndarray, mass: float) -> float:
     """Distance, relative to the total weight, between mass and the nearest
-    prefix share.  When it exceeds the arithmetic error of a caller's
-    summation, that caller must find the same count."""
+    share that the count rule compares with it (the weight ahead of each
+    position; the full sum is never compared).  When it exceeds the arithmetic
+    error of a caller's summation, that caller must find the same count."""
     s = np.asarray(scores, dtype=np.float64)
     w = mass_weights(s)
     order = np.lexsort((np.arange(s.shape[0]), -s))
-    cum = np.concatenate([[0.0], np.cumsum(w[order])])
-    return float(np.min(np.abs(cum / cum[-1] - mass)))
+    ws = w[order]
+    before = np.concatenate([[0.0], np.cumsum(ws)[:-1]])
+    return float(np.min(np.abs(before / ws.sum() - mass)))

@@ -26,7 +26,7 @@ def lib():
 def test_header_declares_the_four_entry_points_and_helpers():
     names = declared_functions()
     for n in ["sa_estimate", "sa_select_topk", "sa_block_sparse_fwd", "sa_gather_decode", "sa_vs_build",
-              "sa_cluster_pack", "sa_last_error", "sa_version", "sa_args_size"]:
+              "sa_cluster_pack", "sa_select_mass", "sa_last_error", "sa_version", "sa_args_size"]:
         assert n in names
 
 
@@ -101,6 +101,29 @@ def test_select_argument_errors(lib):
     assert lib.sa_select_topk(C.byref(a), None, 0, None) == 2
     a.kmax = 7
     assert lib.sa_select_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0
+
+
+def test_select_mass_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    a = F.SelectMassArgs()
+    assert lib.sa_select_mass(None, None) == 1
+    assert lib.sa_select_mass(C.byref(a), None) == 1                 # pointers missing
+    a.scores = a.idx = a.cnt = 256
+    a.rows, a.ncand, a.ld, a.mass, a.k_min, a.k_max, a.kmax = 4, 5000, 5000, 0.5, 1, 64, 64
+    assert lib.sa_select_mass(C.byref(a), None) == 2                 # above 4096 candidates
+    a.ncand = a.ld = 256
+    for bad in (0.0, -0.1, 1.5, float("nan")):
+        a.mass = bad
+        assert lib.sa_select_mass(C.byref(a), None) == 8
+    a.mass = 1.0
+    a.k_min = 65
+    assert lib.sa_select_mass(C.byref(a), None) == 8                 # k_min > k_max
+    a.k_min, a.kmax = 1, 63
+    assert lib.sa_select_mass(C.byref(a), None) == 2                 # kmax < min(k_max, ncand)
+    assert "kmax" in _err(lib)
+    a.ncand = a.ld = 40
+    a.rows = 0                                                       # min(64, 40) = 40 fits; nothing to launch
+    assert lib.sa_select_mass(C.byref(a), None) == 0
 
 
 def test_estimate_and_gather_argument_errors(lib):
