@@ -8,8 +8,8 @@ head_dim 128, synthetic seeded inputs resident in HBM.
 
 value = kept-block FLOP (4*64*64*128 per kept 64x64 block, counted from the
 selected tables) / whole-step time.  ms_per_step = ms per layer at 128K.
-The same run also reports the clustered decode (KV GB/s, us per token), the
-token-indexer prefill with index reuse, and the vertical-slash layer as
+The same run also reports the clustered decode (KV GB/s, us per token; with a
+fixed top-64 and with the adaptive softmax-mass budget), the token-indexer prefill with index reuse, and the vertical-slash layer as
 extras, the roofline of the dominant kernel (the forward), and the CPU oracle
 timed on a bounded sample of the same workload.
 
@@ -125,7 +125,9 @@ def prefill_layer(N, ratio, steps, warmup, seed):
 
 
 # ---------------------------------------------------------------- extras
-def decode_extra(steps, warmup):
+def decode_extra(steps, warmup, mass=None):
+    """Clustered decode step; with ``mass`` the adaptive budget (fewest
+    clusters holding that share of the centroid-score softmax, 1..64)."""
     import torch
     import workloads as W
     from dynamic_sparse_attention_pool_amd.pipelines import ClusterDecode
@@ -134,7 +136,7 @@ def decode_extra(steps, warmup):
     for c in range(4):  # rotate over 4 contexts so no step finds the last one in the 256 MB MALL
         inp = W.decode_clustered(W.CONFIG_SEEDS[4] + 100 * c, T, Hq, Hkv, N, d, C)
         copies.append(ClusterDecode(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev_t(inp.labels),
-                                    dev_t(inp.centroids), n_sel=ksel))
+                                    dev_t(inp.centroids), n_sel=ksel, mass=mass, k_min=1))
     torch.cuda.synchronize()
     for i in range(max(warmup, 4)):
         copies[i % 4].step()
@@ -172,13 +174,18 @@ def decode_extra(steps, warmup):
         ptr = dc.ptr.cpu().numpy().astype(np.int64)
         for g in range(Hkv):
             used = np.unique(sel[:, g * (Hq // Hkv):(g + 1) * (Hq // Hkv), :])
+            used = used[used >= 0]  # -1 pads rows that keep fewer clusters
             kv_bytes += int((ptr[g, used + 1] - ptr[g, used]).sum()) * 2 * d * 2
     kv_bytes //= len(copies)
     small = T * Hq * d * 2 + Hkv * C * d * 4 + T * Hq * d * 4
     step_bytes = kv_bytes + small
     fwd_ms = tm.mean_ms("forward")
-    return {"workload": "clustered decode: 8 queries x 32/8 heads, d128, 65536-key context, top 64 of 256 clusters; "
+    mean_sel = float(np.mean([dc.sel_cnt.float().mean().item() for dc in copies]))
+    rule = ("top 64 of 256 clusters" if mass is None else
+            f"fewest clusters holding {mass:g} of the centroid-score softmax, 1..64 of 256")
+    return {"workload": f"clustered decode: 8 queries x 32/8 heads, d128, 65536-key context, {rule}; "
                         "each step replayed as a HIP graph, rotating 4 contexts",
+            "mean_clusters": mean_sel,
             "us_per_step": ms * 1e3, "us_per_token": ms * 1e3 / T,
             "kv_bytes_per_step": kv_bytes, "GB_per_s_step": step_bytes / (ms * 1e-3) / 1e9,
             "us_gather": fwd_ms * 1e3, "GB_per_s_gather": kv_bytes / (fwd_ms * 1e-3) / 1e9,
@@ -306,7 +313,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extras to run: decode,indexer,vs")
+    ap.add_argument("--only", default="", help="comma list of extras to run: decode,decode_adaptive,indexer,vs")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
@@ -356,6 +363,7 @@ def main():
     only = set(x for x in args.only.split(",") if x)
     if not args.no_extras:
         for name, fn in [("decode", lambda: decode_extra(max(args.steps, 20), args.warmup)),
+                         ("decode_adaptive", lambda: decode_extra(max(args.steps, 20), args.warmup, mass=0.5)),
                          ("indexer", lambda: indexer_extra(max(2, args.steps // 3), 1)),
                          ("vs", lambda: vs_extra(max(2, args.steps // 3), 1, main["inputs"]))]:
             if only and name not in only:

@@ -14,8 +14,8 @@ import math
 from . import _ffi as F
 from ._ffi import SAError, load  # noqa: F401
 
-__all__ = ["sa_estimate", "sa_select_topk", "sa_vs_build", "sa_block_sparse_fwd", "sa_gather_decode",
-           "sa_cluster_pack", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
+__all__ = ["sa_estimate", "sa_select_topk", "sa_select_mass", "sa_vs_build", "sa_block_sparse_fwd",
+           "sa_gather_decode", "sa_cluster_pack", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
 
 BLOCK_MEANPOOL, VSLASH, CENTROID, INDEXER = (F.SA_EST_BLOCK_MEANPOOL, F.SA_EST_VSLASH, F.SA_EST_CENTROID,
                                              F.SA_EST_INDEXER)
@@ -112,6 +112,22 @@ def sa_select_topk(scores, idx, cnt, *, k: int = 0, ratio=None, n_sink: int = 0,
     a.kmax = idx.shape[1]
     a.idx, a.cnt, a.err_flag = _p(idx), _p(cnt), _p(err_flag)
     F.check(lib.sa_select_topk(C.byref(a), None, 0, _stream()))
+
+
+def sa_select_mass(scores, idx, cnt, *, mass: float, k_min: int = 0, k_max=None, ncand=None, err_flag=None):
+    """Adaptive count per row: the fewest best-scored candidates holding
+    ``mass`` of the row's softmax weight, clamped to [k_min, k_max].
+    scores [R, ld] float; idx [R, kmax], cnt [R] int32."""
+    lib = load()
+    a = F.SelectMassArgs()
+    R, ld = scores.shape
+    a.scores, a.rows, a.ld = _p(scores), R, ld
+    a.ncand = ld if ncand is None else ncand
+    a.mass, a.k_min = mass, k_min
+    a.k_max = idx.shape[1] if k_max is None else k_max
+    a.kmax = idx.shape[1]
+    a.idx, a.cnt, a.err_flag = _p(idx), _p(cnt), _p(err_flag)
+    F.check(lib.sa_select_mass(C.byref(a), _stream()))
 
 
 def sa_vs_build(vert, vert_cnt, slash, slash_cnt, iv, iv_cnt, col, col_cnt, seq: int, block_size: int = 64):

@@ -17,7 +17,7 @@ SA_F32, SA_BF16, SA_I32 = 0, 1, 2
 SA_EST_BLOCK_MEANPOOL, SA_EST_VSLASH, SA_EST_CENTROID, SA_EST_INDEXER = 0, 1, 2, 3
 SA_FWD_BLOCK, SA_FWD_VSLASH = 0, 1
 SA_GATHER_CLUSTER, SA_GATHER_TOKEN = 0, 1
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
                 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_LAUNCH", 8: "SA_ERR_VALUE"}
@@ -72,7 +72,13 @@ class ClusterPackArgs(C.Structure):
                 ("perm", P), ("k", P), ("v", P), ("k_packed", P), ("v_packed", P), ("err_flag", P)]
 
 
-STRUCTS = [EstimateArgs, SelectArgs, VsBuildArgs, FwdArgs, GatherArgs, ClusterPackArgs]
+class SelectMassArgs(C.Structure):
+    _fields_ = [("scores", P), ("rows", C.c_int64), ("ncand", C.c_int64), ("ld", C.c_int64),
+                ("mass", C.c_float), ("k_min", C.c_int32), ("k_max", C.c_int32), ("kmax", C.c_int32),
+                ("idx", P), ("cnt", P), ("err_flag", P)]
+
+
+STRUCTS = [EstimateArgs, SelectArgs, VsBuildArgs, FwdArgs, GatherArgs, ClusterPackArgs, SelectMassArgs]
 
 # exported symbol -> (restype, argtypes)
 SYMBOLS = {
@@ -80,6 +86,7 @@ SYMBOLS = {
     "sa_estimate_workspace_bytes": (C.c_int, [C.POINTER(EstimateArgs), C.POINTER(C.c_size_t)]),
     "sa_select_topk": (C.c_int, [C.POINTER(SelectArgs), P, C.c_size_t, P]),
     "sa_select_topk_workspace_bytes": (C.c_int, [C.POINTER(SelectArgs), C.POINTER(C.c_size_t)]),
+    "sa_select_mass": (C.c_int, [C.POINTER(SelectMassArgs), P]),
     "sa_vs_build": (C.c_int, [C.POINTER(VsBuildArgs), P]),
     "sa_block_sparse_fwd": (C.c_int, [C.POINTER(FwdArgs), P, C.c_size_t, P]),
     "sa_block_sparse_fwd_workspace_bytes": (C.c_int, [C.POINTER(FwdArgs), C.POINTER(C.c_size_t)]),

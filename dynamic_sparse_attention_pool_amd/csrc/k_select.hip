@@ -573,6 +573,132 @@ __global__ __launch_bounds__(256) void k_select_small(SelectParams p) {
   }
 }
 
+// ---------------------------------------------------------------- adaptive budget
+// The shortest prefix of the selection order (higher score first, lower index
+// on ties) that holds a given share of the row's softmax weight (Squeezed
+// Attention page, §技术方案: the number of clusters kept follows the
+// distribution of the centroid similarities).  Candidate j weighs
+// exp(s_j - m), m the row maximum, and an entry equal to m weighs exactly 1.
+// One workgroup per row of at most 4096 candidates: (key, ~index) pairs are
+// sorted in LDS by a bitonic network, a block scan sums the weights along that
+// order, and a position is kept while the weight ahead of it is below
+// mass * total.  The kept indices are marked in an LDS bitmap and written in
+// index order.  Weights are fp32 exponentials rounded to multiples of 2^-40
+// and summed as 64-bit integers (4096 * 2^40 < 2^53), so every prefix is exact,
+// the prefixes never decrease, and the last one is the total whatever the
+// thread layout; the comparison with mass * total is made in double.
+constexpr int kMassNT = 256;
+
+__device__ __forceinline__ float key_float(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
+}
+
+__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t x = __shfl_up(v, off);
+    if (lane >= off) v += x;
+  }
+  return v;
+}
+
+__global__ __launch_bounds__(kMassNT) void k_select_mass(MassParams p) {
+  constexpr int NT = kMassNT, NW = NT / 64;
+  __shared__ uint64_t kv[kMassMax];
+  __shared__ uint32_t bm[kMassMax / 32];
+  __shared__ uint64_t wtmp[NW];
+  __shared__ uint32_t utmp[NW];
+  __shared__ uint32_t shnan;
+  const int tid = threadIdx.x, wv = tid >> 6;
+  const int64_t r = blockIdx.x;
+  const float* row = p.scores + r * p.ld;
+  const int n = (int)p.ncand;
+  int P = 64;
+  while (P < n) P <<= 1;
+  bool nan_seen = false;
+  for (int i = tid; i < P; i += NT) {
+    uint64_t e = 0ull;  // padding sorts last: every real key is above 0
+    if (i < n) {
+      const float f = row[i];
+      nan_seen |= is_nan(f);
+      e = ((uint64_t)order_key(f) << 32) | (uint64_t)(~(uint32_t)i);
+    }
+    kv[i] = e;
+  }
+  const int nw = (n + 31) >> 5;
+  for (int w = tid; w < nw; w += NT) bm[w] = 0u;
+  if (tid == 0) shnan = 0u;
+  __syncthreads();
+  if (nan_seen) atomicOr(&shnan, 1u);
+  // bitonic network, descending: runs of length kk alternate direction until the last merge
+  for (int kk = 2; kk <= P; kk <<= 1) {
+    for (int j = kk >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < P / 2; i += NT) {
+        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1)), hi = lo + j;
+        const uint64_t a = kv[lo], b = kv[hi];
+        if ((a < b) == ((lo & kk) == 0)) {
+          kv[lo] = b;
+          kv[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // weights along the sorted order: thread t owns positions [t*E, t*E + E)
+  const float m = key_float((uint32_t)(kv[0] >> 32));
+  const int E = P >= NT ? P / NT : 1;
+  const int j0 = tid * E, j1 = min(n, j0 + E);
+  auto weight = [&](int j) -> uint64_t {  // in units of 2^-40
+    const float s = key_float((uint32_t)(kv[j] >> 32));
+    const float w = s == m ? 1.f : expf(s - m);
+    return __double2ull_rn((double)w * 1099511627776.0);
+  };
+  uint64_t part = 0ull;
+  for (int j = j0; j < j1; ++j) part += weight(j);
+  const uint64_t incl = wave_incl_scan_u64(part);
+  if ((tid & 63) == 63) wtmp[wv] = incl;
+  __syncthreads();
+  uint64_t ahead = incl - part, total = 0ull;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    const uint64_t x = wtmp[w];
+    ahead += w < wv ? x : 0ull;
+    total += x;
+  }
+  const double thr = (double)p.mass * (double)total;
+  uint32_t kept_here = 0u;
+  for (int j = j0; j < j1; ++j) {
+    kept_here += (double)ahead < thr ? 1u : 0u;
+    ahead += weight(j);
+  }
+  uint32_t c_raw;
+  block_excl_scan<NT>(kept_here, utmp, c_raw);
+  int c = max((int)c_raw, p.k_min);
+  c = min(c, min(p.k_max, n));
+  for (int j = tid; j < c; j += NT) {
+    const uint32_t i = ~(uint32_t)kv[j];
+    atomicOr(&bm[i >> 5], 1u << (i & 31u));
+  }
+  __syncthreads();
+  // emission in index order: thread t owns bitmap word t (nw <= 128 < NT)
+  const uint32_t word = tid < nw ? bm[tid] : 0u;
+  uint32_t tot;
+  uint32_t at = block_excl_scan<NT>((uint32_t)__popc(word), utmp, tot);
+  int32_t* out = p.idx + r * p.kmax;
+  uint32_t bits = word;
+  while (bits) {
+    const int b = __builtin_ctz(bits);
+    bits &= bits - 1u;
+    out[at++] = 32 * tid + b;
+  }
+  for (int j = c + tid; j < p.kmax; j += NT) out[j] = -1;
+  if (tid == 0) {
+    p.cnt[r] = c;
+    if (shnan && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
+  }
+}
+
 // ---------------------------------------------------------------- vertical-slash tables
 // One thread per (row, query block).  Offsets arrive ascending, so walking
 // them backwards yields tile starts 64i-o in ascending order; overlapping or
@@ -707,6 +833,12 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
     hipLaunchKernelGGL((k_select_long<1024>), grid, dim3(1024), 0, stream, p);
   else
     hipLaunchKernelGGL((k_select<1024, false>), grid, dim3(1024), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_mass(const MassParams& p, hipStream_t stream) {
+  if (p.rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_select_mass, dim3((unsigned)p.rows), dim3(kMassNT), 0, stream, p);
   return hipGetLastError();
 }
 

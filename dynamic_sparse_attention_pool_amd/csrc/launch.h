@@ -54,6 +54,18 @@ struct SelectParams {
 };
 hipError_t launch_select(const SelectParams& p, hipStream_t stream);
 
+constexpr int kMassMax = 4096;  // candidates per row of the adaptive selection
+struct MassParams {
+  const float* scores;
+  int64_t rows, ncand, ld;
+  float mass;
+  int32_t k_min, k_max, kmax;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* err;
+};
+hipError_t launch_select_mass(const MassParams& p, hipStream_t stream);
+
 struct VsBuildParams {
   int64_t rows, seq;
   int32_t bs, n_vert, n_slash;

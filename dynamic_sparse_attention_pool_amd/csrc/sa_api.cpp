@@ -137,7 +137,8 @@ int64_t select_max_count(const sa_select_args* a) {
 
 int check_select(const sa_select_args* a) {
   if (!a) return fail(SA_ERR_NULL, "sa_select_topk: args is NULL");
-  if (!a->scores || !a->idx || !a->cnt) return fail(SA_ERR_NULL, "sa_select_topk: scores, idx and cnt are required");
+  if (a->rows != 0 && (!a->scores || !a->idx || !a->cnt))
+    return fail(SA_ERR_NULL, "sa_select_topk: scores, idx and cnt are required");
   if (a->rows < 0 || a->ncand <= 0 || a->ld < a->ncand) return fail(SA_ERR_SHAPE, "sa_select_topk: need ncand > 0 and ld >= ncand");
   if (a->ncand > (int64_t)1 << 24) return fail(SA_ERR_SHAPE, "sa_select_topk: ncand above 2^24");
   if (a->rows > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_select_topk: too many rows");
@@ -168,6 +169,7 @@ size_t sa_args_size(int which) {
     case 3: return sizeof(sa_fwd_args);
     case 4: return sizeof(sa_gather_args);
     case 5: return sizeof(sa_cluster_pack_args);
+    case 6: return sizeof(sa_select_mass_args);
     default: return 0;
   }
 }
@@ -259,6 +261,33 @@ int sa_select_topk(const sa_select_args* a, void* workspace, size_t workspace_by
   p.cnt = a->cnt;
   p.err = a->err_flag;
   return launched(sa::launch_select(p, as_stream(stream)), "sa_select_topk");
+}
+
+int sa_select_mass(const sa_select_mass_args* a, void* stream) {
+  if (!a) return fail(SA_ERR_NULL, "sa_select_mass: args is NULL");
+  if (a->rows != 0 && (!a->scores || !a->idx || !a->cnt))
+    return fail(SA_ERR_NULL, "sa_select_mass: scores, idx and cnt are required");
+  if (a->rows < 0 || a->rows > 0x7fffffff || a->ncand <= 0 || a->ld < a->ncand)
+    return fail(SA_ERR_SHAPE, "sa_select_mass: need rows >= 0, ncand > 0 and ld >= ncand");
+  if (a->ncand > sa::kMassMax) return fail(SA_ERR_SHAPE, "sa_select_mass: ncand above %d", sa::kMassMax);
+  if (!(a->mass > 0.f && a->mass <= 1.f)) return fail(SA_ERR_VALUE, "sa_select_mass: mass must lie in (0, 1]");
+  if (a->k_min < 0 || a->k_max < a->k_min) return fail(SA_ERR_VALUE, "sa_select_mass: need 0 <= k_min <= k_max");
+  const int64_t need = a->k_max < a->ncand ? a->k_max : a->ncand;
+  if (a->kmax <= 0 || a->kmax < need)
+    return fail(SA_ERR_SHAPE, "sa_select_mass: kmax %d is below min(k_max, ncand) = %lld", a->kmax, (long long)need);
+  sa::MassParams p;
+  p.scores = a->scores;
+  p.rows = a->rows;
+  p.ncand = a->ncand;
+  p.ld = a->ld;
+  p.mass = a->mass;
+  p.k_min = a->k_min;
+  p.k_max = a->k_max;
+  p.kmax = a->kmax;
+  p.idx = a->idx;
+  p.cnt = a->cnt;
+  p.err = a->err_flag;
+  return launched(sa::launch_select_mass(p, as_stream(stream)), "sa_select_mass");
 }
 
 // ---------------------------------------------------------------- vertical-slash tables

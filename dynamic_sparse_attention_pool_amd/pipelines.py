@@ -9,7 +9,7 @@ from __future__ import annotations
 import math
 
 from . import (BLOCK_MEANPOOL, CENTROID, INDEXER, VSLASH, sa_block_sparse_fwd, sa_cluster_pack, sa_estimate,
-               sa_gather_decode, sa_select_topk, sa_vs_build)
+               sa_gather_decode, sa_select_mass, sa_select_topk, sa_vs_build)
 
 
 def _t():
@@ -124,13 +124,18 @@ class ClusterDecode:
     """Clustered fixed-context decode: offline pack, then per step
     centroid scores -> top clusters -> gathered attention."""
 
-    def __init__(self, q, k, v, labels, centroids, *, n_sel: int, out_dtype=None, scale=None, with_lse=False):
+    def __init__(self, q, k, v, labels, centroids, *, n_sel: int, mass=None, k_min: int = 1, out_dtype=None,
+                 scale=None, with_lse=False):
+        """n_sel clusters per query head, or, with ``mass`` set, the fewest
+        clusters holding that share of the softmax of the centroid scores,
+        between k_min and n_sel (sa_select_mass)."""
         torch = _t()
         T, Hq, d = q.shape
         Hkv, N, _ = k.shape
         C = centroids.shape[1]
         dev = q.device
         self.q, self.centroids, self.C, self.n_sel = q, centroids, C, n_sel
+        self.mass, self.k_min = mass, k_min
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
         self.ptr = torch.empty((Hkv, C + 1), dtype=torch.int32, device=dev)
         self.perm = torch.empty((Hkv, N), dtype=torch.int32, device=dev)
@@ -150,7 +155,11 @@ class ClusterDecode:
         sa_estimate(CENTROID, self.q, self.k, self.scores, centroids=self.centroids, scale=self.scale)
 
     def select(self):
-        sa_select_topk(self.scores.view(-1, self.C), self.sel.view(-1, self.n_sel), self.sel_cnt, k=self.n_sel)
+        if self.mass is None:
+            sa_select_topk(self.scores.view(-1, self.C), self.sel.view(-1, self.n_sel), self.sel_cnt, k=self.n_sel)
+        else:
+            sa_select_mass(self.scores.view(-1, self.C), self.sel.view(-1, self.n_sel), self.sel_cnt, mass=self.mass,
+                           k_min=self.k_min, k_max=self.n_sel)
 
     def forward(self):
         self.ws = sa_gather_decode(self.q, self.k, self.v, self.out, cluster_ptr=self.ptr, sel=self.sel,

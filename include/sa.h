@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 1
+#define SA_ABI_VERSION 2
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -140,6 +140,7 @@ int sa_estimate(const sa_estimate_args* args, void* workspace, size_t workspace_
  *     largest possible count fits kmax (SA_ERR_SHAPE otherwise).
  * err_flag: optional device int32; set to 1 when a candidate score is NaN
  *     (that row's output is then unspecified).  Never cleared by the library.
+ * rows = 0 launches nothing (scores, idx and cnt may then be NULL).
  * Rows with up to 4096 candidates are ranked in LDS; rows with up to 131072
  * are read once (sampled bracket, LDS bitmaps); longer rows (up to 2^24) are
  * read twice, or more when the sample does not bracket the k-th score.
@@ -166,6 +167,47 @@ typedef struct sa_select_args {
 
 int sa_select_topk_workspace_bytes(const sa_select_args* args, size_t* bytes);
 int sa_select_topk(const sa_select_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
+ * sa_select_mass — adaptive budget: the fewest best-scored candidates that
+ * hold a given share of the row's softmax weight.
+ *
+ * Squeezed Attention page, §技术方案 (key technical points): the number of
+ * clusters kept adapts to the distribution of the query's centroid
+ * similarities.  The page gives no rule; the one taken here treats a row's
+ * scores as logits.  Candidate j weighs w_j = exp(s_j - m), m the row maximum
+ * (an entry equal to m weighs exactly 1, so +inf entries share all the weight
+ * and an all -inf row weighs uniformly).  Ranked in sa_select_topk's order
+ * (higher score first, lower index on ties), the row keeps the shortest
+ * prefix whose weight reaches mass * sum(w); that count is then clamped to
+ * [k_min, k_max] and to ncand.  Weights are fp32 exponentials rounded to
+ * multiples of 2^-40 and summed exactly as integers (the count does not depend
+ * on the summation order); mass * sum is compared in double.
+ *
+ * scores: [rows, ld] float, row r uses scores[r*ld + 0 .. ncand-1];
+ *   1 <= ncand <= 4096 (cluster tables), ld >= ncand.
+ * mass in (0, 1]; 0 <= k_min <= k_max.
+ * Output: idx [rows, kmax] int32 ascending, padded with -1 (kmax must be at
+ *   least min(k_max, ncand), SA_ERR_SHAPE otherwise); cnt [rows] int32.
+ * err_flag: optional device int32 set to 1 when a score is NaN (that row's
+ *   output is then unspecified).  No workspace.  rows = 0 launches nothing
+ *   (scores, idx and cnt may then be NULL).
+ * ====================================================================== */
+typedef struct sa_select_mass_args {
+  const float* scores;
+  int64_t rows;
+  int64_t ncand;
+  int64_t ld;
+  float mass;
+  int32_t k_min;
+  int32_t k_max;
+  int32_t kmax;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* err_flag;
+} sa_select_mass_args;
+
+int sa_select_mass(const sa_select_mass_args* args, void* stream);
 
 /* ======================================================================
  * sa_vs_build — vertical-slash selections -> per-query-block key tables.
@@ -342,7 +384,8 @@ const char* sa_last_error(void);
 /* SA_ABI_VERSION of the built library. */
 int sa_version(void);
 /* sizeof of the argument structs as compiled, so bindings can check layout:
- * which = 0 estimate, 1 select, 2 vs_build, 3 fwd, 4 gather, 5 cluster_pack. */
+ * which = 0 estimate, 1 select, 2 vs_build, 3 fwd, 4 gather, 5 cluster_pack,
+ * 6 select_mass. */
 size_t sa_args_size(int which);
 
 #ifdef __cplusplus

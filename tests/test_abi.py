@@ -107,6 +107,7 @@ def test_select_mass_argument_errors(lib):
     from dynamic_sparse_attention_pool_amd import _ffi as F
     a = F.SelectMassArgs()
     assert lib.sa_select_mass(None, None) == 1
+    a.rows = 4
     assert lib.sa_select_mass(C.byref(a), None) == 1                 # pointers missing
     a.scores = a.idx = a.cnt = 256
     a.rows, a.ncand, a.ld, a.mass, a.k_min, a.k_max, a.kmax = 4, 5000, 5000, 0.5, 1, 64, 64
@@ -124,6 +125,15 @@ def test_select_mass_argument_errors(lib):
     a.ncand = a.ld = 40
     a.rows = 0                                                       # min(64, 40) = 40 fits; nothing to launch
     assert lib.sa_select_mass(C.byref(a), None) == 0
+    a.scores = a.idx = a.cnt = None                                  # empty tensors carry NULL pointers
+    assert lib.sa_select_mass(C.byref(a), None) == 0
+    a.rows = 1
+    assert lib.sa_select_mass(C.byref(a), None) == 1
+    t = F.SelectArgs()
+    t.rows, t.ncand, t.ld, t.k, t.kmax = 0, 10, 10, 2, 2
+    assert lib.sa_select_topk(C.byref(t), None, 0, None) == 0
+    t.rows = 3
+    assert lib.sa_select_topk(C.byref(t), None, 0, None) == 1
 
 
 def test_estimate_and_gather_argument_errors(lib):
