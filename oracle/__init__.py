@@ -7,7 +7,8 @@ constant or table with it (the HIP path lives in
 ``dynamic_sparse_attention_pool_amd``).
 
 Sources (cited by page title and section in each function):
-  * "MInference 1.0" article — §方法介紹 (block-sparse estimate by mean-pooled
+  * "MInference 1.0" article — §方法介紹 (three per-head patterns: A-shape,
+    vertical-slash and block-sparse; block-sparse estimate by mean-pooled
     Q and K, vertical-slash estimate from the last queries) and
     §延遲和內核中的稀疏模式, Fig. 4 (verticals in 1x64 pieces, slashes in
     64x64 blocks).
@@ -32,6 +33,7 @@ from .blocksparse import mean_pool, block_scores, block_select, block_sparse_att
 from .vslash import vs_estimate, vs_select, vs_block_keys, vs_block_tables, vs_attention
 from .cluster import centroid_scores, cluster_select, cluster_select_mass, cluster_pack, cluster_decode
 from .indexer import indexer_scores, indexer_select, gathered_attention, index_cache_forward
+from .patterns import A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, ashape_blocks, ashape_attention, mixed_layer
 
 __all__ = [
     "candidate_count", "forced_set", "budget", "topk_row", "select_rows", "certified_row",
@@ -40,4 +42,5 @@ __all__ = [
     "vs_estimate", "vs_select", "vs_block_keys", "vs_block_tables", "vs_attention",
     "centroid_scores", "cluster_select", "cluster_select_mass", "cluster_pack", "cluster_decode",
     "indexer_scores", "indexer_select", "gathered_attention", "index_cache_forward",
+    "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "ashape_blocks", "ashape_attention", "mixed_layer",
 ]

@@ -362,6 +362,57 @@ def test_mass_count_invariants_and_special_rows():
     with pytest.raises(ValueError):
         oracle.mass_count(np.array([1.0, np.nan]), 0.5)
 
+
+# ------------------------------------------------------------------ A-shape and per-head patterns
+def ashape_mask(N, bs, n_sink, n_local):
+    """Token-level A-shape mask from its definition: key c is visible to row
+    r when c <= r and c lies in the first n_sink blocks or in the n_local
+    blocks ending at r's block."""
+    m = np.zeros((N, N), bool)
+    for r in range(N):
+        for c in range(r + 1):
+            m[r, c] = c < bs * n_sink or c >= bs * (r // bs - n_local + 1)
+    return m
+
+
+@pytest.mark.parametrize("n_sink,n_local", [(1, 2), (0, 1), (2, 3), (1, 100), (0, 0)])
+def test_ashape_matches_token_mask(n_sink, n_local):
+    bs, N, d = 4, 32, 5
+    Q, K, V = rnd(71, 1, 2, N, d), rnd(72, 1, 1, N, d), rnd(73, 1, 1, N, d)
+    O, L = oracle.ashape_attention(Q, K, V, n_sink, n_local, bs, 0.6)
+    mask = ashape_mask(N, bs, n_sink, n_local)
+    for h in range(2):
+        On, Ln = naive_masked_attention(Q[0, h], K[0, 0], V[0, 0], mask, 0.6)
+        assert np.max(np.abs(O[0, h] - On)) < 1e-12
+        assert np.array_equal(np.isneginf(L[0, h]), np.isneginf(Ln))
+        fin = np.isfinite(Ln)
+        assert np.max(np.abs(L[0, h][fin] - Ln[fin]), initial=0.0) < 1e-12
+    if n_local >= N // bs:                      # the window covers every causal block: dense causal
+        Od, _ = naive_masked_attention(Q[0, 0], K[0, 0], V[0, 0], np.tril(np.ones((N, N), bool)), 0.6)
+        assert np.max(np.abs(O[0, 0] - Od)) < 1e-12
+
+
+def test_mixed_layer_heads_match_single_pattern_layers():
+    """Each head of a mixed layer equals the same head of a layer that runs
+    its pattern on every head (independent slicing and KV-head mapping)."""
+    bs, N, d, Hq, Hkv = 8, 64, 6, 4, 2
+    Q, K, V = rnd(81, 1, Hq, N, d), rnd(82, 1, Hkv, N, d), rnd(83, 1, Hkv, N, d)
+    scale = 0.5
+    block = dict(n_sink=1, n_local=1, k=2)
+    pats = ["BS", "A", "VS", "BS"]
+    O, L, sel = oracle.mixed_layer(Q, K, V, pats, bs=bs, scale=scale, a_shape=(1, 2), block=block,
+                                   vslash=(9, 5), last_q=8)
+    Ob, _ = oracle.block_sparse_attention(Q, K, V, oracle.block_select(oracle.block_scores(Q, K, bs, scale),
+                                                                         **block), bs, scale)
+    Oa, _ = oracle.ashape_attention(Q, K, V, 1, 2, bs, scale)
+    vsel = [[oracle.vs_select(*oracle.vs_estimate(Q[0, h, N - 8:], K[0, h * Hkv // Hq], np.arange(N - 8, N), scale),
+                              9, 5) for h in range(Hq)]]
+    Ov, _ = oracle.vs_attention(Q, K, V, vsel, bs, scale)
+    ref = {"BS": Ob, "A": Oa, "VS": Ov}
+    for h, p in enumerate(pats):
+        assert np.max(np.abs(O[0, h] - ref[p][0, h])) < 1e-12, (h, p)
+    assert list(sel[0][1][5]) == [0, 4, 5]
+
 # ------------------------------------------------------------------ clustered decode
 def test_cluster_rule_from_page():
     g = gold("page_facts.json")["squeezed_cluster_rule"]
