@@ -8,10 +8,12 @@ head_dim 128, synthetic seeded inputs resident in HBM.
 
 value = kept-block FLOP (4*64*64*128 per kept 64x64 block, counted from the
 selected tables) / whole-step time.  ms_per_step = ms per layer at 128K.
-The same run also reports the clustered decode (KV GB/s, us per token; with a
-fixed top-64 and with the adaptive softmax-mass budget), the token-indexer prefill with index reuse, and the vertical-slash layer as
-extras, the roofline of the dominant kernel (the forward), and the CPU oracle
-timed on a bounded sample of the same workload.
+The same run also reports, as extras, the clustered decode (KV GB/s, us per
+token; with a fixed top-64 and with the adaptive softmax-mass budget), the
+token-indexer prefill with index reuse, the vertical-slash layer and a layer
+mixing A-shape, vertical-slash and block-sparse heads; then the roofline of
+the dominant kernel (the forward) and the CPU oracle timed on a bounded sample
+of the same workload.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-extras] [--no-cpu]
 """
@@ -243,22 +245,64 @@ def vs_extra(steps, warmup, inp):
         tm.span("select", layer.select)
         tm.span("forward", layer.forward)
     torch.cuda.synchronize()
-    # kept keys per query block, counted from the built tables (diagonal tiles whole)
-    ivc = layer.iv.cpu().numpy()
-    ivn = layer.iv_cnt.cpu().numpy()
-    coln = layer.col_cnt.cpu().numpy().astype(np.int64)
-    keys = int(coln.sum())
-    B, Hq, nb = ivn.shape
-    for b in range(B):
-        for h in range(Hq):
-            for i in range(nb):
-                n = ivn[b, h, i]
-                keys += int((ivc[b, h, i, :n, 1] - ivc[b, h, i, :n, 0]).sum())
-    flop = keys * 4 * 64 * 128
+    flop = vs_table_keys(layer) * 4 * 64 * 128
     fwd = tm.mean_ms("forward")
     return {"workload": "vertical-slash layer at 131072: last-64-query estimate, top 1000 columns + top 64 offsets",
             "ms_layer": tm.mean_ms("estimate") + tm.mean_ms("select") + fwd, "ms_estimate": tm.mean_ms("estimate"),
             "ms_select_build": tm.mean_ms("select"), "ms_forward": fwd, "kept_key_flop": flop,
+            "forward_TFLOP_per_s": flop / (fwd * 1e-3) / 1e12}
+
+
+def vs_table_keys(layer):
+    """Kept keys over all query blocks of a vertical-slash layer, counted from
+    its built tables (diagonal tiles whole)."""
+    ivc = layer.iv.cpu().numpy()
+    ivn = layer.iv_cnt.cpu().numpy()
+    keys = int(layer.col_cnt.cpu().numpy().astype(np.int64).sum())
+    B, H, nb = ivn.shape
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                n = ivn[b, h, i]
+                keys += int((ivc[b, h, i, :n, 1] - ivc[b, h, i, :n, 0]).sum())
+    return keys
+
+
+def mixed_extra(steps, warmup, inp):
+    """The 128K layer with a per-head pattern assignment: in every group of 4
+    query heads sharing a KV head, one A-shape head (sink + 4 local blocks),
+    one vertical-slash head (1000 columns, 64 offsets) and two block-sparse
+    heads (sink + 4 local + ceil(5%))."""
+    import torch
+    from dynamic_sparse_attention_pool_amd.pipelines import MixedPatternLayer
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    Hq, N = q.shape[1], q.shape[2]
+    pats = [("A", "VS", "BS", "BS")[h % 4] for h in range(Hq)]
+    layer = MixedPatternLayer(q, k, v, pats, a_shape=(1, 4), block=dict(n_sink=1, n_local=4, ratio=(5, 100)),
+                              vslash=(1000, 64), out_dtype=torch.bfloat16)
+    for _ in range(warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    tm = Timer()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        tm.span("estimate", layer.estimate)
+        tm.span("select", layer.select)
+        tm.span("forward", layer.forward)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    parts = {type(p).__name__: p for p in layer.parts}
+    nb = N // 64
+    a_blocks = sum(len(set(range(min(1, i + 1))) | set(range(max(0, i - 3), i + 1))) for i in range(nb))
+    flop = (int(parts["BlockSparseLayer"].cnt.sum().item()) + a_blocks * len(layer.groups["A"])) * FLOP_PER_BLOCK
+    flop += vs_table_keys(parts["VerticalSlashLayer"]) * 4 * 64 * 128
+    fwd = tm.mean_ms("forward")
+    return {"workload": "mixed-pattern layer at 131072, GQA 32/8, d128: per KV head 1 A-shape (sink + 4 local), "
+                        "1 vertical-slash (1000 cols, 64 offsets), 2 block-sparse (sink + 4 local + ceil(5%)) heads",
+            "ms_layer": ms, "ms_estimate": tm.mean_ms("estimate"), "ms_select": tm.mean_ms("select"),
+            "ms_forward": fwd, "kept_flop": flop, "TFLOP_per_s_layer": flop / (ms * 1e-3) / 1e12,
             "forward_TFLOP_per_s": flop / (fwd * 1e-3) / 1e12}
 
 
@@ -313,7 +357,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extras to run: decode,decode_adaptive,indexer,vs")
+    ap.add_argument("--only", default="", help="comma list of extras to run: decode,decode_adaptive,indexer,vs,mixed")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
@@ -365,7 +409,8 @@ def main():
         for name, fn in [("decode", lambda: decode_extra(max(args.steps, 20), args.warmup)),
                          ("decode_adaptive", lambda: decode_extra(max(args.steps, 20), args.warmup, mass=0.5)),
                          ("indexer", lambda: indexer_extra(max(2, args.steps // 3), 1)),
-                         ("vs", lambda: vs_extra(max(2, args.steps // 3), 1, main["inputs"]))]:
+                         ("vs", lambda: vs_extra(max(2, args.steps // 3), 1, main["inputs"])),
+                         ("mixed", lambda: mixed_extra(max(2, args.steps // 3), 1, main["inputs"]))]:
             if only and name not in only:
                 continue
             try:

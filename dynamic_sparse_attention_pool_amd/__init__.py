@@ -51,6 +51,16 @@ def _stream():
     return _torch().cuda.current_stream().cuda_stream
 
 
+def _heads(a, heads):
+    """Host head list -> (ctypes int32 array kept alive by the caller, count)."""
+    if heads is None:
+        return None
+    arr = (C.c_int32 * len(heads))(*[int(h) for h in heads])
+    a.head_list = C.cast(arr, C.c_void_p)
+    a.n_heads_list = len(heads)
+    return arr
+
+
 def _workspace(nbytes: int, like):
     if nbytes == 0:
         return None, 0
@@ -59,10 +69,13 @@ def _workspace(nbytes: int, like):
 
 
 def sa_estimate(kind: int, q, k, scores, *, scores2=None, centroids=None, weights=None, scale=None,
-                block_size: int = 64, last_q: int = 64, q_pos0: int = 0, pooled_q=None, pooled_k=None):
+                block_size: int = 64, last_q: int = 64, q_pos0: int = 0, pooled_q=None, pooled_k=None,
+                heads=None):
     """Estimator scores (see sa.h).  Shapes:
     BLOCK_MEANPOOL / VSLASH: q [B,Hq,N,d], k [B,Hkv,N,d];
-    CENTROID: q [T,Hq,d], centroids [Hkv,C,d]; INDEXER: q [T,Hi,di], k [Nk,di], weights [Hi]."""
+    CENTROID: q [T,Hq,d], centroids [Hkv,C,d]; INDEXER: q [T,Hi,di], k [Nk,di], weights [Hi].
+    heads: optional sequence of query heads (BLOCK_MEANPOOL, VSLASH); outputs
+    are then compact over the listed heads."""
     lib = load()
     a = F.EstimateArgs()
     a.kind = kind
@@ -87,6 +100,7 @@ def sa_estimate(kind: int, q, k, scores, *, scores2=None, centroids=None, weight
     a.centroids, a.weights = _p(centroids), _p(weights)
     a.scores, a.scores2 = _p(scores), _p(scores2)
     a.pooled_q, a.pooled_k = _p(pooled_q), _p(pooled_k)
+    keep = _heads(a, heads)  # noqa: F841  (the array must outlive the calls)
     nb = C.c_size_t(0)
     F.check(lib.sa_estimate_workspace_bytes(C.byref(a), C.byref(nb)))
     ws, n = _workspace(nb.value, q)
@@ -142,21 +156,28 @@ def sa_vs_build(vert, vert_cnt, slash, slash_cnt, iv, iv_cnt, col, col_cnt, seq:
 
 
 def sa_block_sparse_fwd(q, k, v, out, *, block_idx=None, block_cnt=None, iv=None, iv_cnt=None, col=None,
-                        col_cnt=None, lse=None, scale=None, block_size: int = 64):
-    """Sparse attention forward; q [B,Hq,N,d], k/v [B,Hkv,N,d], out [B,Hq,N,d]."""
+                        col_cnt=None, ashape=None, lse=None, scale=None, block_size: int = 64, heads=None):
+    """Sparse attention forward; q [B,Hq,N,d], k/v [B,Hkv,N,d], out [B,Hq,N,d].
+    Keys from block tables, vertical-slash tables, or ashape=(n_sink, n_local)
+    blocks; heads: optional sequence of query heads (tables compact over them)."""
     lib = load()
     a = F.FwdArgs()
     B, Hq, N, d = q.shape
-    a.mode = F.SA_FWD_BLOCK if block_idx is not None else F.SA_FWD_VSLASH
+    if ashape is not None:
+        a.mode = F.SA_FWD_ASHAPE
+        a.n_sink, a.n_local = ashape
+    else:
+        a.mode = F.SA_FWD_BLOCK if block_idx is not None else F.SA_FWD_VSLASH
     a.dtype, a.out_dtype, a.block_size = _dt(q), _dt(out), block_size
     a.batch, a.heads_q, a.heads_kv, a.seq, a.head_dim = B, Hq, k.shape[1], N, d
     a.scale = (1.0 / math.sqrt(d)) if scale is None else scale
     a.q, a.k, a.v, a.out, a.lse = _p(q), _p(k), _p(v), _p(out), _p(lse)
-    if block_idx is not None:
+    if a.mode == F.SA_FWD_BLOCK:
         a.block_idx, a.block_cnt, a.kmax = _p(block_idx), _p(block_cnt), block_idx.shape[-1]
-    else:
+    elif a.mode == F.SA_FWD_VSLASH:
         a.iv, a.iv_cnt, a.col, a.col_cnt = _p(iv), _p(iv_cnt), _p(col), _p(col_cnt)
         a.max_iv, a.max_col = iv.shape[-2], col.shape[-1]
+    keep = _heads(a, heads)  # noqa: F841
     F.check(lib.sa_block_sparse_fwd(C.byref(a), None, 0, _stream()))
 
 

@@ -15,9 +15,9 @@ LIB_PATH = os.path.join(HERE, "libsa.so")
 SA_OK = 0
 SA_F32, SA_BF16, SA_I32 = 0, 1, 2
 SA_EST_BLOCK_MEANPOOL, SA_EST_VSLASH, SA_EST_CENTROID, SA_EST_INDEXER = 0, 1, 2, 3
-SA_FWD_BLOCK, SA_FWD_VSLASH = 0, 1
+SA_FWD_BLOCK, SA_FWD_VSLASH, SA_FWD_ASHAPE = 0, 1, 2
 SA_GATHER_CLUSTER, SA_GATHER_TOKEN = 0, 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
                 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_LAUNCH", 8: "SA_ERR_VALUE"}
@@ -33,7 +33,7 @@ class EstimateArgs(C.Structure):
                 ("n_centroids", C.c_int64), ("q_pos0", C.c_int64), ("block_size", C.c_int32),
                 ("last_q", C.c_int32), ("scale", C.c_float), ("reserved0", C.c_int32), ("q", P), ("k", P),
                 ("centroids", P), ("weights", P), ("scores", P), ("scores2", P), ("pooled_q", P),
-                ("pooled_k", P)]
+                ("pooled_k", P), ("head_list", P), ("n_heads_list", C.c_int32), ("reserved1", C.c_int32)]
 
 
 class SelectArgs(C.Structure):
@@ -55,7 +55,9 @@ class FwdArgs(C.Structure):
                 ("batch", C.c_int64), ("heads_q", C.c_int64), ("heads_kv", C.c_int64), ("seq", C.c_int64),
                 ("head_dim", C.c_int64), ("scale", C.c_float), ("kmax", C.c_int32), ("q", P), ("k", P),
                 ("v", P), ("out", P), ("lse", P), ("block_idx", P), ("block_cnt", P), ("iv", P),
-                ("iv_cnt", P), ("col", P), ("col_cnt", P), ("max_iv", C.c_int32), ("max_col", C.c_int32)]
+                ("iv_cnt", P), ("col", P), ("col_cnt", P), ("max_iv", C.c_int32), ("max_col", C.c_int32),
+                ("n_sink", C.c_int32), ("n_local", C.c_int32), ("head_list", P), ("n_heads_list", C.c_int32),
+                ("reserved1", C.c_int32)]
 
 
 class GatherArgs(C.Structure):

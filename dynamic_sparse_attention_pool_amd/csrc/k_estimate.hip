@@ -19,7 +19,7 @@ constexpr int kBlk = 64;
 // loads (HBM-streaming), fp32 partial sums per thread, a fixed-order
 // reduction through LDS, then the mean.
 template <typename T, int D>
-__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, int64_t seq, int nb,
+__global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, int hq, HeadList hl, int64_t seq, int nb,
                                               float* __restrict__ out) {
   constexpr int E = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = D / E;         // chunks per row
@@ -29,7 +29,9 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, int64_t s
   const int64_t r = blockIdx.x / nb;
   const int j = blockIdx.x % nb;
   const int rp = tid / CPR, c = tid % CPR;
-  const T* base = x + (r * seq + (int64_t)j * kBlk) * D + c * E;
+  int sb, sh;
+  listed_row(r, hq, hl, sb, sh);
+  const T* base = x + (((int64_t)sb * hq + sh) * seq + (int64_t)j * kBlk) * D + c * E;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -60,7 +62,7 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, int64_t s
 // 64x64 output tile per workgroup, 4x4 per thread, fp32 FMAs in dimension
 // order.  Tiles strictly above the diagonal only write -inf.
 __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ pq, const float* __restrict__ pk,
-                                                     int hq, int hkv, int nb, int D, float scale,
+                                                     int hq, int hkv, HeadList hl, int nb, int D, float scale,
                                                      float* __restrict__ S) {
   __shared__ float Qs[64][33];
   __shared__ float Ks[64][33];
@@ -69,7 +71,8 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
   const int bh = blockIdx.x / (nbt * nbt);
   const int tile = blockIdx.x % (nbt * nbt);
   const int ti = tile / nbt, tj = tile % nbt;
-  const int b = bh / hq, h = bh % hq;
+  int b, h;
+  listed_row(bh, hq, hl, b, h);
   const int g = (h * hkv) / hq;
   float* Sb = S + (int64_t)bh * nb * nb;
   if (tj > ti) {
@@ -125,7 +128,7 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
 // MFMA tiles.  Tiles above the diagonal only write -inf.
 template <int D>
 __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restrict__ pq, const float* __restrict__ pk,
-                                                          int hq, int hkv, int nb, float scale,
+                                                          int hq, int hkv, HeadList hl, int nb, float scale,
                                                           float* __restrict__ S) {
   constexpr int T = 128, DC = 32, P = DC + 2;
   __shared__ float Qs[T * P];
@@ -135,7 +138,8 @@ __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restric
   const int bh = blockIdx.x / (nbt * nbt);
   const int tile = blockIdx.x % (nbt * nbt);
   const int ti = tile / nbt, tj = tile % nbt;
-  const int b = bh / hq, h = bh % hq;
+  int b, h;
+  listed_row(bh, hq, hl, b, h);
   const int g = (h * hkv) / hq;
   float* Sb = S + (int64_t)bh * nb * nb;
   if (tj > ti) {
@@ -250,44 +254,45 @@ __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q,
 
 }  // namespace
 
-hipError_t launch_pool(const void* x, int64_t rows, int64_t seq, int head_dim, bool bf16, int block,
-                       float* out, hipStream_t stream) {
+hipError_t launch_pool(const void* x, int64_t batch, int hq, const HeadList& hl, int64_t seq, int head_dim,
+                       bool bf16, int block, float* out, hipStream_t stream) {
   if (block != kBlk) return hipErrorInvalidValue;
   const int nb = (int)(seq / kBlk);
-  const int64_t nblk = rows * nb;
+  const int64_t nblk = batch * (hl.n > 0 ? hl.n : hq) * nb;
   if (nblk == 0) return hipSuccess;
   const dim3 grid((unsigned)nblk);
   if (bf16 && head_dim == 128)
-    hipLaunchKernelGGL((k_pool<uint16_t, 128>), grid, dim3(256), 0, stream, (const uint16_t*)x, seq, nb, out);
+    hipLaunchKernelGGL((k_pool<uint16_t, 128>), grid, dim3(256), 0, stream, (const uint16_t*)x, hq, hl, seq, nb, out);
   else if (bf16 && head_dim == 64)
-    hipLaunchKernelGGL((k_pool<uint16_t, 64>), grid, dim3(256), 0, stream, (const uint16_t*)x, seq, nb, out);
+    hipLaunchKernelGGL((k_pool<uint16_t, 64>), grid, dim3(256), 0, stream, (const uint16_t*)x, hq, hl, seq, nb, out);
   else if (!bf16 && head_dim == 128)
-    hipLaunchKernelGGL((k_pool<float, 128>), grid, dim3(256), 0, stream, (const float*)x, seq, nb, out);
+    hipLaunchKernelGGL((k_pool<float, 128>), grid, dim3(256), 0, stream, (const float*)x, hq, hl, seq, nb, out);
   else if (!bf16 && head_dim == 64)
-    hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, stream, (const float*)x, seq, nb, out);
+    hipLaunchKernelGGL((k_pool<float, 64>), grid, dim3(256), 0, stream, (const float*)x, hq, hl, seq, nb, out);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
-hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, int nb,
-                              int head_dim, float scale, float* scores, hipStream_t stream) {
+hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, const HeadList& hl,
+                              int nb, int head_dim, float scale, float* scores, hipStream_t stream) {
+  const int64_t rows = (int64_t)batch * (hl.n > 0 ? hl.n : hq);
   if (head_dim == 128 || head_dim == 64) {
     const int nbt2 = (nb + 127) / 128;
-    const int64_t n2 = (int64_t)batch * hq * nbt2 * nbt2;
+    const int64_t n2 = rows * nbt2 * nbt2;
     if (n2 == 0) return hipSuccess;
     if (head_dim == 128)
-      hipLaunchKernelGGL((k_block_score_mfma<128>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, nb,
-                         scale, scores);
+      hipLaunchKernelGGL((k_block_score_mfma<128>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, hl,
+                         nb, scale, scores);
     else
-      hipLaunchKernelGGL((k_block_score_mfma<64>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, nb,
-                         scale, scores);
+      hipLaunchKernelGGL((k_block_score_mfma<64>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, hl,
+                         nb, scale, scores);
     return hipGetLastError();
   }
   const int nbt = (nb + 63) / 64;
-  const int64_t n = (int64_t)batch * hq * nbt * nbt;
+  const int64_t n = rows * nbt * nbt;
   if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_block_score, dim3((unsigned)n), dim3(256), 0, stream, pq, pk, hq, hkv, nb, head_dim,
+  hipLaunchKernelGGL(k_block_score, dim3((unsigned)n), dim3(256), 0, stream, pq, pk, hq, hkv, hl, nb, head_dim,
                      scale, scores);
   return hipGetLastError();
 }

@@ -157,6 +157,43 @@ __device__ __forceinline__ void item_of(int bid, int n_items, int grp, int nqb, 
   bg = rest / nqb;
 }
 
+// Workgroup -> batch b, query head h, query block iblk and the row of the index
+// tables.  With a head list the launch's items are (b, listed head j), each its
+// own group, and the tables are indexed compactly by b*n + j.
+struct Item {
+  int b, h, iblk;
+  int64_t trow;
+};
+
+__device__ __forceinline__ Item item_at(const FwdParams& p, int bid, int n_items, int order) {
+  const int grp = p.heads_q / p.heads_kv;
+  int hh, ii, bg;
+  Item it;
+  if (p.hl.n > 0) {
+    item_of(bid, n_items, 1, p.nqb, order, hh, ii, bg);
+    it.b = bg / p.hl.n;
+    it.h = p.hl.h[bg % p.hl.n];
+  } else {
+    item_of(bid, n_items, grp, p.nqb, order, hh, ii, bg);
+    it.b = bg / p.heads_kv;
+    it.h = (bg % p.heads_kv) * grp + hh;
+  }
+  it.iblk = p.nqb - 1 - ii;  // long rows first
+  const int64_t r = p.hl.n > 0 ? (int64_t)bg : (int64_t)it.b * p.heads_q + it.h;
+  it.trow = r * p.nqb + it.iblk;
+  return it;
+}
+
+// A-shape rows need no table: blocks 0 .. n_sink-1 and the n_local blocks
+// ending at the diagonal, ascending and each once.  Returns the count.
+__device__ __forceinline__ int ashape_list(int32_t* dst, int iblk, int n_sink, int n_local, int tid, int nt) {
+  const int se = min(n_sink, iblk + 1);
+  const int lb = max(se, iblk - n_local + 1);
+  const int cnt = se + (iblk + 1 - lb);
+  for (int e = tid; e < cnt; e += nt) dst[e] = e < se ? e : lb + (e - se);
+  return cnt;
+}
+
 // Element offset of 16-byte chunk `chunk` of row `row` in a swizzled tile.
 template <int D>
 __device__ __forceinline__ int swz(int row, int chunk) {
@@ -170,15 +207,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   __shared__ int32_t meta[MODE == 0 ? 2048 : kMetaMax];
   constexpr int NDMA = D / 16;  // direct-to-LDS copies per wave per tile (K or V)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int grp = p.heads_q / p.heads_kv;
-  int hh, ii, bg;
-  item_of(blockIdx.x, gridDim.x, grp, p.nqb, p.order, hh, ii, bg);
-  const int g = bg % p.heads_kv;
-  const int b = bg / p.heads_kv;
-  const int iblk = p.nqb - 1 - ii;  // long rows first
-  const int h = g * grp + hh;
+  const Item item = item_at(p, blockIdx.x, gridDim.x, p.order);
+  const int b = item.b, h = item.h, iblk = item.iblk;
+  const int g = h / (p.heads_q / p.heads_kv);
   const int64_t N = p.seq;
-  const int64_t row_id = ((int64_t)b * p.heads_q + h) * p.nqb + iblk;
+  const int64_t row_id = item.trow;
 
   const uint16_t* qb = reinterpret_cast<const uint16_t*>(p.q) + (((int64_t)b * p.heads_q + h) * N + (int64_t)iblk * kBlk) * D;
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + ((int64_t)b * p.heads_kv + g) * N * D;
@@ -188,9 +221,14 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   TileIter<MODE> it;
   const int32_t* cols = nullptr;
   if (MODE == 0) {
-    const int cnt = min(p.block_cnt[row_id], 2048);
-    const int32_t* src = p.block_idx + row_id * p.kmax;
-    for (int e = tid; e < cnt; e += kThreads) meta[e] = src[e];
+    int cnt;
+    if (p.ashape) {
+      cnt = ashape_list(meta, iblk, p.n_sink, p.n_local, tid, kThreads);
+    } else {
+      cnt = min(p.block_cnt[row_id], 2048);
+      const int32_t* src = p.block_idx + row_id * p.kmax;
+      for (int e = tid; e < cnt; e += kThreads) meta[e] = src[e];
+    }
     it.bidx = meta;
     it.cnt = cnt;
     it.iblk = iblk;
@@ -395,20 +433,13 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
   __shared__ float Ks[kBlk][D];
   __shared__ float Vs[kBlk][D];
   __shared__ int32_t keyS[kBlk];
+  __shared__ int32_t ash[MODE == 0 ? 2048 : 1];
   const int tid = threadIdx.x;
-  const int item = xcd_remap(blockIdx.x, gridDim.x);
-  const int grp = p.heads_q / p.heads_kv;
-  int rest = item;
-  const int hh = rest % grp;
-  rest /= grp;
-  const int ii = rest % p.nqb;
-  rest /= p.nqb;
-  const int g = rest % p.heads_kv;
-  const int b = rest / p.heads_kv;
-  const int iblk = p.nqb - 1 - ii;
-  const int h = g * grp + hh;
+  const Item item = item_at(p, blockIdx.x, gridDim.x, 0);
+  const int b = item.b, h = item.h, iblk = item.iblk;
+  const int g = h / (p.heads_q / p.heads_kv);
   const int64_t N = p.seq;
-  const int64_t row_id = ((int64_t)b * p.heads_q + h) * p.nqb + iblk;
+  const int64_t row_id = item.trow;
   const int qpos = iblk * kBlk + tid;
   const float* qr = reinterpret_cast<const float*>(p.q) + (((int64_t)b * p.heads_q + h) * N + qpos) * D;
   const float* kb = reinterpret_cast<const float*>(p.k) + ((int64_t)b * p.heads_kv + g) * N * D;
@@ -417,8 +448,14 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
   TileIter<MODE> it;
   const int32_t* cols = nullptr;
   if (MODE == 0) {
-    it.bidx = p.block_idx + row_id * p.kmax;
-    it.cnt = p.block_cnt[row_id];
+    if (p.ashape) {
+      it.cnt = ashape_list(ash, iblk, p.n_sink, p.n_local, tid, 64);
+      it.bidx = ash;
+      __syncthreads();
+    } else {
+      it.bidx = p.block_idx + row_id * p.kmax;
+      it.cnt = p.block_cnt[row_id];
+    }
     it.iblk = iblk;
   } else {
     it.iv = p.iv + row_id * p.max_iv * 2;
@@ -476,7 +513,7 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
 
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, bool out_bf16,
                       hipStream_t stream) {
-  const int n_items = p.batch * p.heads_q * p.nqb;
+  const int n_items = p.batch * (p.hl.n > 0 ? p.hl.n : p.heads_q) * p.nqb;
   if (n_items == 0) return hipSuccess;
   const dim3 grid(n_items);
   // KV-head-major order once the K/V of all heads (bf16) outgrows ~192 MB,

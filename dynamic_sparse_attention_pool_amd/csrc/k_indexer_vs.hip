@@ -289,17 +289,19 @@ struct VsOps {
 // pass 1: per (head row, chunk of tiles, query) running max / sum (log2 domain)
 template <int D>
 __global__ __launch_bounds__(128) void k_vs_stats(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                  int hq, int hkv, int64_t N, float sl2, int nchunk,
+                                                  int hq, int hkv, HeadList hl, int64_t N, float sl2, int nchunk,
                                                   float* __restrict__ stats) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
-  const int b = bh / hq, h = bh % hq, g = h * hkv / hq;
+  int b, h;
+  listed_row(bh, hq, hl, b, h);
+  const int g = h * hkv / hq;
   const int r = 32 * wv + l32;  // query row among the last 64
   const int64_t qpos = N - kVsLast + r;
   const uint16_t* kb = k + ((int64_t)b * hkv + g) * N * D;
   bf16x8 qv[D / 16];
   {
-    const uint16_t* qr = q + ((int64_t)bh * N + qpos) * D + (D / 2) * hf;
+    const uint16_t* qr = q + (((int64_t)b * hq + h) * N + qpos) * D + (D / 2) * hf;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qv[s] = as_bf16x8(ldg16(qr + 8 * s));
   }
@@ -350,19 +352,21 @@ __global__ __launch_bounds__(64) void k_vs_stats_merge(const float* __restrict__
 // pass 2: probabilities per tile -> column sums (final) and diagonal partials
 template <int D>
 __global__ __launch_bounds__(128) void k_vs_accum(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                  int hq, int hkv, int64_t N, float sl2, int nchunk,
+                                                  int hq, int hkv, HeadList hl, int64_t N, float sl2, int nchunk,
                                                   const float* __restrict__ ml, float* __restrict__ a_v,
                                                   float* __restrict__ dpart) {
   __shared__ float P[64][kVsLast + 1];  // [key][query row]
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, l32 = lane & 31;
   const int bh = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
-  const int b = bh / hq, h = bh % hq, g = h * hkv / hq;
+  int b, h;
+  listed_row(bh, hq, hl, b, h);
+  const int g = h * hkv / hq;
   const int r = 32 * wv + l32;
   const int64_t qpos = N - kVsLast + r;
   const uint16_t* kb = k + ((int64_t)b * hkv + g) * N * D;
   bf16x8 qv[D / 16];
   {
-    const uint16_t* qr = q + ((int64_t)bh * N + qpos) * D + (D / 2) * hf;
+    const uint16_t* qr = q + (((int64_t)b * hq + h) * N + qpos) * D + (D / 2) * hf;
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) qv[s] = as_bf16x8(ldg16(qr + 8 * s));
   }
@@ -454,11 +458,11 @@ size_t vs_workspace_bytes(int64_t rows, int64_t seq) {
          a256((size_t)(rows * ntile * 128) * 4);
 }
 
-hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv, int64_t seq,
-                              int head_dim, int last_q, float scale, float* a_v, float* a_s, void* ws,
-                              hipStream_t stream) {
+hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv,
+                              const HeadList& hl, int64_t seq, int head_dim, int last_q, float scale, float* a_v,
+                              float* a_s, void* ws, hipStream_t stream) {
   if (last_q != kVsLast) return hipErrorInvalidValue;
-  const int rows = batch * hq;
+  const int rows = batch * (hl.n > 0 ? hl.n : hq);
   const int64_t ntile = (seq + 63) / 64;
   const int nchunk = (int)((ntile + kVsTilesPerWg - 1) / kVsTilesPerWg);
   char* p = static_cast<char*>(ws);
@@ -470,13 +474,13 @@ hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, i
   const float sl2 = scale * kLog2e;
   const dim3 grid((unsigned)((int64_t)rows * nchunk));
   if (head_dim == 128) {
-    hipLaunchKernelGGL((k_vs_stats<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, stats);
+    hipLaunchKernelGGL((k_vs_stats<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, stats);
     hipLaunchKernelGGL(k_vs_stats_merge, dim3(rows), dim3(64), 0, stream, stats, nchunk, ml);
-    hipLaunchKernelGGL((k_vs_accum<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, ml, a_v, dpart);
+    hipLaunchKernelGGL((k_vs_accum<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, ml, a_v, dpart);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((k_vs_stats<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, stats);
+    hipLaunchKernelGGL((k_vs_stats<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, stats);
     hipLaunchKernelGGL(k_vs_stats_merge, dim3(rows), dim3(64), 0, stream, stats, nchunk, ml);
-    hipLaunchKernelGGL((k_vs_accum<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, seq, sl2, nchunk, ml, a_v, dpart);
+    hipLaunchKernelGGL((k_vs_accum<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, ml, a_v, dpart);
   } else {
     return hipErrorInvalidValue;
   }

@@ -7,6 +7,27 @@
 
 namespace sa {
 
+// Query heads covered by one launch.  n == 0: every head, in order.  n > 0:
+// the launch covers (b, h[j]) for j < n; q, k, v, out and lse keep their full
+// [B, Hq, ...] layout, while per-row scores and tables of the launch are
+// indexed compactly by b*n + j.  Passed by value in the kernel arguments.
+constexpr int kMaxListedHeads = 256;
+struct HeadList {
+  int32_t n;
+  int16_t h[kMaxListedHeads];
+};
+
+// Compact row bh -> (batch, query head).
+__host__ __device__ inline void listed_row(int64_t bh, int hq, const HeadList& hl, int& b, int& h) {
+  if (hl.n > 0) {
+    b = (int)(bh / hl.n);
+    h = hl.h[bh % hl.n];
+  } else {
+    b = (int)(bh / hq);
+    h = (int)(bh % hq);
+  }
+}
+
 // ---------------------------------------------------------------- forward
 struct FwdParams {
   const void* q;
@@ -25,23 +46,27 @@ struct FwdParams {
   int32_t kmax, max_iv, max_col;
   float scale;
   int32_t order;  // workgroup order of the bf16 kernel, chosen by launch_fwd
+  int32_t ashape, n_sink, n_local;  // block lists generated: blocks 0..n_sink-1 and the n_local up to the diagonal
+  HeadList hl;
 };
 hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, bool out_bf16,
                       hipStream_t stream);
 
 // ---------------------------------------------------------------- estimate
-hipError_t launch_pool(const void* x, int64_t rows, int64_t seq, int head_dim, bool bf16, int block,
-                       float* out, hipStream_t stream);
-hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, int nb,
-                              int head_dim, float scale, float* scores, hipStream_t stream);
+// rows of x: batch*hq rows of seq tokens; with a head list, the listed rows only
+// (out compact).
+hipError_t launch_pool(const void* x, int64_t batch, int hq, const HeadList& hl, int64_t seq, int head_dim,
+                       bool bf16, int block, float* out, hipStream_t stream);
+hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, const HeadList& hl,
+                              int nb, int head_dim, float scale, float* scores, hipStream_t stream);
 hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,
                                  int C, int head_dim, float scale, float* out, hipStream_t stream);
 hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
                           int64_t pos0, float* out, hipStream_t stream);
 size_t vs_workspace_bytes(int64_t rows, int64_t seq);
-hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv, int64_t seq,
-                              int head_dim, int last_q, float scale, float* a_v, float* a_s, void* ws,
-                              hipStream_t stream);
+hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv,
+                              const HeadList& hl, int64_t seq, int head_dim, int last_q, float scale, float* a_v,
+                              float* a_s, void* ws, hipStream_t stream);
 
 // ---------------------------------------------------------------- select
 struct SelectParams {

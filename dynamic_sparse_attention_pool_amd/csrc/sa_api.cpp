@@ -49,6 +49,25 @@ hipStream_t as_stream(void* s) {
 
 constexpr int kBlock = 64;
 
+// Host head list -> launch-argument form; rejects duplicates and heads outside
+// [0, hq).  A NULL list means every head.
+int make_head_list(const int32_t* list, int32_t n, int64_t hq, const char* who, sa::HeadList& hl) {
+  hl.n = 0;
+  if (!list) return ok();
+  if (n <= 0 || n > sa::kMaxListedHeads || n > hq)
+    return fail(SA_ERR_VALUE, "%s: n_heads_list must lie in [1, min(heads_q, %d)]", who, sa::kMaxListedHeads);
+  bool seen[sa::kMaxListedHeads] = {};
+  for (int j = 0; j < n; ++j) {
+    const int32_t h = list[j];
+    if (h < 0 || h >= hq || h >= sa::kMaxListedHeads) return fail(SA_ERR_VALUE, "%s: head_list[%d] = %d is not a query head", who, j, h);
+    if (seen[h]) return fail(SA_ERR_VALUE, "%s: head %d listed twice", who, h);
+    seen[h] = true;
+    hl.h[j] = (int16_t)h;
+  }
+  hl.n = n;
+  return ok();
+}
+
 // ---------------------------------------------------------------- estimate
 int check_estimate(const sa_estimate_args* a, size_t* ws) {
   if (!a) return fail(SA_ERR_NULL, "sa_estimate: args is NULL");
@@ -67,8 +86,11 @@ int check_estimate(const sa_estimate_args* a, size_t* ws) {
       if (a->seq_q != a->seq_k) return fail(SA_ERR_SHAPE, "sa_estimate(BLOCK): seq_q must equal seq_k (prefill)");
       if (a->seq_q % kBlock) return fail(SA_ERR_SHAPE, "sa_estimate(BLOCK): seq must be a multiple of 64");
       if (!(a->scale > 0.f)) return fail(SA_ERR_VALUE, "sa_estimate: scale must be > 0");
+      sa::HeadList hl;
+      if (const int rc = make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_estimate(BLOCK)", hl)) return rc;
       const int64_t nb = a->seq_q / kBlock;
-      if (!a->pooled_q) *ws += align256((size_t)(a->batch * a->heads_q * nb * a->head_dim) * 4);
+      const int64_t nh = hl.n > 0 ? hl.n : a->heads_q;
+      if (!a->pooled_q) *ws += align256((size_t)(a->batch * nh * nb * a->head_dim) * 4);
       if (!a->pooled_k) *ws += align256((size_t)(a->batch * a->heads_kv * nb * a->head_dim) * 4);
       return ok();
     }
@@ -81,10 +103,13 @@ int check_estimate(const sa_estimate_args* a, size_t* ws) {
       if (a->seq_q != a->seq_k || a->seq_q % kBlock) return fail(SA_ERR_SHAPE, "sa_estimate(VSLASH): seq_q == seq_k, a multiple of 64");
       if (!a->scores2) return fail(SA_ERR_NULL, "sa_estimate(VSLASH): scores2 (slash scores) is required");
       if (!(a->scale > 0.f)) return fail(SA_ERR_VALUE, "sa_estimate: scale must be > 0");
-      *ws = sa::vs_workspace_bytes(a->batch * a->heads_q, a->seq_q);
+      sa::HeadList hl;
+      if (const int rc = make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_estimate(VSLASH)", hl)) return rc;
+      *ws = sa::vs_workspace_bytes(a->batch * (hl.n > 0 ? hl.n : a->heads_q), a->seq_q);
       return ok();
     }
     case SA_EST_CENTROID: {
+      if (a->head_list) return fail(SA_ERR_UNSUPPORTED, "sa_estimate(CENTROID): no head list");
       if (a->dtype != SA_F32 && a->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "sa_estimate(CENTROID): dtype must be F32 or BF16");
       if (!a->centroids) return fail(SA_ERR_NULL, "sa_estimate(CENTROID): centroids required");
       if (a->n_centroids <= 0) return fail(SA_ERR_SHAPE, "sa_estimate(CENTROID): n_centroids must be positive");
@@ -96,6 +121,7 @@ int check_estimate(const sa_estimate_args* a, size_t* ws) {
       return ok();
     }
     case SA_EST_INDEXER: {
+      if (a->head_list) return fail(SA_ERR_UNSUPPORTED, "sa_estimate(INDEXER): no head list");
       if (a->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "sa_estimate(INDEXER): dtype must be BF16");
       if (!a->weights) return fail(SA_ERR_NULL, "sa_estimate(INDEXER): weights required");
       if (a->head_dim != 64) return fail(SA_ERR_UNSUPPORTED, "sa_estimate(INDEXER): head_dim must be 64");
@@ -194,28 +220,36 @@ int sa_estimate(const sa_estimate_args* a, void* workspace, size_t workspace_byt
   const hipStream_t st = as_stream(stream);
   switch (a->kind) {
     case SA_EST_BLOCK_MEANPOOL: {
+      sa::HeadList hl, all;
+      all.n = 0;
+      make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_estimate(BLOCK)", hl);  // checked above
       const int64_t nb = a->seq_q / kBlock;
+      const int64_t nh = hl.n > 0 ? hl.n : a->heads_q;
       char* w = static_cast<char*>(workspace);
       float* pq = a->pooled_q;
       float* pk = a->pooled_k;
       if (!pq) {
         pq = reinterpret_cast<float*>(w);
-        w += align256((size_t)(a->batch * a->heads_q * nb * a->head_dim) * 4);
+        w += align256((size_t)(a->batch * nh * nb * a->head_dim) * 4);
       }
       if (!pk) pk = reinterpret_cast<float*>(w);
       const bool bf = a->dtype == SA_BF16;
-      hipError_t e = sa::launch_pool(a->q, a->batch * a->heads_q, a->seq_q, (int)a->head_dim, bf, kBlock, pq, st);
-      if (e == hipSuccess) e = sa::launch_pool(a->k, a->batch * a->heads_kv, a->seq_k, (int)a->head_dim, bf, kBlock, pk, st);
+      hipError_t e = sa::launch_pool(a->q, a->batch, (int)a->heads_q, hl, a->seq_q, (int)a->head_dim, bf, kBlock, pq, st);
       if (e == hipSuccess)
-        e = sa::launch_block_score(pq, pk, (int)a->batch, (int)a->heads_q, (int)a->heads_kv, (int)nb, (int)a->head_dim,
-                                   a->scale, a->scores, st);
+        e = sa::launch_pool(a->k, a->batch, (int)a->heads_kv, all, a->seq_k, (int)a->head_dim, bf, kBlock, pk, st);
+      if (e == hipSuccess)
+        e = sa::launch_block_score(pq, pk, (int)a->batch, (int)a->heads_q, (int)a->heads_kv, hl, (int)nb,
+                                   (int)a->head_dim, a->scale, a->scores, st);
       return launched(e, "sa_estimate(BLOCK)");
     }
-    case SA_EST_VSLASH:
+    case SA_EST_VSLASH: {
+      sa::HeadList hl;
+      make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_estimate(VSLASH)", hl);  // checked above
       return launched(sa::launch_vs_estimate((const uint16_t*)a->q, (const uint16_t*)a->k, (int)a->batch, (int)a->heads_q,
-                                             (int)a->heads_kv, a->seq_q, (int)a->head_dim, a->last_q, a->scale, a->scores,
-                                             a->scores2, workspace, st),
+                                             (int)a->heads_kv, hl, a->seq_q, (int)a->head_dim, a->last_q, a->scale,
+                                             a->scores, a->scores2, workspace, st),
                       "sa_estimate(VSLASH)");
+    }
     case SA_EST_CENTROID:
       return launched(sa::launch_centroid_score(a->q, a->dtype == SA_BF16, a->centroids, (int)a->seq_q, (int)a->heads_q,
                                                 (int)a->heads_kv, (int)a->n_centroids, (int)a->head_dim, a->scale, a->scores,
@@ -343,10 +377,15 @@ static int check_fwd(const sa_fwd_args* a) {
     if (a->max_iv <= 0 || a->max_col <= 0) return fail(SA_ERR_SHAPE, "sa_block_sparse_fwd(VSLASH): capacities must be positive");
     if (a->dtype == SA_BF16 && (a->max_iv > 64 || a->max_col > 2048))
       return fail(SA_ERR_UNSUPPORTED, "sa_block_sparse_fwd(VSLASH): bf16 path stages at most 64 intervals and 2048 columns per row");
+  } else if (a->mode == SA_FWD_ASHAPE) {
+    if (a->n_sink < 0 || a->n_local < 0) return fail(SA_ERR_VALUE, "sa_block_sparse_fwd(ASHAPE): n_sink and n_local must be >= 0");
+    if ((int64_t)a->n_sink + a->n_local > 2048)
+      return fail(SA_ERR_UNSUPPORTED, "sa_block_sparse_fwd(ASHAPE): n_sink + n_local above 2048 blocks");
   } else {
     return fail(SA_ERR_VALUE, "sa_block_sparse_fwd: unknown mode %d", a->mode);
   }
-  return ok();
+  sa::HeadList hl;
+  return make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_block_sparse_fwd", hl);
 }
 
 int sa_block_sparse_fwd_workspace_bytes(const sa_fwd_args* a, size_t* bytes) {
@@ -384,7 +423,13 @@ int sa_block_sparse_fwd(const sa_fwd_args* a, void* workspace, size_t workspace_
   p.max_col = a->max_col;
   p.scale = a->scale;
   p.order = 0;
-  return launched(sa::launch_fwd(p, (int)a->head_dim, a->mode, a->dtype == SA_BF16, a->out_dtype == SA_BF16,
+  p.ashape = a->mode == SA_FWD_ASHAPE;
+  p.n_sink = a->n_sink;
+  p.n_local = a->n_local;
+  make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_block_sparse_fwd", p.hl);  // checked above
+  // the A-shape lists are generated by the block-mode kernels
+  const int kmode = a->mode == SA_FWD_VSLASH ? 1 : 0;
+  return launched(sa::launch_fwd(p, (int)a->head_dim, kmode, a->dtype == SA_BF16, a->out_dtype == SA_BF16,
                                  as_stream(stream)),
                   "sa_block_sparse_fwd");
 }

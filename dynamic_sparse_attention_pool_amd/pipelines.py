@@ -1,4 +1,4 @@
-"""Chained calls of the libsa entry points for the four workload families.
+"""Chained calls of the libsa entry points for the workload families.
 
 Each class allocates its device buffers once (torch is the allocator) and
 exposes the steps of its path as methods that only enqueue libsa calls on
@@ -28,31 +28,45 @@ def max_kept_blocks(nb: int, n_sink: int, n_local: int, k=None, ratio=None) -> i
     return best
 
 
+def _out_buffers(q, out_dtype, with_lse, out=None, lse=None):
+    torch = _t()
+    B, Hq, N, _ = q.shape
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=q.device)
+    if lse is None and with_lse:
+        lse = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    return out, lse
+
+
 class BlockSparseLayer:
-    """Block-sparse prefill: pooled estimate -> top-k with sink/local -> forward."""
+    """Block-sparse prefill: pooled estimate -> top-k with sink/local -> forward.
+    ``heads`` restricts the layer to those query heads (tables compact over
+    them); ``out``/``lse`` may be shared with other layers of the same heads'
+    tensor."""
 
     def __init__(self, q, k, v, *, n_sink: int, n_local: int, ratio=None, k_fixed=None, out_dtype=None,
-                 scale=None, with_lse=False):
+                 scale=None, with_lse=False, heads=None, out=None, lse=None):
         torch = _t()
         self.q, self.k, self.v = q, k, v
         B, Hq, N, d = q.shape
+        self.heads = None if heads is None else [int(h) for h in heads]
+        nh = Hq if heads is None else len(self.heads)
         self.nb = N // 64
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
         self.n_sink, self.n_local, self.ratio, self.k_fixed = n_sink, n_local, ratio, k_fixed
         self.kmax = max_kept_blocks(self.nb, n_sink, n_local, k_fixed, ratio)
         dev = q.device
-        self.scores = torch.empty((B, Hq, self.nb, self.nb), dtype=torch.float32, device=dev)
-        self.pooled_q = torch.empty((B, Hq, self.nb, d), dtype=torch.float32, device=dev)
+        self.scores = torch.empty((B, nh, self.nb, self.nb), dtype=torch.float32, device=dev)
+        self.pooled_q = torch.empty((B, nh, self.nb, d), dtype=torch.float32, device=dev)
         self.pooled_k = torch.empty((B, k.shape[1], self.nb, d), dtype=torch.float32, device=dev)
-        self.idx = torch.empty((B, Hq, self.nb, self.kmax), dtype=torch.int32, device=dev)
-        self.cnt = torch.empty((B, Hq, self.nb), dtype=torch.int32, device=dev)
-        self.out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
-        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if with_lse else None
+        self.idx = torch.empty((B, nh, self.nb, self.kmax), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((B, nh, self.nb), dtype=torch.int32, device=dev)
+        self.out, self.lse = _out_buffers(q, out_dtype, with_lse, out, lse)
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def estimate(self):
         sa_estimate(BLOCK_MEANPOOL, self.q, self.k, self.scores, scale=self.scale, pooled_q=self.pooled_q,
-                    pooled_k=self.pooled_k)
+                    pooled_k=self.pooled_k, heads=self.heads)
 
     def select(self):
         kw = dict(n_sink=self.n_sink, n_local=self.n_local, causal=True, causal_period=self.nb,
@@ -65,7 +79,7 @@ class BlockSparseLayer:
 
     def forward(self):
         sa_block_sparse_fwd(self.q, self.k, self.v, self.out, block_idx=self.idx, block_cnt=self.cnt,
-                            lse=self.lse, scale=self.scale)
+                            lse=self.lse, scale=self.scale, heads=self.heads)
 
     def step(self):
         self.estimate()
@@ -77,31 +91,34 @@ class VerticalSlashLayer:
     """Vertical-slash prefill: last-64-query estimate -> top columns and top
     offsets -> per-block tables -> forward."""
 
-    def __init__(self, q, k, v, *, n_vert: int, n_slash: int, out_dtype=None, scale=None, with_lse=False):
+    def __init__(self, q, k, v, *, n_vert: int, n_slash: int, out_dtype=None, scale=None, with_lse=False,
+                 heads=None, out=None, lse=None):
         torch = _t()
         self.q, self.k, self.v = q, k, v
         B, Hq, N, d = q.shape
-        self.N, self.R = N, B * Hq
+        self.heads = None if heads is None else [int(h) for h in heads]
+        nh = Hq if heads is None else len(self.heads)
+        self.N, self.R = N, B * nh
         self.nb = N // 64
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
         self.n_vert, self.n_slash = min(n_vert, N), min(n_slash, N)
         dev = q.device
-        self.a_v = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
-        self.a_s = torch.empty((B, Hq, N), dtype=torch.float32, device=dev)
+        self.a_v = torch.empty((B, nh, N), dtype=torch.float32, device=dev)
+        self.a_s = torch.empty((B, nh, N), dtype=torch.float32, device=dev)
         self.vert = torch.empty((self.R, self.n_vert), dtype=torch.int32, device=dev)
         self.vert_cnt = torch.empty(self.R, dtype=torch.int32, device=dev)
         self.slash = torch.empty((self.R, self.n_slash), dtype=torch.int32, device=dev)
         self.slash_cnt = torch.empty(self.R, dtype=torch.int32, device=dev)
-        self.iv = torch.empty((B, Hq, self.nb, self.n_slash, 2), dtype=torch.int32, device=dev)
-        self.iv_cnt = torch.empty((B, Hq, self.nb), dtype=torch.int32, device=dev)
-        self.col = torch.empty((B, Hq, self.nb, self.n_vert), dtype=torch.int32, device=dev)
-        self.col_cnt = torch.empty((B, Hq, self.nb), dtype=torch.int32, device=dev)
-        self.out = torch.empty(q.shape, dtype=out_dtype or q.dtype, device=dev)
-        self.lse = torch.empty((B, Hq, N), dtype=torch.float32, device=dev) if with_lse else None
+        self.iv = torch.empty((B, nh, self.nb, self.n_slash, 2), dtype=torch.int32, device=dev)
+        self.iv_cnt = torch.empty((B, nh, self.nb), dtype=torch.int32, device=dev)
+        self.col = torch.empty((B, nh, self.nb, self.n_vert), dtype=torch.int32, device=dev)
+        self.col_cnt = torch.empty((B, nh, self.nb), dtype=torch.int32, device=dev)
+        self.out, self.lse = _out_buffers(q, out_dtype, with_lse, out, lse)
         self.ws = None
 
     def estimate(self):
-        self.ws = sa_estimate(VSLASH, self.q, self.k, self.a_v, scores2=self.a_s, scale=self.scale)
+        self.ws = sa_estimate(VSLASH, self.q, self.k, self.a_v, scores2=self.a_s, scale=self.scale,
+                              heads=self.heads)
 
     def select(self):
         sa_select_topk(self.a_v.view(self.R, self.N), self.vert, self.vert_cnt, k=self.n_vert)
@@ -112,7 +129,79 @@ class VerticalSlashLayer:
 
     def forward(self):
         sa_block_sparse_fwd(self.q, self.k, self.v, self.out, iv=self.iv, iv_cnt=self.iv_cnt, col=self.col,
-                            col_cnt=self.col_cnt, lse=self.lse, scale=self.scale)
+                            col_cnt=self.col_cnt, lse=self.lse, scale=self.scale, heads=self.heads)
+
+    def step(self):
+        self.estimate()
+        self.select()
+        self.forward()
+
+
+class AShapeLayer:
+    """A-shape prefill: sink blocks plus a local window of blocks, no estimate."""
+
+    def __init__(self, q, k, v, *, n_sink: int, n_local: int, out_dtype=None, scale=None, with_lse=False,
+                 heads=None, out=None, lse=None):
+        self.q, self.k, self.v = q, k, v
+        self.heads = None if heads is None else [int(h) for h in heads]
+        self.n_sink, self.n_local = n_sink, n_local
+        self.scale = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+        self.out, self.lse = _out_buffers(q, out_dtype, with_lse, out, lse)
+
+    def estimate(self):
+        pass
+
+    def select(self):
+        pass
+
+    def forward(self):
+        sa_block_sparse_fwd(self.q, self.k, self.v, self.out, ashape=(self.n_sink, self.n_local), lse=self.lse,
+                            scale=self.scale, heads=self.heads)
+
+    def step(self):
+        self.forward()
+
+
+class MixedPatternLayer:
+    """One prefill layer whose query heads follow different patterns, from a
+    given head -> pattern assignment ("A", "VS" or "BS").  Each pattern's heads
+    run as one group: its estimate, selection and forward launch cover only
+    those heads, writing into the shared output."""
+
+    def __init__(self, q, k, v, patterns, *, a_shape=(1, 4), block=None, vslash=None, out_dtype=None,
+                 scale=None, with_lse=False):
+        Hq = q.shape[1]
+        if len(patterns) != Hq:
+            raise ValueError("one pattern per query head")
+        self.out, self.lse = _out_buffers(q, out_dtype, with_lse)
+        groups = {p: [h for h in range(Hq) if patterns[h] == p] for p in ("A", "VS", "BS")}
+        unknown = set(patterns) - set(groups)
+        if unknown:
+            raise ValueError(f"unknown patterns {sorted(unknown)}")
+        share = dict(out=self.out, lse=self.lse, scale=scale)
+        self.parts = []
+        if groups["BS"]:
+            self.parts.append(BlockSparseLayer(q, k, v, heads=groups["BS"], **(block or {}), **share))
+        if groups["VS"]:
+            n_vert, n_slash = vslash
+            self.parts.append(VerticalSlashLayer(q, k, v, n_vert=n_vert, n_slash=n_slash, heads=groups["VS"],
+                                                 **share))
+        if groups["A"]:
+            self.parts.append(AShapeLayer(q, k, v, n_sink=a_shape[0], n_local=a_shape[1], heads=groups["A"],
+                                          **share))
+        self.groups = groups
+
+    def estimate(self):
+        for p in self.parts:
+            p.estimate()
+
+    def select(self):
+        for p in self.parts:
+            p.select()
+
+    def forward(self):
+        for p in self.parts:
+            p.forward()
 
     def step(self):
         self.estimate()

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 2
+#define SA_ABI_VERSION 3
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -86,6 +86,14 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_I32 = 2 } sa_dtype;
  *   k [Nk,di] (BF16; seq_k = Nk, heads_kv = 1), weights [Hi] float.
  *   scores [T,Nk] float, -INFINITY where s > q_pos0 + t.  No scale.
  *   di must be 64; Hi a multiple of 8.
+ *
+ * Head list (BLOCK_MEANPOOL and VSLASH; "MInference 1.0" article, §方法介紹:
+ * each head runs the estimate of its own pattern): head_list, when not NULL,
+ * is a HOST array of n_heads_list distinct query-head indices in [0, Hq)
+ * (at most 256; copied into the launch, so it may be freed on return).  Only
+ * those heads are estimated, and every per-head output is compact: scores
+ * [B,n,nb,nb] (BLOCK) or [B,n,N] (VSLASH), pooled_q [B,n,nb,d], with row
+ * b*n + j for listed head j.  q, k and pooled_k keep their full layouts.
  * ====================================================================== */
 enum { SA_EST_BLOCK_MEANPOOL = 0, SA_EST_VSLASH = 1, SA_EST_CENTROID = 2, SA_EST_INDEXER = 3 };
 
@@ -112,6 +120,9 @@ typedef struct sa_estimate_args {
   float* scores2;         /* VSLASH slash scores */
   float* pooled_q;        /* BLOCK, optional */
   float* pooled_k;        /* BLOCK, optional */
+  const int32_t* head_list; /* BLOCK, VSLASH: optional host array */
+  int32_t n_heads_list;
+  int32_t reserved1;
 } sa_estimate_args;
 
 int sa_estimate_workspace_bytes(const sa_estimate_args* args, size_t* bytes);
@@ -262,9 +273,21 @@ int sa_vs_build(const sa_vs_build_args* args, void* stream);
  *   Every listed block must satisfy 0 <= j <= i.
  * mode = SA_FWD_VSLASH: the sa_vs_build tables (iv/iv_cnt with capacity
  *   max_iv, col/col_cnt with capacity max_col); keys = intervals ∪ columns.
+ * mode = SA_FWD_ASHAPE ("MInference 1.0" article, §方法介紹, the A-shape
+ *   pattern; "稀疏注意力机制解析" explainer, §1.2, global plus local-window
+ *   attention): no tables; query block i keeps blocks 0 .. n_sink-1 and the
+ *   n_local blocks i-n_local+1 .. i (clipped at 0, each block once);
+ *   n_sink + n_local <= 2048.
+ * Head list ("MInference 1.0" article, §方法介紹: every head runs the pattern
+ * assigned to it, so one layer mixes patterns by heads): head_list, when not
+ * NULL, is a HOST array of n_heads_list distinct query-head indices in
+ * [0, Hq) (at most 256; copied into the launch).  Only those heads are
+ * computed; out and lse keep their full layouts (other heads untouched) while
+ * the tables are compact, with row b*n + j for listed head j: block_idx
+ * [B,n,nqb,kmax], block_cnt [B,n,nqb], and the VS tables [B*n, nqb, ...].
  * A row with no admissible key gets out = 0 and lse = -INFINITY.
  * ====================================================================== */
-enum { SA_FWD_BLOCK = 0, SA_FWD_VSLASH = 1 };
+enum { SA_FWD_BLOCK = 0, SA_FWD_VSLASH = 1, SA_FWD_ASHAPE = 2 };
 
 typedef struct sa_fwd_args {
   int32_t mode;
@@ -291,6 +314,11 @@ typedef struct sa_fwd_args {
   const int32_t* col_cnt;
   int32_t max_iv;
   int32_t max_col;
+  int32_t n_sink;         /* ASHAPE */
+  int32_t n_local;        /* ASHAPE */
+  const int32_t* head_list; /* optional host array */
+  int32_t n_heads_list;
+  int32_t reserved1;
 } sa_fwd_args;
 
 int sa_block_sparse_fwd_workspace_bytes(const sa_fwd_args* args, size_t* bytes);

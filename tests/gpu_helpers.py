@@ -132,3 +132,43 @@ def certify_prefill(inp: W.PrefillInputs, seed: int, bs: int, scale: float, n_si
                         seed, b, h, i, attempt, bs, d, inp.u, q_shift, inp.dtype)
                     redrawn += 1
     return redrawn
+
+
+# ---------------------------------------------------------------- forward on the oracle's own sets
+def fwd_on_oracle_blocks(sa, q, k, v, h: int, rows: dict, kmax: int):
+    """Run the bf16 forward for query head h alone (head-list launch) on block
+    lists chosen by the oracle: rows maps query block -> ascending blocks; all
+    other rows are empty.  Returns out [N, d] (float32) of head h."""
+    t = torch()
+    B, Hq, N, d = q.shape
+    nb = N // 64
+    lists = [np.asarray(rows.get(i, np.zeros(0, np.int64))) for i in range(nb)]
+    idx, cnt = pad_table(lists, kmax)
+    out = t.zeros((B, Hq, N, d), dtype=t.float32, device=q.device)
+    sa.sa_block_sparse_fwd(q, k, v, out, block_idx=dev_i32(idx.reshape(1, 1, nb, kmax)),
+                           block_cnt=dev_i32(cnt.reshape(1, 1, nb)), heads=[h])
+    t.cuda.synchronize()
+    return host(out[0, h])
+
+
+def fwd_on_oracle_vs(sa, q, k, v, h: int, cols: np.ndarray, offs: np.ndarray, max_iv: int, max_col: int):
+    """Run the bf16 forward for query head h alone on the vertical-slash tables
+    the oracle builds from its own (cols, offs).  Returns out [N, d] of head h."""
+    t = torch()
+    B, Hq, N, d = q.shape
+    nb = N // 64
+    iv = np.zeros((nb, max_iv, 2), np.int32)
+    ivc = np.zeros(nb, np.int32)
+    col = np.zeros((nb, max_col), np.int32)
+    colc = np.zeros(nb, np.int32)
+    for i, (ivs, vert) in enumerate(oracle.vs_block_tables(cols, offs, N, 64)):
+        ivc[i] = len(ivs)
+        for j, (a, e) in enumerate(ivs):
+            iv[i, j] = (a, e)
+        colc[i] = len(vert)
+        col[i, :len(vert)] = vert
+    out = t.zeros((B, Hq, N, d), dtype=t.float32, device=q.device)
+    sa.sa_block_sparse_fwd(q, k, v, out, iv=dev_i32(iv[None]), iv_cnt=dev_i32(ivc[None]), col=dev_i32(col[None]),
+                           col_cnt=dev_i32(colc[None]), heads=[h])
+    t.cuda.synchronize()
+    return host(out[0, h])

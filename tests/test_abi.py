@@ -136,6 +136,39 @@ def test_select_mass_argument_errors(lib):
     assert lib.sa_select_topk(C.byref(t), None, 0, None) == 1
 
 
+def test_head_list_and_ashape_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    a = F.FwdArgs()
+    a.q = a.k = a.v = a.out = 256
+    a.dtype, a.out_dtype, a.block_size, a.head_dim = F.SA_BF16, F.SA_F32, 64, 128
+    a.batch, a.heads_q, a.heads_kv, a.seq, a.scale = 1, 8, 2, 128, 0.1
+    a.mode = F.SA_FWD_ASHAPE
+    a.n_sink, a.n_local = -1, 4
+    assert lib.sa_block_sparse_fwd_workspace_bytes(C.byref(a), C.byref(C.c_size_t())) == 8
+    a.n_sink, a.n_local = 1000, 1049
+    assert lib.sa_block_sparse_fwd_workspace_bytes(C.byref(a), C.byref(C.c_size_t())) == 6
+    a.n_sink, a.n_local = 1, 4
+    assert lib.sa_block_sparse_fwd_workspace_bytes(C.byref(a), C.byref(C.c_size_t())) == 0
+    for heads, code in [([3, 3], 8), ([8], 8), ([-1], 8), ([], 8), (list(range(8)), 0), ([7, 0, 2], 0)]:
+        arr = (C.c_int32 * max(1, len(heads)))(*heads)
+        a.head_list, a.n_heads_list = C.cast(arr, C.c_void_p), len(heads)
+        assert lib.sa_block_sparse_fwd_workspace_bytes(C.byref(a), C.byref(C.c_size_t())) == code, heads
+    e = F.EstimateArgs()
+    e.q = e.k = e.scores = e.centroids = 256
+    e.kind, e.dtype, e.batch, e.heads_q, e.heads_kv, e.seq_q, e.seq_k, e.head_dim = 0, F.SA_BF16, 1, 4, 2, 128, 128, 128
+    e.block_size, e.scale, e.n_centroids = 64, 0.1, 16
+    n = C.c_size_t(0)
+    assert lib.sa_estimate_workspace_bytes(C.byref(e), C.byref(n)) == 0
+    full = n.value
+    arr = (C.c_int32 * 1)(2)
+    e.head_list, e.n_heads_list = C.cast(arr, C.c_void_p), 1
+    assert lib.sa_estimate_workspace_bytes(C.byref(e), C.byref(n)) == 0 and n.value < full   # one pooled head
+    e.n_heads_list = 5
+    assert lib.sa_estimate_workspace_bytes(C.byref(e), C.byref(n)) == 8
+    e.kind, e.n_heads_list = F.SA_EST_CENTROID, 1
+    assert lib.sa_estimate_workspace_bytes(C.byref(e), C.byref(n)) == 6
+
+
 def test_estimate_and_gather_argument_errors(lib):
     from dynamic_sparse_attention_pool_amd import _ffi as F
     e = F.EstimateArgs()

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import (assert_attention_close, assert_scores_close, dev_bf16, dev_i32, host,
+from gpu_helpers import (assert_attention_close, assert_scores_close, dev_bf16, dev_i32, fwd_on_oracle_vs, host,
                          tie_tolerant_valid, torch)
 
 pytestmark = pytest.mark.gpu
@@ -159,16 +159,22 @@ def test_vs_full_size_sampled(sa):
         wv, ws = oracle_vs_scores(inp, h, scale)
         assert_scores_close(av_all[0, h][None], wv[None], f"vertical h{h}")
         assert_scores_close(as_all[0, h][None], ws[None], f"slash h{h}")
+        same = True
         for got, sc, kk in [(vh[h], wv, 1000), (sh[h], ws, 64)]:
             if oracle.certified_row(sc, kk, NONE):
                 assert np.array_equal(got, oracle.topk_row(sc, kk, NONE))
             else:
                 assert tie_tolerant_valid(got, sc, kk, NONE)
+            same = same and np.array_equal(got, oracle.topk_row(sc, kk, NONE))
+        cols, offs = oracle.vs_select(wv, ws, 1000, 64)
         sel = [[None] * 32]
-        sel[0][h] = (vh[h], sh[h])
+        sel[0][h] = (cols, offs)
         blocks = [0, 1, 1000, 2047]
         wo, _ = oracle.vs_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), sel, 64, scale, heads=[h], blocks=blocks)
-        o = host(layer.out[0, h])
-        for i in blocks:
-            rows = slice(64 * i, 64 * i + 64)
-            assert_attention_close(o[rows], wo[0, h, rows], bf16=True, what=f"h{h} block {i}")
+        # the layer's own output where its selection is the oracle's; the forward on the oracle's tables always
+        outs = [host(layer.out[0, h])] if same else []
+        outs.append(fwd_on_oracle_vs(sa, layer.q, layer.k, layer.v, h, cols, offs, 64, 1000))
+        for o in outs:
+            for i in blocks:
+                rows = slice(64 * i, 64 * i + 64)
+                assert_attention_close(o[rows], wo[0, h, rows], bf16=True, what=f"h{h} block {i}")
