@@ -13,8 +13,9 @@ Sources (cited by page title and section in each function):
     §延遲和內核中的稀疏模式, Fig. 4 (verticals in 1x64 pieces, slashes in
     64x64 blocks).
   * "Squeezed Attention：基于语义聚类的长上下文LLM推理加速" — §技术方案
-    (query-centroid similarity, top-K clusters, attention over their keys;
-    the number of clusters adapting to the similarity distribution) and
+    (offline k-means of the context keys; query-centroid similarity, top-K
+    clusters, attention over their keys; the number of clusters adapting to
+    the similarity distribution) and
     §部署建议 (K = sqrt(N) clusters, select 1/4 to 1/2 of them).
   * IndexCache article — §长文本的算力困境 (lightning indexer keeps a token
     subset per layer) and §"偷懒"的艺术 (shared layers copy the nearest full
@@ -33,6 +34,7 @@ from .blocksparse import mean_pool, block_scores, block_select, block_sparse_att
 from .vslash import vs_estimate, vs_select, vs_block_keys, vs_block_tables, vs_attention
 from .cluster import centroid_scores, cluster_select, cluster_select_mass, cluster_pack, cluster_decode
 from .indexer import indexer_scores, indexer_select, gathered_attention, index_cache_forward
+from .kmeans import kmeans, objective as kmeans_objective
 from .patterns import A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, ashape_blocks, ashape_attention, mixed_layer
 
 __all__ = [
@@ -43,4 +45,5 @@ __all__ = [
     "centroid_scores", "cluster_select", "cluster_select_mass", "cluster_pack", "cluster_decode",
     "indexer_scores", "indexer_select", "gathered_attention", "index_cache_forward",
     "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "ashape_blocks", "ashape_attention", "mixed_layer",
+    "kmeans", "kmeans_objective",
 ]

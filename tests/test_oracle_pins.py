@@ -413,6 +413,59 @@ def test_mixed_layer_heads_match_single_pattern_layers():
         assert np.max(np.abs(O[0, h] - ref[p][0, h])) < 1e-12, (h, p)
     assert list(sel[0][1][5]) == [0, 4, 5]
 
+
+# ------------------------------------------------------------------ offline k-means
+def test_kmeans_equals_scipy_lloyd():
+    from scipy.cluster.vq import kmeans2
+    r = np.random.default_rng(61)
+    for trial in range(6):
+        C, d, N = int(r.integers(2, 9)), int(r.integers(2, 12)), int(r.integers(20, 300))
+        X = np.concatenate([r.normal(r.normal(0, 3, d), 1.0, (N // C + 1, d)) for _ in range(C)])[:N]
+        mu0 = X[r.choice(N, C, replace=False)] + 0.01
+        it = int(r.integers(1, 6))
+        mu, lab, margins = oracle.kmeans(X, mu0, it)
+        if margins.min() < 1e-9:
+            continue
+        with np.errstate(all="ignore"):
+            import warnings
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                smu, slab = kmeans2(X, mu0.copy(), iter=it, minit="matrix", missing="warn")
+        assert np.array_equal(lab, slab)
+        assert np.max(np.abs(mu - smu)) < 1e-12
+
+
+def test_kmeans_separated_mixture_closed_form_and_fixed_point():
+    r = np.random.default_rng(62)
+    C, d, N = 6, 16, 600
+    means = r.normal(0, 1, (C, d)) * 10
+    true = r.integers(0, C, N)
+    X = means[true] + r.normal(0, 0.3, (N, d))
+    mu, lab, _ = oracle.kmeans(X, means + 0.5, 1)
+    assert np.array_equal(lab, true)
+    for c in range(C):
+        assert np.max(np.abs(mu[c] - X[true == c].mean(axis=0))) < 1e-12
+    mu2, lab2, _ = oracle.kmeans(X, mu, 3)
+    assert np.array_equal(lab2, true) and np.max(np.abs(mu2 - mu)) < 1e-12
+
+
+def test_kmeans_objective_never_increases_and_empty_and_tied_clusters():
+    r = np.random.default_rng(63)
+    X = r.normal(0, 1, (400, 5))
+    mu = X[:7].copy()
+    prev = np.inf
+    for _ in range(6):
+        mu_next, lab, _ = oracle.kmeans(X, mu, 1)
+        obj = oracle.kmeans_objective(X, mu_next, lab)
+        assert obj <= prev + 1e-9
+        prev, mu = obj, mu_next
+    far = np.vstack([X[:3], np.full((1, 5), 1e6)])            # a centroid no key is near
+    mu_f, lab_f, _ = oracle.kmeans(X, far, 2)
+    assert np.all(lab_f != 3) and np.array_equal(mu_f[3], far[3])
+    dup = np.vstack([X[:1], X[:1], X[1:2]])                   # equal centroids: the lower index wins
+    _, lab_d, _ = oracle.kmeans(X, dup, 1)
+    assert not np.any(lab_d == 1)
+
 # ------------------------------------------------------------------ clustered decode
 def test_cluster_rule_from_page():
     g = gold("page_facts.json")["squeezed_cluster_rule"]
