@@ -10,8 +10,9 @@ value = kept-block FLOP (4*64*64*128 per kept 64x64 block, counted from the
 selected tables) / whole-step time.  ms_per_step = ms per layer at 128K.
 The same run also reports, as extras, the clustered decode (KV GB/s, us per
 token; with a fixed top-64 and with the adaptive softmax-mass budget), the
-token-indexer prefill with index reuse, the vertical-slash layer and a layer
-mixing A-shape, vertical-slash and block-sparse heads; then the roofline of
+token-indexer prefill with index reuse, the vertical-slash layer, a layer
+mixing A-shape, vertical-slash and block-sparse heads, and the offline k-means
+of the decode context; then the roofline of
 the dominant kernel (the forward) and the CPU oracle timed on a bounded sample
 of the same workload.
 
@@ -306,6 +307,39 @@ def mixed_extra(steps, warmup, inp):
             "forward_TFLOP_per_s": flop / (fwd * 1e-3) / 1e12}
 
 
+def kmeans_extra(steps, iters=10):
+    """Offline clustering of the decode context: 8 KV heads x 65536 keys, d128,
+    256 clusters, Lloyd iterations from sampled keys."""
+    import torch
+    import workloads as W
+    from dynamic_sparse_attention_pool_amd import sa_kmeans
+    Hkv, N, d, C = 8, 65536, 128, 256
+    inp = W.decode_clustered(W.CONFIG_SEEDS[4], 1, Hkv, Hkv, N, d, C)
+    k = dev_bf16(inp.k)
+    init = dev_t(W.kmeans_init(W.CONFIG_SEEDS[4], inp.k, C))
+    cent = init.clone()
+    labels = torch.empty((Hkv, N), dtype=torch.int32, device=k.device)
+    ptr = torch.empty((Hkv, C + 1), dtype=torch.int32, device=k.device)
+    perm = torch.empty((Hkv, N), dtype=torch.int32, device=k.device)
+    ws = sa_kmeans(k, cent, labels, iters=1, cluster_ptr=ptr, perm=perm)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    total = 0.0
+    for _ in range(steps):
+        cent.copy_(init)
+        start.record()
+        sa_kmeans(k, cent, labels, iters=iters, cluster_ptr=ptr, perm=perm, workspace=ws)
+        end.record()
+        torch.cuda.synchronize()
+        total += start.elapsed_time(end)
+    ms = total / steps
+    flop = 2.0 * Hkv * N * C * d * iters   # distance dot products of the assignments
+    return {"workload": f"k-means of the decode context: 8 KV heads x 65536 keys, d128, 256 clusters, {iters} "
+                        "Lloyd iterations from sampled keys",
+            "ms_total": ms, "ms_per_iteration": ms / iters, "assign_TFLOP_per_s": flop / (ms * 1e-3) / 1e12,
+            "frac_fp32_peak": flop / (ms * 1e-3) / 1e12 / 157.3}
+
+
 # ---------------------------------------------------------------- CPU oracle baseline
 def cpu_baseline(inp, ratio, budget_s=20.0):
     """The fp64 oracle on head 0 of the same layer: pooled estimate of head 0
@@ -357,7 +391,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extras to run: decode,decode_adaptive,indexer,vs,mixed")
+    ap.add_argument("--only", default="", help="comma list of extras to run: decode,decode_adaptive,indexer,vs,mixed,kmeans")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
@@ -410,7 +444,8 @@ def main():
                          ("decode_adaptive", lambda: decode_extra(max(args.steps, 20), args.warmup, mass=0.5)),
                          ("indexer", lambda: indexer_extra(max(2, args.steps // 3), 1)),
                          ("vs", lambda: vs_extra(max(2, args.steps // 3), 1, main["inputs"])),
-                         ("mixed", lambda: mixed_extra(max(2, args.steps // 3), 1, main["inputs"]))]:
+                         ("mixed", lambda: mixed_extra(max(2, args.steps // 3), 1, main["inputs"])),
+                         ("kmeans", lambda: kmeans_extra(3))]:
             if only and name not in only:
                 continue
             try:

@@ -15,7 +15,7 @@ from . import _ffi as F
 from ._ffi import SAError, load  # noqa: F401
 
 __all__ = ["sa_estimate", "sa_select_topk", "sa_select_mass", "sa_vs_build", "sa_block_sparse_fwd",
-           "sa_gather_decode", "sa_cluster_pack", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
+           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
 
 BLOCK_MEANPOOL, VSLASH, CENTROID, INDEXER = (F.SA_EST_BLOCK_MEANPOOL, F.SA_EST_VSLASH, F.SA_EST_CENTROID,
                                              F.SA_EST_INDEXER)
@@ -224,3 +224,21 @@ def sa_cluster_pack(labels, cluster_ptr, perm, n_clusters: int, *, k=None, v=Non
     ws, n = _workspace(nb.value, labels)
     F.check(lib.sa_cluster_pack(C.byref(a), _p(ws), n, _stream()))
     return ws
+
+
+def sa_kmeans(k, centroids, labels, *, iters: int, cluster_ptr=None, perm=None, workspace=None):
+    """Lloyd iterations per KV head: k [Hkv,N,d], centroids [Hkv,C,d] float
+    (in: initial, out: final), labels [Hkv,N] int32; optional cluster_ptr
+    [Hkv,C+1] and perm [Hkv,N] of the final labels.  Returns the workspace."""
+    lib = load()
+    a = F.KmeansArgs()
+    Hkv, N, d = k.shape
+    a.heads_kv, a.n_ctx, a.head_dim, a.n_clusters, a.iters, a.dtype = Hkv, N, d, centroids.shape[1], iters, _dt(k)
+    a.k, a.centroids, a.labels = _p(k), _p(centroids), _p(labels)
+    a.cluster_ptr, a.perm = _p(cluster_ptr), _p(perm)
+    nb = C.c_size_t(0)
+    F.check(lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(nb)))
+    if workspace is None or workspace.numel() < nb.value:
+        workspace, _ = _workspace(nb.value, k)
+    F.check(lib.sa_kmeans(C.byref(a), _p(workspace), nb.value, _stream()))
+    return workspace

@@ -196,6 +196,7 @@ size_t sa_args_size(int which) {
     case 4: return sizeof(sa_gather_args);
     case 5: return sizeof(sa_cluster_pack_args);
     case 6: return sizeof(sa_select_mass_args);
+    case 7: return sizeof(sa_kmeans_args);
     default: return 0;
   }
 }
@@ -432,6 +433,57 @@ int sa_block_sparse_fwd(const sa_fwd_args* a, void* workspace, size_t workspace_
   return launched(sa::launch_fwd(p, (int)a->head_dim, kmode, a->dtype == SA_BF16, a->out_dtype == SA_BF16,
                                  as_stream(stream)),
                   "sa_block_sparse_fwd");
+}
+
+// ---------------------------------------------------------------- offline k-means
+static int check_kmeans(const sa_kmeans_args* a, size_t* ws) {
+  if (!a) return fail(SA_ERR_NULL, "sa_kmeans: args is NULL");
+  *ws = 0;
+  if (!a->k || !a->centroids || !a->labels) return fail(SA_ERR_NULL, "sa_kmeans: k, centroids and labels are required");
+  if ((a->cluster_ptr == nullptr) != (a->perm == nullptr))
+    return fail(SA_ERR_NULL, "sa_kmeans: give both cluster_ptr and perm, or neither");
+  if (!aligned16(a->k) || !aligned16(a->centroids)) return fail(SA_ERR_ALIGN, "sa_kmeans: k and centroids must be 16-byte aligned");
+  if (a->dtype != SA_F32 && a->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "sa_kmeans: dtype must be F32 or BF16");
+  if (a->head_dim != 64 && a->head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "sa_kmeans: head_dim must be 64 or 128");
+  if (a->heads_kv <= 0 || a->n_ctx <= 0) return fail(SA_ERR_SHAPE, "sa_kmeans: sizes must be positive");
+  if (a->n_ctx > 0x7fffffff || a->heads_kv * a->n_ctx > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_kmeans: too many keys");
+  if (a->n_clusters < 1 || a->n_clusters > 4096) return fail(SA_ERR_SHAPE, "sa_kmeans: n_clusters must lie in [1, 4096]");
+  if (a->heads_kv * a->n_clusters > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_kmeans: too many clusters");
+  if (a->iters < 1) return fail(SA_ERR_VALUE, "sa_kmeans: iters must be >= 1");
+  *ws = sa::kmeans_workspace_bytes(a->heads_kv, a->n_ctx, a->n_clusters);
+  if (!a->cluster_ptr)
+    *ws += align256((size_t)(a->heads_kv * (a->n_clusters + 1)) * 4) + align256((size_t)(a->heads_kv * a->n_ctx) * 4);
+  return ok();
+}
+
+int sa_kmeans_workspace_bytes(const sa_kmeans_args* a, size_t* bytes) {
+  if (!bytes) return fail(SA_ERR_NULL, "sa_kmeans_workspace_bytes: bytes is NULL");
+  size_t ws = 0;
+  const int rc = check_kmeans(a, &ws);
+  if (rc) return rc;
+  *bytes = ws;
+  return ok();
+}
+
+int sa_kmeans(const sa_kmeans_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t ws = 0;
+  const int rc = check_kmeans(a, &ws);
+  if (rc) return rc;
+  if (!workspace || workspace_bytes < ws) return fail(SA_ERR_WORKSPACE, "sa_kmeans: workspace of %zu bytes required", ws);
+  if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "sa_kmeans: workspace must be 16-byte aligned");
+  char* w = static_cast<char*>(workspace);
+  void* pack_ws = w;
+  w += align256(sa::kmeans_workspace_bytes(a->heads_kv, a->n_ctx, a->n_clusters));
+  int32_t* ptr = a->cluster_ptr;
+  int32_t* perm = a->perm;
+  if (!ptr) {
+    ptr = reinterpret_cast<int32_t*>(w);
+    w += align256((size_t)(a->heads_kv * (a->n_clusters + 1)) * 4);
+    perm = reinterpret_cast<int32_t*>(w);
+  }
+  return launched(sa::launch_kmeans(a->k, a->dtype == SA_BF16, a->heads_kv, a->n_ctx, (int)a->head_dim, a->n_clusters,
+                                    a->iters, a->centroids, a->labels, ptr, perm, pack_ws, as_stream(stream)),
+                  "sa_kmeans");
 }
 
 // ---------------------------------------------------------------- gather / decode

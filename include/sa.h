@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 3
+#define SA_ABI_VERSION 4
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -405,6 +405,45 @@ int sa_cluster_pack_workspace_bytes(const sa_cluster_pack_args* args, size_t* by
 int sa_cluster_pack(const sa_cluster_pack_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * sa_kmeans — offline clustering of a fixed context's keys.
+ *
+ * Squeezed Attention page, §技术方案, offline stage: the keys are clustered,
+ * each cluster gets a centroid and each key an index to its cluster.  Lloyd
+ * iterations per KV head, `iters` times: assign every key to the centroid at
+ * the smallest squared Euclidean distance (ties -> lower cluster index), then
+ * move every centroid to the mean of its keys (a cluster with no key keeps its
+ * centroid).  Distances are |mu|^2 - 2 k.mu in fp32 (the |k|^2 term is common
+ * to all centroids of a key); means are fp32 sums in token order, so results
+ * are deterministic.
+ *
+ * k [Hkv,N,d] (BF16 or F32, d = 64 or 128, 16-byte aligned).
+ * centroids [Hkv,C,d] float: in, the initial table; out, the table after the
+ *   last update (each non-empty cluster's centroid is the mean of its keys).
+ * labels [Hkv,N] int32 out: the last assignment.
+ * cluster_ptr [Hkv,C+1] and perm [Hkv,N] int32: optional outputs, the
+ *   cluster-major order of the final labels exactly as sa_cluster_pack writes
+ *   it (both or neither; when absent they live in the workspace).
+ * 1 <= C <= 4096, iters >= 1.  Requires a workspace.
+ * ====================================================================== */
+typedef struct sa_kmeans_args {
+  int64_t heads_kv;
+  int64_t n_ctx;
+  int64_t head_dim;
+  int32_t n_clusters;
+  int32_t iters;
+  int32_t dtype;
+  int32_t reserved0;
+  const void* k;
+  float* centroids;
+  int32_t* labels;
+  int32_t* cluster_ptr;
+  int32_t* perm;
+} sa_kmeans_args;
+
+int sa_kmeans_workspace_bytes(const sa_kmeans_args* args, size_t* bytes);
+int sa_kmeans(const sa_kmeans_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
  * Library information.
  * ====================================================================== */
 /* Message of the last failing call on this thread ("" if none). */
@@ -413,7 +452,7 @@ const char* sa_last_error(void);
 int sa_version(void);
 /* sizeof of the argument structs as compiled, so bindings can check layout:
  * which = 0 estimate, 1 select, 2 vs_build, 3 fwd, 4 gather, 5 cluster_pack,
- * 6 select_mass. */
+ * 6 select_mass, 7 kmeans. */
 size_t sa_args_size(int which);
 
 #ifdef __cplusplus

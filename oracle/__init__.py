@@ -34,7 +34,7 @@ from .blocksparse import mean_pool, block_scores, block_select, block_sparse_att
 from .vslash import vs_estimate, vs_select, vs_block_keys, vs_block_tables, vs_attention
 from .cluster import centroid_scores, cluster_select, cluster_select_mass, cluster_pack, cluster_decode
 from .indexer import indexer_scores, indexer_select, gathered_attention, index_cache_forward
-from .kmeans import kmeans, objective as kmeans_objective
+from .kmeans import assign as kmeans_assign, kmeans, objective as kmeans_objective
 from .patterns import A_SHAPE, VERTICAL_SLASH, BLOCK_SPARSE, ashape_blocks, ashape_attention, mixed_layer
 
 __all__ = [
@@ -45,5 +45,5 @@ __all__ = [
     "centroid_scores", "cluster_select", "cluster_select_mass", "cluster_pack", "cluster_decode",
     "indexer_scores", "indexer_select", "gathered_attention", "index_cache_forward",
     "A_SHAPE", "VERTICAL_SLASH", "BLOCK_SPARSE", "ashape_blocks", "ashape_attention", "mixed_layer",
-    "kmeans", "kmeans_objective",
+    "kmeans", "kmeans_assign", "kmeans_objective",
 ]

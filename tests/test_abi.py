@@ -26,7 +26,7 @@ def lib():
 def test_header_declares_the_four_entry_points_and_helpers():
     names = declared_functions()
     for n in ["sa_estimate", "sa_select_topk", "sa_block_sparse_fwd", "sa_gather_decode", "sa_vs_build",
-              "sa_cluster_pack", "sa_select_mass", "sa_last_error", "sa_version", "sa_args_size"]:
+              "sa_cluster_pack", "sa_select_mass", "sa_kmeans", "sa_last_error", "sa_version", "sa_args_size"]:
         assert n in names
 
 
@@ -167,6 +167,31 @@ def test_head_list_and_ashape_argument_errors(lib):
     assert lib.sa_estimate_workspace_bytes(C.byref(e), C.byref(n)) == 8
     e.kind, e.n_heads_list = F.SA_EST_CENTROID, 1
     assert lib.sa_estimate_workspace_bytes(C.byref(e), C.byref(n)) == 6
+
+
+def test_kmeans_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    a = F.KmeansArgs()
+    n = C.c_size_t(0)
+    assert lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(n)) == 1
+    a.k = a.centroids = a.labels = 256
+    a.heads_kv, a.n_ctx, a.head_dim, a.n_clusters, a.iters, a.dtype = 8, 65536, 128, 256, 3, F.SA_BF16
+    assert lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(n)) == 0 and n.value > 8 * 65536 * 4
+    with_ws = n.value
+    a.cluster_ptr = 512
+    assert lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(n)) == 1        # ptr without perm
+    a.perm = 1024
+    assert lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(n)) == 0 and n.value < with_ws
+    for field, bad, code in [("n_clusters", 0, 2), ("n_clusters", 5000, 2), ("iters", 0, 8), ("head_dim", 96, 6),
+                             ("dtype", F.SA_I32, 3)]:
+        good = getattr(a, field)
+        setattr(a, field, bad)
+        assert lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(n)) == code, field
+        setattr(a, field, good)
+    a.k = 264
+    assert lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(n)) == 4
+    a.k = 256
+    assert lib.sa_kmeans(C.byref(a), None, 0, None) == 5                      # workspace missing
 
 
 def test_estimate_and_gather_argument_errors(lib):

@@ -23,7 +23,7 @@ import numpy as np
 S_Q, S_K, S_V, S_SHIFT_POS, S_SHIFT_U = 0, 1, 2, 3, 4
 S_LABELS, S_KMEANS, S_VMEANS, S_DECQ, S_IDXW = 5, 6, 7, 8, 9
 S_IDXQ, S_IDXK, S_LAYER, S_REDRAW_QB, S_REDRAW_DECQ = 10, 11, 12, 13, 14
-S_PLANT, S_TOPK = 15, 16
+S_PLANT, S_TOPK, S_KMINIT = 15, 16, 17
 
 CONFIG_SEEDS = {1: 1, 2: 2, 3: 3, 4: 4, 5: 5}
 
@@ -207,6 +207,18 @@ def decode_clustered(seed: int, T: int, Hq: int, Hkv: int, Nctx: int, d: int, C:
     for t in range(T):
         q[t] = f32_to_bf16(normal(seed, (Hq, d), S_DECQ, t))
     return DecodeInputs(q, k, v, labels, mu, nu)
+
+
+def kmeans_init(seed: int, k_bits: np.ndarray, C: int) -> np.ndarray:
+    """Initial centroid table [Hkv, C, d] float32: C distinct keys per KV head,
+    drawn without replacement from a seeded substream (the keys' own bf16
+    values, widened exactly)."""
+    Hkv, N, d = k_bits.shape
+    out = np.empty((Hkv, C, d), np.float32)
+    for g in range(Hkv):
+        pick = rng(seed, S_KMINIT, g).choice(N, size=C, replace=False)
+        out[g] = bf16_to_f32(k_bits[g][np.sort(pick)])
+    return out
 
 
 def redraw_decode_query(seed: int, t: int, h: int, attempt: int, d: int) -> np.ndarray:
