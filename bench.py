@@ -307,6 +307,35 @@ def mixed_extra(steps, warmup, inp):
             "forward_TFLOP_per_s": flop / (fwd * 1e-3) / 1e12}
 
 
+def fused_extra(steps, inp):
+    """Block estimate + top-k at 131072 tokens: the fused call (no score
+    matrix) against pooled scores followed by the separate selection."""
+    import torch
+    from dynamic_sparse_attention_pool_amd.pipelines import BlockSparseLayer
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    res = {"workload": "block estimate + top-k at 131072, GQA 32/8, d128, sink + 4 local + ceil(5%)"}
+    for name, fused in (("separate", False), ("fused", True)):
+        layer = BlockSparseLayer(q, k, v, n_sink=1, n_local=4, ratio=(5, 100), fused=fused)
+        layer.estimate()
+        layer.select()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(steps):
+            layer.estimate()
+            layer.select()
+        end.record()
+        torch.cuda.synchronize()
+        res[f"ms_{name}"] = start.elapsed_time(end) / steps
+        if fused:
+            res["identical_tables"] = bool(torch.equal(layer.cnt, ref_cnt) and torch.equal(layer.idx, ref_idx))
+        else:
+            ref_idx, ref_cnt = layer.idx.clone(), layer.cnt.clone()
+        del layer
+        torch.cuda.empty_cache()
+    return res
+
+
 def kmeans_extra(steps, iters=10):
     """Offline clustering of the decode context: 8 KV heads x 65536 keys, d128,
     256 clusters, Lloyd iterations from sampled keys."""
@@ -391,7 +420,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-extras", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--only", default="", help="comma list of extras to run: decode,decode_adaptive,indexer,vs,mixed,kmeans")
+    ap.add_argument("--only", default="", help="comma list of extras to run: decode,decode_adaptive,indexer,vs,mixed,kmeans,fused")
     ap.add_argument("--pmc-copy", action="store_true",
                     help="first run a plain 1 GiB device copy, the known-size reference for HBM counters")
     args = ap.parse_args()
@@ -445,7 +474,8 @@ def main():
                          ("indexer", lambda: indexer_extra(max(2, args.steps // 3), 1)),
                          ("vs", lambda: vs_extra(max(2, args.steps // 3), 1, main["inputs"])),
                          ("mixed", lambda: mixed_extra(max(2, args.steps // 3), 1, main["inputs"])),
-                         ("kmeans", lambda: kmeans_extra(3))]:
+                         ("kmeans", lambda: kmeans_extra(3)),
+                         ("fused", lambda: fused_extra(max(5, args.steps), main["inputs"]))]:
             if only and name not in only:
                 continue
             try:

@@ -15,7 +15,7 @@ from . import _ffi as F
 from ._ffi import SAError, load  # noqa: F401
 
 __all__ = ["sa_estimate", "sa_select_topk", "sa_select_mass", "sa_vs_build", "sa_block_sparse_fwd",
-           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
+           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "sa_estimate_topk", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
 
 BLOCK_MEANPOOL, VSLASH, CENTROID, INDEXER = (F.SA_EST_BLOCK_MEANPOOL, F.SA_EST_VSLASH, F.SA_EST_CENTROID,
                                              F.SA_EST_INDEXER)
@@ -142,6 +142,35 @@ def sa_select_mass(scores, idx, cnt, *, mass: float, k_min: int = 0, k_max=None,
     a.kmax = idx.shape[1]
     a.idx, a.cnt, a.err_flag = _p(idx), _p(cnt), _p(err_flag)
     F.check(lib.sa_select_mass(C.byref(a), _stream()))
+
+
+def sa_estimate_topk(q, k, idx, cnt, *, n_sink: int = 0, n_local: int = 0, k_fixed: int = 0, ratio=None,
+                     scale=None, pooled_q=None, pooled_k=None, heads=None, err_flag=None, workspace=None):
+    """Block-sparse estimate and per-row top-k in one call (no score matrix):
+    q [B,Hq,N,d], k [B,Hkv,N,d]; idx [B,n,nb,kmax], cnt [B,n,nb] int32.
+    Returns the workspace (reusable by later calls of the same shape)."""
+    lib = load()
+    a = F.EstimateTopkArgs()
+    B, Hq, N, d = q.shape
+    a.kind, a.dtype, a.block_size = F.SA_EST_BLOCK_MEANPOOL, _dt(q), 64
+    a.batch, a.heads_q, a.heads_kv, a.seq, a.head_dim = B, Hq, k.shape[1], N, d
+    a.scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    a.n_sink, a.n_local = n_sink, n_local
+    if ratio is not None:
+        a.ratio_num, a.ratio_den = ratio
+    else:
+        a.k = k_fixed
+    a.kmax = idx.shape[-1]
+    a.q, a.k_ptr = _p(q), _p(k)
+    a.pooled_q, a.pooled_k = _p(pooled_q), _p(pooled_k)
+    a.idx, a.cnt, a.err_flag = _p(idx), _p(cnt), _p(err_flag)
+    keep = _heads(a, heads)  # noqa: F841
+    nb = C.c_size_t(0)
+    F.check(lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(nb)))
+    if nb.value and (workspace is None or workspace.numel() < nb.value):
+        workspace, _ = _workspace(nb.value, q)
+    F.check(lib.sa_estimate_topk(C.byref(a), _p(workspace) if nb.value else None, nb.value, _stream()))
+    return workspace
 
 
 def sa_vs_build(vert, vert_cnt, slash, slash_cnt, iv, iv_cnt, col, col_cnt, seq: int, block_size: int = 64):

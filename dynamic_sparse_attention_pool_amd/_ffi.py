@@ -17,7 +17,7 @@ SA_F32, SA_BF16, SA_I32 = 0, 1, 2
 SA_EST_BLOCK_MEANPOOL, SA_EST_VSLASH, SA_EST_CENTROID, SA_EST_INDEXER = 0, 1, 2, 3
 SA_FWD_BLOCK, SA_FWD_VSLASH, SA_FWD_ASHAPE = 0, 1, 2
 SA_GATHER_CLUSTER, SA_GATHER_TOKEN = 0, 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
                 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_LAUNCH", 8: "SA_ERR_VALUE"}
@@ -86,7 +86,17 @@ class KmeansArgs(C.Structure):
                 ("labels", P), ("cluster_ptr", P), ("perm", P)]
 
 
-STRUCTS = [EstimateArgs, SelectArgs, VsBuildArgs, FwdArgs, GatherArgs, ClusterPackArgs, SelectMassArgs, KmeansArgs]
+class EstimateTopkArgs(C.Structure):
+    _fields_ = [("kind", C.c_int32), ("dtype", C.c_int32), ("batch", C.c_int64), ("heads_q", C.c_int64),
+                ("heads_kv", C.c_int64), ("seq", C.c_int64), ("head_dim", C.c_int64), ("block_size", C.c_int32),
+                ("scale", C.c_float), ("n_sink", C.c_int32), ("n_local", C.c_int32), ("k", C.c_int32),
+                ("ratio_num", C.c_int32), ("ratio_den", C.c_int32), ("kmax", C.c_int32), ("q", P), ("k_ptr", P),
+                ("pooled_q", P), ("pooled_k", P), ("head_list", P), ("n_heads_list", C.c_int32),
+                ("reserved0", C.c_int32), ("idx", P), ("cnt", P), ("err_flag", P)]
+
+
+STRUCTS = [EstimateArgs, SelectArgs, VsBuildArgs, FwdArgs, GatherArgs, ClusterPackArgs, SelectMassArgs, KmeansArgs,
+           EstimateTopkArgs]
 
 # exported symbol -> (restype, argtypes)
 SYMBOLS = {
@@ -103,6 +113,8 @@ SYMBOLS = {
     "sa_cluster_pack": (C.c_int, [C.POINTER(ClusterPackArgs), P, C.c_size_t, P]),
     "sa_cluster_pack_workspace_bytes": (C.c_int, [C.POINTER(ClusterPackArgs), C.POINTER(C.c_size_t)]),
     "sa_kmeans": (C.c_int, [C.POINTER(KmeansArgs), P, C.c_size_t, P]),
+    "sa_estimate_topk": (C.c_int, [C.POINTER(EstimateTopkArgs), P, C.c_size_t, P]),
+    "sa_estimate_topk_workspace_bytes": (C.c_int, [C.POINTER(EstimateTopkArgs), C.POINTER(C.c_size_t)]),
     "sa_kmeans_workspace_bytes": (C.c_int, [C.POINTER(KmeansArgs), C.POINTER(C.c_size_t)]),
     "sa_last_error": (C.c_char_p, []),
     "sa_version": (C.c_int, []),

@@ -68,6 +68,21 @@ hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, i
                               const HeadList& hl, int64_t seq, int head_dim, int last_q, float scale, float* a_v,
                               float* a_s, void* ws, hipStream_t stream);
 
+// pooled block scores and per-row top-k in one pass (at most 2048 blocks per row)
+constexpr int kBlockTopkMaxBlocks = 2048;
+struct BlockTopkParams {
+  const float* pq;  // pooled queries, rows compact as in the head list
+  const float* pk;  // pooled keys [B*Hkv, nb, d]
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* err;
+  int32_t batch, hq, hkv, nb, kmax;
+  int32_t n_sink, n_local, k, rnum, rden;
+  float scale;
+  HeadList hl;
+};
+hipError_t launch_block_topk(const BlockTopkParams& p, int head_dim, hipStream_t stream);
+
 // ---------------------------------------------------------------- select
 struct SelectParams {
   const float* scores;

@@ -197,6 +197,7 @@ size_t sa_args_size(int which) {
     case 5: return sizeof(sa_cluster_pack_args);
     case 6: return sizeof(sa_select_mass_args);
     case 7: return sizeof(sa_kmeans_args);
+    case 8: return sizeof(sa_estimate_topk_args);
     default: return 0;
   }
 }
@@ -323,6 +324,106 @@ int sa_select_mass(const sa_select_mass_args* a, void* stream) {
   p.cnt = a->cnt;
   p.err = a->err_flag;
   return launched(sa::launch_select_mass(p, as_stream(stream)), "sa_select_mass");
+}
+
+// ---------------------------------------------------------------- fused block estimate + top-k
+static int check_estimate_topk(const sa_estimate_topk_args* a, size_t* ws, sa::HeadList& hl) {
+  if (!a) return fail(SA_ERR_NULL, "sa_estimate_topk: args is NULL");
+  *ws = 0;
+  if (a->kind != SA_EST_BLOCK_MEANPOOL) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk: only BLOCK_MEANPOOL");
+  if (!a->q || !a->k_ptr || !a->idx || !a->cnt) return fail(SA_ERR_NULL, "sa_estimate_topk: q, k, idx and cnt are required");
+  if (!aligned16(a->q) || !aligned16(a->k_ptr)) return fail(SA_ERR_ALIGN, "sa_estimate_topk: q and k must be 16-byte aligned");
+  if ((a->pooled_q && !aligned16(a->pooled_q)) || (a->pooled_k && !aligned16(a->pooled_k)))
+    return fail(SA_ERR_ALIGN, "sa_estimate_topk: pooled buffers must be 16-byte aligned");
+  if (a->dtype != SA_F32 && a->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "sa_estimate_topk: dtype must be F32 or BF16");
+  if (a->block_size != kBlock) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk: block_size must be 64");
+  if (a->head_dim != 64 && a->head_dim != 128) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk: head_dim must be 64 or 128");
+  if (a->batch <= 0 || a->heads_q <= 0 || a->heads_kv <= 0 || a->seq <= 0) return fail(SA_ERR_SHAPE, "sa_estimate_topk: sizes must be positive");
+  if (a->heads_q % a->heads_kv) return fail(SA_ERR_SHAPE, "sa_estimate_topk: heads_q must be a multiple of heads_kv");
+  if (a->seq % kBlock) return fail(SA_ERR_SHAPE, "sa_estimate_topk: seq must be a multiple of 64");
+  const int64_t nb = a->seq / kBlock;
+  if (nb > sa::kBlockTopkMaxBlocks) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk: at most %d blocks per row", sa::kBlockTopkMaxBlocks);
+  if (!(a->scale > 0.f)) return fail(SA_ERR_VALUE, "sa_estimate_topk: scale must be > 0");
+  if (a->n_sink < 0 || a->n_local < 0) return fail(SA_ERR_VALUE, "sa_estimate_topk: n_sink and n_local must be >= 0");
+  if (a->ratio_den < 0 || a->ratio_num < 0 || (a->ratio_den == 0 && a->k < 0))
+    return fail(SA_ERR_VALUE, "sa_estimate_topk: budget must be k >= 0 or ratio_num/ratio_den with both >= 0");
+  if (const int rc = make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_estimate_topk", hl)) return rc;
+  // the largest count of any row
+  int64_t need = 0;
+  for (int64_t i = 0; i < nb; ++i) {
+    const int64_t n = i + 1;
+    const int64_t pb = n < a->n_sink ? n : a->n_sink;
+    const int64_t pe = (n - a->n_local) > pb ? (n - a->n_local) : pb;
+    int64_t kk = a->ratio_den > 0 ? ((int64_t)a->ratio_num * n + a->ratio_den - 1) / a->ratio_den : a->k;
+    if (kk > pe - pb) kk = pe - pb;
+    if (kk < 0) kk = 0;
+    const int64_t c = n - (pe - pb) + kk;
+    if (c > need) need = c;
+  }
+  if (a->kmax <= 0 || a->kmax < need)
+    return fail(SA_ERR_SHAPE, "sa_estimate_topk: kmax %d is below the largest possible count %lld", a->kmax, (long long)need);
+  const int64_t nh = hl.n > 0 ? hl.n : a->heads_q;
+  if (!a->pooled_q) *ws += align256((size_t)(a->batch * nh * nb * a->head_dim) * 4);
+  if (!a->pooled_k) *ws += align256((size_t)(a->batch * a->heads_kv * nb * a->head_dim) * 4);
+  return ok();
+}
+
+int sa_estimate_topk_workspace_bytes(const sa_estimate_topk_args* a, size_t* bytes) {
+  if (!bytes) return fail(SA_ERR_NULL, "sa_estimate_topk_workspace_bytes: bytes is NULL");
+  size_t ws = 0;
+  sa::HeadList hl;
+  const int rc = check_estimate_topk(a, &ws, hl);
+  if (rc) return rc;
+  *bytes = ws;
+  return ok();
+}
+
+int sa_estimate_topk(const sa_estimate_topk_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t ws = 0;
+  sa::HeadList hl, all;
+  all.n = 0;
+  const int rc = check_estimate_topk(a, &ws, hl);
+  if (rc) return rc;
+  if (ws > 0 && (!workspace || workspace_bytes < ws))
+    return fail(SA_ERR_WORKSPACE, "sa_estimate_topk: workspace of %zu bytes required", ws);
+  if (workspace && !aligned16(workspace)) return fail(SA_ERR_ALIGN, "sa_estimate_topk: workspace must be 16-byte aligned");
+  const hipStream_t st = as_stream(stream);
+  const int64_t nb = a->seq / kBlock;
+  const int64_t nh = hl.n > 0 ? hl.n : a->heads_q;
+  char* w = static_cast<char*>(workspace);
+  float* pq = a->pooled_q;
+  float* pk = a->pooled_k;
+  if (!pq) {
+    pq = reinterpret_cast<float*>(w);
+    w += align256((size_t)(a->batch * nh * nb * a->head_dim) * 4);
+  }
+  if (!pk) pk = reinterpret_cast<float*>(w);
+  const bool bf = a->dtype == SA_BF16;
+  hipError_t e = sa::launch_pool(a->q, a->batch, (int)a->heads_q, hl, a->seq, (int)a->head_dim, bf, kBlock, pq, st);
+  if (e == hipSuccess)
+    e = sa::launch_pool(a->k_ptr, a->batch, (int)a->heads_kv, all, a->seq, (int)a->head_dim, bf, kBlock, pk, st);
+  if (e == hipSuccess) {
+    sa::BlockTopkParams p;
+    p.pq = pq;
+    p.pk = pk;
+    p.idx = a->idx;
+    p.cnt = a->cnt;
+    p.err = a->err_flag;
+    p.batch = (int32_t)a->batch;
+    p.hq = (int32_t)a->heads_q;
+    p.hkv = (int32_t)a->heads_kv;
+    p.nb = (int32_t)nb;
+    p.kmax = a->kmax;
+    p.n_sink = a->n_sink;
+    p.n_local = a->n_local;
+    p.k = a->k;
+    p.rnum = a->ratio_num;
+    p.rden = a->ratio_den;
+    p.scale = a->scale;
+    p.hl = hl;
+    e = sa::launch_block_topk(p, (int)a->head_dim, st);
+  }
+  return launched(e, "sa_estimate_topk");
 }
 
 // ---------------------------------------------------------------- vertical-slash tables

@@ -9,7 +9,7 @@ from __future__ import annotations
 import math
 
 from . import (BLOCK_MEANPOOL, CENTROID, INDEXER, VSLASH, sa_block_sparse_fwd, sa_cluster_pack, sa_estimate,
-               sa_gather_decode, sa_select_mass, sa_select_topk, sa_vs_build)
+               sa_estimate_topk, sa_gather_decode, sa_select_mass, sa_select_topk, sa_vs_build)
 
 
 def _t():
@@ -42,10 +42,12 @@ class BlockSparseLayer:
     """Block-sparse prefill: pooled estimate -> top-k with sink/local -> forward.
     ``heads`` restricts the layer to those query heads (tables compact over
     them); ``out``/``lse`` may be shared with other layers of the same heads'
-    tensor."""
+    tensor.  ``fused``: estimate and select in one call that never writes the
+    score matrix (sa_estimate_topk); ``estimate`` then does both and
+    ``select`` nothing."""
 
     def __init__(self, q, k, v, *, n_sink: int, n_local: int, ratio=None, k_fixed=None, out_dtype=None,
-                 scale=None, with_lse=False, heads=None, out=None, lse=None):
+                 scale=None, with_lse=False, heads=None, out=None, lse=None, fused=False):
         torch = _t()
         self.q, self.k, self.v = q, k, v
         B, Hq, N, d = q.shape
@@ -56,7 +58,8 @@ class BlockSparseLayer:
         self.n_sink, self.n_local, self.ratio, self.k_fixed = n_sink, n_local, ratio, k_fixed
         self.kmax = max_kept_blocks(self.nb, n_sink, n_local, k_fixed, ratio)
         dev = q.device
-        self.scores = torch.empty((B, nh, self.nb, self.nb), dtype=torch.float32, device=dev)
+        self.fused = fused
+        self.scores = None if fused else torch.empty((B, nh, self.nb, self.nb), dtype=torch.float32, device=dev)
         self.pooled_q = torch.empty((B, nh, self.nb, d), dtype=torch.float32, device=dev)
         self.pooled_k = torch.empty((B, k.shape[1], self.nb, d), dtype=torch.float32, device=dev)
         self.idx = torch.empty((B, nh, self.nb, self.kmax), dtype=torch.int32, device=dev)
@@ -65,10 +68,18 @@ class BlockSparseLayer:
         self.err = torch.zeros(1, dtype=torch.int32, device=dev)
 
     def estimate(self):
+        if self.fused:
+            budget = dict(ratio=self.ratio) if self.ratio is not None else dict(k_fixed=self.k_fixed)
+            sa_estimate_topk(self.q, self.k, self.idx, self.cnt, n_sink=self.n_sink, n_local=self.n_local,
+                             scale=self.scale, pooled_q=self.pooled_q, pooled_k=self.pooled_k, heads=self.heads,
+                             err_flag=self.err, **budget)
+            return
         sa_estimate(BLOCK_MEANPOOL, self.q, self.k, self.scores, scale=self.scale, pooled_q=self.pooled_q,
                     pooled_k=self.pooled_k, heads=self.heads)
 
     def select(self):
+        if self.fused:
+            return
         kw = dict(n_sink=self.n_sink, n_local=self.n_local, causal=True, causal_period=self.nb,
                   err_flag=self.err)
         if self.ratio is not None:

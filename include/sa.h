@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 4
+#define SA_ABI_VERSION 5
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -219,6 +219,57 @@ typedef struct sa_select_mass_args {
 } sa_select_mass_args;
 
 int sa_select_mass(const sa_select_mass_args* args, void* stream);
+
+/* ======================================================================
+ * sa_estimate_topk — block estimate and selection in one call, without the
+ * score matrix.
+ *
+ * "MInference 1.0" article, §方法介紹 (block indices from mean-pooled Q and K)
+ * with the selection of sa_select_topk.  The result equals
+ * sa_estimate(BLOCK_MEANPOOL) followed by sa_select_topk on its score rows
+ * with causal = 1 and causal_period = nb (row i of a head has the candidate
+ * blocks 0..i), with the same n_sink / n_local / k or ratio budget, order and
+ * output format.  The scores are never written to
+ * memory: a workgroup scores 16 consecutive rows, keeps them in registers and
+ * selects from them.
+ *
+ * kind = SA_EST_BLOCK_MEANPOOL only.  q [B,Hq,N,d], k [B,Hkv,N,d] (F32 or
+ * BF16, d = 64 or 128), N a multiple of 64 with N/64 <= 2048.
+ * idx [B,n,nb,kmax] int32, cnt [B,n,nb] int32 (n = Hq, or n_heads_list with a
+ * host head list as in sa_estimate); kmax must hold the largest count.
+ * pooled_q / pooled_k: optional outputs as in sa_estimate.  err_flag: as in
+ * sa_select_topk.  Requires a workspace unless both pooled buffers are given.
+ * ====================================================================== */
+typedef struct sa_estimate_topk_args {
+  int32_t kind;
+  int32_t dtype;
+  int64_t batch;
+  int64_t heads_q;
+  int64_t heads_kv;
+  int64_t seq;
+  int64_t head_dim;
+  int32_t block_size;     /* 64 */
+  float scale;
+  int32_t n_sink;
+  int32_t n_local;
+  int32_t k;
+  int32_t ratio_num;
+  int32_t ratio_den;
+  int32_t kmax;
+  const void* q;
+  const void* k_ptr;
+  float* pooled_q;
+  float* pooled_k;
+  const int32_t* head_list;
+  int32_t n_heads_list;
+  int32_t reserved0;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* err_flag;
+} sa_estimate_topk_args;
+
+int sa_estimate_topk_workspace_bytes(const sa_estimate_topk_args* args, size_t* bytes);
+int sa_estimate_topk(const sa_estimate_topk_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
  * sa_vs_build — vertical-slash selections -> per-query-block key tables.
@@ -452,7 +503,7 @@ const char* sa_last_error(void);
 int sa_version(void);
 /* sizeof of the argument structs as compiled, so bindings can check layout:
  * which = 0 estimate, 1 select, 2 vs_build, 3 fwd, 4 gather, 5 cluster_pack,
- * 6 select_mass, 7 kmeans. */
+ * 6 select_mass, 7 kmeans, 8 estimate_topk. */
 size_t sa_args_size(int which);
 
 #ifdef __cplusplus

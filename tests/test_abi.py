@@ -26,7 +26,8 @@ def lib():
 def test_header_declares_the_four_entry_points_and_helpers():
     names = declared_functions()
     for n in ["sa_estimate", "sa_select_topk", "sa_block_sparse_fwd", "sa_gather_decode", "sa_vs_build",
-              "sa_cluster_pack", "sa_select_mass", "sa_kmeans", "sa_last_error", "sa_version", "sa_args_size"]:
+              "sa_cluster_pack", "sa_select_mass", "sa_kmeans", "sa_estimate_topk", "sa_last_error", "sa_version",
+              "sa_args_size"]:
         assert n in names
 
 
@@ -192,6 +193,30 @@ def test_kmeans_argument_errors(lib):
     assert lib.sa_kmeans_workspace_bytes(C.byref(a), C.byref(n)) == 4
     a.k = 256
     assert lib.sa_kmeans(C.byref(a), None, 0, None) == 5                      # workspace missing
+
+
+def test_estimate_topk_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    a = F.EstimateTopkArgs()
+    n = C.c_size_t(0)
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 1
+    a.q = a.k_ptr = a.idx = a.cnt = 256
+    a.kind, a.dtype, a.block_size, a.scale = F.SA_EST_BLOCK_MEANPOOL, F.SA_BF16, 64, 0.1
+    a.batch, a.heads_q, a.heads_kv, a.seq, a.head_dim = 1, 32, 8, 131072, 128
+    a.n_sink, a.n_local, a.ratio_num, a.ratio_den, a.kmax = 1, 4, 5, 100, 107
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 2      # largest row keeps 5 + 103
+    a.kmax = 108
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0 and n.value > 0
+    a.pooled_q = a.pooled_k = 4096
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0 and n.value == 0
+    a.seq = 131072 * 2
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 6      # above 2048 blocks
+    a.seq = 131072
+    a.kind = F.SA_EST_INDEXER
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 6
+    a.kind = F.SA_EST_BLOCK_MEANPOOL
+    a.n_local = -1
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 8
 
 
 def test_estimate_and_gather_argument_errors(lib):
