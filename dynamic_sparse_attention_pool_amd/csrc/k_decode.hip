@@ -56,20 +56,48 @@ __global__ __launch_bounds__(256) void k_pack_count(const int32_t* __restrict__ 
 }
 
 // Exclusive scan in (cluster, segment) order -> per-segment bases and cluster_ptr.
-__global__ __launch_bounds__(64) void k_pack_scan(int C, int nseg, int32_t* __restrict__ seg, int32_t* __restrict__ ptr) {
-  const int g = blockIdx.x;
-  if (threadIdx.x != 0) return;
+// One workgroup per KV head: thread t owns a run of consecutive (cluster,
+// segment) entries, sums it, takes its base from a workgroup scan, then writes
+// the running bases; the first entry of every cluster gives cluster_ptr.
+constexpr int kScanThreads = 1024;
+
+__global__ __launch_bounds__(kScanThreads) void k_pack_scan(int C, int nseg, int32_t* __restrict__ seg,
+                                                            int32_t* __restrict__ ptr) {
+  __shared__ int32_t wsum[kScanThreads / 64];
+  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t total = (int64_t)C * nseg;
+  const int64_t per = (total + kScanThreads - 1) / kScanThreads;
+  const int64_t e0 = min(total, (int64_t)tid * per), e1 = min(total, e0 + per);
+  int32_t* sg = seg + (int64_t)g * nseg * C;
+  auto at = [&](int64_t e) -> int32_t& {  // entry e = cluster e / nseg, segment e % nseg
+    return sg[(e % nseg) * C + e / nseg];
+  };
   int32_t run = 0;
-  for (int c = 0; c < C; ++c) {
-    ptr[(int64_t)g * (C + 1) + c] = run;
-    for (int s = 0; s < nseg; ++s) {
-      int32_t* e = &seg[((int64_t)g * nseg + s) * C + c];
-      const int32_t x = *e;
-      *e = run;
-      run += x;
-    }
+  for (int64_t e = e0; e < e1; ++e) run += at(e);
+  // workgroup exclusive scan of the per-thread sums
+  int32_t incl = run;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
   }
-  ptr[(int64_t)g * (C + 1) + C] = run;
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int32_t base = incl - run, all = 0;
+#pragma unroll
+  for (int x = 0; x < kScanThreads / 64; ++x) {
+    const int32_t v = wsum[x];
+    base += x < wv ? v : 0;
+    all += v;
+  }
+  for (int64_t e = e0; e < e1; ++e) {
+    int32_t& cell = at(e);
+    const int32_t x = cell;
+    if (e % nseg == 0) ptr[(int64_t)g * (C + 1) + e / nseg] = base;
+    cell = base;
+    base += x;
+  }
+  if (tid == 0) ptr[(int64_t)g * (C + 1) + C] = all;
 }
 
 // Each thread owns clusters; walking the segment in token order keeps the sort stable.
@@ -583,7 +611,7 @@ hipError_t launch_cluster_pack(const int32_t* labels, int64_t hkv, int64_t n, in
   int32_t* seg = reinterpret_cast<int32_t*>(ws);
   const dim3 grid((unsigned)(hkv * nseg));
   hipLaunchKernelGGL(k_pack_count, grid, dim3(256), (size_t)C * 4, stream, labels, n, C, nseg, seg, err);
-  hipLaunchKernelGGL(k_pack_scan, dim3((unsigned)hkv), dim3(64), 0, stream, C, nseg, seg, ptr);
+  hipLaunchKernelGGL(k_pack_scan, dim3((unsigned)hkv), dim3(kScanThreads), 0, stream, C, nseg, seg, ptr);
   hipLaunchKernelGGL(k_pack_scatter, grid, dim3(256), 0, stream, labels, n, C, nseg, seg, perm);
   if (kp != nullptr) {
     const int row_bytes = head_dim * elem_bytes;
