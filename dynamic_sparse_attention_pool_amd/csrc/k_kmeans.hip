@@ -106,12 +106,24 @@ __global__ __launch_bounds__(D) void k_km_update(const T* __restrict__ keys, con
   if (e <= b) return;  // empty cluster: the centroid stays
   const T* kg = keys + (int64_t)g * n * D;
   const int32_t* pg = perm + (int64_t)g * n;
+  auto val = [&](int64_t row) -> float {
+    if constexpr (sizeof(T) == 2) return bf2f(kg[row * D + d]);
+    else return kg[row * D + d];
+  };
+  // 8 rows' loads in flight at a time; the sum still runs in token order
   float s = 0.f;
-  for (int32_t r = b; r < e; ++r) {
-    const int64_t row = pg[r];
-    if constexpr (sizeof(T) == 2) s += bf2f(kg[row * D + d]);
-    else s += kg[row * D + d];
+  int32_t r = b;
+  for (; r + 8 <= e; r += 8) {
+    int64_t rows[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) rows[x] = pg[r + x];
+    float v[8];
+#pragma unroll
+    for (int x = 0; x < 8; ++x) v[x] = val(rows[x]);
+#pragma unroll
+    for (int x = 0; x < 8; ++x) s += v[x];
   }
+  for (; r < e; ++r) s += val(pg[r]);
   cent[((int64_t)g * C + c) * D + d] = s / (float)(e - b);
 }
 
