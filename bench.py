@@ -139,7 +139,7 @@ def decode_extra(steps, warmup, mass=None):
     for c in range(4):  # rotate over 4 contexts so no step finds the last one in the 256 MB MALL
         inp = W.decode_clustered(W.CONFIG_SEEDS[4] + 100 * c, T, Hq, Hkv, N, d, C)
         copies.append(ClusterDecode(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev_t(inp.labels),
-                                    dev_t(inp.centroids), n_sel=ksel, mass=mass, k_min=1))
+                                    dev_t(inp.centroids), n_sel=ksel, mass=mass, k_min=1, fused=mass is None))
     torch.cuda.synchronize()
     for i in range(max(warmup, 4)):
         copies[i % 4].step()
@@ -184,7 +184,7 @@ def decode_extra(steps, warmup, mass=None):
     step_bytes = kv_bytes + small
     fwd_ms = tm.mean_ms("forward")
     mean_sel = float(np.mean([dc.sel_cnt.float().mean().item() for dc in copies]))
-    rule = ("top 64 of 256 clusters" if mass is None else
+    rule = ("top 64 of 256 clusters (scores and selection in one call)" if mass is None else
             f"fewest clusters holding {mass:g} of the centroid-score softmax, 1..64 of 256")
     return {"workload": f"clustered decode: 8 queries x 32/8 heads, d128, 65536-key context, {rule}; "
                         "each step replayed as a HIP graph, rotating 4 contexts",

@@ -15,7 +15,7 @@ from . import _ffi as F
 from ._ffi import SAError, load  # noqa: F401
 
 __all__ = ["sa_estimate", "sa_select_topk", "sa_select_mass", "sa_vs_build", "sa_block_sparse_fwd",
-           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "sa_estimate_topk", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
+           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "sa_estimate_topk", "sa_estimate_topk_centroid", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
 
 BLOCK_MEANPOOL, VSLASH, CENTROID, INDEXER = (F.SA_EST_BLOCK_MEANPOOL, F.SA_EST_VSLASH, F.SA_EST_CENTROID,
                                              F.SA_EST_INDEXER)
@@ -171,6 +171,22 @@ def sa_estimate_topk(q, k, idx, cnt, *, n_sink: int = 0, n_local: int = 0, k_fix
         workspace, _ = _workspace(nb.value, q)
     F.check(lib.sa_estimate_topk(C.byref(a), _p(workspace) if nb.value else None, nb.value, _stream()))
     return workspace
+
+
+def sa_estimate_topk_centroid(q, centroids, sel, cnt, *, k: int, scale=None, err_flag=None):
+    """Centroid scores and top-k clusters in one call: q [T,Hq,d],
+    centroids [Hkv,C,d] float; sel [T,Hq,kmax], cnt [T,Hq] int32."""
+    lib = load()
+    a = F.EstimateTopkArgs()
+    T, Hq, d = q.shape
+    a.kind, a.dtype = F.SA_EST_CENTROID, _dt(q)
+    a.batch, a.heads_q, a.heads_kv, a.seq, a.head_dim = 1, Hq, centroids.shape[0], T, d
+    a.n_centroids = centroids.shape[1]
+    a.scale = (1.0 / math.sqrt(d)) if scale is None else scale
+    a.k, a.kmax = k, sel.shape[-1]
+    a.q, a.k_ptr = _p(q), _p(centroids)
+    a.idx, a.cnt, a.err_flag = _p(sel), _p(cnt), _p(err_flag)
+    F.check(lib.sa_estimate_topk(C.byref(a), None, 0, _stream()))
 
 
 def sa_vs_build(vert, vert_cnt, slash, slash_cnt, iv, iv_cnt, col, col_cnt, seq: int, block_size: int = 64):

@@ -187,7 +187,7 @@ __device__ __forceinline__ void wave_sync() {
 
 // ================================================================ cluster decode
 constexpr int kDecWaves = 4;
-constexpr int kRowsPerSplit = 1024;
+constexpr int kRowsPerSplit = 2048;
 
 int decode_splits(int64_t n_ctx) { return (int)((n_ctx + kRowsPerSplit - 1) / kRowsPerSplit); }
 

@@ -252,7 +252,197 @@ __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q,
   }
 }
 
+// ---------------------------------------------------------------- k_centroid_topk
+// Centroid scores and the per-row top-k in one pass, for decode: one workgroup
+// per (token, KV head) covers the grp query heads that share the KV head.
+// Thread c owns centroids c, c+256, ...: it reads each centroid row once and
+// computes its score for every query of the group (dimension order, fp32, as
+// k_centroid_score), keeping order-preserving keys in LDS.  Per row, an
+// MSB-first radix select (8-bit digits, LDS histograms, 32 threads per row for
+// the digit) finds the k-th key T; candidates above T and the lowest-index
+// keys equal to T are written in cluster order.
+constexpr int kCtThreads = 256;
+constexpr int kCtMaxRows = 8;
+constexpr int kCtMaxC = 1024;
+
+template <typename T>
+__global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restrict__ q, const float* __restrict__ cent,
+                                                              int hq, int hkv, int C, int D, float scale, int k,
+                                                              int kmax, int32_t* __restrict__ idx,
+                                                              int32_t* __restrict__ cnt, int32_t* err) {
+  __shared__ float qs[kCtMaxRows][128];
+  __shared__ uint32_t keys[kCtMaxRows][kCtMaxC];
+  __shared__ uint32_t hist[kCtMaxRows][256];
+  __shared__ uint32_t s_digit[kCtMaxRows][2];
+  __shared__ int32_t s_need[kCtMaxRows];
+  __shared__ uint32_t s_wave[kCtThreads / 64][kCtMaxRows][2];
+  __shared__ uint32_t s_nan;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int grp = hq / hkv;
+  const int t = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  const int kr = min(k, C);
+  if (tid == 0) s_nan = 0u;
+  for (int e = tid; e < grp * D; e += kCtThreads) {
+    const int hh = e / D, d = e % D;
+    const T* qp = q + ((int64_t)t * hq + g * grp + hh) * D + d;
+    if constexpr (sizeof(T) == 2) qs[hh][d] = bf2f(*reinterpret_cast<const uint16_t*>(qp));
+    else qs[hh][d] = *reinterpret_cast<const float*>(qp);
+  }
+  if (tid < grp) s_need[tid] = kr;
+  __syncthreads();
+  // ---- scores -> keys
+  bool nan_seen = false;
+  for (int c = tid; c < C; c += kCtThreads) {
+    const float* cr = cent + ((int64_t)g * C + c) * D;
+    float acc[kCtMaxRows];
+#pragma unroll
+    for (int hh = 0; hh < kCtMaxRows; ++hh) acc[hh] = 0.f;
+    for (int d0 = 0; d0 < D; d0 += 4) {
+      const f32x4 m4 = *reinterpret_cast<const f32x4*>(cr + d0);
+#pragma unroll
+      for (int hh = 0; hh < kCtMaxRows; ++hh)
+        if (hh < grp) {
+          acc[hh] = fmaf(qs[hh][d0], m4[0], acc[hh]);
+          acc[hh] = fmaf(qs[hh][d0 + 1], m4[1], acc[hh]);
+          acc[hh] = fmaf(qs[hh][d0 + 2], m4[2], acc[hh]);
+          acc[hh] = fmaf(qs[hh][d0 + 3], m4[3], acc[hh]);
+        }
+    }
+#pragma unroll
+    for (int hh = 0; hh < kCtMaxRows; ++hh)
+      if (hh < grp) {
+        const float sc = acc[hh] * scale;
+        nan_seen |= is_nan(sc);
+        keys[hh][c] = order_key(sc);
+      }
+  }
+  if (nan_seen) atomicOr(&s_nan, 1u);
+  // ---- radix select: T[hh] = the kr-th largest key of row hh
+  uint32_t Tk[kCtMaxRows];
+#pragma unroll
+  for (int hh = 0; hh < kCtMaxRows; ++hh) Tk[hh] = 0u;
+  constexpr int TPR = kCtThreads / kCtMaxRows;  // 32 threads per row in the digit search
+#pragma unroll 1
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    const uint32_t hmask = shift == 24 ? 0u : ~((1u << (shift + 8)) - 1u);
+    for (int e = tid; e < kCtMaxRows * 256; e += kCtThreads) (&hist[0][0])[e] = 0u;
+    __syncthreads();
+    for (int c = tid; c < C; c += kCtThreads)
+#pragma unroll
+      for (int hh = 0; hh < kCtMaxRows; ++hh)
+        if (hh < grp) {
+          const uint32_t key = keys[hh][c];
+          if ((key & hmask) == (Tk[hh] & hmask)) atomicAdd(&hist[hh][(key >> shift) & 255u], 1u);
+        }
+    __syncthreads();
+    {
+      const int row = tid / TPR, seg = tid % TPR;
+      if (row < grp) {
+        const int rneed = s_need[row];
+        uint32_t loc = 0u;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) loc += hist[row][8 * seg + x];
+        uint32_t incl = loc;
+#pragma unroll
+        for (int off = 1; off < TPR; off <<= 1) {
+          const uint32_t o = __shfl_down(incl, off, TPR);
+          if (seg + off < TPR) incl += o;
+        }
+        const uint32_t above = incl - loc;
+        if (rneed == 0) {
+          if (seg == TPR - 1) {
+            s_digit[row][0] = 255u;
+            s_digit[row][1] = 0u;
+          }
+        } else if (above < (uint32_t)rneed && (uint32_t)rneed <= incl) {
+          uint32_t acc = above;
+          for (int dg = 8 * seg + 7; dg >= 8 * seg; --dg) {
+            const uint32_t hc = hist[row][dg];
+            if (acc + hc >= (uint32_t)rneed) {
+              s_digit[row][0] = (uint32_t)dg;
+              s_digit[row][1] = acc;
+              break;
+            }
+            acc += hc;
+          }
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < kCtMaxRows; ++hh)
+      if (hh < grp) Tk[hh] |= s_digit[hh][0] << shift;
+    if (tid < grp) s_need[tid] -= (int)s_digit[tid][1];  // read again after two more barriers
+  }
+  __syncthreads();
+  // ---- emission in cluster order: chunks of 256 candidates, ballots per wave
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int base_f[kCtMaxRows], base_t[kCtMaxRows];
+#pragma unroll
+  for (int hh = 0; hh < kCtMaxRows; ++hh) base_f[hh] = base_t[hh] = 0;
+  for (int c0 = 0; c0 < C; c0 += kCtThreads) {
+    const int c = c0 + tid;
+    uint64_t mf[kCtMaxRows], mt[kCtMaxRows];
+#pragma unroll
+    for (int hh = 0; hh < kCtMaxRows; ++hh) {
+      const uint32_t key = (c < C && hh < grp) ? keys[hh][c] : 0u;
+      const bool live = c < C && hh < grp;
+      mf[hh] = __ballot(live && key > Tk[hh]);
+      mt[hh] = __ballot(live && key == Tk[hh]);
+      if (lane == 0) {
+        s_wave[wv][hh][0] = (uint32_t)__popcll(mf[hh]);
+        s_wave[wv][hh][1] = (uint32_t)__popcll(mt[hh]);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int hh = 0; hh < kCtMaxRows; ++hh) {
+      if (hh >= grp) continue;
+      int wf = 0, wt = 0, af = 0, at = 0;
+      for (int x = 0; x < kCtThreads / 64; ++x) {
+        const int f = (int)s_wave[x][hh][0], e = (int)s_wave[x][hh][1];
+        if (x < wv) {
+          wf += f;
+          wt += e;
+        }
+        af += f;
+        at += e;
+      }
+      const int need = s_need[hh];
+      const int fb = base_f[hh] + wf + (int)__popcll(mf[hh] & lt);
+      const int tb = base_t[hh] + wt + (int)__popcll(mt[hh] & lt);
+      int32_t* out = idx + ((int64_t)t * hq + g * grp + hh) * kmax;
+      if ((mf[hh] >> lane) & 1ull) out[fb + min(tb, need)] = c;
+      else if (((mt[hh] >> lane) & 1ull) && tb < need) out[fb + tb] = c;
+      base_f[hh] += af;
+      base_t[hh] += at;
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < grp * kmax; e += kCtThreads) {
+    const int hh = e / kmax, pos = e % kmax;
+    const int64_t row = (int64_t)t * hq + g * grp + hh;
+    if (pos >= kr) idx[row * kmax + pos] = -1;
+    if (pos == 0) cnt[row] = kr;
+  }
+  if (tid == 0 && s_nan && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
+}
+
 }  // namespace
+
+hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv, int C,
+                                int head_dim, float scale, int k, int kmax, int32_t* idx, int32_t* cnt, int32_t* err,
+                                hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  const dim3 grid((unsigned)(T * hkv));
+  if (q_bf16)
+    hipLaunchKernelGGL((k_centroid_topk<uint16_t>), grid, dim3(kCtThreads), 0, stream, (const uint16_t*)q, cent, hq,
+                       hkv, C, head_dim, scale, k, kmax, idx, cnt, err);
+  else
+    hipLaunchKernelGGL((k_centroid_topk<float>), grid, dim3(kCtThreads), 0, stream, (const float*)q, cent, hq, hkv,
+                       C, head_dim, scale, k, kmax, idx, cnt, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_pool(const void* x, int64_t batch, int hq, const HeadList& hl, int64_t seq, int head_dim,
                        bool bf16, int block, float* out, hipStream_t stream) {

@@ -61,6 +61,11 @@ hipError_t launch_block_score(const float* pq, const float* pk, int batch, int h
                               int nb, int head_dim, float scale, float* scores, hipStream_t stream);
 hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,
                                  int C, int head_dim, float scale, float* out, hipStream_t stream);
+// centroid scores and a per-row top-k in one pass (query heads per KV head <= 8,
+// clusters <= 1024, head_dim <= 128)
+hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv, int C,
+                                int head_dim, float scale, int k, int kmax, int32_t* idx, int32_t* cnt, int32_t* err,
+                                hipStream_t stream);
 hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
                           int64_t pos0, float* out, hipStream_t stream);
 size_t vs_workspace_bytes(int64_t rows, int64_t seq);

@@ -327,10 +327,31 @@ int sa_select_mass(const sa_select_mass_args* a, void* stream) {
 }
 
 // ---------------------------------------------------------------- fused block estimate + top-k
+static int check_centroid_topk(const sa_estimate_topk_args* a) {
+  if (!a->q || !a->k_ptr || !a->idx || !a->cnt) return fail(SA_ERR_NULL, "sa_estimate_topk(CENTROID): q, centroids, idx and cnt are required");
+  if (!aligned16(a->q) || !aligned16(a->k_ptr)) return fail(SA_ERR_ALIGN, "sa_estimate_topk(CENTROID): q and centroids must be 16-byte aligned");
+  if (a->dtype != SA_F32 && a->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "sa_estimate_topk(CENTROID): dtype must be F32 or BF16");
+  if (a->head_list || a->n_sink || a->n_local || a->ratio_den)
+    return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk(CENTROID): fixed k only (no head list, forced members or ratio)");
+  if (a->seq < 0 || a->heads_q <= 0 || a->heads_kv <= 0 || a->head_dim <= 0) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): sizes must be positive");
+  if (a->heads_q % a->heads_kv || a->heads_q / a->heads_kv > 8)
+    return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk(CENTROID): heads_q must be 1..8 times heads_kv");
+  if (a->head_dim > 128 || a->head_dim % 4) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk(CENTROID): head_dim must be a multiple of 4, at most 128");
+  if (a->n_centroids < 1 || a->n_centroids > 1024) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): n_centroids must lie in [1, 1024]");
+  if (a->seq * a->heads_kv > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): too many queries");
+  if (!(a->scale > 0.f)) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): scale must be > 0");
+  if (a->k < 0) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): k must be >= 0");
+  const int32_t need = a->k < a->n_centroids ? a->k : a->n_centroids;
+  if (a->kmax <= 0 || a->kmax < need) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): kmax %d is below min(k, C) = %d", a->kmax, need);
+  return ok();
+}
+
 static int check_estimate_topk(const sa_estimate_topk_args* a, size_t* ws, sa::HeadList& hl) {
   if (!a) return fail(SA_ERR_NULL, "sa_estimate_topk: args is NULL");
   *ws = 0;
-  if (a->kind != SA_EST_BLOCK_MEANPOOL) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk: only BLOCK_MEANPOOL");
+  hl.n = 0;
+  if (a->kind == SA_EST_CENTROID) return check_centroid_topk(a);
+  if (a->kind != SA_EST_BLOCK_MEANPOOL) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk: only BLOCK_MEANPOOL and CENTROID");
   if (!a->q || !a->k_ptr || !a->idx || !a->cnt) return fail(SA_ERR_NULL, "sa_estimate_topk: q, k, idx and cnt are required");
   if (!aligned16(a->q) || !aligned16(a->k_ptr)) return fail(SA_ERR_ALIGN, "sa_estimate_topk: q and k must be 16-byte aligned");
   if ((a->pooled_q && !aligned16(a->pooled_q)) || (a->pooled_k && !aligned16(a->pooled_k)))
@@ -388,6 +409,11 @@ int sa_estimate_topk(const sa_estimate_topk_args* a, void* workspace, size_t wor
     return fail(SA_ERR_WORKSPACE, "sa_estimate_topk: workspace of %zu bytes required", ws);
   if (workspace && !aligned16(workspace)) return fail(SA_ERR_ALIGN, "sa_estimate_topk: workspace must be 16-byte aligned");
   const hipStream_t st = as_stream(stream);
+  if (a->kind == SA_EST_CENTROID)
+    return launched(sa::launch_centroid_topk(a->q, a->dtype == SA_BF16, static_cast<const float*>(a->k_ptr), (int)a->seq,
+                                             (int)a->heads_q, (int)a->heads_kv, a->n_centroids, (int)a->head_dim,
+                                             a->scale, a->k, a->kmax, a->idx, a->cnt, a->err_flag, st),
+                    "sa_estimate_topk(CENTROID)");
   const int64_t nb = a->seq / kBlock;
   const int64_t nh = hl.n > 0 ? hl.n : a->heads_q;
   char* w = static_cast<char*>(workspace);

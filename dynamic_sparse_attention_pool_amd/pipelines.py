@@ -9,7 +9,8 @@ from __future__ import annotations
 import math
 
 from . import (BLOCK_MEANPOOL, CENTROID, INDEXER, VSLASH, sa_block_sparse_fwd, sa_cluster_pack, sa_estimate,
-               sa_estimate_topk, sa_gather_decode, sa_select_mass, sa_select_topk, sa_vs_build)
+               sa_estimate_topk, sa_estimate_topk_centroid, sa_gather_decode, sa_select_mass, sa_select_topk,
+               sa_vs_build)
 
 
 def _t():
@@ -225,10 +226,11 @@ class ClusterDecode:
     centroid scores -> top clusters -> gathered attention."""
 
     def __init__(self, q, k, v, labels, centroids, *, n_sel: int, mass=None, k_min: int = 1, out_dtype=None,
-                 scale=None, with_lse=False):
+                 scale=None, with_lse=False, fused=False):
         """n_sel clusters per query head, or, with ``mass`` set, the fewest
         clusters holding that share of the softmax of the centroid scores,
-        between k_min and n_sel (sa_select_mass)."""
+        between k_min and n_sel (sa_select_mass).  ``fused`` (fixed n_sel
+        only): scores and top clusters in one call, ``estimate`` doing both."""
         torch = _t()
         T, Hq, d = q.shape
         Hkv, N, _ = k.shape
@@ -236,6 +238,9 @@ class ClusterDecode:
         dev = q.device
         self.q, self.centroids, self.C, self.n_sel = q, centroids, C, n_sel
         self.mass, self.k_min = mass, k_min
+        if fused and mass is not None:
+            raise ValueError("the fused centroid top-k takes a fixed number of clusters")
+        self.fused = fused
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
         self.ptr = torch.empty((Hkv, C + 1), dtype=torch.int32, device=dev)
         self.perm = torch.empty((Hkv, N), dtype=torch.int32, device=dev)
@@ -252,9 +257,15 @@ class ClusterDecode:
         self.ws = None
 
     def estimate(self):
+        if self.fused:
+            sa_estimate_topk_centroid(self.q, self.centroids, self.sel, self.sel_cnt.view(self.sel.shape[0], -1),
+                                      k=self.n_sel, scale=self.scale)
+            return
         sa_estimate(CENTROID, self.q, self.k, self.scores, centroids=self.centroids, scale=self.scale)
 
     def select(self):
+        if self.fused:
+            return
         if self.mass is None:
             sa_select_topk(self.scores.view(-1, self.C), self.sel.view(-1, self.n_sel), self.sel_cnt, k=self.n_sel)
         else:

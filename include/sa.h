@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 5
+#define SA_ABI_VERSION 6
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -233,12 +233,22 @@ int sa_select_mass(const sa_select_mass_args* args, void* stream);
  * memory: a workgroup scores 16 consecutive rows, keeps them in registers and
  * selects from them.
  *
- * kind = SA_EST_BLOCK_MEANPOOL only.  q [B,Hq,N,d], k [B,Hkv,N,d] (F32 or
- * BF16, d = 64 or 128), N a multiple of 64 with N/64 <= 2048.
+ * kind = SA_EST_BLOCK_MEANPOOL: q [B,Hq,N,d], k [B,Hkv,N,d] (F32 or BF16,
+ * d = 64 or 128), N a multiple of 64 with N/64 <= 2048.
  * idx [B,n,nb,kmax] int32, cnt [B,n,nb] int32 (n = Hq, or n_heads_list with a
  * host head list as in sa_estimate); kmax must hold the largest count.
- * pooled_q / pooled_k: optional outputs as in sa_estimate.  err_flag: as in
- * sa_select_topk.  Requires a workspace unless both pooled buffers are given.
+ * pooled_q / pooled_k: optional outputs as in sa_estimate.  Requires a
+ * workspace unless both pooled buffers are given.
+ *
+ * kind = SA_EST_CENTROID (Squeezed Attention page, §技术方案: query-centroid
+ * similarity, then the top-K clusters): equals sa_estimate(CENTROID) followed
+ * by sa_select_topk with k and no forced members, bit for bit (the scores use
+ * the same arithmetic).  q [T,Hq,d] (F32 or BF16; seq = T), k_ptr = the
+ * centroid table [Hkv,C,d] float, n_centroids = C <= 1024, d <= 128, at most 8
+ * query heads per KV head.  idx [T,Hq,kmax], cnt [T,Hq]; kmax >= min(k, C).
+ * No workspace; head lists, ratios and forced members are not supported.
+ *
+ * err_flag: as in sa_select_topk.
  * ====================================================================== */
 typedef struct sa_estimate_topk_args {
   int32_t kind;
@@ -262,7 +272,7 @@ typedef struct sa_estimate_topk_args {
   float* pooled_k;
   const int32_t* head_list;
   int32_t n_heads_list;
-  int32_t reserved0;
+  int32_t n_centroids;    /* CENTROID */
   int32_t* idx;
   int32_t* cnt;
   int32_t* err_flag;

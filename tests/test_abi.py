@@ -214,6 +214,19 @@ def test_estimate_topk_argument_errors(lib):
     a.seq = 131072
     a.kind = F.SA_EST_INDEXER
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 6
+    c = F.EstimateTopkArgs()                                                     # centroid kind
+    c.q = c.k_ptr = c.idx = c.cnt = 256
+    c.kind, c.dtype, c.scale, c.k, c.kmax = F.SA_EST_CENTROID, F.SA_BF16, 0.1, 64, 64
+    c.heads_q, c.heads_kv, c.seq, c.head_dim, c.n_centroids = 32, 8, 8, 128, 256
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 0 and n.value == 0
+    c.kmax = 63
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 2
+    c.kmax, c.n_centroids = 64, 2000
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 2
+    c.n_centroids, c.heads_q = 256, 80                                           # 10 query heads per KV head
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 6
+    c.heads_q, c.n_sink = 32, 1
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 6
     a.kind = F.SA_EST_BLOCK_MEANPOOL
     a.n_local = -1
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 8

@@ -162,3 +162,80 @@ def test_token_gather_mqa(sa, T, N, ntok):
                                        1 / math.sqrt(128))
     assert_attention_close(host(out), wo, bf16=True, what="token gather")
     assert np.max(np.abs(host(lse) - wl)) < 1e-3
+
+
+@pytest.mark.parametrize("T,Hq,Hkv,C,k,dt", [(8, 32, 8, 256, 64, "bf16"), (3, 6, 2, 1000, 37, "f32"),
+                                            (2, 8, 1, 300, 400, "bf16"), (5, 4, 4, 17, 5, "f32")])
+def test_fused_centroid_topk_matches_oracle_and_separate_path(sa, T, Hq, Hkv, C, k, dt):
+    """sa_estimate_topk(CENTROID) keeps the oracle's clusters on certified rows
+    and equals the separate scores + selection bit for bit (same arithmetic)."""
+    print(f"fused centroid T{T} Hq{Hq} Hkv{Hkv} C{C} k{k} {dt}", flush=True)
+    t = torch()
+    inp = W.decode_clustered(61, T, Hq, Hkv, 64, 128, C)
+    qf = W.bf16_to_f32(inp.q)
+    q = dev_bf16(inp.q) if dt == "bf16" else dev_f32(qf)
+    cent = dev_f32(inp.centroids)
+    if k == 5:   # tied scores: duplicate centroids
+        c2 = inp.centroids.copy()
+        c2[:, 1::2] = c2[:, 0::2][:, :c2[:, 1::2].shape[1]]
+        cent = dev_f32(c2)
+        inp.centroids = c2
+    kmax = min(k, C) + 2
+    sel = t.full((T, Hq, kmax), 9, dtype=t.int32, device="cuda:0")
+    cnt = t.full((T, Hq), -1, dtype=t.int32, device="cuda:0")
+    sa.sa_estimate_topk_centroid(q, cent, sel, cnt, k=k, scale=1 / math.sqrt(128))
+    s = t.empty((T, Hq, C), dtype=t.float32, device="cuda:0")
+    sa.sa_estimate(sa.CENTROID, q, q, s, centroids=cent, scale=1 / math.sqrt(128))
+    sel2 = t.full((T * Hq, kmax), 9, dtype=t.int32, device="cuda:0")
+    cnt2 = t.full((T * Hq,), -1, dtype=t.int32, device="cuda:0")
+    sa.sa_select_topk(s.view(T * Hq, C), sel2, cnt2, k=k)
+    t.cuda.synchronize()
+    got, gcnt = host(sel), host(cnt)
+    assert np.array_equal(got.reshape(T * Hq, kmax), host(sel2)) and np.array_equal(gcnt.reshape(-1), host(cnt2))
+    assert np.all(gcnt == min(k, C)) and np.all(got[:, :, min(k, C):] == -1)
+    want_s = oracle.centroid_scores(qf, inp.centroids, 1 / math.sqrt(128))
+    none = np.zeros(0, np.int64)
+    for tt in range(T):
+        for h in range(Hq):
+            if oracle.certified_row(want_s[tt, h], min(k, C), none):
+                assert np.array_equal(got[tt, h, :min(k, C)], oracle.topk_row(want_s[tt, h], k, none)), (tt, h)
+
+
+def test_fused_centroid_topk_nan_flag(sa):
+    t = torch()
+    inp = W.decode_clustered(62, 2, 8, 2, 64, 128, 40)
+    qf = W.bf16_to_f32(inp.q).copy()
+    qf[1, 5, 3] = np.nan
+    sel = t.empty((2, 8, 10), dtype=t.int32, device="cuda:0")
+    cnt = t.empty((2, 8), dtype=t.int32, device="cuda:0")
+    err = t.zeros(1, dtype=t.int32, device="cuda:0")
+    sa.sa_estimate_topk_centroid(dev_f32(qf), dev_f32(inp.centroids), sel, cnt, k=10, err_flag=err)
+    t.cuda.synchronize()
+    assert int(host(err)[0]) == 1
+
+
+def test_decode_end_to_end_full_size_fused_estimate(sa):
+    """The full-size decode step with the fused centroid top-k: same clusters
+    as the oracle on certified rows, outputs within the bf16 bounds."""
+    from dynamic_sparse_attention_pool_amd.pipelines import ClusterDecode
+    seed = W.CONFIG_SEEDS[4]
+    T, Hq, Hkv, N, d, C, ksel = 8, 32, 8, 65536, 128, 256, 64
+    inp = W.decode_clustered(seed, T, Hq, Hkv, N, d, C)
+    scale = 1 / math.sqrt(d)
+    dc = ClusterDecode(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev_i32(inp.labels),
+                       dev_f32(inp.centroids), n_sel=ksel, with_lse=True, fused=True)
+    dc.step()
+    torch().cuda.synchronize()
+    s = oracle.centroid_scores(W.bf16_to_f32(inp.q), inp.centroids, scale)
+    none = np.zeros(0, np.int64)
+    got = host(dc.sel)
+    rows = [(t, h) for t in range(T) for h in range(Hq) if oracle.certified_row(s[t, h], ksel, none)]
+    assert len(rows) > 0.6 * T * Hq
+    sel = oracle.cluster_select(s, ksel)
+    for t, h in rows:
+        assert np.array_equal(got[t, h], sel[t][h]), (t, h)
+    wo, _ = oracle.cluster_decode(W.bf16_to_f32(inp.q), W.bf16_to_f32(inp.k), W.bf16_to_f32(inp.v), inp.labels,
+                                  sel, scale)
+    o = host(dc.out)
+    idx = np.array(rows)
+    assert_attention_close(o[idx[:, 0], idx[:, 1]], wo[idx[:, 0], idx[:, 1]], bf16=True, what="fused decode")
