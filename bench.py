@@ -222,14 +222,23 @@ def indexer_extra(steps, warmup):
         tm.span("select", lambda: __import__("dynamic_sparse_attention_pool_amd").sa_select_topk(
             ip.scores, ip.idx, ip.cnt, k=k_sel, causal=True, causal_period=T, causal_offset=ip.pos0))
         tm.span("attend", lambda: ip.attend(1))
+    fu = IndexerPrefill(ip.qi, ip.ki, ip.w, ind.pos0, layers, k_sel=k_sel, out_dtype=torch.bfloat16, fused=True)
+    fu.index()
     torch.cuda.synchronize()
+    for _ in range(steps):
+        tm.span("index_fused", fu.index)
+        tm.span("total_reuse_fused", lambda: fu.step(reuse=True))
+    torch.cuda.synchronize()
+    same = bool(torch.equal(fu.idx, ip.idx)) and int(fu.err.item()) == 0
     pairs = sum(ind.pos0 + t + 1 for t in range(T))
     idx_ms = tm.mean_ms("indexer")
     return {"workload": "token top-2048 prefill chunk: 4096 queries at the end of 131072, 64x64 indexer, "
                         "MQA 16/1 d128, 4 layers, layer 1 full / 2-4 shared",
             "ms_4layers_with_reuse": tm.mean_ms("total_reuse"), "ms_4layers_without_reuse": tm.mean_ms("total_noreuse"),
             "ms_indexer": idx_ms, "indexer_TFLOP_per_s": pairs * 8192 / (idx_ms * 1e-3) / 1e12,
-            "ms_select": tm.mean_ms("select"), "ms_attend_layer": tm.mean_ms("attend")}
+            "ms_select": tm.mean_ms("select"), "ms_attend_layer": tm.mean_ms("attend"),
+            "ms_index_fused": tm.mean_ms("index_fused"), "ms_4layers_with_reuse_fused": tm.mean_ms("total_reuse_fused"),
+            "fused_index_equals_two_call": same}
 
 
 def vs_extra(steps, warmup, inp):

@@ -15,7 +15,7 @@ from . import _ffi as F
 from ._ffi import SAError, load  # noqa: F401
 
 __all__ = ["sa_estimate", "sa_select_topk", "sa_select_mass", "sa_vs_build", "sa_block_sparse_fwd",
-           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "sa_estimate_topk", "sa_estimate_topk_centroid", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
+           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "sa_estimate_topk", "sa_estimate_topk_centroid", "sa_indexer_topk", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
 
 BLOCK_MEANPOOL, VSLASH, CENTROID, INDEXER = (F.SA_EST_BLOCK_MEANPOOL, F.SA_EST_VSLASH, F.SA_EST_CENTROID,
                                              F.SA_EST_INDEXER)
@@ -187,6 +187,26 @@ def sa_estimate_topk_centroid(q, centroids, sel, cnt, *, k: int, scale=None, err
     a.q, a.k_ptr = _p(q), _p(centroids)
     a.idx, a.cnt, a.err_flag = _p(sel), _p(cnt), _p(err_flag)
     F.check(lib.sa_estimate_topk(C.byref(a), None, 0, _stream()))
+
+
+def sa_indexer_topk(qi, ki, idx, cnt, *, weights, q_pos0: int, k: int, err_flag=None, workspace=None):
+    """Indexer scores and each query's top-k causal keys in one call (no score
+    matrix): qi [T,Hi,64], ki [Nk,64] bf16, weights [Hi] float; idx [T,kmax],
+    cnt [T] int32.  Rows whose sampled threshold does not hold get cnt = -1
+    (and value 2 in err_flag).  Returns the workspace."""
+    lib = load()
+    a = F.IndexerTopkArgs()
+    T, Hi, di = qi.shape
+    a.seq_q, a.seq_k, a.q_pos0 = T, ki.shape[0], q_pos0
+    a.heads, a.head_dim, a.k, a.kmax = Hi, di, k, idx.shape[-1]
+    a.q, a.k_ptr, a.weights = _p(qi), _p(ki), _p(weights)
+    a.idx, a.cnt, a.err_flag = _p(idx), _p(cnt), _p(err_flag)
+    nb = C.c_size_t(0)
+    F.check(lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(nb)))
+    if nb.value and (workspace is None or workspace.numel() < nb.value):
+        workspace, _ = _workspace(nb.value, qi)
+    F.check(lib.sa_indexer_topk(C.byref(a), _p(workspace) if nb.value else None, nb.value, _stream()))
+    return workspace
 
 
 def sa_vs_build(vert, vert_cnt, slash, slash_cnt, iv, iv_cnt, col, col_cnt, seq: int, block_size: int = 64):

@@ -17,7 +17,7 @@ SA_F32, SA_BF16, SA_I32 = 0, 1, 2
 SA_EST_BLOCK_MEANPOOL, SA_EST_VSLASH, SA_EST_CENTROID, SA_EST_INDEXER = 0, 1, 2, 3
 SA_FWD_BLOCK, SA_FWD_VSLASH, SA_FWD_ASHAPE = 0, 1, 2
 SA_GATHER_CLUSTER, SA_GATHER_TOKEN = 0, 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
                 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_LAUNCH", 8: "SA_ERR_VALUE"}
@@ -95,8 +95,14 @@ class EstimateTopkArgs(C.Structure):
                 ("n_centroids", C.c_int32), ("idx", P), ("cnt", P), ("err_flag", P)]
 
 
+class IndexerTopkArgs(C.Structure):
+    _fields_ = [("seq_q", C.c_int64), ("seq_k", C.c_int64), ("q_pos0", C.c_int64), ("heads", C.c_int32),
+                ("head_dim", C.c_int32), ("k", C.c_int32), ("kmax", C.c_int32), ("q", P), ("k_ptr", P),
+                ("weights", P), ("idx", P), ("cnt", P), ("err_flag", P)]
+
+
 STRUCTS = [EstimateArgs, SelectArgs, VsBuildArgs, FwdArgs, GatherArgs, ClusterPackArgs, SelectMassArgs, KmeansArgs,
-           EstimateTopkArgs]
+           EstimateTopkArgs, IndexerTopkArgs]
 
 # exported symbol -> (restype, argtypes)
 SYMBOLS = {
@@ -116,6 +122,8 @@ SYMBOLS = {
     "sa_estimate_topk": (C.c_int, [C.POINTER(EstimateTopkArgs), P, C.c_size_t, P]),
     "sa_estimate_topk_workspace_bytes": (C.c_int, [C.POINTER(EstimateTopkArgs), C.POINTER(C.c_size_t)]),
     "sa_kmeans_workspace_bytes": (C.c_int, [C.POINTER(KmeansArgs), C.POINTER(C.c_size_t)]),
+    "sa_indexer_topk": (C.c_int, [C.POINTER(IndexerTopkArgs), P, C.c_size_t, P]),
+    "sa_indexer_topk_workspace_bytes": (C.c_int, [C.POINTER(IndexerTopkArgs), C.POINTER(C.c_size_t)]),
     "sa_last_error": (C.c_char_p, []),
     "sa_version": (C.c_int, []),
     "sa_args_size": (C.c_size_t, [C.c_int]),

@@ -25,6 +25,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "select_util.h"
 
 namespace sa {
 namespace {
@@ -148,19 +149,35 @@ constexpr int idx2_qpw() { return HG == 1 ? 4 : 3; }
 // chunk c of row r of a 64 x 128-byte K tile sits at position c ^ ((r >> 1) & 7)
 __device__ __forceinline__ int idx2_swz(int r, int c) { return r * 64 + 8 * (c ^ ((r >> 1) & 7)); }
 
-template <int HG>
+// Candidate output of the indexer when the scores are not stored: for every
+// query a threshold (-inf keeps every key), and per chunk of keys a run of
+// slots at a fixed place in the query's row of the candidate buffer.
+struct IdxCand {
+  const float* thr;     // [T]
+  int2* cand;           // [T, rs] (key, score bits), ascending keys within a chunk
+  int32_t* segc;        // [T, nseg] keys kept per chunk (may exceed the slots)
+  int32_t* err;         // bit 0: a NaN score; bit 1: a failed row
+  int64_t rs;
+  int nseg;
+  int expect;           // expected kept keys of a full row
+};
+
+template <int HG, bool CAND>
 __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const float* __restrict__ w, int T, int Hi,
-                                                               int64_t Nk, int64_t pos0, float* __restrict__ out) {
+                                                               int64_t Nk, int kstride, int chunk, int64_t pos0,
+                                                               float* __restrict__ out, IdxCand cd) {
   constexpr int kIdx2Qpw = idx2_qpw<HG>(), kIdx2Q = kIdx2Waves * kIdx2Qpw;
   __shared__ __attribute__((aligned(1024))) uint16_t Kt[2][64 * kIdxD];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int nchunk = (int)((Nk + kIdxChunk - 1) / kIdxChunk);
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nchunk = (int)((Nk + chunk - 1) / chunk);
   const int tq = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
   const int t0 = tq * kIdx2Q;
-  const int64_t c0 = (int64_t)ck * kIdxChunk, c1 = std::min(Nk, c0 + kIdxChunk);
-  const int64_t lim_max = pos0 + std::min(t0 + kIdx2Q - 1, T - 1);  // largest causal key of the queries
+  const int64_t c0 = (int64_t)ck * chunk, c1 = std::min(Nk, c0 + chunk);
+  // column c scores key c * kstride; the largest causal column of the queries
+  const int64_t lim_max = (pos0 + std::min(t0 + kIdx2Q - 1, T - 1)) / kstride;
   // A operands: query t0 + 4wv + j, head 32g + l32, dims 16s + 8hf .. +7
   bf16x8 qa[kIdx2Qpw][HG][4];
 #pragma unroll
@@ -179,6 +196,24 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
   for (int g = 0; g < HG; ++g)
 #pragma unroll
     for (int r = 0; r < 16; ++r) wr[g][r] = w[32 * g + 8 * (r / 4) + 4 * hf + (r % 4)];
+  // candidate mode: per query its threshold, last causal key of the chunk,
+  // slot run and running count
+  float thr[kIdx2Qpw];
+  int lim[kIdx2Qpw], nslot[kIdx2Qpw], found[kIdx2Qpw];
+  int2* run[kIdx2Qpw];
+  if constexpr (CAND) {
+#pragma unroll
+    for (int j = 0; j < kIdx2Qpw; ++j) {
+      const int t = t0 + kIdx2Qpw * wv + j;
+      const int64_t n = std::min(Nk, pos0 + t + 1);
+      const bool any = t < T && c0 < n;
+      thr[j] = any ? cd.thr[t] : 0.f;
+      lim[j] = any ? (int)(std::min(n, c1) - 1) : -1;
+      nslot[j] = any ? (int)idx_slots(n, ck, chunk, cd.expect) : 0;
+      run[j] = cd.cand + (any ? (int64_t)t * cd.rs + ck * idx_slots(n, 0, chunk, cd.expect) : 0);
+      found[j] = 0;
+    }
+  }
   drain_vmem();
 
   const int64_t s_end = std::min(c1, lim_max + 1);  // keys past every query's limit are only written
@@ -186,7 +221,7 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
   // one 1 KB copy per wave: rows 8wv .. 8wv+7 of the tile
   auto copy = [&](int tl, int buf) {
     const int r = 8 * wv + lane / 8, c = lane % 8;
-    const int64_t row = std::min(c0 + 64 * (int64_t)tl + r, Nk - 1);
+    const int64_t row = std::min(c0 + 64 * (int64_t)tl + r, Nk - 1) * kstride;
     const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[buf][0]) + (uint32_t)wv * 1024u);
     dma16(dst, k + row * kIdxD + 8 * (c ^ ((r >> 1) & 7)));
   };
@@ -232,19 +267,225 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
         if (g == HG - 1) {
           const float tot = sum + __shfl_xor(sum, 32);
           const int t = t0 + kIdx2Qpw * wv + j;
-          if (hf == 0 && t < T && key < c1) out[(int64_t)t * Nk + key] = key > pos0 + t ? -INFINITY : tot;
+          if constexpr (CAND) {
+            // lanes 0..31 hold keys s0+32hv .. +31 in order: a ballot ranks
+            // the kept ones, so every chunk's run is stored ascending.  A NaN
+            // score is kept (the exact select reports it).
+            const bool take = hf == 0 && (int)key <= lim[j] && !(tot < thr[j]);
+            const uint64_t m = __ballot(take);
+            if (take) {
+              const int pos = found[j] + (int)__builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u);
+              if (pos < nslot[j]) run[j][pos] = make_int2((int)key, __float_as_int(tot));
+            }
+            found[j] += __popcll(m);
+          } else {
+            if (hf == 0 && t < T && key < c1) out[(int64_t)t * Nk + key] = key * kstride > pos0 + t ? -INFINITY : tot;
+          }
           sum = 0.f;
         }
       }
     }
   }
-  // keys of the chunk beyond every query's causal limit
-  for (int64_t sidx = std::max(c0, s_end) + lane; sidx < c1; sidx += 64)
+  if constexpr (CAND) {
 #pragma unroll
     for (int j = 0; j < kIdx2Qpw; ++j) {
       const int t = t0 + kIdx2Qpw * wv + j;
-      if (t < T) out[(int64_t)t * Nk + sidx] = -INFINITY;
+      if (lane == 0 && nslot[j] > 0) cd.segc[(int64_t)t * cd.nseg + ck] = found[j];
     }
+  } else {
+    // keys of the chunk beyond every query's causal limit
+    for (int64_t sidx = std::max(c0, s_end) + lane; sidx < c1; sidx += 64)
+#pragma unroll
+      for (int j = 0; j < kIdx2Qpw; ++j) {
+        const int t = t0 + kIdx2Qpw * wv + j;
+        if (t < T) out[(int64_t)t * Nk + sidx] = -INFINITY;
+      }
+  }
+}
+
+// ---------------------------------------------------------------- indexer top-k
+// The top k of a query's scores without the score matrix.  A pass over every
+// 16th key (kIdxStride) gives each query a threshold: the m-th largest sampled
+// score, m = ceil(k/8), so about 16m ~ 2k keys of the full row reach it.  The
+// full pass keeps only the keys at or above the threshold; when at least k of
+// them are kept, the row's top k are exactly the top k of the kept keys (every
+// other key scores below the threshold, hence below the k-th kept one), and a
+// radix select over them ends the row.
+constexpr int kIdxStride = 16;
+constexpr int kIdxSampleChunk = 1024;  // sampled keys per workgroup
+constexpr int kIdxSelCap = 8192;       // kept keys a row may have in the exact select
+constexpr int kIdxSelNT = 256;
+constexpr int kIdxThrCap = 8192;       // sampled scores staged in LDS by the threshold kernel
+
+// Threshold per query: the m-th largest of its causal sampled scores, or
+// -inf (every key) when it has fewer than m.  A NaN sample sets bit 0 of err.
+__global__ __launch_bounds__(256) void k_idx_thresh(const float* __restrict__ smp, int64_t ns, int64_t pos0,
+                                                    int m, float* __restrict__ thr, int32_t* __restrict__ err) {
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t tmp[4];
+  __shared__ uint32_t shv[4];
+  __shared__ uint32_t keys[kIdxThrCap];
+  const int t = blockIdx.x;
+  const int64_t n = std::min(ns, (pos0 + t) / kIdxStride + 1);
+  if (n < m) {
+    if (threadIdx.x == 0) thr[t] = -INFINITY;
+    return;
+  }
+  const float* row = smp + (int64_t)t * ns;
+  bool nan_seen = false;
+  const bool staged = n <= kIdxThrCap;
+  // batches of 8 independent loads per thread keep the row's reads in flight
+  for (int64_t b = 0; b < n; b += 256 * 8) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = b + u * 256 + threadIdx.x;
+      v[u] = i < n ? row[i] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int64_t i = b + u * 256 + threadIdx.x;
+      if (i < n) {
+        nan_seen |= is_nan(v[u]);
+        if (staged) keys[i] = order_key(v[u]);
+      }
+    }
+  }
+  __syncthreads();
+  if (nan_seen && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
+  uint32_t kth;
+  int64_t need;
+  if (staged)
+    radix_kth<256>([&](int64_t i) { return keys[i]; }, 0, n, m, hist, tmp, shv, kth, need);
+  else
+    radix_kth<256>([&](int64_t i) { return order_key(row[i]); }, 0, n, m, hist, tmp, shv, kth, need);
+  // back from the order key to the float (the k-th key is never a NaN's
+  // unless the row holds NaNs, which err reports)
+  if (threadIdx.x == 0) thr[t] = __uint_as_float((kth & 0x80000000u) ? (kth ^ 0x80000000u) : ~kth);
+}
+
+// Exact top k of one query over its kept keys.  The chunks' runs are copied
+// into LDS in chunk order, so the kept keys lie ascending; the k-th largest
+// order key is found by radix select and one pass emits, ascending, every key
+// above it and the lowest-index keys equal to it.  A row whose runs overflowed
+// or that kept fewer than k keys gets cnt = -1, idx all -1 and bit 1 of err.
+__global__ __launch_bounds__(kIdxSelNT) void k_idx_select(IdxCand cd, int64_t Nk, int64_t pos0, int chunk, int k,
+                                                          int kmax, int32_t* __restrict__ idx,
+                                                          int32_t* __restrict__ cnt) {
+  constexpr int NT = kIdxSelNT;
+  __shared__ uint32_t sk[kIdxSelCap];
+  __shared__ int32_t si[kIdxSelCap];
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t tmp[NT / 64];
+  __shared__ uint32_t shv[4];
+  __shared__ int pre[NT + 1];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int64_t n = std::min(Nk, pos0 + t + 1);
+  const int64_t kr = std::min<int64_t>(k, n);
+  int32_t* out = idx + (int64_t)t * kmax;
+  if (kr == n) {  // the row keeps every causal key
+    for (int64_t j = tid; j < kmax; j += NT) out[j] = j < n ? (int32_t)j : -1;
+    if (tid == 0) cnt[t] = (int32_t)n;
+    return;
+  }
+  const int nch = (int)((n + chunk - 1) / chunk);
+  const int64_t run = idx_slots(n, 0, chunk, cd.expect);
+  const int2* src = cd.cand + (int64_t)t * cd.rs;
+  int total = 0;
+  bool bad = false, nan_seen = false;
+  // chunks in groups of NT: thread c reads chunk c's count, a scan places the
+  // runs, and every thread copies kept keys of any run (8 loads in flight)
+  for (int g0 = 0; g0 < nch && !bad; g0 += NT) {
+    const int c = g0 + tid;
+    const int fc = c < nch ? cd.segc[(int64_t)t * cd.nseg + c] : 0;
+    const bool over = c < nch && fc > idx_slots(n, c, chunk, cd.expect);
+    uint32_t gtot;
+    const uint32_t before = block_excl_scan<NT>((uint32_t)fc, tmp, gtot);
+    pre[tid] = (int)before;
+    if (tid == 0) pre[NT] = (int)gtot;
+    if (__syncthreads_or(over) || total + (int64_t)gtot > kIdxSelCap) {
+      bad = true;
+      break;
+    }
+    const int ng = min(NT, nch - g0);
+    for (int f0 = 0; f0 < (int)gtot; f0 += NT * 8) {
+      int2 e[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = f0 + u * NT + tid;
+        e[u] = make_int2(0, 0);
+        if (f < (int)gtot) {
+          int lo = 0, hi = ng - 1;  // the run holding flat position f: last lo with pre[lo] <= f
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (pre[mid] <= f) lo = mid;
+            else hi = mid - 1;
+          }
+          e[u] = src[(int64_t)(g0 + lo) * run + (f - pre[lo])];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int f = f0 + u * NT + tid;
+        if (f < (int)gtot) {
+          const float v = __int_as_float(e[u].y);
+          nan_seen |= is_nan(v);
+          sk[total + f] = order_key(v);
+          si[total + f] = e[u].x;
+        }
+      }
+    }
+    total += (int)gtot;
+    __syncthreads();  // pre[] is rewritten by the next group
+  }
+  if (__syncthreads_or(nan_seen) && tid == 0 && cd.err != nullptr)
+    atomicOr(reinterpret_cast<unsigned int*>(cd.err), 1u);
+  if (bad || total < kr) {
+    for (int64_t j = tid; j < kmax; j += NT) out[j] = -1;
+    if (tid == 0) {
+      cnt[t] = -1;
+      if (cd.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(cd.err), 2u);
+    }
+    return;
+  }
+  __syncthreads();
+  uint32_t kth;
+  int64_t need;
+  radix_kth<NT>([&](int64_t i) { return sk[i]; }, 0, total, kr, hist, tmp, shv, kth, need);
+  // emission in LDS (= key) order, tiles of NT*4 kept keys
+  uint32_t gt_run = 0u, eq_run = 0u;
+  for (int b0 = 0; b0 < total; b0 += NT * 4) {
+    const int i0 = b0 + tid * 4;
+    uint32_t f[4];
+    uint32_t c_gt = 0u, c_eq = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e;
+      const uint32_t kk = i < total ? sk[i] : 0u;
+      f[e] = i < total ? (kk > kth ? 1u : (kk == kth ? 2u : 0u)) : 0u;
+      c_gt += f[e] == 1u;
+      c_eq += f[e] == 2u;
+    }
+    uint32_t tot;
+    const uint32_t ex = block_excl_scan<NT>((c_eq << 16) | c_gt, tmp, tot);
+    uint32_t g_before = gt_run + (ex & 0xffffu);
+    uint32_t e_before = eq_run + (ex >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = i0 + e;
+      if (f[e] == 1u) {
+        out[g_before + (uint32_t)min((int64_t)e_before, need)] = si[i];
+        ++g_before;
+      } else if (f[e] == 2u) {
+        if ((int64_t)e_before < need) out[g_before + e_before] = si[i];
+        ++e_before;
+      }
+    }
+    gt_run += tot & 0xffffu;
+    eq_run += tot >> 16;
+  }
+  for (int64_t j = kr + tid; j < kmax; j += NT) out[j] = -1;
+  if (tid == 0) cnt[t] = (int32_t)kr;
 }
 
 // ================================================================ vertical-slash estimate
@@ -430,13 +671,15 @@ hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, 
   if (hi == 32) {
     constexpr int nq = kIdx2Waves * idx2_qpw<1>();
     const dim3 grid2((unsigned)(((T + nq - 1) / nq) * nchunk));
-    hipLaunchKernelGGL((k_indexer2<1>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, pos0, out);
+    hipLaunchKernelGGL((k_indexer2<1, false>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, 1, kIdxChunk,
+                       pos0, out, IdxCand{});
     return hipGetLastError();
   }
   if (hi == 64) {
     constexpr int nq = kIdx2Waves * idx2_qpw<2>();
     const dim3 grid2((unsigned)(((T + nq - 1) / nq) * nchunk));
-    hipLaunchKernelGGL((k_indexer2<2>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, pos0, out);
+    hipLaunchKernelGGL((k_indexer2<2, false>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, 1, kIdxChunk,
+                       pos0, out, IdxCand{});
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(((T + 31) / 32) * nchunk));
@@ -448,6 +691,72 @@ hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, 
     case 8: hipLaunchKernelGGL((k_indexer<8>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+namespace {
+struct IdxTopkLayout {
+  int64_t ns, nseg, rs;
+  int m, expect;
+  size_t o_thr, o_segc, o_cand, bytes;
+};
+IdxTopkLayout idx_topk_layout(int T, int64_t nk, int64_t pos0, int k) {
+  IdxTopkLayout L;
+  L.ns = (nk + kIdxStride - 1) / kIdxStride;
+  L.m = (k + 7) / 8;
+  L.expect = L.m * kIdxStride;
+  const int64_t nmax = std::min(nk, pos0 + T);
+  L.nseg = (nmax + kIdxChunk - 1) / kIdxChunk;
+  L.rs = (2 * (int64_t)L.expect + 128 * L.nseg + 63) / 64 * 64;
+  L.o_thr = a256((size_t)T * L.ns * 4);
+  L.o_segc = L.o_thr + a256((size_t)T * 4);
+  L.o_cand = L.o_segc + a256((size_t)(T * L.nseg) * 4);
+  L.bytes = L.o_cand + a256((size_t)(T * L.rs) * 8);
+  return L;
+}
+}  // namespace
+
+size_t indexer_topk_workspace_bytes(int T, int64_t nk, int64_t pos0, int k) {
+  return idx_topk_layout(T, nk, pos0, k).bytes;
+}
+
+hipError_t launch_indexer_topk(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
+                               int64_t pos0, int kk, int kmax, int32_t* idx, int32_t* cnt, int32_t* err, void* ws,
+                               hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  if (hi != 32 && hi != 64) return hipErrorInvalidValue;
+  const IdxTopkLayout L = idx_topk_layout(T, nk, pos0, kk);
+  char* base = static_cast<char*>(ws);
+  float* smp = reinterpret_cast<float*>(base);
+  IdxCand cd;
+  float* thr = reinterpret_cast<float*>(base + L.o_thr);
+  cd.thr = thr;
+  cd.segc = reinterpret_cast<int32_t*>(base + L.o_segc);
+  cd.cand = reinterpret_cast<int2*>(base + L.o_cand);
+  cd.err = err;
+  cd.rs = L.rs;
+  cd.nseg = (int)L.nseg;
+  cd.expect = L.expect;
+  const int nq = kIdx2Waves * (hi == 32 ? idx2_qpw<1>() : idx2_qpw<2>());
+  const unsigned nqt = (unsigned)((T + nq - 1) / nq);
+  const dim3 g_smp(nqt * (unsigned)((L.ns + kIdxSampleChunk - 1) / kIdxSampleChunk));
+  const dim3 g_full(nqt * (unsigned)((nk + kIdxChunk - 1) / kIdxChunk));
+  const dim3 blk(64 * kIdx2Waves);
+  if (hi == 32)
+    hipLaunchKernelGGL((k_indexer2<1, false>), g_smp, blk, 0, stream, q, k, w, T, hi, L.ns, kIdxStride,
+                       kIdxSampleChunk, pos0, smp, IdxCand{});
+  else
+    hipLaunchKernelGGL((k_indexer2<2, false>), g_smp, blk, 0, stream, q, k, w, T, hi, L.ns, kIdxStride,
+                       kIdxSampleChunk, pos0, smp, IdxCand{});
+  hipLaunchKernelGGL(k_idx_thresh, dim3((unsigned)T), dim3(256), 0, stream, smp, L.ns, pos0, L.m, thr, err);
+  if (hi == 32)
+    hipLaunchKernelGGL((k_indexer2<1, true>), g_full, blk, 0, stream, q, k, w, T, hi, nk, 1, kIdxChunk, pos0,
+                       nullptr, cd);
+  else
+    hipLaunchKernelGGL((k_indexer2<2, true>), g_full, blk, 0, stream, q, k, w, T, hi, nk, 1, kIdxChunk, pos0,
+                       nullptr, cd);
+  hipLaunchKernelGGL(k_idx_select, dim3((unsigned)T), dim3(kIdxSelNT), 0, stream, cd, nk, pos0, kIdxChunk, kk, kmax,
+                     idx, cnt);
   return hipGetLastError();
 }
 

@@ -68,6 +68,23 @@ hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, i
                                 hipStream_t stream);
 hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
                           int64_t pos0, float* out, hipStream_t stream);
+// Candidate slots of chunk c (keys c*chunk ..) of an indexer row with n causal
+// keys when `expect` kept keys are expected over the row: twice the chunk's
+// share plus 64, rounded up to a multiple of 64, at most the chunk's keys.
+// Every chunk of a row but the last is full, so chunk c's run starts at
+// c * idx_slots(n, 0, ...).  32-bit arithmetic: n < 2^31, chunk <= 8192 and
+// expect <= 4096 keep 2 * expect * len + n below 2^32.
+__host__ __device__ inline int64_t idx_slots(int64_t n, int64_t c, int64_t chunk, int64_t expect) {
+  const uint32_t nn = (uint32_t)n;
+  const uint32_t len = (uint32_t)(n - c * chunk < chunk ? n - c * chunk : chunk);
+  const uint32_t share = (2u * (uint32_t)expect * len + nn - 1u) / nn;
+  const uint32_t s = (share + 63u) / 64u * 64u + 64u;
+  return s < len ? s : len;
+}
+size_t indexer_topk_workspace_bytes(int T, int64_t nk, int64_t pos0, int k);
+hipError_t launch_indexer_topk(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
+                               int64_t pos0, int kk, int kmax, int32_t* idx, int32_t* cnt, int32_t* err, void* ws,
+                               hipStream_t stream);
 size_t vs_workspace_bytes(int64_t rows, int64_t seq);
 hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv,
                               const HeadList& hl, int64_t seq, int head_dim, int last_q, float scale, float* a_v,

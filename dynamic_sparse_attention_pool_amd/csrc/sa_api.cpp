@@ -198,6 +198,7 @@ size_t sa_args_size(int which) {
     case 6: return sizeof(sa_select_mass_args);
     case 7: return sizeof(sa_kmeans_args);
     case 8: return sizeof(sa_estimate_topk_args);
+    case 9: return sizeof(sa_indexer_topk_args);
     default: return 0;
   }
 }
@@ -725,6 +726,47 @@ int sa_cluster_pack(const sa_cluster_pack_args* a, void* workspace, size_t works
                                           a->v, a->k_packed, a->v_packed, (int)a->head_dim, eb, a->err_flag, workspace,
                                           as_stream(stream)),
                   "sa_cluster_pack");
+}
+
+// ---------------------------------------------------------------- indexer top-k
+static int check_indexer_topk(const sa_indexer_topk_args* a) {
+  if (!a) return fail(SA_ERR_NULL, "sa_indexer_topk: args is NULL");
+  if (a->seq_q < 0 || a->seq_k <= 0) return fail(SA_ERR_SHAPE, "sa_indexer_topk: seq_q must be >= 0 and seq_k > 0");
+  if (a->seq_q == 0) return ok();
+  if (!a->q || !a->k_ptr || !a->weights || !a->idx || !a->cnt)
+    return fail(SA_ERR_NULL, "sa_indexer_topk: q, k, weights, idx and cnt are required");
+  if (!aligned16(a->q) || !aligned16(a->k_ptr)) return fail(SA_ERR_ALIGN, "sa_indexer_topk: q and k must be 16-byte aligned");
+  if (a->heads != 32 && a->heads != 64) return fail(SA_ERR_UNSUPPORTED, "sa_indexer_topk: heads must be 32 or 64");
+  if (a->head_dim != 64) return fail(SA_ERR_UNSUPPORTED, "sa_indexer_topk: head_dim must be 64");
+  if (a->q_pos0 < 0) return fail(SA_ERR_VALUE, "sa_indexer_topk: q_pos0 must be >= 0");
+  if (a->seq_q > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_indexer_topk: seq_q too large");
+  if (a->seq_k > ((int64_t)1 << 31) - 64) return fail(SA_ERR_SHAPE, "sa_indexer_topk: seq_k too large");
+  if (a->k < 1 || a->k > 2048) return fail(SA_ERR_VALUE, "sa_indexer_topk: k must lie in [1, 2048]");
+  const int64_t nmax = a->seq_k < a->q_pos0 + a->seq_q ? a->seq_k : a->q_pos0 + a->seq_q;
+  const int64_t need = a->k < nmax ? a->k : nmax;
+  if (a->kmax < need) return fail(SA_ERR_SHAPE, "sa_indexer_topk: kmax %d is below min(k, longest row) = %lld", a->kmax, (long long)need);
+  return ok();
+}
+
+int sa_indexer_topk_workspace_bytes(const sa_indexer_topk_args* a, size_t* bytes) {
+  if (!bytes) return fail(SA_ERR_NULL, "sa_indexer_topk_workspace_bytes: bytes is NULL");
+  const int rc = check_indexer_topk(a);
+  if (rc) return rc;
+  *bytes = a->seq_q == 0 ? 0 : sa::indexer_topk_workspace_bytes((int)a->seq_q, a->seq_k, a->q_pos0, a->k);
+  return ok();
+}
+
+int sa_indexer_topk(const sa_indexer_topk_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  const int rc = check_indexer_topk(a);
+  if (rc) return rc;
+  if (a->seq_q == 0) return ok();
+  const size_t ws = sa::indexer_topk_workspace_bytes((int)a->seq_q, a->seq_k, a->q_pos0, a->k);
+  if (!workspace || workspace_bytes < ws) return fail(SA_ERR_WORKSPACE, "sa_indexer_topk: workspace of %zu bytes required", ws);
+  if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "sa_indexer_topk: workspace must be 16-byte aligned");
+  return launched(sa::launch_indexer_topk(static_cast<const uint16_t*>(a->q), static_cast<const uint16_t*>(a->k_ptr),
+                                          a->weights, (int)a->seq_q, a->heads, a->seq_k, a->q_pos0, a->k, a->kmax,
+                                          a->idx, a->cnt, a->err_flag, workspace, as_stream(stream)),
+                  "sa_indexer_topk");
 }
 
 }  // extern "C"

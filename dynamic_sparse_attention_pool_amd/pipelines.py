@@ -9,8 +9,8 @@ from __future__ import annotations
 import math
 
 from . import (BLOCK_MEANPOOL, CENTROID, INDEXER, VSLASH, sa_block_sparse_fwd, sa_cluster_pack, sa_estimate,
-               sa_estimate_topk, sa_estimate_topk_centroid, sa_gather_decode, sa_select_mass, sa_select_topk,
-               sa_vs_build)
+               sa_estimate_topk, sa_estimate_topk_centroid, sa_gather_decode, sa_indexer_topk, sa_select_mass,
+               sa_select_topk, sa_vs_build)
 
 
 def _t():
@@ -288,7 +288,7 @@ class IndexerPrefill:
     attend through the same index buffer."""
 
     def __init__(self, qi, ki, w, pos0: int, layers, *, k_sel: int, full_layers=(0,), out_dtype=None,
-                 scale=None):
+                 scale=None, fused: bool = False):
         torch = _t()
         T = qi.shape[0]
         N = ki.shape[0]
@@ -297,18 +297,38 @@ class IndexerPrefill:
         self.layers = layers                      # list of (q [T,Hq,d], k [Hkv,N,d], v)
         self.full = set(full_layers)
         self.k_sel = k_sel
+        self.fused = fused
         d = layers[0][0].shape[-1]
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
-        self.scores = torch.empty((T, N), dtype=torch.float32, device=dev)
+        # the score matrix only for the two-call index (or a fused call's fallback)
+        self.scores = None if fused else torch.empty((T, N), dtype=torch.float32, device=dev)
         self.idx = torch.empty((T, k_sel), dtype=torch.int32, device=dev)   # the index cache
         self.cnt = torch.empty(T, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
         self.outs = [torch.empty(L[0].shape, dtype=out_dtype or torch.float32, device=dev) for L in layers]
         self.ws = None
+        self.ws_index = None
 
-    def index(self):
+    def index_two_call(self):
+        """Indexer scores into [T, N], then the causal top-k of every row."""
+        if self.scores is None:
+            self.scores = _t().empty((self.T, self.N), dtype=_t().float32, device=self.qi.device)
         sa_estimate(INDEXER, self.qi, self.ki, self.scores, weights=self.w, q_pos0=self.pos0)
         sa_select_topk(self.scores, self.idx, self.cnt, k=self.k_sel, causal=True, causal_period=self.T,
                        causal_offset=self.pos0)
+
+    def index(self, check: bool = False):
+        """The index of the full layer.  Fused: one call without the score
+        matrix; with check=True the host reads the error flag (a device sync)
+        and redoes the chunk with two calls when a row's threshold failed."""
+        if not self.fused:
+            self.index_two_call()
+            return
+        self.ws_index = sa_indexer_topk(self.qi, self.ki, self.idx, self.cnt, weights=self.w, q_pos0=self.pos0,
+                                        k=self.k_sel, err_flag=self.err, workspace=self.ws_index)
+        if check and int(self.err.item()) & 2:
+            self.err.zero_()
+            self.index_two_call()
 
     def attend(self, layer: int):
         q, k, v = self.layers[layer]

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 6
+#define SA_ABI_VERSION 7
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -505,6 +505,54 @@ int sa_kmeans_workspace_bytes(const sa_kmeans_args* args, size_t* bytes);
 int sa_kmeans(const sa_kmeans_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * sa_indexer_topk — indexer scores and the per-query top k in one call,
+ * without the score matrix.
+ *
+ * IndexCache article, §长文本的算力困境: the indexer scores every causal key
+ * for each query and its top-k keys are kept.  The result equals
+ * sa_estimate(INDEXER) followed by sa_select_topk on its rows with k, no
+ * forced members, causal = 1, causal_period = T and causal_offset = q_pos0
+ * (row t keeps min(k, n_t) of its n_t = min(Nk, q_pos0 + t + 1) keys, higher
+ * score first, lower index on ties, ascending, padded with -1).
+ *
+ * q [T,Hi,64] BF16, k [Nk,64] BF16, weights [Hi] float, as in
+ * sa_estimate(INDEXER); Hi must be 32 or 64.  1 <= k <= 2048,
+ * kmax >= min(k, Nk); idx [T,kmax] int32, cnt [T] int32.
+ *
+ * Method: every 16th key is scored first; a query's threshold is the
+ * ceil(k/8)-th largest of its sampled scores (about 2k of its keys reach it).
+ * The full pass keeps only keys at or above the threshold, in per-chunk runs
+ * of the workspace, and an exact radix select over them ends the row.  When
+ * fewer than k keys reach the threshold, or a run overflows (neither happens
+ * for scores without structure at the sampling period; see the method's
+ * notes), the row gets cnt = -1 and idx all -1, and bit 1 (value 2) of
+ * err_flag is set: the caller recomputes such rows with the two-call path.
+ * err_flag bit 0 (value 1): a NaN score (the output is then unspecified).
+ * err_flag is optional and never cleared by the library.
+ *
+ * Workspace: sa_indexer_topk_workspace_bytes (about T * (Nk/16 + 4k) * 4
+ * bytes plus small tables).  seq_q = 0 launches nothing.
+ * ====================================================================== */
+typedef struct sa_indexer_topk_args {
+  int64_t seq_q;          /* T */
+  int64_t seq_k;          /* Nk */
+  int64_t q_pos0;         /* absolute position of query 0, >= 0 */
+  int32_t heads;          /* Hi: 32 or 64 */
+  int32_t head_dim;       /* 64 */
+  int32_t k;
+  int32_t kmax;
+  const void* q;
+  const void* k_ptr;
+  const float* weights;
+  int32_t* idx;
+  int32_t* cnt;
+  int32_t* err_flag;
+} sa_indexer_topk_args;
+
+int sa_indexer_topk_workspace_bytes(const sa_indexer_topk_args* args, size_t* bytes);
+int sa_indexer_topk(const sa_indexer_topk_args* args, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ======================================================================
  * Library information.
  * ====================================================================== */
 /* Message of the last failing call on this thread ("" if none). */
@@ -513,7 +561,7 @@ const char* sa_last_error(void);
 int sa_version(void);
 /* sizeof of the argument structs as compiled, so bindings can check layout:
  * which = 0 estimate, 1 select, 2 vs_build, 3 fwd, 4 gather, 5 cluster_pack,
- * 6 select_mass, 7 kmeans, 8 estimate_topk. */
+ * 6 select_mass, 7 kmeans, 8 estimate_topk, 9 indexer_topk. */
 size_t sa_args_size(int which);
 
 #ifdef __cplusplus

@@ -26,7 +26,8 @@ def lib():
 def test_header_declares_the_four_entry_points_and_helpers():
     names = declared_functions()
     for n in ["sa_estimate", "sa_select_topk", "sa_block_sparse_fwd", "sa_gather_decode", "sa_vs_build",
-              "sa_cluster_pack", "sa_select_mass", "sa_kmeans", "sa_estimate_topk", "sa_last_error", "sa_version",
+              "sa_cluster_pack", "sa_select_mass", "sa_kmeans", "sa_estimate_topk", "sa_indexer_topk", "sa_last_error",
+              "sa_version",
               "sa_args_size"]:
         assert n in names
 
@@ -230,6 +231,42 @@ def test_estimate_topk_argument_errors(lib):
     a.kind = F.SA_EST_BLOCK_MEANPOOL
     a.n_local = -1
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 8
+
+
+def test_indexer_topk_argument_errors(lib):
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    a = F.IndexerTopkArgs()
+    n = C.c_size_t(0)
+    assert lib.sa_indexer_topk_workspace_bytes(None, C.byref(n)) == 1
+    a.seq_k = 131072
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0 and n.value == 0   # no queries
+    assert lib.sa_indexer_topk(C.byref(a), None, 0, None) == 0
+    a.seq_q, a.q_pos0, a.heads, a.head_dim, a.k, a.kmax = 4096, 126976, 64, 64, 2048, 2048
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 1                    # NULL pointers
+    a.q = a.k_ptr = a.weights = a.idx = a.cnt = 256
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0
+    # sampled scores [T, N/16], thresholds, run counts, and runs of 2k + 128 per chunk
+    assert n.value >= 4096 * (8192 + 1 + 16 + 2 * 10240) * 4
+    assert lib.sa_indexer_topk(C.byref(a), None, 0, None) == 5                                 # no workspace
+    assert lib.sa_indexer_topk(C.byref(a), C.c_void_p(4096), n.value - 1, None) == 5
+    a.heads = 16
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 6
+    a.heads, a.head_dim = 32, 128
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 6
+    a.head_dim, a.k = 64, 4096
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 8
+    a.k = 0
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 8
+    a.k, a.kmax = 2048, 2047
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 2
+    a.seq_k, a.q_pos0, a.seq_q = 1000, 0, 1000                                                 # rows of 1..1000 keys
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0
+    a.kmax = 999
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 2
+    a.kmax, a.q_pos0 = 1000, -1
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 8
+    a.q_pos0, a.q = 0, 258
+    assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 4
 
 
 def test_estimate_and_gather_argument_errors(lib):
