@@ -304,33 +304,41 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
 }
 
 // ---------------------------------------------------------------- indexer top-k
-// The top k of a query's scores without the score matrix.  A pass over every
-// 16th key (kIdxStride) gives each query a threshold: the m-th largest sampled
-// score, m = ceil(k/8), so about 16m ~ 2k keys of the full row reach it.  The
-// full pass keeps only the keys at or above the threshold; when at least k of
-// them are kept, the row's top k are exactly the top k of the kept keys (every
-// other key scores below the threshold, hence below the k-th kept one), and a
-// radix select over them ends the row.
+// The top k of a query's scores without the score matrix.  A row of at most
+// kIdxSelCap keys keeps all of them.  For a longer row, a pass over every 16th
+// key (kIdxStride) gives the query a threshold, the kIdxRank-th largest
+// sampled score, which about 16 * kIdxRank = 4096 keys of the full row reach
+// (relative spread ~1/sqrt(kIdxRank), so k <= 2048 lies 8 spreads below).
+// The full pass keeps only the keys at or above the threshold; when at least k
+// of them are kept, the row's top k are exactly the top k of the kept keys
+// (every other key scores below the threshold, hence below the k-th kept
+// one), and a radix select over them ends the row.
 constexpr int kIdxStride = 16;
+constexpr int kIdxRank = 256;
+constexpr int kIdxExpect = kIdxStride * kIdxRank;  // kept keys expected in a long row
 constexpr int kIdxSampleChunk = 1024;  // sampled keys per workgroup
 constexpr int kIdxSelCap = 8192;       // kept keys a row may have in the exact select
 constexpr int kIdxSelNT = 256;
 constexpr int kIdxThrCap = 8192;       // sampled scores staged in LDS by the threshold kernel
 
-// Threshold per query: the m-th largest of its causal sampled scores, or
-// -inf (every key) when it has fewer than m.  A NaN sample sets bit 0 of err.
-__global__ __launch_bounds__(256) void k_idx_thresh(const float* __restrict__ smp, int64_t ns, int64_t pos0,
-                                                    int m, float* __restrict__ thr, int32_t* __restrict__ err) {
+// Threshold per query: -inf (every key) for a row of at most kIdxSelCap keys,
+// else the kIdxRank-th largest of its causal sampled scores.  A NaN sample
+// sets bit 0 of err.
+__global__ __launch_bounds__(256) void k_idx_thresh(const float* __restrict__ smp, int64_t ns, int64_t Nk,
+                                                    int64_t pos0, float* __restrict__ thr,
+                                                    int32_t* __restrict__ err) {
   __shared__ uint32_t hist[256];
   __shared__ uint32_t tmp[4];
   __shared__ uint32_t shv[4];
   __shared__ uint32_t keys[kIdxThrCap];
   const int t = blockIdx.x;
-  const int64_t n = std::min(ns, (pos0 + t) / kIdxStride + 1);
-  if (n < m) {
+  if (std::min(Nk, pos0 + t + 1) <= kIdxSelCap) {
     if (threadIdx.x == 0) thr[t] = -INFINITY;
     return;
   }
+  // causal sampled keys: 16c <= pos0 + t; more than kIdxSelCap / 16 >= kIdxRank of them
+  const int64_t n = std::min(ns, (pos0 + t) / kIdxStride + 1);
+  const int m = kIdxRank;
   const float* row = smp + (int64_t)t * ns;
   bool nan_seen = false;
   const bool staged = n <= kIdxThrCap;
@@ -697,18 +705,18 @@ hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, 
 namespace {
 struct IdxTopkLayout {
   int64_t ns, nseg, rs;
-  int m, expect;
+  int expect;
   size_t o_thr, o_segc, o_cand, bytes;
 };
 IdxTopkLayout idx_topk_layout(int T, int64_t nk, int64_t pos0, int k) {
   IdxTopkLayout L;
   L.ns = (nk + kIdxStride - 1) / kIdxStride;
-  L.m = (k + 7) / 8;
-  L.expect = L.m * kIdxStride;
+  L.expect = kIdxExpect;
   const int64_t nmax = std::min(nk, pos0 + T);
   L.nseg = (nmax + kIdxChunk - 1) / kIdxChunk;
   L.rs = (2 * (int64_t)L.expect + 128 * L.nseg + 63) / 64 * 64;
-  L.o_thr = a256((size_t)T * L.ns * 4);
+  (void)k;  // the layout does not depend on k (at most 2048)
+  L.o_thr = nmax > kIdxSelCap ? a256((size_t)T * L.ns * 4) : 0;  // sampled scores only for long rows
   L.o_segc = L.o_thr + a256((size_t)T * 4);
   L.o_cand = L.o_segc + a256((size_t)(T * L.nseg) * 4);
   L.bytes = L.o_cand + a256((size_t)(T * L.rs) * 8);
@@ -742,13 +750,15 @@ hipError_t launch_indexer_topk(const uint16_t* q, const uint16_t* k, const float
   const dim3 g_smp(nqt * (unsigned)((L.ns + kIdxSampleChunk - 1) / kIdxSampleChunk));
   const dim3 g_full(nqt * (unsigned)((nk + kIdxChunk - 1) / kIdxChunk));
   const dim3 blk(64 * kIdx2Waves);
-  if (hi == 32)
-    hipLaunchKernelGGL((k_indexer2<1, false>), g_smp, blk, 0, stream, q, k, w, T, hi, L.ns, kIdxStride,
-                       kIdxSampleChunk, pos0, smp, IdxCand{});
-  else
-    hipLaunchKernelGGL((k_indexer2<2, false>), g_smp, blk, 0, stream, q, k, w, T, hi, L.ns, kIdxStride,
-                       kIdxSampleChunk, pos0, smp, IdxCand{});
-  hipLaunchKernelGGL(k_idx_thresh, dim3((unsigned)T), dim3(256), 0, stream, smp, L.ns, pos0, L.m, thr, err);
+  if (std::min(nk, pos0 + T) > kIdxSelCap) {  // some row is long enough to need the sampled threshold
+    if (hi == 32)
+      hipLaunchKernelGGL((k_indexer2<1, false>), g_smp, blk, 0, stream, q, k, w, T, hi, L.ns, kIdxStride,
+                         kIdxSampleChunk, pos0, smp, IdxCand{});
+    else
+      hipLaunchKernelGGL((k_indexer2<2, false>), g_smp, blk, 0, stream, q, k, w, T, hi, L.ns, kIdxStride,
+                         kIdxSampleChunk, pos0, smp, IdxCand{});
+  }
+  hipLaunchKernelGGL(k_idx_thresh, dim3((unsigned)T), dim3(256), 0, stream, smp, L.ns, nk, pos0, thr, err);
   if (hi == 32)
     hipLaunchKernelGGL((k_indexer2<1, true>), g_full, blk, 0, stream, q, k, w, T, hi, nk, 1, kIdxChunk, pos0,
                        nullptr, cd);

@@ -519,19 +519,23 @@ int sa_kmeans(const sa_kmeans_args* args, void* workspace, size_t workspace_byte
  * sa_estimate(INDEXER); Hi must be 32 or 64.  1 <= k <= 2048,
  * kmax >= min(k, Nk); idx [T,kmax] int32, cnt [T] int32.
  *
- * Method: every 16th key is scored first; a query's threshold is the
- * ceil(k/8)-th largest of its sampled scores (about 2k of its keys reach it).
+ * Method: a row of at most 8192 keys keeps all of them.  For a longer row
+ * every 16th key is scored first and the query's threshold is the 256th
+ * largest of its causal sampled scores (about 4096 of its keys reach it).
  * The full pass keeps only keys at or above the threshold, in per-chunk runs
- * of the workspace, and an exact radix select over them ends the row.  When
- * fewer than k keys reach the threshold, or a run overflows (neither happens
- * for scores without structure at the sampling period; see the method's
- * notes), the row gets cnt = -1 and idx all -1, and bit 1 (value 2) of
- * err_flag is set: the caller recomputes such rows with the two-call path.
- * err_flag bit 0 (value 1): a NaN score (the output is then unspecified).
- * err_flag is optional and never cleared by the library.
+ * of the workspace, and an exact radix select over the kept keys ends the
+ * row.  When fewer than k keys reach the threshold, or a run overflows
+ * (neither happens for scores without structure at the sampling period: k
+ * lies 8 relative spreads below the expected count, the cap 16 above), the
+ * row gets cnt = -1 and idx all -1, and bit 1 (value 2) of err_flag is set:
+ * the caller recomputes such rows with the two-call path.
+ * err_flag bit 0 (value 1): a NaN among the scores the method ranks (the
+ * output is then unspecified).  err_flag is optional and never cleared by
+ * the library.
  *
- * Workspace: sa_indexer_topk_workspace_bytes (about T * (Nk/16 + 4k) * 4
- * bytes plus small tables).  seq_q = 0 launches nothing.
+ * Workspace: sa_indexer_topk_workspace_bytes (T * Nk/16 * 4 bytes of sampled
+ * scores when some row exceeds 8192 keys, plus T * (8192 + 128 * Nk/8192) * 8
+ * bytes of runs).  seq_q = 0 launches nothing.
  * ====================================================================== */
 typedef struct sa_indexer_topk_args {
   int64_t seq_q;          /* T */

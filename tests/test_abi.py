@@ -261,6 +261,8 @@ def test_indexer_topk_argument_errors(lib):
     assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 2
     a.seq_k, a.q_pos0, a.seq_q = 1000, 0, 1000                                                 # rows of 1..1000 keys
     assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 0
+    # no sampled scores (every row keeps all its keys): thresholds, run counts, runs of 8192 + 128 pairs
+    assert n.value == 4096 + 4096 + 1000 * (8192 + 128) * 8
     a.kmax = 999
     assert lib.sa_indexer_topk_workspace_bytes(C.byref(a), C.byref(n)) == 2
     a.kmax, a.q_pos0 = 1000, -1

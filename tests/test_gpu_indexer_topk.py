@@ -1,9 +1,10 @@
 """GPU parity of the fused indexer top-k (sa_indexer_topk) against the CPU
 oracle, and against the two-call path (sa_estimate INDEXER + sa_select_topk).
 
-The fused call scores every 16th key first, takes per query the ceil(k/8)-th
-largest sampled score as a threshold, keeps the keys at or above it in
-per-chunk runs and selects exactly among them.  On inputs whose scores are
+The fused call keeps every key of a row of at most 8192 keys; for a longer
+row it scores every 16th key first, takes the 256th largest causal sampled
+score as a threshold, keeps the keys at or above it in per-chunk runs and
+selects exactly among them.  On inputs whose scores are
 exact in fp32 (small integers, weights m/64) the GPU scores equal the oracle's,
 so the outcome of that bracket is known in advance: `predict_failed` applies
 the same rule to the oracle's scores, and rows must fail exactly where it says
@@ -19,7 +20,8 @@ from gpu_helpers import dev_bf16, dev_f32, host, tie_tolerant_valid, torch
 
 pytestmark = pytest.mark.gpu
 
-STRIDE, CHUNK, SEL_CAP = 16, 8192, 8192
+STRIDE, CHUNK, SEL_CAP, RANK = 16, 8192, 8192, 256
+EXPECT = STRIDE * RANK
 
 
 @pytest.fixture(scope="module")
@@ -54,28 +56,26 @@ def run_two_call(sa, qi, ki, w, pos0, k, kmax=None):
     return host(idx), host(cnt)
 
 
-def slots(n, c, k):
+def slots(n, c):
     """Slots of chunk c of a row with n causal keys (twice its share of the
-    16*ceil(k/8) expected kept keys, plus 64, rounded up to 64, at most the
-    chunk's keys)."""
-    expect = STRIDE * -(-k // 8)
+    4096 expected kept keys, plus 64, rounded up to 64, at most the chunk's
+    keys)."""
     ln = min(CHUNK, n - c * CHUNK)
-    share = -(-2 * expect * ln // n)
+    share = -(-2 * EXPECT * ln // n)
     return min(ln, -(-share // 64) * 64 + 64)
 
 
 def predict_failed(I_row, n, k):
     """Whether the bracket of a row with exact scores I_row[:n] fails."""
-    if k >= n:
+    if k >= n or n <= SEL_CAP:
         return False
-    m = -(-k // 8)
     smp = I_row[:n:STRIDE]
-    thr = -np.inf if smp.shape[0] < m else np.sort(smp)[::-1][m - 1]
+    thr = np.sort(smp)[::-1][RANK - 1]
     kept = I_row[:n] >= thr
     total = 0
     for c in range(-(-n // CHUNK)):
         fc = int(kept[c * CHUNK:(c + 1) * CHUNK].sum())
-        if fc > slots(n, c, k):
+        if fc > slots(n, c):
             return True
         total += fc
     return total > SEL_CAP or total < k
@@ -126,9 +126,10 @@ def test_indexer_topk_exact_integer_inputs(sa, T, Hi, N, back, k, span, unit_w):
     assert np.array_equal(idx[ok], ridx[ok]) and np.array_equal(cnt[ok], rcnt[ok])
 
 
-@pytest.mark.parametrize("T,Hi,N,pos0,k", [(3000, 64, 6000, 3000, 2048),   # sampled and every-key thresholds
+@pytest.mark.parametrize("T,Hi,N,pos0,k", [(3000, 64, 12000, 6000, 2048),  # every-key and sampled rows
                                            (2500, 32, 2500, 0, 2048),      # prefill from 0: short rows
-                                           (100, 64, 50004, 49000, 512)])  # ragged last chunk
+                                           (100, 64, 50004, 49000, 512),   # ragged last chunk
+                                           (64, 64, 40000, 30000, 1)])     # k = 1
 def test_indexer_topk_random(sa, T, Hi, N, pos0, k):
     """Random indexer inputs: no row fails; every row equals the two-call
     path's bit for bit; sampled rows against the oracle (certified rows
@@ -140,8 +141,9 @@ def test_indexer_topk_random(sa, T, Hi, N, pos0, k):
     assert np.array_equal(cnt, np.minimum(k, n_rows))
     ridx, rcnt = run_two_call(sa, ind.qi, ind.ki, ind.w, pos0, k)
     assert np.array_equal(idx, ridx) and np.array_equal(cnt, rcnt)
-    rows = np.unique(np.concatenate([np.linspace(0, T - 1, 12).astype(np.int64),
-                                     np.nonzero(np.diff((pos0 + np.arange(T)) // STRIDE + 1 >= -(-k // 8)))[0]]))
+    # evenly spread rows and the rows on both sides of the every-key / sampled boundary
+    edge = np.nonzero(np.diff(n_rows > SEL_CAP))[0]
+    rows = np.unique(np.concatenate([np.linspace(0, T - 1, 12).astype(np.int64), edge, edge + 1]))
     I = oracle.indexer_scores(W.bf16_to_f32(ind.qi), W.bf16_to_f32(ind.ki), ind.w, pos0, rows)
     sel = oracle.indexer_select(I, rows, pos0, k)
     none = np.zeros(0, np.int64)
@@ -152,6 +154,22 @@ def test_indexer_topk_random(sa, T, Hi, N, pos0, k):
             assert np.array_equal(got, sel[r]), t
         else:
             assert tie_tolerant_valid(got, I[r, :n], k, none), t
+
+
+@pytest.mark.parametrize("T,Hi,N,pos0,k", [(1, 64, 1, 0, 1),          # one key
+                                           (5, 32, 17, 12, 16),      # rows of 13..17 keys around k
+                                           (3, 64, 40, 0, 2048),     # k above every row
+                                           (7, 64, 8200, 8190, 2048),  # rows of 8191..8197 keys: both rules
+                                           (9, 32, 8195, 8180, 100)])
+def test_indexer_topk_small_and_boundary_rows(sa, T, Hi, N, pos0, k):
+    """Exact integer inputs on tiny contexts and on rows around the 8192-key
+    boundary between keeping every key and the sampled threshold: every row
+    equals the oracle's top-k."""
+    qi = W.integer_bf16(97, (T, Hi, 64), -4, 4, 0)
+    ki = W.integer_bf16(97, (N, 64), -4, 4, 1)
+    w = (np.random.default_rng(97).integers(0, 65, size=Hi) / 64.0).astype(np.float32)
+    idx, cnt, err = run_fused(sa, qi, ki, w, pos0, k)
+    assert check_exact(qi, ki, w, pos0, k, idx, cnt) == 0 and err == 0
 
 
 def test_indexer_topk_kmax_padding(sa):
