@@ -43,7 +43,7 @@ typedef enum sa_status {
   SA_ERR_DTYPE = 3,       /* unsupported element type */
   SA_ERR_ALIGN = 4,       /* pointer not 16-byte aligned */
   SA_ERR_WORKSPACE = 5,   /* workspace missing or smaller than required */
-  SA_ERR_UNSUPPORTED = 6, /* valid request this build does not implement */
+  SA_ERR_UNSUPPORTED = 6, /* a valid request the library does not implement */
   SA_ERR_LAUNCH = 7,      /* HIP reported an error at launch */
   SA_ERR_VALUE = 8        /* a parameter value is invalid (e.g. scale, k) */
 } sa_status;
