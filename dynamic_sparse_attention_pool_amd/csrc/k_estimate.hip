@@ -253,11 +253,13 @@ __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q,
 }
 
 // ---------------------------------------------------------------- k_centroid_topk
-// Centroid scores and the per-row top-k in one pass, for decode: one workgroup
-// per (token, KV head) covers the grp query heads that share the KV head.
-// Thread c owns centroids c, c+256, ...: it reads each centroid row once and
-// computes its score for every query of the group (dimension order, fp32, as
-// k_centroid_score), keeping order-preserving keys in LDS.  Per row, an
+// Centroid scores and the per-row top-k in one pass, for decode: a workgroup
+// covers nrow query heads of one token that share a KV head (one head per
+// workgroup at launch, which spreads the centroid rows' loads over four times
+// as many CUs as one workgroup per KV head).  Thread c owns centroids c, c+256,
+// ...: it reads each centroid row (its loads issued together) and computes its
+// score for every row (dimension order, fp32, as k_centroid_score), keeping
+// order-preserving keys in LDS.  Per row, an
 // MSB-first radix select (8-bit digits, LDS histograms, 32 threads per row for
 // the digit) finds the k-th key T; candidates above T and the lowest-index
 // keys equal to T are written in cluster order.
@@ -268,7 +270,7 @@ constexpr int kCtMaxC = 1024;
 template <typename T>
 __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restrict__ q, const float* __restrict__ cent,
                                                               int hq, int hkv, int C, int D, float scale, int k,
-                                                              int kmax, int32_t* __restrict__ idx,
+                                                              int kmax, int nsub, int32_t* __restrict__ idx,
                                                               int32_t* __restrict__ cnt, int32_t* err) {
   __shared__ float qs[kCtMaxRows][128];
   __shared__ uint32_t keys[kCtMaxRows][kCtMaxC];
@@ -278,17 +280,20 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
   __shared__ uint32_t s_wave[kCtThreads / 64][kCtMaxRows][2];
   __shared__ uint32_t s_nan;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int grp = hq / hkv;
-  const int t = blockIdx.x / hkv, g = blockIdx.x % hkv;
+  // workgroup (t, s, g): token t, KV head g (innermost, so one KV head's
+  // centroid rows stay in one XCD's L2), rows s*nrow .. of the g's query heads
+  const int grp = hq / hkv, nrow = grp / nsub;
+  const int g = blockIdx.x % hkv, ts = blockIdx.x / hkv;
+  const int t = ts / nsub, h0 = g * grp + (ts % nsub) * nrow;
   const int kr = min(k, C);
   if (tid == 0) s_nan = 0u;
-  for (int e = tid; e < grp * D; e += kCtThreads) {
+  for (int e = tid; e < nrow * D; e += kCtThreads) {
     const int hh = e / D, d = e % D;
-    const T* qp = q + ((int64_t)t * hq + g * grp + hh) * D + d;
+    const T* qp = q + ((int64_t)t * hq + h0 + hh) * D + d;
     if constexpr (sizeof(T) == 2) qs[hh][d] = bf2f(*reinterpret_cast<const uint16_t*>(qp));
     else qs[hh][d] = *reinterpret_cast<const float*>(qp);
   }
-  if (tid < grp) s_need[tid] = kr;
+  if (tid < nrow) s_need[tid] = kr;
   __syncthreads();
   // ---- scores -> keys
   bool nan_seen = false;
@@ -297,20 +302,30 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
     float acc[kCtMaxRows];
 #pragma unroll
     for (int hh = 0; hh < kCtMaxRows; ++hh) acc[hh] = 0.f;
-    for (int d0 = 0; d0 < D; d0 += 4) {
-      const f32x4 m4 = *reinterpret_cast<const f32x4*>(cr + d0);
+    auto fma4 = [&](int d0, const f32x4& m4) {
 #pragma unroll
       for (int hh = 0; hh < kCtMaxRows; ++hh)
-        if (hh < grp) {
+        if (hh < nrow) {
           acc[hh] = fmaf(qs[hh][d0], m4[0], acc[hh]);
           acc[hh] = fmaf(qs[hh][d0 + 1], m4[1], acc[hh]);
           acc[hh] = fmaf(qs[hh][d0 + 2], m4[2], acc[hh]);
           acc[hh] = fmaf(qs[hh][d0 + 3], m4[3], acc[hh]);
         }
+    };
+    // the row's loads are issued before its products (16 in flight), so one
+    // memory latency covers a 64-dimension half instead of one per 4 dimensions
+    int d0 = 0;
+    for (; d0 + 64 <= D; d0 += 64) {
+      f32x4 m4[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) m4[u] = *reinterpret_cast<const f32x4*>(cr + d0 + 4 * u);
+#pragma unroll
+      for (int u = 0; u < 16; ++u) fma4(d0 + 4 * u, m4[u]);
     }
+    for (; d0 < D; d0 += 4) fma4(d0, *reinterpret_cast<const f32x4*>(cr + d0));
 #pragma unroll
     for (int hh = 0; hh < kCtMaxRows; ++hh)
-      if (hh < grp) {
+      if (hh < nrow) {
         const float sc = acc[hh] * scale;
         nan_seen |= is_nan(sc);
         keys[hh][c] = order_key(sc);
@@ -330,14 +345,14 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
     for (int c = tid; c < C; c += kCtThreads)
 #pragma unroll
       for (int hh = 0; hh < kCtMaxRows; ++hh)
-        if (hh < grp) {
+        if (hh < nrow) {
           const uint32_t key = keys[hh][c];
           if ((key & hmask) == (Tk[hh] & hmask)) atomicAdd(&hist[hh][(key >> shift) & 255u], 1u);
         }
     __syncthreads();
     {
       const int row = tid / TPR, seg = tid % TPR;
-      if (row < grp) {
+      if (row < nrow) {
         const int rneed = s_need[row];
         uint32_t loc = 0u;
 #pragma unroll
@@ -371,8 +386,8 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
     __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < kCtMaxRows; ++hh)
-      if (hh < grp) Tk[hh] |= s_digit[hh][0] << shift;
-    if (tid < grp) s_need[tid] -= (int)s_digit[tid][1];  // read again after two more barriers
+      if (hh < nrow) Tk[hh] |= s_digit[hh][0] << shift;
+    if (tid < nrow) s_need[tid] -= (int)s_digit[tid][1];  // read again after two more barriers
   }
   __syncthreads();
   // ---- emission in cluster order: chunks of 256 candidates, ballots per wave
@@ -385,8 +400,8 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
     uint64_t mf[kCtMaxRows], mt[kCtMaxRows];
 #pragma unroll
     for (int hh = 0; hh < kCtMaxRows; ++hh) {
-      const uint32_t key = (c < C && hh < grp) ? keys[hh][c] : 0u;
-      const bool live = c < C && hh < grp;
+      const uint32_t key = (c < C && hh < nrow) ? keys[hh][c] : 0u;
+      const bool live = c < C && hh < nrow;
       mf[hh] = __ballot(live && key > Tk[hh]);
       mt[hh] = __ballot(live && key == Tk[hh]);
       if (lane == 0) {
@@ -397,7 +412,7 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
     __syncthreads();
 #pragma unroll
     for (int hh = 0; hh < kCtMaxRows; ++hh) {
-      if (hh >= grp) continue;
+      if (hh >= nrow) continue;
       int wf = 0, wt = 0, af = 0, at = 0;
       for (int x = 0; x < kCtThreads / 64; ++x) {
         const int f = (int)s_wave[x][hh][0], e = (int)s_wave[x][hh][1];
@@ -411,7 +426,7 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
       const int need = s_need[hh];
       const int fb = base_f[hh] + wf + (int)__popcll(mf[hh] & lt);
       const int tb = base_t[hh] + wt + (int)__popcll(mt[hh] & lt);
-      int32_t* out = idx + ((int64_t)t * hq + g * grp + hh) * kmax;
+      int32_t* out = idx + ((int64_t)t * hq + h0 + hh) * kmax;
       if ((mf[hh] >> lane) & 1ull) out[fb + min(tb, need)] = c;
       else if (((mt[hh] >> lane) & 1ull) && tb < need) out[fb + tb] = c;
       base_f[hh] += af;
@@ -419,9 +434,9 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
     }
     __syncthreads();
   }
-  for (int e = tid; e < grp * kmax; e += kCtThreads) {
+  for (int e = tid; e < nrow * kmax; e += kCtThreads) {
     const int hh = e / kmax, pos = e % kmax;
-    const int64_t row = (int64_t)t * hq + g * grp + hh;
+    const int64_t row = (int64_t)t * hq + h0 + hh;
     if (pos >= kr) idx[row * kmax + pos] = -1;
     if (pos == 0) cnt[row] = kr;
   }
@@ -434,13 +449,16 @@ hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, i
                                 int head_dim, float scale, int k, int kmax, int32_t* idx, int32_t* cnt, int32_t* err,
                                 hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  const dim3 grid((unsigned)(T * hkv));
+  // one query head per workgroup: four times the workgroups of one per KV head,
+  // so the centroid rows' loads spread over more CUs
+  const int nsub = hq / hkv;
+  const dim3 grid((unsigned)(T * hkv * nsub));
   if (q_bf16)
     hipLaunchKernelGGL((k_centroid_topk<uint16_t>), grid, dim3(kCtThreads), 0, stream, (const uint16_t*)q, cent, hq,
-                       hkv, C, head_dim, scale, k, kmax, idx, cnt, err);
+                       hkv, C, head_dim, scale, k, kmax, nsub, idx, cnt, err);
   else
     hipLaunchKernelGGL((k_centroid_topk<float>), grid, dim3(kCtThreads), 0, stream, (const float*)q, cent, hq, hkv,
-                       C, head_dim, scale, k, kmax, idx, cnt, err);
+                       C, head_dim, scale, k, kmax, nsub, idx, cnt, err);
   return hipGetLastError();
 }
 
