@@ -500,154 +500,274 @@ __global__ __launch_bounds__(kIdxSelNT) void k_idx_select(IdxCand cd, int64_t Nk
 constexpr int kVsLast = 64;
 constexpr int kVsTilesPerWg = 16;
 
-template <int D>
-struct VsOps {
-  static constexpr int NS = D / 16;  // k-steps
-  // A operand: K rows s0+32mt+l32, dims (D/2)hf + 8s .. +7
-  __device__ static void load_k(bf16x8 (&ka)[2][NS], const uint16_t* kb, int64_t s0, int64_t N, int l32, int hf) {
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-      const int64_t row = std::min(s0 + 32 * mt + l32, N - 1);
-      const uint16_t* kr = kb + row * D + (D / 2) * hf;
-#pragma unroll
-      for (int s = 0; s < NS; ++s) ka[mt][s] = as_bf16x8(ldg16(kr + 8 * s));
-    }
-  }
-  __device__ static void scores(float (&x)[32], const bf16x8 (&ka)[2][NS], const bf16x8 (&qv)[NS], float sl2,
-                                int64_t s0, int64_t qpos, int64_t N, int hf) {
-    f32x16 a0, a1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      a0[r] = 0.f;
-      a1[r] = 0.f;
-    }
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      a0 = mfma32x32x16(ka[0][s], qv[s], a0);
-      a1 = mfma32x32x16(ka[1][s], qv[s], a1);
-    }
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      const int key = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
-      const float v = (r < 16 ? a0[r] : a1[r - 16]) * sl2;
-      x[r] = (s0 + key > qpos || s0 + key >= N) ? -INFINITY : v;
-    }
-  }
-};
+// One workgroup per (batch, KV head, block of up to 4 of its query heads,
+// chunk of 16 key tiles): the 64-key K tiles go into LDS once, by direct
+// copies (double-buffered), and serve every listed query head of the KV head.
+// Wave w takes query head slot w/2 and key half w%2 (32 keys) of each tile,
+// for all 64 last queries of that head (two 32-query operand tiles kept in
+// registers).  Lane (l32, hf) reads key row l32 of its half, dims 8hf + 16s ..
+// +7 at step s, from LDS; the rows' 16-byte chunks sit XOR-swizzled so that
+// eight consecutive rows read the same chunk from distinct banks.
+constexpr int kVsWaves = 8;
 
-// pass 1: per (head row, chunk of tiles, query) running max / sum (log2 domain)
 template <int D>
-__global__ __launch_bounds__(128) void k_vs_stats(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                  int hq, int hkv, HeadList hl, int64_t N, float sl2, int nchunk,
-                                                  float* __restrict__ stats) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
-  int b, h;
-  listed_row(bh, hq, hl, b, h);
-  const int g = h * hkv / hq;
-  const int r = 32 * wv + l32;  // query row among the last 64
-  const int64_t qpos = N - kVsLast + r;
+__device__ __forceinline__ int vs_swz(int r, int c) {
+  return D == 128 ? (c ^ (r & 15)) : (c ^ ((r >> 1) & 7));
+}
+
+// Compact output row of query head h of batch b (-1 when a head list leaves it out).
+__device__ __forceinline__ int vs_row(const HeadList& hl, int hq, int b, int h) {
+  if (hl.n == 0) return b * hq + h;
+  for (int i = 0; i < hl.n; ++i)
+    if (hl.h[i] == h) return b * hl.n + i;
+  return -1;
+}
+
+// PASS 2 = false: per (row, chunk, query) running max and sum (log2 domain).
+// PASS 2 = true: probabilities (exp2(s * sl2 - M') with M' = M + log2 L)
+// reduced along the queries (column sums, final) and along the diagonals of
+// each 64 x 64 tile (partials, merged by k_vs_slash).
+template <int D, bool PASS2>
+__global__ __launch_bounds__(64 * kVsWaves) void k_vs_pass(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                                                           int hq, int hkv, HeadList hl, int64_t N, float sl2,
+                                                           int nchunk, int nhs, const float* __restrict__ ml,
+                                                           float* __restrict__ stats, float* __restrict__ a_v,
+                                                           float* __restrict__ dpart) {
+  constexpr int NS = D / 16, CPR = D / 8;  // k-steps; 16-byte chunks per row
+  constexpr int NB = PASS2 ? 2 : 3;  // K tile buffers: pass 1 copies two tiles ahead
+  __shared__ __attribute__((aligned(1024))) uint16_t Kt[NB][64 * D];
+  __shared__ __attribute__((aligned(16))) float Pl[PASS2 ? 4 : 1][64][kVsLast + 4];  // [head slot][key][query]
+  __shared__ float st[4][2][kVsLast][2];             // pass 1: [head slot][key half][query](m, l)
+  // pass 2: the chunk's column sums and diagonal partials, written out after
+  // the loop so that no store sits in front of the per-tile copy wait
+  __shared__ float av_s[PASS2 ? 4 : 1][PASS2 ? kVsTilesPerWg * 64 : 1];
+  __shared__ float dp_s[PASS2 ? 4 : 1][PASS2 ? kVsTilesPerWg : 1][128];
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31, tid = threadIdx.x;
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ck = blockIdx.x % nchunk, rest = blockIdx.x / nchunk;
+  const int hs = rest % nhs, bg = rest / nhs;
+  const int b = bg / hkv, g = bg % hkv;
+  const int grp = hq / hkv;
+  const int js = wv >> 1, kh = wv & 1;
+  // rows of the four head slots (every thread, for the diagonal pass)
+  int rows[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) rows[j] = (4 * hs + j < grp) ? vs_row(hl, hq, b, g * grp + 4 * hs + j) : -1;
+  const int row = rows[js];
+  const bool active = row >= 0;
+  const int h = g * grp + 4 * hs + js;
   const uint16_t* kb = k + ((int64_t)b * hkv + g) * N * D;
-  bf16x8 qv[D / 16];
-  {
-    const uint16_t* qr = q + (((int64_t)b * hq + h) * N + qpos) * D + (D / 2) * hf;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qv[s] = as_bf16x8(ldg16(qr + 8 * s));
-  }
-  const int64_t ntile = (N + 63) / 64;
+  const int64_t ntile = N / 64;
   const int64_t tb = (int64_t)ck * kVsTilesPerWg, te = std::min(ntile, tb + kVsTilesPerWg);
-  float m = -INFINITY, l = 0.f;
-  for (int64_t t = tb; t < te; ++t) {
-    const int64_t s0 = t * 64;
-    if (s0 > N - 1) break;
-    bf16x8 ka[2][D / 16];
-    VsOps<D>::load_k(ka, kb, s0, N, l32, hf);
-    float x[32];
-    VsOps<D>::scores(x, ka, qv, sl2, s0, qpos, N, hf);
-    float mx = x[0];
+  const int nt = (int)(te - tb);
+  // query operands: query 32qt + l32 of the last 64, dims 8hf + 16s .. +7
+  bf16x8 qv[2][NS];
 #pragma unroll
-    for (int i = 1; i < 32; ++i) mx = fmaxf(mx, x[i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mnew = fmaxf(m, mx);
-    const float muse = mnew == -INFINITY ? 0.f : mnew;
-    float ps = 0.f;
+  for (int qt = 0; qt < 2; ++qt) {
+    const uint16_t* qr = q + (((int64_t)b * hq + (active ? h : 0)) * N + (N - kVsLast) + 32 * qt + l32) * D + 8 * hf;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) ps += fast_exp2(x[i] - muse);
-    ps += __shfl_xor(ps, 32);
-    l = l * fast_exp2(m - muse) + ps;
-    m = mnew;
+    for (int s4 = 0; s4 < NS; ++s4) qv[qt][s4] = as_bf16x8(ldg16(qr + 16 * s4));
   }
-  if (hf == 0) {
-    float* sp = stats + (((int64_t)bh * nchunk + ck) * kVsLast + r) * 2;
-    sp[0] = m;
-    sp[1] = l;
+  // pass 2: M' of the 16 queries this lane's accumulator rows hold per query tile
+  float mq[2][16];
+  if constexpr (PASS2) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int qi = 32 * qt + 8 * (r / 4) + 4 * hf + (r % 4);
+        const float* mp = ml + ((int64_t)(active ? row : 0) * kVsLast + qi) * 2;
+        const float M = mp[0], invL = mp[1];
+        mq[qt][r] = invL > 0.f ? M - __log2f(invL) : INFINITY;
+      }
+  }
+  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  // one tile = 64 rows x D: 64*D*2/1024 copies of 1 KB, spread over the waves
+  constexpr int kCopies = 64 * D * 2 / 1024;
+  static_assert(kCopies % kVsWaves == 0, "every wave issues the same number of copies per tile");
+  auto copy = [&](int tl, int buf) {
+    for (int n = wv; n < kCopies; n += kVsWaves) {
+      const int r = (1024 / (D * 2)) * n + lane / CPR, cpos = lane % CPR;
+      const int c = D == 128 ? (cpos ^ (r & 15)) : (cpos ^ ((r >> 1) & 7));
+      const int64_t grow = std::min((tb + tl) * 64 + r, N - 1);
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[buf][0]) + (uint32_t)n * 1024u);
+      dma16(dst, kb + grow * D + 8 * c);
+    }
+  };
+  // Pass 1 keeps two tiles in flight: its loop issues no other memory
+  // operation, so waiting until one tile's copies (kCopies / kVsWaves per
+  // wave) remain outstanding means tile tl has landed.  Pass 2 (no room for a
+  // third tile in LDS) waits for its one copy in flight.
+  constexpr int kCpw = kCopies / kVsWaves;
+  if (nt > 0) copy(0, 0);
+  if (!PASS2 && nt > 1) copy(1, 1);
+  for (int tl = 0; tl < nt; ++tl) {
+    const int buf = tl % NB;
+    if (!PASS2 && tl + 1 < nt) wait_vmcnt<kCpw>();
+    else wait_vmcnt<0>();
+    __syncthreads();  // tile tl landed; the buffer refilled next and the P tiles are free
+    if (tl + NB - 1 < nt) copy(tl + NB - 1, (tl + NB - 1) % NB);
+    const int64_t s0 = (tb + tl) * 64;
+    const bool last = s0 + 64 == N;
+    if (active) {
+      bf16x8 kr[NS];
+      const int kr_row = 32 * kh + l32;
+#pragma unroll
+      for (int s4 = 0; s4 < NS; ++s4)
+        kr[s4] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kt[buf][kr_row * D + 8 * vs_swz<D>(kr_row, 2 * s4 + hf)]));
+      if constexpr (!PASS2) {
+        // S^T[key][query]: lane = query 32qt + l32, rows = keys 32kh + 8(r/4) + 4hf + r%4
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x16 acc = mfma32x32x16(kr[0], qv[qt][0], f32x16{});
+#pragma unroll
+          for (int s4 = 1; s4 < NS; ++s4) acc = mfma32x32x16(kr[s4], qv[qt][s4], acc);
+          // only the last tile holds keys past a query (the queries are the last 64 positions)
+          if (last) {
+            const int qloc = 32 * qt + l32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (32 * kh + 8 * (r / 4) + 4 * hf + (r % 4) > qloc) acc[r] = -INFINITY;
+          }
+          // the maximum of the raw scores, scaled once (sl2 > 0)
+          float mx = acc[0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+          const float mnew = fmaxf(m[qt], mx);
+          const float muse = mnew == -INFINITY ? 0.f : mnew;
+          float ps = 0.f;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) ps += fast_exp2(fmaf(acc[r], sl2, -muse));
+          ps += __shfl_xor(ps, 32);
+          l[qt] = l[qt] * fast_exp2(m[qt] - muse) + ps;
+          m[qt] = mnew;
+        }
+      } else {
+        // S[query][key]: lane = key 32kh + l32, rows = queries 32qt + 8(r/4) + 4hf + r%4
+        const int64_t key = s0 + 32 * kh + l32;
+        float cs = 0.f;
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          f32x16 acc = mfma32x32x16(qv[qt][0], kr[0], f32x16{});
+#pragma unroll
+          for (int s4 = 1; s4 < NS; ++s4) acc = mfma32x32x16(qv[qt][s4], kr[s4], acc);
+          float pv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int qi = 32 * qt + 8 * (r / 4) + 4 * hf + (r % 4);
+            pv[r] = fast_exp2(fmaf(acc[r], sl2, -mq[qt][r]));
+            if (last && 32 * kh + l32 > qi) pv[r] = 0.f;  // key past the query: last tile only
+            cs += pv[r];
+          }
+          // P^T row of this key: four consecutive queries per 16-byte store
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4)
+            *reinterpret_cast<f32x4*>(&Pl[js][32 * kh + l32][32 * qt + 8 * r4 + 4 * hf]) =
+                f32x4{pv[4 * r4], pv[4 * r4 + 1], pv[4 * r4 + 2], pv[4 * r4 + 3]};
+        }
+        cs += __shfl_xor(cs, 32);
+        if (hf == 0) av_s[js][tl * 64 + 32 * kh + l32] = cs;
+      }
+    }
+    if constexpr (PASS2) {
+      __syncthreads();  // every slot's P tile is in LDS
+      // Diagonals d = query - key in [-63, 63].  The cyclic diagonal p
+      // (query = (key + p) mod 64) holds d = p for keys < 64 - p and d = p - 64
+      // for the rest: 64 elements, so every lane does the same work.  Slot
+      // tid/128; p = 32 * (wave in slot) + lane%32; lane half hh sums keys
+      // 32hh .. 32hh+31 (the halves read distinct banks), combined by one
+      // exchange.
+      const int jj = tid >> 7, pc = 32 * ((tid >> 6) & 1) + l32;
+      if (rows[jj] >= 0) {
+        float sa = 0.f, sb = 0.f;
+#pragma unroll
+        for (int e0 = 0; e0 < 32; e0 += 8) {
+          float v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            const int e = 32 * hf + e0 + u;
+            v[u] = Pl[jj][e][(e + pc) & 63];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            if (32 * hf + e0 + u < 64 - pc) sa += v[u];
+            else sb += v[u];
+          }
+        }
+        sa += __shfl_xor(sa, 32);
+        sb += __shfl_xor(sb, 32);
+        if (hf == 0) {
+          dp_s[jj][tl][pc + 63] = sa;           // d = pc
+          if (pc > 0) dp_s[jj][tl][pc - 1] = sb;  // d = pc - 64
+        }
+      }
+    }
+  }
+  if constexpr (PASS2) {
+    __syncthreads();
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      if (rows[jj] < 0) continue;
+      for (int i = tid; i < nt * 64; i += 64 * kVsWaves) a_v[(int64_t)rows[jj] * N + tb * 64 + i] = av_s[jj][i];
+      for (int i = tid; i < nt * 128; i += 64 * kVsWaves)
+        if ((i & 127) < 127) dpart[((int64_t)rows[jj] * ntile + tb) * 128 + i] = dp_s[jj][i >> 7][i & 127];
+    }
+  }
+  if constexpr (!PASS2) {
+    // merge the two key halves of each head slot, then one write per query
+    if (active && hf == 0) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        st[js][kh][32 * qt + l32][0] = m[qt];
+        st[js][kh][32 * qt + l32][1] = l[qt];
+      }
+    }
+    __syncthreads();
+    if (active && kh == 0 && hf == 0) {
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const int qi = 32 * qt + l32;
+        const float m0 = st[js][0][qi][0], l0 = st[js][0][qi][1], m1 = st[js][1][qi][0], l1 = st[js][1][qi][1];
+        const float M = fmaxf(m0, m1);
+        const float Mu = M == -INFINITY ? 0.f : M;
+        float* sp = stats + (((int64_t)row * nchunk + ck) * kVsLast + qi) * 2;
+        sp[0] = M;
+        sp[1] = l0 * fast_exp2(m0 - Mu) + l1 * fast_exp2(m1 - Mu);
+      }
+    }
   }
 }
 
+// Merge of the per-chunk statistics: thread = (row, query); 8 chunks' loads in
+// flight, chunks combined in order.
 __global__ __launch_bounds__(64) void k_vs_stats_merge(const float* __restrict__ stats, int nchunk, float* __restrict__ ml) {
   const int bh = blockIdx.x, r = threadIdx.x;
+  const float* sp0 = stats + ((int64_t)bh * nchunk * kVsLast + r) * 2;
+  constexpr int U = 8;
   float M = -INFINITY;
-  for (int c = 0; c < nchunk; ++c) M = fmaxf(M, stats[(((int64_t)bh * nchunk + c) * kVsLast + r) * 2]);
+  for (int c0 = 0; c0 < nchunk; c0 += U) {
+    float v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = c0 + u < nchunk ? sp0[(int64_t)(c0 + u) * kVsLast * 2] : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) M = fmaxf(M, v[u]);
+  }
   const float Mu = M == -INFINITY ? 0.f : M;
   float L = 0.f;
-  for (int c = 0; c < nchunk; ++c) {
-    const float* sp = stats + (((int64_t)bh * nchunk + c) * kVsLast + r) * 2;
-    L += sp[1] * fast_exp2(sp[0] - Mu);
+  for (int c0 = 0; c0 < nchunk; c0 += U) {
+    float mv[U], lv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const bool in = c0 + u < nchunk;
+      mv[u] = in ? sp0[(int64_t)(c0 + u) * kVsLast * 2] : -INFINITY;
+      lv[u] = in ? sp0[(int64_t)(c0 + u) * kVsLast * 2 + 1] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) L += lv[u] * fast_exp2(mv[u] - Mu);
   }
   ml[((int64_t)bh * kVsLast + r) * 2] = Mu;
   ml[((int64_t)bh * kVsLast + r) * 2 + 1] = L > 0.f ? 1.f / L : 0.f;
-}
-
-// pass 2: probabilities per tile -> column sums (final) and diagonal partials
-template <int D>
-__global__ __launch_bounds__(128) void k_vs_accum(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-                                                  int hq, int hkv, HeadList hl, int64_t N, float sl2, int nchunk,
-                                                  const float* __restrict__ ml, float* __restrict__ a_v,
-                                                  float* __restrict__ dpart) {
-  __shared__ float P[64][kVsLast + 1];  // [key][query row]
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int bh = blockIdx.x / nchunk, ck = blockIdx.x % nchunk;
-  int b, h;
-  listed_row(bh, hq, hl, b, h);
-  const int g = h * hkv / hq;
-  const int r = 32 * wv + l32;
-  const int64_t qpos = N - kVsLast + r;
-  const uint16_t* kb = k + ((int64_t)b * hkv + g) * N * D;
-  bf16x8 qv[D / 16];
-  {
-    const uint16_t* qr = q + (((int64_t)b * hq + h) * N + qpos) * D + (D / 2) * hf;
-#pragma unroll
-    for (int s = 0; s < D / 16; ++s) qv[s] = as_bf16x8(ldg16(qr + 8 * s));
-  }
-  const float M = ml[((int64_t)bh * kVsLast + r) * 2], invL = ml[((int64_t)bh * kVsLast + r) * 2 + 1];
-  const int64_t ntile = (N + 63) / 64;
-  const int64_t tb = (int64_t)ck * kVsTilesPerWg, te = std::min(ntile, tb + kVsTilesPerWg);
-  for (int64_t t = tb; t < te; ++t) {
-    const int64_t s0 = t * 64;
-    bf16x8 ka[2][D / 16];
-    VsOps<D>::load_k(ka, kb, s0, N, l32, hf);
-    float x[32];
-    VsOps<D>::scores(x, ka, qv, sl2, s0, qpos, N, hf);
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const int key = 32 * (i / 16) + 8 * ((i % 16) / 4) + 4 * hf + (i % 4);
-      P[key][r] = fast_exp2(x[i] - M) * invL;
-    }
-    __syncthreads();
-    if (tid < 64) {  // column sum over the 64 query rows
-      float s = 0.f;
-      for (int rr = 0; rr < kVsLast; ++rr) s += P[tid][rr];
-      if (s0 + tid < N) a_v[(int64_t)bh * N + s0 + tid] = s;
-    }
-    // diagonal d = row - key in [-63, 63]
-    for (int dg = tid; dg < 127; dg += 128) {
-      const int delta = dg - 63;
-      float s = 0.f;
-      for (int key = std::max(0, -delta); key < 64 && key + delta < kVsLast; ++key) s += P[key][key + delta];
-      dpart[((int64_t)bh * ntile + t) * 128 + dg] = s;
-    }
-  }
 }
 
 // a_s[o] = sum over the (at most two) tiles whose diagonals reach offset o
@@ -791,15 +911,20 @@ hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, i
   p += a256((size_t)((int64_t)rows * kVsLast * 2) * 4);
   float* dpart = reinterpret_cast<float*>(p);
   const float sl2 = scale * kLog2e;
-  const dim3 grid((unsigned)((int64_t)rows * nchunk));
+  const int grp = hq / hkv, nhs = (grp + 3) / 4;
+  const dim3 grid((unsigned)((int64_t)batch * hkv * nhs * nchunk)), blk(64 * kVsWaves);
   if (head_dim == 128) {
-    hipLaunchKernelGGL((k_vs_stats<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, stats);
+    hipLaunchKernelGGL((k_vs_pass<128, false>), grid, blk, 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, nhs,
+                       nullptr, stats, nullptr, nullptr);
     hipLaunchKernelGGL(k_vs_stats_merge, dim3(rows), dim3(64), 0, stream, stats, nchunk, ml);
-    hipLaunchKernelGGL((k_vs_accum<128>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, ml, a_v, dpart);
+    hipLaunchKernelGGL((k_vs_pass<128, true>), grid, blk, 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, nhs, ml,
+                       nullptr, a_v, dpart);
   } else if (head_dim == 64) {
-    hipLaunchKernelGGL((k_vs_stats<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, stats);
+    hipLaunchKernelGGL((k_vs_pass<64, false>), grid, blk, 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, nhs,
+                       nullptr, stats, nullptr, nullptr);
     hipLaunchKernelGGL(k_vs_stats_merge, dim3(rows), dim3(64), 0, stream, stats, nchunk, ml);
-    hipLaunchKernelGGL((k_vs_accum<64>), grid, dim3(128), 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, ml, a_v, dpart);
+    hipLaunchKernelGGL((k_vs_pass<64, true>), grid, blk, 0, stream, q, k, hq, hkv, hl, seq, sl2, nchunk, nhs, ml,
+                       nullptr, a_v, dpart);
   } else {
     return hipErrorInvalidValue;
   }
