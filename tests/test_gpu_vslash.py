@@ -44,6 +44,28 @@ def test_vs_estimate(sa, N, d):
         assert abs(host(av)[0, h].sum() - 64) < 1e-3 and abs(host(as_)[0, h].sum() - 64) < 1e-3
 
 
+@pytest.mark.parametrize("Hq,Hkv,heads", [(8, 1, None), (16, 2, [3, 9, 12, 15, 4]), (3, 3, None), (6, 1, [5, 0])])
+def test_vs_estimate_group_shapes(sa, Hq, Hkv, heads):
+    """Query heads per KV head 8, 1 and 6 (workgroups cover up to four of a KV
+    head's query heads, so these need two blocks, a partial block or one head
+    per block), with and without a head list, batch 2."""
+    B, N, d = 2, 1024, 128
+    inp = W.prefill_bf16(53, B, Hq, Hkv, N, d)
+    lst = list(range(Hq)) if heads is None else heads
+    t = torch()
+    av = t.empty((B, len(lst), N), dtype=t.float32, device="cuda:0")
+    as_ = t.empty_like(av)
+    scale = 1 / math.sqrt(d)
+    sa.sa_estimate(sa.VSLASH, dev_bf16(inp.q), dev_bf16(inp.k), av, scores2=as_, scale=scale, heads=heads)
+    t.cuda.synchronize()
+    for b in range(B):
+        for j, h in enumerate(lst):
+            g = oracle.gqa_group(h, Hq, Hkv)
+            wv, ws = oracle.vs_estimate(inp.f32("q")[b, h, N - 64:], inp.f32("k")[b, g], np.arange(N - 64, N), scale)
+            assert_scores_close(host(av)[b, j][None], wv[None], f"vertical b{b} h{h}")
+            assert_scores_close(host(as_)[b, j][None], ws[None], f"slash b{b} h{h}")
+
+
 @pytest.mark.parametrize("ns", [40, 64, 100])  # up to 64 offsets: one wave per row; more: one thread per row
 def test_vs_build_tables_exact(sa, ns):
     N, R, nv = 4096, 5, 300
