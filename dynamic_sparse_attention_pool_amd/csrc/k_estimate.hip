@@ -122,17 +122,20 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
 
 // 128x128 tile of S per workgroup on the fp32 matrix cores
 // (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation).  The pooled Q
-// and K rows of the tile pass through LDS 32 dimensions at a time, row pitch
-// 34 floats, so the 32 rows x 2 columns read by one MFMA operand hit 64
-// different banks; wave (wi, wj) computes the 64x64 quarter (wi, wj) as 2x2
-// MFMA tiles.  Tiles above the diagonal only write -inf.
+// and K rows of the tile pass through LDS 32 dimensions at a time.  Step kk of
+// the product takes dimension 2kk + hf from lane half hf, so within each group
+// of 8 dimensions LDS holds the even ones, then the odd ones: one 16-byte read
+// gives a lane its operands for four steps.  Row pitch 36 floats: sixteen
+// consecutive rows' 16-byte reads hit distinct banks.  Wave (wi, wj) computes
+// the 64x64 quarter (wi, wj) as 2x2 MFMA tiles.  Tiles above the diagonal only
+// write -inf.
 template <int D>
 __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restrict__ pq, const float* __restrict__ pk,
                                                           int hq, int hkv, HeadList hl, int nb, float scale,
                                                           float* __restrict__ S) {
-  constexpr int T = 128, DC = 32, P = DC + 2;
-  __shared__ float Qs[T * P];
-  __shared__ float Ks[T * P];
+  constexpr int T = 128, DC = 32, P = DC + 4;
+  __shared__ __attribute__((aligned(16))) float Qs[T * P];
+  __shared__ __attribute__((aligned(16))) float Ks[T * P];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, l32 = lane & 31;
   const int nbt = (nb + T - 1) / T;
   const int bh = blockIdx.x / (nbt * nbt);
@@ -170,23 +173,28 @@ __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restric
       const f32x4 vk = kj < nb ? *reinterpret_cast<const f32x4*>(Kb + (int64_t)kj * D + d0 + 4 * c4) : z;
 #pragma unroll
       for (int x = 0; x < 4; ++x) {
-        Qs[rr * P + 4 * c4 + x] = vq[x];
-        Ks[rr * P + 4 * c4 + x] = vk[x];
+        const int j = 4 * c4 + x, pos = (j & ~7) + 4 * (j & 1) + ((j & 7) >> 1);  // even dims, then odd ones
+        Qs[rr * P + pos] = vq[x];
+        Ks[rr * P + pos] = vk[x];
       }
     }
     __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < DC / 2; ++kk) {
-      float qa[2], kb[2];
+#pragma unroll
+    for (int k8 = 0; k8 < DC / 8; ++k8) {
+      // steps 4k8 .. 4k8+3: dimensions 8k8 + 2x + hf
+      f32x4 qa[2], kb[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        qa[m] = Qs[(64 * wi + 32 * m + l32) * P + 2 * kk + hf];  // A[i][k]: row i = l32, k = hf
-        kb[m] = Ks[(64 * wj + 32 * m + l32) * P + 2 * kk + hf];  // B[k][j] = K[j][k]: column j = l32
+        qa[m] = *reinterpret_cast<const f32x4*>(&Qs[(64 * wi + 32 * m + l32) * P + 8 * k8 + 4 * hf]);  // A: row l32
+        kb[m] = *reinterpret_cast<const f32x4*>(&Ks[(64 * wj + 32 * m + l32) * P + 8 * k8 + 4 * hf]);  // B: column l32
       }
 #pragma unroll
-      for (int m = 0; m < 2; ++m)
+      for (int x = 0; x < 4; ++x)
 #pragma unroll
-        for (int n = 0; n < 2; ++n) acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[m], kb[n], acc[m][n], 0, 0, 0);
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int n = 0; n < 2; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[m][x], kb[n][x], acc[m][n], 0, 0, 0);
     }
     __syncthreads();
   }
