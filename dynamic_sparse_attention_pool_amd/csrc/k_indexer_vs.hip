@@ -17,10 +17,12 @@
 // diagonal sums of each 64-key tile are written as partials and merged in a
 // fixed order by a last kernel, so the result is deterministic.
 //
-// Both kernels feed K rows straight from memory into the A operand of
-// v_mfma_f32_32x32x16_bf16 (S^T = K . Q^T): lane half hf reads the contiguous
-// half [hf*D/2, (hf+1)*D/2) of a row over the k-steps, and the Q^T operand
-// walks the head dimension in the same order.
+// Both stage 64-key K tiles in LDS by direct copies, shared by every wave of
+// the workgroup (the indexer's query groups, or the query heads of one KV
+// head), and feed them to v_mfma_f32_32x32x16_bf16.
+//
+// The indexer's fused top-k (a sampled threshold, a pass that keeps only the
+// keys reaching it, an exact select over those) lives here too.
 #include <algorithm>
 
 #include "common.h"
