@@ -17,9 +17,10 @@
 // diagonal sums of each 64-key tile are written as partials and merged in a
 // fixed order by a last kernel, so the result is deterministic.
 //
-// Both stage 64-key K tiles in LDS by direct copies, shared by every wave of
-// the workgroup (the indexer's query groups, or the query heads of one KV
-// head), and feed them to v_mfma_f32_32x32x16_bf16.
+// k_indexer2 and the vertical-slash passes stage 64-key K tiles in LDS by
+// direct copies, shared by every wave of the workgroup (the indexer's query
+// groups, or the query heads of one KV head), and feed them to
+// v_mfma_f32_32x32x16_bf16; k_indexer reads its K rows into registers.
 //
 // The indexer's fused top-k (a sampled threshold, a pass that keeps only the
 // keys reaching it, an exact select over those) lives here too.
