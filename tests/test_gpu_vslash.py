@@ -44,12 +44,15 @@ def test_vs_estimate(sa, N, d):
         assert abs(host(av)[0, h].sum() - 64) < 1e-3 and abs(host(as_)[0, h].sum() - 64) < 1e-3
 
 
-@pytest.mark.parametrize("Hq,Hkv,heads", [(8, 1, None), (16, 2, [3, 9, 12, 15, 4]), (3, 3, None), (6, 1, [5, 0])])
-def test_vs_estimate_group_shapes(sa, Hq, Hkv, heads):
-    """Query heads per KV head 8, 1 and 6 (workgroups cover up to four of a KV
-    head's query heads, so these need two blocks, a partial block or one head
-    per block), with and without a head list, batch 2."""
-    B, N, d = 2, 1024, 128
+@pytest.mark.parametrize("Hq,Hkv,heads,N,d", [(8, 1, None, 1024, 128), (16, 2, [3, 9, 12, 15, 4], 1024, 128),
+                                            (3, 3, None, 1024, 128), (6, 1, [5, 0], 1024, 128),
+                                            (4, 1, None, 64, 128), (8, 2, [7], 128, 64), (5, 5, None, 1088, 64)])
+def test_vs_estimate_group_shapes(sa, Hq, Hkv, heads, N, d):
+    """Query heads per KV head 8, 1, 6 and 4 (workgroups cover up to four of a
+    KV head's query heads, so these need two blocks, a partial block or one
+    head per block), with and without a head list, batch 2; one- and two-tile
+    contexts and a chunk of one tile (17 tiles)."""
+    B = 2
     inp = W.prefill_bf16(53, B, Hq, Hkv, N, d)
     lst = list(range(Hq)) if heads is None else heads
     t = torch()
