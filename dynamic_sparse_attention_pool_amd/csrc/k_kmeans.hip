@@ -6,14 +6,20 @@
 // ties to the lower cluster index) + update (each centroid becomes the mean of
 // its keys; an empty cluster keeps its centroid).
 //
-// Assignment: one thread per key with the key row in registers; centroids pass
-// through LDS 32 at a time together with their squared norms, and the thread
-// keeps the smallest |mu|^2 - 2 x.mu (the |x|^2 term is the same for every
-// centroid of a key).  Dot products run in dimension order in fp32.
+// Assignment of fp32 keys: one thread per key with the key row in registers;
+// centroids pass through LDS 32 at a time together with their squared norms,
+// and the thread keeps the smallest |mu|^2 - 2 x.mu (the |x|^2 term is the same
+// for every centroid of a key).  Dot products run in dimension order in fp32.
+// Assignment of bf16 keys on the matrix cores: every centroid is split into
+// three bf16 parts (hi = bf16(mu), lo = bf16(mu - hi), lo2 = bf16(mu - hi -
+// lo); their sum is mu to about 2^-24 relative), so x.mu = x.hi + x.lo + x.lo2
+// with exact bf16 products accumulated in fp32 by v_mfma_f32_32x32x16_bf16.
 // Update: the cluster-major order of the labels (the stable counting sort of
 // the cluster pack) gives each cluster's keys in token order; one workgroup
 // per (KV head, cluster) sums them in that order, one thread per dimension,
 // so the centroids are deterministic without atomics.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -21,6 +27,7 @@ namespace sa {
 namespace {
 
 constexpr int kKmKeys = 256;   // keys (threads) per assignment workgroup
+size_t km_a256(size_t x) { return (x + 255) & ~size_t(255); }
 constexpr int kKmChunk = 32;   // centroids staged per pass
 
 template <typename T, int D>
@@ -96,6 +103,105 @@ __global__ __launch_bounds__(kKmKeys) void k_km_assign(const T* __restrict__ key
   if (live) labels[(int64_t)g * n + t] = arg;
 }
 
+// Centroid split for the matrix-core assignment: parts [g][c][3][D] bf16 and
+// the squared norm (fp32, dimension order) of every centroid.
+template <int D>
+__global__ __launch_bounds__(D) void k_km_split(const float* __restrict__ cent, int C, uint16_t* __restrict__ parts,
+                                               float* __restrict__ nrm) {
+  __shared__ float sq[D];
+  const int gc = blockIdx.x, d = threadIdx.x;
+  const float m = cent[(int64_t)gc * D + d];
+  const uint32_t hi = f2bf(m);
+  const float r1 = m - bf2f((uint16_t)hi);
+  const uint32_t lo = f2bf(r1);
+  const uint32_t lo2 = f2bf(r1 - bf2f((uint16_t)lo));
+  uint16_t* pr = parts + (int64_t)gc * 3 * D;
+  pr[d] = (uint16_t)hi;
+  pr[D + d] = (uint16_t)lo;
+  pr[2 * D + d] = (uint16_t)lo2;
+  sq[d] = m;
+  __syncthreads();
+  if (d == 0) {
+    float s = 0.f;
+    for (int e = 0; e < D; ++e) s = fmaf(sq[e], sq[e], s);
+    nrm[gc] = s;
+  }
+}
+
+// C x key tiles of |mu|^2 - 2 (mu . x): wave = 64 keys (two operand tiles held
+// in registers), workgroup = 4 waves.  For each tile of 32 centroids the three
+// parts' rows (A operand, read from the L2-resident split table) multiply the
+// keys (B operand); lane (l32, hf) then holds key 32kt + l32 and the 16
+// centroids 32ct + 8(r/4) + 4hf + r%4, ascending in r, so a strict compare in
+// that order keeps the lowest index among equal distances; the two lane halves
+// are merged by one exchange with the same rule.
+constexpr int kKmWaves = 4;
+constexpr int kKmKeysPerWave = 64;
+
+template <int D>
+__global__ __launch_bounds__(64 * kKmWaves) void k_km_assign_mfma(const uint16_t* __restrict__ keys,
+                                                                 const uint16_t* __restrict__ parts,
+                                                                 const float* __restrict__ nrm, int64_t n, int C,
+                                                                 int32_t* __restrict__ labels) {
+  constexpr int NS = D / 16;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31, wv = threadIdx.x >> 6;
+  constexpr int kPerWg = kKmWaves * kKmKeysPerWave;
+  const int64_t nblk = (n + kPerWg - 1) / kPerWg;
+  const int g = (int)(blockIdx.x / nblk);
+  const int64_t k0 = (blockIdx.x % nblk) * kPerWg + (int64_t)wv * kKmKeysPerWave;
+  const uint16_t* kg = keys + (int64_t)g * n * D;
+  bf16x8 xb[2][NS];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const int64_t row = std::min(k0 + 32 * kt + l32, n - 1);
+#pragma unroll
+    for (int s4 = 0; s4 < NS; ++s4) xb[kt][s4] = as_bf16x8(ldg16(kg + row * D + 16 * s4 + 8 * hf));
+  }
+  const uint16_t* pg = parts + (int64_t)g * C * 3 * D;
+  const float* ng = nrm + (int64_t)g * C;
+  float best[2] = {INFINITY, INFINITY};
+  int arg[2] = {0, 0};
+  const int nct = (C + 31) / 32;
+  for (int ct = 0; ct < nct; ++ct) {
+    const int crow = std::min(32 * ct + l32, C - 1);
+    const uint16_t* pr = pg + (int64_t)crow * 3 * D + 8 * hf;
+    f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      bf16x8 a[NS];
+#pragma unroll
+      for (int s4 = 0; s4 < NS; ++s4) a[s4] = as_bf16x8(ldg16(pr + part * D + 16 * s4));
+#pragma unroll
+      for (int s4 = 0; s4 < NS; ++s4)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma32x32x16(a[s4], xb[kt][s4], acc[kt]);
+    }
+    float nr[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) nr[r] = ng[std::min(32 * ct + 8 * (r / 4) + 4 * hf + (r % 4), C - 1)];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int c = 32 * ct + 8 * (r / 4) + 4 * hf + (r % 4);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        const float dist = fmaf(-2.f, acc[kt][r], nr[r]);
+        if (c < C && dist < best[kt]) {
+          best[kt] = dist;
+          arg[kt] = c;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+    const float ob = __shfl_xor(best[kt], 32);
+    const int oa = __shfl_xor(arg[kt], 32);
+    if (ob < best[kt] || (ob == best[kt] && oa < arg[kt])) arg[kt] = oa;
+    const int64_t key = k0 + 32 * kt + l32;
+    if (hf == 0 && key < n) labels[(int64_t)g * n + key] = arg[kt];
+  }
+}
+
 // One workgroup per (KV head, cluster), one thread per dimension.
 template <typename T, int D>
 __global__ __launch_bounds__(D) void k_km_update(const T* __restrict__ keys, const int32_t* __restrict__ ptr,
@@ -129,36 +235,51 @@ __global__ __launch_bounds__(D) void k_km_update(const T* __restrict__ keys, con
 
 }  // namespace
 
-size_t kmeans_workspace_bytes(int64_t hkv, int64_t n, int C) {
-  return cluster_pack_workspace_bytes(hkv, n, C);
+// pack workspace, then (bf16 keys) the centroid parts and squared norms
+size_t kmeans_workspace_bytes(int64_t hkv, int64_t n, int C, int head_dim) {
+  return km_a256(cluster_pack_workspace_bytes(hkv, n, C)) + km_a256((size_t)(hkv * C) * 3 * head_dim * 2) +
+         km_a256((size_t)(hkv * C) * 4);
 }
 
 hipError_t launch_kmeans(const void* keys, bool bf16, int64_t hkv, int64_t n, int head_dim, int C, int iters,
                          float* cent, int32_t* labels, int32_t* ptr, int32_t* perm, void* ws, hipStream_t stream) {
   if (hkv == 0 || n == 0) return hipSuccess;
   const dim3 ga((unsigned)(hkv * ((n + kKmKeys - 1) / kKmKeys)));
+  const dim3 gm((unsigned)(hkv * ((n + kKmWaves * kKmKeysPerWave - 1) / (kKmWaves * kKmKeysPerWave))));
   const dim3 gu((unsigned)(hkv * C));
+  char* wsb = static_cast<char*>(ws);
+  void* pack_ws = wsb;
+  uint16_t* parts = reinterpret_cast<uint16_t*>(wsb + km_a256(cluster_pack_workspace_bytes(hkv, n, C)));
+  float* nrm = reinterpret_cast<float*>(reinterpret_cast<char*>(parts) + km_a256((size_t)(hkv * C) * 3 * head_dim * 2));
   for (int it = 0; it < iters; ++it) {
-#define SA_KM_STEP(T_, D_)                                                                                        \
-  hipLaunchKernelGGL((k_km_assign<T_, D_>), ga, dim3(kKmKeys), 0, stream, (const T_*)keys, cent, n, C, labels); \
+#define SA_KM_ASSIGN_F32(D_) \
+  hipLaunchKernelGGL((k_km_assign<float, D_>), ga, dim3(kKmKeys), 0, stream, (const float*)keys, cent, n, C, labels);
+#define SA_KM_ASSIGN_BF16(D_)                                                                                     \
+  hipLaunchKernelGGL((k_km_split<D_>), dim3((unsigned)(hkv * C)), dim3(D_), 0, stream, cent, C, parts, nrm);     \
+  hipLaunchKernelGGL((k_km_assign_mfma<D_>), gm, dim3(64 * kKmWaves), 0, stream, (const uint16_t*)keys, parts, nrm, \
+                     n, C, labels);
+#define SA_KM_STEP(T_, D_, ASSIGN)                                                                                \
+  ASSIGN                                                                                                          \
   {                                                                                                               \
     const hipError_t e = launch_cluster_pack(labels, hkv, n, C, ptr, perm, nullptr, nullptr, nullptr, nullptr,   \
-                                             head_dim, 0, nullptr, ws, stream);                                   \
+                                             head_dim, 0, nullptr, pack_ws, stream);                              \
     if (e != hipSuccess) return e;                                                                                \
   }                                                                                                               \
   hipLaunchKernelGGL((k_km_update<T_, D_>), gu, dim3(D_), 0, stream, (const T_*)keys, ptr, perm, n, C, cent);
     if (bf16 && head_dim == 128) {
-      SA_KM_STEP(uint16_t, 128)
+      SA_KM_STEP(uint16_t, 128, SA_KM_ASSIGN_BF16(128))
     } else if (bf16 && head_dim == 64) {
-      SA_KM_STEP(uint16_t, 64)
+      SA_KM_STEP(uint16_t, 64, SA_KM_ASSIGN_BF16(64))
     } else if (!bf16 && head_dim == 128) {
-      SA_KM_STEP(float, 128)
+      SA_KM_STEP(float, 128, SA_KM_ASSIGN_F32(128))
     } else if (!bf16 && head_dim == 64) {
-      SA_KM_STEP(float, 64)
+      SA_KM_STEP(float, 64, SA_KM_ASSIGN_F32(64))
     } else {
       return hipErrorInvalidValue;
     }
 #undef SA_KM_STEP
+#undef SA_KM_ASSIGN_F32
+#undef SA_KM_ASSIGN_BF16
   }
   return hipGetLastError();
 }

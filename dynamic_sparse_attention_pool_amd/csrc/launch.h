@@ -168,7 +168,7 @@ hipError_t launch_cluster_pack(const int32_t* labels, int64_t hkv, int64_t n, in
                                int head_dim, int elem_bytes, int32_t* err, void* ws, hipStream_t stream);
 
 // ---------------------------------------------------------------- offline k-means
-size_t kmeans_workspace_bytes(int64_t hkv, int64_t n, int C);
+size_t kmeans_workspace_bytes(int64_t hkv, int64_t n, int C, int head_dim);
 hipError_t launch_kmeans(const void* keys, bool bf16, int64_t hkv, int64_t n, int head_dim, int C, int iters,
                          float* cent, int32_t* labels, int32_t* ptr, int32_t* perm, void* ws, hipStream_t stream);
 

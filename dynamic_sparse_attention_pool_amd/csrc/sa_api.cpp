@@ -578,7 +578,7 @@ static int check_kmeans(const sa_kmeans_args* a, size_t* ws) {
   if (a->n_clusters < 1 || a->n_clusters > 4096) return fail(SA_ERR_SHAPE, "sa_kmeans: n_clusters must lie in [1, 4096]");
   if (a->heads_kv * a->n_clusters > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_kmeans: too many clusters");
   if (a->iters < 1) return fail(SA_ERR_VALUE, "sa_kmeans: iters must be >= 1");
-  *ws = sa::kmeans_workspace_bytes(a->heads_kv, a->n_ctx, a->n_clusters);
+  *ws = sa::kmeans_workspace_bytes(a->heads_kv, a->n_ctx, a->n_clusters, (int)a->head_dim);
   if (!a->cluster_ptr)
     *ws += align256((size_t)(a->heads_kv * (a->n_clusters + 1)) * 4) + align256((size_t)(a->heads_kv * a->n_ctx) * 4);
   return ok();
@@ -601,7 +601,7 @@ int sa_kmeans(const sa_kmeans_args* a, void* workspace, size_t workspace_bytes, 
   if (!aligned16(workspace)) return fail(SA_ERR_ALIGN, "sa_kmeans: workspace must be 16-byte aligned");
   char* w = static_cast<char*>(workspace);
   void* pack_ws = w;
-  w += align256(sa::kmeans_workspace_bytes(a->heads_kv, a->n_ctx, a->n_clusters));
+  w += align256(sa::kmeans_workspace_bytes(a->heads_kv, a->n_ctx, a->n_clusters, (int)a->head_dim));
   int32_t* ptr = a->cluster_ptr;
   int32_t* perm = a->perm;
   if (!ptr) {

@@ -1,10 +1,12 @@
 """GPU parity of the offline k-means (sa_kmeans) against the CPU oracle.
 
 Labels are integers decided by floating point (fp32 |mu|^2 - 2 k.mu on the GPU,
-fp64 distances in the oracle).  A 128-term fp32 dot product and norm carry at
-most about 128 * 2^-24 relative error on sums whose size is bounded by
-|k|^2 + |mu|^2, so MARGIN_REL = 2e-5 of that scale bounds the GPU's distance
-error.  Keys whose oracle margin (second-nearest minus nearest squared
+fp64 distances in the oracle).  For fp32 keys the dot product is 128 fp32
+FMAs; for bf16 keys it is 3 x 128 exact products (the centroid split into
+three bf16 parts, which sum to it within about 2^-26) accumulated in fp32,
+at most 384 * 2^-24 |k||mu| <= 1.2e-5 (|k|^2 + |mu|^2); the 128-term norm
+adds at most 7.6e-6 |mu|^2.  So MARGIN_REL = 2e-5 of |k|^2 + |mu|^2 bounds
+the GPU's distance error.  Keys whose oracle margin (second-nearest minus nearest squared
 distance) exceeds it must get the oracle's label; any other key may take a
 centroid whose oracle distance is within that tolerance of the nearest.
 Several iterations are compared only on trajectories where every key of every
