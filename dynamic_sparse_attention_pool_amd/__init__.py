@@ -173,9 +173,11 @@ def sa_estimate_topk(q, k, idx, cnt, *, n_sink: int = 0, n_local: int = 0, k_fix
     return workspace
 
 
-def sa_estimate_topk_centroid(q, centroids, sel, cnt, *, k: int, scale=None, err_flag=None):
+def sa_estimate_topk_centroid(q, centroids, sel, cnt, *, k: int, scale=None, err_flag=None, mass=None,
+                              k_min: int = 0):
     """Centroid scores and top-k clusters in one call: q [T,Hq,d],
-    centroids [Hkv,C,d] float; sel [T,Hq,kmax], cnt [T,Hq] int32."""
+    centroids [Hkv,C,d] float; sel [T,Hq,kmax], cnt [T,Hq] int32.  With
+    ``mass``, the adaptive budget of sa_select_mass (k_min .. k clusters)."""
     lib = load()
     a = F.EstimateTopkArgs()
     T, Hq, d = q.shape
@@ -186,6 +188,8 @@ def sa_estimate_topk_centroid(q, centroids, sel, cnt, *, k: int, scale=None, err
     a.k, a.kmax = k, sel.shape[-1]
     a.q, a.k_ptr = _p(q), _p(centroids)
     a.idx, a.cnt, a.err_flag = _p(sel), _p(cnt), _p(err_flag)
+    if mass is not None:
+        a.mass, a.k_min = mass, k_min
     F.check(lib.sa_estimate_topk(C.byref(a), None, 0, _stream()))
 
 

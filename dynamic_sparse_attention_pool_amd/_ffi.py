@@ -17,7 +17,7 @@ SA_F32, SA_BF16, SA_I32 = 0, 1, 2
 SA_EST_BLOCK_MEANPOOL, SA_EST_VSLASH, SA_EST_CENTROID, SA_EST_INDEXER = 0, 1, 2, 3
 SA_FWD_BLOCK, SA_FWD_VSLASH, SA_FWD_ASHAPE = 0, 1, 2
 SA_GATHER_CLUSTER, SA_GATHER_TOKEN = 0, 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
                 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_LAUNCH", 8: "SA_ERR_VALUE"}
@@ -92,7 +92,8 @@ class EstimateTopkArgs(C.Structure):
                 ("scale", C.c_float), ("n_sink", C.c_int32), ("n_local", C.c_int32), ("k", C.c_int32),
                 ("ratio_num", C.c_int32), ("ratio_den", C.c_int32), ("kmax", C.c_int32), ("q", P), ("k_ptr", P),
                 ("pooled_q", P), ("pooled_k", P), ("head_list", P), ("n_heads_list", C.c_int32),
-                ("n_centroids", C.c_int32), ("idx", P), ("cnt", P), ("err_flag", P)]
+                ("n_centroids", C.c_int32), ("idx", P), ("cnt", P), ("err_flag", P), ("mass", C.c_float),
+                ("k_min", C.c_int32)]
 
 
 class IndexerTopkArgs(C.Structure):

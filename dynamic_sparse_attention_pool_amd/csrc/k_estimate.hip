@@ -8,6 +8,7 @@
 // cluster centroid, the centroids being held in on-chip shared memory.
 #include "common.h"
 #include "launch.h"
+#include "select_util.h"
 
 namespace sa {
 namespace {
@@ -275,11 +276,15 @@ constexpr int kCtThreads = 256;
 constexpr int kCtMaxRows = 8;
 constexpr int kCtMaxC = 1024;
 
-template <typename T>
+// MASS: one row per workgroup; instead of the fixed top-k, the adaptive
+// budget of sa_select_mass (mass_select_lds) on the row's keys, with k as the
+// upper clamp.
+template <typename T, bool MASS>
 __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restrict__ q, const float* __restrict__ cent,
                                                               int hq, int hkv, int C, int D, float scale, int k,
-                                                              int kmax, int nsub, int32_t* __restrict__ idx,
-                                                              int32_t* __restrict__ cnt, int32_t* err) {
+                                                              int kmax, int nsub, float mass, int k_min,
+                                                              int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+                                                              int32_t* err) {
   __shared__ float qs[kCtMaxRows][128];
   __shared__ uint32_t keys[kCtMaxRows][kCtMaxC];
   __shared__ uint32_t hist[kCtMaxRows][256];
@@ -340,6 +345,23 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
       }
   }
   if (nan_seen) atomicOr(&s_nan, 1u);
+  if constexpr (MASS) {
+    // one row: (key << 32 | ~index) pairs, padded to a power of two, then the adaptive budget
+    __shared__ uint64_t kv[kCtMaxC];
+    __shared__ uint32_t bm[kCtMaxC / 32];
+    __shared__ uint64_t wtmp[kCtThreads / 64];
+    __shared__ uint32_t utmp[kCtThreads / 64];
+    __syncthreads();
+    int P = 64;
+    while (P < C) P <<= 1;
+    for (int c = tid; c < P; c += kCtThreads)
+      kv[c] = c < C ? (((uint64_t)keys[0][c] << 32) | (uint64_t)(~(uint32_t)c)) : 0ull;
+    __syncthreads();
+    const int64_t row = (int64_t)t * hq + h0;
+    mass_select_lds<kCtThreads>(kv, bm, wtmp, utmp, C, P, mass, k_min, k, idx + row * kmax, kmax, cnt + row);
+    if (tid == 0 && s_nan && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
+    return;
+  }
   // ---- radix select: T[hh] = the kr-th largest key of row hh
   uint32_t Tk[kCtMaxRows];
 #pragma unroll
@@ -454,19 +476,24 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
 }  // namespace
 
 hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv, int C,
-                                int head_dim, float scale, int k, int kmax, int32_t* idx, int32_t* cnt, int32_t* err,
-                                hipStream_t stream) {
+                                int head_dim, float scale, int k, int kmax, float mass, int k_min, int32_t* idx,
+                                int32_t* cnt, int32_t* err, hipStream_t stream) {
   if (T == 0) return hipSuccess;
   // one query head per workgroup: four times the workgroups of one per KV head,
   // so the centroid rows' loads spread over more CUs
   const int nsub = hq / hkv;
   const dim3 grid((unsigned)(T * hkv * nsub));
-  if (q_bf16)
-    hipLaunchKernelGGL((k_centroid_topk<uint16_t>), grid, dim3(kCtThreads), 0, stream, (const uint16_t*)q, cent, hq,
-                       hkv, C, head_dim, scale, k, kmax, nsub, idx, cnt, err);
-  else
-    hipLaunchKernelGGL((k_centroid_topk<float>), grid, dim3(kCtThreads), 0, stream, (const float*)q, cent, hq, hkv,
-                       C, head_dim, scale, k, kmax, nsub, idx, cnt, err);
+#define SA_CT_LAUNCH(TQ, M)                                                                                 \
+  hipLaunchKernelGGL((k_centroid_topk<TQ, M>), grid, dim3(kCtThreads), 0, stream, (const TQ*)q, cent, hq, hkv, C, \
+                     head_dim, scale, k, kmax, nsub, mass, k_min, idx, cnt, err)
+  if (q_bf16) {
+    if (mass > 0.f) SA_CT_LAUNCH(uint16_t, true);
+    else SA_CT_LAUNCH(uint16_t, false);
+  } else {
+    if (mass > 0.f) SA_CT_LAUNCH(float, true);
+    else SA_CT_LAUNCH(float, false);
+  }
+#undef SA_CT_LAUNCH
   return hipGetLastError();
 }
 

@@ -509,28 +509,14 @@ __global__ __launch_bounds__(256) void k_select_small(SelectParams p) {
 // thread layout; the comparison with mass * total is made in double.
 constexpr int kMassNT = 256;
 
-__device__ __forceinline__ float key_float(uint32_t k) {
-  return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
-}
-
-__device__ __forceinline__ uint64_t wave_incl_scan_u64(uint64_t v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t x = __shfl_up(v, off);
-    if (lane >= off) v += x;
-  }
-  return v;
-}
-
 __global__ __launch_bounds__(kMassNT) void k_select_mass(MassParams p) {
-  constexpr int NT = kMassNT, NW = NT / 64;
+  constexpr int NT = kMassNT;
   __shared__ uint64_t kv[kMassMax];
   __shared__ uint32_t bm[kMassMax / 32];
-  __shared__ uint64_t wtmp[NW];
-  __shared__ uint32_t utmp[NW];
+  __shared__ uint64_t wtmp[NT / 64];
+  __shared__ uint32_t utmp[NT / 64];
   __shared__ uint32_t shnan;
-  const int tid = threadIdx.x, wv = tid >> 6;
+  const int tid = threadIdx.x;
   const int64_t r = blockIdx.x;
   const float* row = p.scores + r * p.ld;
   const int n = (int)p.ncand;
@@ -546,77 +532,11 @@ __global__ __launch_bounds__(kMassNT) void k_select_mass(MassParams p) {
     }
     kv[i] = e;
   }
-  const int nw = (n + 31) >> 5;
-  for (int w = tid; w < nw; w += NT) bm[w] = 0u;
   if (tid == 0) shnan = 0u;
   __syncthreads();
   if (nan_seen) atomicOr(&shnan, 1u);
-  // bitonic network, descending: runs of length kk alternate direction until the last merge
-  for (int kk = 2; kk <= P; kk <<= 1) {
-    for (int j = kk >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < P / 2; i += NT) {
-        const int lo = ((i & ~(j - 1)) << 1) | (i & (j - 1)), hi = lo + j;
-        const uint64_t a = kv[lo], b = kv[hi];
-        if ((a < b) == ((lo & kk) == 0)) {
-          kv[lo] = b;
-          kv[hi] = a;
-        }
-      }
-      __syncthreads();
-    }
-  }
-  // weights along the sorted order: thread t owns positions [t*E, t*E + E)
-  const float m = key_float((uint32_t)(kv[0] >> 32));
-  const int E = P >= NT ? P / NT : 1;
-  const int j0 = tid * E, j1 = min(n, j0 + E);
-  auto weight = [&](int j) -> uint64_t {  // in units of 2^-40
-    const float s = key_float((uint32_t)(kv[j] >> 32));
-    const float w = s == m ? 1.f : expf(s - m);
-    return __double2ull_rn((double)w * 1099511627776.0);
-  };
-  uint64_t part = 0ull;
-  for (int j = j0; j < j1; ++j) part += weight(j);
-  const uint64_t incl = wave_incl_scan_u64(part);
-  if ((tid & 63) == 63) wtmp[wv] = incl;
-  __syncthreads();
-  uint64_t ahead = incl - part, total = 0ull;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const uint64_t x = wtmp[w];
-    ahead += w < wv ? x : 0ull;
-    total += x;
-  }
-  const double thr = (double)p.mass * (double)total;
-  uint32_t kept_here = 0u;
-  for (int j = j0; j < j1; ++j) {
-    kept_here += (double)ahead < thr ? 1u : 0u;
-    ahead += weight(j);
-  }
-  uint32_t c_raw;
-  block_excl_scan<NT>(kept_here, utmp, c_raw);
-  int c = max((int)c_raw, p.k_min);
-  c = min(c, min(p.k_max, n));
-  for (int j = tid; j < c; j += NT) {
-    const uint32_t i = ~(uint32_t)kv[j];
-    atomicOr(&bm[i >> 5], 1u << (i & 31u));
-  }
-  __syncthreads();
-  // emission in index order: thread t owns bitmap word t (nw <= 128 < NT)
-  const uint32_t word = tid < nw ? bm[tid] : 0u;
-  uint32_t tot;
-  uint32_t at = block_excl_scan<NT>((uint32_t)__popc(word), utmp, tot);
-  int32_t* out = p.idx + r * p.kmax;
-  uint32_t bits = word;
-  while (bits) {
-    const int b = __builtin_ctz(bits);
-    bits &= bits - 1u;
-    out[at++] = 32 * tid + b;
-  }
-  for (int j = c + tid; j < p.kmax; j += NT) out[j] = -1;
-  if (tid == 0) {
-    p.cnt[r] = c;
-    if (shnan && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
-  }
+  mass_select_lds<NT>(kv, bm, wtmp, utmp, n, P, p.mass, p.k_min, p.k_max, p.idx + r * p.kmax, p.kmax, p.cnt + r);
+  if (tid == 0 && shnan && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
 }
 
 // ---------------------------------------------------------------- vertical-slash tables

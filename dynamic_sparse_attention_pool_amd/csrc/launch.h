@@ -64,8 +64,8 @@ hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, 
 // centroid scores and a per-row top-k in one pass (query heads per KV head <= 8,
 // clusters <= 1024, head_dim <= 128)
 hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv, int C,
-                                int head_dim, float scale, int k, int kmax, int32_t* idx, int32_t* cnt, int32_t* err,
-                                hipStream_t stream);
+                                int head_dim, float scale, int k, int kmax, float mass, int k_min, int32_t* idx,
+                                int32_t* cnt, int32_t* err, hipStream_t stream);
 hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
                           int64_t pos0, float* out, hipStream_t stream);
 // Candidate slots of chunk c (keys c*chunk ..) of an indexer row with n causal

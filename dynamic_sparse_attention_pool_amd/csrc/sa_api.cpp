@@ -342,6 +342,10 @@ static int check_centroid_topk(const sa_estimate_topk_args* a) {
   if (a->seq * a->heads_kv > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): too many queries");
   if (!(a->scale > 0.f)) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): scale must be > 0");
   if (a->k < 0) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): k must be >= 0");
+  if (a->mass != 0.f) {
+    if (!(a->mass > 0.f && a->mass <= 1.f)) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): mass must lie in (0, 1]");
+    if (a->k_min < 0 || a->k_min > a->k) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): need 0 <= k_min <= k");
+  }
   const int32_t need = a->k < a->n_centroids ? a->k : a->n_centroids;
   if (a->kmax <= 0 || a->kmax < need) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): kmax %d is below min(k, C) = %d", a->kmax, need);
   return ok();
@@ -413,7 +417,8 @@ int sa_estimate_topk(const sa_estimate_topk_args* a, void* workspace, size_t wor
   if (a->kind == SA_EST_CENTROID)
     return launched(sa::launch_centroid_topk(a->q, a->dtype == SA_BF16, static_cast<const float*>(a->k_ptr), (int)a->seq,
                                              (int)a->heads_q, (int)a->heads_kv, a->n_centroids, (int)a->head_dim,
-                                             a->scale, a->k, a->kmax, a->idx, a->cnt, a->err_flag, st),
+                                             a->scale, a->k, a->kmax, a->mass, a->k_min, a->idx, a->cnt, a->err_flag,
+                                             st),
                     "sa_estimate_topk(CENTROID)");
   const int64_t nb = a->seq / kBlock;
   const int64_t nh = hl.n > 0 ? hl.n : a->heads_q;

@@ -229,8 +229,8 @@ class ClusterDecode:
                  scale=None, with_lse=False, fused=False):
         """n_sel clusters per query head, or, with ``mass`` set, the fewest
         clusters holding that share of the softmax of the centroid scores,
-        between k_min and n_sel (sa_select_mass).  ``fused`` (fixed n_sel
-        only): scores and top clusters in one call, ``estimate`` doing both."""
+        between k_min and n_sel (sa_select_mass).  ``fused``: scores and the
+        selection in one call, ``estimate`` doing both."""
         torch = _t()
         T, Hq, d = q.shape
         Hkv, N, _ = k.shape
@@ -238,8 +238,6 @@ class ClusterDecode:
         dev = q.device
         self.q, self.centroids, self.C, self.n_sel = q, centroids, C, n_sel
         self.mass, self.k_min = mass, k_min
-        if fused and mass is not None:
-            raise ValueError("the fused centroid top-k takes a fixed number of clusters")
         self.fused = fused
         self.scale = 1.0 / math.sqrt(d) if scale is None else scale
         self.ptr = torch.empty((Hkv, C + 1), dtype=torch.int32, device=dev)
@@ -259,7 +257,8 @@ class ClusterDecode:
     def estimate(self):
         if self.fused:
             sa_estimate_topk_centroid(self.q, self.centroids, self.sel, self.sel_cnt.view(self.sel.shape[0], -1),
-                                      k=self.n_sel, scale=self.scale)
+                                      k=self.n_sel, scale=self.scale, mass=self.mass, k_min=self.k_min,
+                                      err_flag=self.err)
             return
         sa_estimate(CENTROID, self.q, self.k, self.scores, centroids=self.centroids, scale=self.scale)
 

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 7
+#define SA_ABI_VERSION 8
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -246,6 +246,9 @@ int sa_select_mass(const sa_select_mass_args* args, void* stream);
  * the same arithmetic).  q [T,Hq,d] (F32 or BF16; seq = T), k_ptr = the
  * centroid table [Hkv,C,d] float, n_centroids = C <= 1024, d <= 128, at most 8
  * query heads per KV head.  idx [T,Hq,kmax], cnt [T,Hq]; kmax >= min(k, C).
+ * With mass > 0 (the adaptive budget, Squeezed Attention page, §技术方案),
+ * the selection is sa_select_mass's instead, with k_max = k and k_min, bit for
+ * bit: 0 < mass <= 1, 0 <= k_min <= k.
  * No workspace; head lists, ratios and forced members are not supported.
  *
  * err_flag: as in sa_select_topk.
@@ -276,6 +279,8 @@ typedef struct sa_estimate_topk_args {
   int32_t* idx;
   int32_t* cnt;
   int32_t* err_flag;
+  float mass;             /* CENTROID: > 0 selects the adaptive budget */
+  int32_t k_min;          /* CENTROID with mass */
 } sa_estimate_topk_args;
 
 int sa_estimate_topk_workspace_bytes(const sa_estimate_topk_args* args, size_t* bytes);

@@ -228,6 +228,13 @@ def test_estimate_topk_argument_errors(lib):
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 6
     c.heads_q, c.n_sink = 32, 1
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 6
+    c.n_sink, c.mass, c.k_min = 0, 0.5, 1                                        # adaptive budget
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 0 and n.value == 0
+    c.mass = 1.5
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 8
+    c.mass, c.k_min = 0.5, 65                                                   # above k
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 8
+    c.mass, c.k_min = 0.0, 0
     a.kind = F.SA_EST_BLOCK_MEANPOOL
     a.n_local = -1
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(a), C.byref(n)) == 8

@@ -117,10 +117,45 @@ def mass_certified(s, mass, k_min, k_max, gap_rel=1e-3):
     return oracle.certified_row(s, c, np.zeros(0, np.int64), gap_rel)
 
 
-def test_adaptive_decode_full_size_certified(sa):
+@pytest.mark.parametrize("T,Hq,Hkv,C,d,k_min,k_max,mass,dt", [(3, 8, 2, 256, 128, 1, 64, 0.5, "bf16"),
+                                                                (2, 4, 4, 100, 64, 0, 100, 0.9, "f32"),
+                                                                (2, 16, 2, 1024, 128, 3, 200, 0.2, "bf16"),
+                                                                (1, 8, 1, 37, 128, 37, 37, 0.5, "bf16")])
+def test_fused_centroid_mass_matches_separate_path_and_oracle(sa, T, Hq, Hkv, C, d, k_min, k_max, mass, dt):
+    """sa_estimate_topk(CENTROID) with a mass: the same clusters and counts as
+    sa_estimate(CENTROID) + sa_select_mass, bit for bit (same score
+    arithmetic), and the oracle's counts and sets up to the margin."""
+    t = torch()
+    r = np.random.default_rng(95 + C)
+    qf = r.standard_normal((T, Hq, d)).astype(np.float32)
+    cent = (r.standard_normal((Hkv, C, d)) * 0.7).astype(np.float32)
+    q = dev_bf16(W.f32_to_bf16(qf)) if dt == "bf16" else dev_f32(qf)
+    qh = W.bf16_to_f32(W.f32_to_bf16(qf)) if dt == "bf16" else qf
+    scale = 1 / math.sqrt(d)
+    kmax = min(k_max, C)
+    sel = t.full((T, Hq, kmax), 9, dtype=t.int32, device="cuda:0")
+    cnt = t.full((T, Hq), -3, dtype=t.int32, device="cuda:0")
+    err = t.zeros(1, dtype=t.int32, device="cuda:0")
+    sa.sa_estimate_topk_centroid(q, dev_f32(cent), sel, cnt, k=k_max, scale=scale, mass=mass, k_min=k_min,
+                                 err_flag=err)
+    scores = t.empty((T, Hq, C), dtype=t.float32, device="cuda:0")
+    sa.sa_estimate(sa.CENTROID, q, q, scores, centroids=dev_f32(cent), scale=scale)
+    sel2 = t.full((T * Hq, kmax), 9, dtype=t.int32, device="cuda:0")
+    cnt2 = t.full((T * Hq,), -3, dtype=t.int32, device="cuda:0")
+    sa.sa_select_mass(scores.view(-1, C), sel2, cnt2, mass=mass, k_min=k_min, k_max=k_max)
+    t.cuda.synchronize()
+    assert int(host(err)[0]) == 0
+    assert np.array_equal(host(sel).reshape(T * Hq, kmax), host(sel2)) and np.array_equal(host(cnt).ravel(), host(cnt2))
+    s = oracle.centroid_scores(qh, cent, scale).reshape(T * Hq, C)
+    check_rows(s, host(sel).reshape(T * Hq, kmax), host(cnt).ravel(), mass, k_min, k_max)
+
+
+@pytest.mark.parametrize("fused", [False, True])
+def test_adaptive_decode_full_size_certified(sa, fused):
     """8 queries x 32/8 heads over 65536 clustered keys, 256 centroids: the
     clusters holding half of the softmax weight of the centroid scores, at
-    least 1 and at most 64, then the gathered attention over them."""
+    least 1 and at most 64, then the gathered attention over them (scores and
+    selection as two calls, or in one)."""
     from dynamic_sparse_attention_pool_amd.pipelines import ClusterDecode
     seed = W.CONFIG_SEEDS[4]
     T, Hq, Hkv, N, d, C, kcap, mass = 8, 32, 8, 65536, 128, 256, 64, 0.5
@@ -136,7 +171,7 @@ def test_adaptive_decode_full_size_certified(sa):
                 assert a < 200
                 inp.q[t, h] = W.redraw_decode_query(seed, t, h, 1000 + a, d)
     dc = ClusterDecode(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), dev_i32(inp.labels),
-                       dev_f32(inp.centroids), n_sel=kcap, mass=mass, k_min=1, with_lse=True)
+                       dev_f32(inp.centroids), n_sel=kcap, mass=mass, k_min=1, with_lse=True, fused=fused)
     dc.step()
     torch().cuda.synchronize()
     s = oracle.centroid_scores(W.bf16_to_f32(inp.q), inp.centroids, scale)
