@@ -231,23 +231,45 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
   const int nq = p.T * grp;
   const int64_t N = p.n_ctx;
   const int C = p.C;
-  for (int c = threadIdx.x; c <= C; c += blockDim.x) ptr_s[c] = p.cluster_ptr[(int64_t)g * (C + 1) + c];
-  for (int c = threadIdx.x; c < C; c += blockDim.x) mask_s[c] = 0ull;
-  __syncthreads();
+  // Set-up: the cluster pointers, the selected cluster ids and Q are all
+  // requested before the first of them is used, so the workgroup waits for one
+  // memory latency instead of one per loop trip.
+  constexpr int kNT = 64 * kDecWaves;
+  constexpr int kPtrPer = (kDecMaxC + kNT) / kNT;  // covers C + 1 <= kDecMaxC + 1 pointers
+  constexpr int kSelPer = 8;
+  for (int c = threadIdx.x; c < C; c += kNT) mask_s[c] = 0ull;
+  int32_t pv_[kPtrPer];
+#pragma unroll
+  for (int u = 0; u < kPtrPer; ++u) {
+    const int c = threadIdx.x + u * kNT;
+    pv_[u] = c <= C ? p.cluster_ptr[(int64_t)g * (C + 1) + c] : 0;
+  }
   // mask_s[c] bit j <=> query j of this KV head (token t, head-in-group hh: j = t*grp + hh)
   // selected cluster c; duplicate and out-of-range ids fall out naturally
-  for (int e = threadIdx.x; e < nq * p.n_sel; e += blockDim.x) {
-    const int qi = e / p.n_sel, sidx = e % p.n_sel;
-    const int t = qi / grp, hh = qi % grp;
-    const int c = p.sel[((int64_t)t * p.hq + g * grp + hh) * p.n_sel + sidx];
-    if (c >= 0 && c < C) atomicOr(reinterpret_cast<unsigned long long*>(&mask_s[c]), 1ull << qi);
-  }
-  const uint16_t* kb = p.k + (int64_t)g * N * kD;
-  const uint16_t* vb = p.v + (int64_t)g * N * kD;
-  const int64_t p0 = (int64_t)split * kRowsPerSplit;
-  const int64_t p1 = min(N, p0 + kRowsPerSplit);
-  const int ntile = (int)((p1 - p0 + kDecRows - 1) / kDecRows);
-  const float sl2 = p.scale * kLog2e;
+  const int nsel_all = nq * p.n_sel;
+  auto sel_load = [&](int e0, int32_t* cv) {
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+      const int e = e0 + u * kNT;
+      cv[u] = -1;
+      if (e < nsel_all) {
+        const int qi = e / p.n_sel, sidx = e % p.n_sel;
+        const int t = qi / grp, hh = qi % grp;
+        cv[u] = p.sel[((int64_t)t * p.hq + g * grp + hh) * p.n_sel + sidx];
+      }
+    }
+  };
+  auto sel_mark = [&](int e0, const int32_t* cv) {
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) {
+      const int e = e0 + u * kNT;
+      const int c = cv[u];
+      if (e < nsel_all && c >= 0 && c < C)
+        atomicOr(reinterpret_cast<unsigned long long*>(&mask_s[c]), 1ull << (e / p.n_sel));
+    }
+  };
+  int32_t cv0[kSelPer];
+  sel_load(threadIdx.x, cv0);
 
   // Q^T: lane holds query 32nt+l32, dims 16s + 8hf .. +7 at step s
   bf16x8 qv[NQT][8];
@@ -259,6 +281,24 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
 #pragma unroll
     for (int s = 0; s < 8; ++s) qv[nt][s] = as_bf16x8(ldg16(qr + 16 * s));
   }
+#pragma unroll
+  for (int u = 0; u < kPtrPer; ++u) {
+    const int c = threadIdx.x + u * kNT;
+    if (c <= C) ptr_s[c] = pv_[u];
+  }
+  __syncthreads();  // mask_s cleared, ptr_s complete
+  sel_mark(threadIdx.x, cv0);
+  for (int e0 = threadIdx.x + kSelPer * kNT; e0 < nsel_all; e0 += kSelPer * kNT) {
+    int32_t cv[kSelPer];
+    sel_load(e0, cv);
+    sel_mark(e0, cv);
+  }
+  const uint16_t* kb = p.k + (int64_t)g * N * kD;
+  const uint16_t* vb = p.v + (int64_t)g * N * kD;
+  const int64_t p0 = (int64_t)split * kRowsPerSplit;
+  const int64_t p1 = min(N, p0 + kRowsPerSplit);
+  const int ntile = (int)((p1 - p0 + kDecRows - 1) / kDecRows);
+  const float sl2 = p.scale * kLog2e;
   __syncthreads();
 
   f32x16 o[NQT][4];
