@@ -439,6 +439,137 @@ __global__ __launch_bounds__(NT) void k_select_long(SelectParams p) {
   if (tid == 0) p.cnt[r] = (int32_t)total;
 }
 
+// Rows of 257 .. 2048 candidates (block-sparse rows up to 128K tokens): one
+// wave per row and no workgroup barriers.  Lane l keeps candidates 64u + l of
+// the row as keys in registers (all loads in flight together); a radix select
+// over a per-wave LDS histogram (8-bit digits, lane l owning digits
+// 255-4l .. 252-4l) finds the k-th pool key T and the number of keys equal to
+// T that are taken; the emission walks the row in chunks of 64 in index order
+// and places every kept candidate with two ballots.  Same result as k_select.
+constexpr int kSwWaves = 4;
+constexpr int kSwPer = 32;  // keys per lane
+constexpr int kSwMax = 64 * kSwPer;
+
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__global__ __launch_bounds__(64 * kSwWaves) void k_select_wave(SelectParams p) {
+  __shared__ uint32_t hist_s[kSwWaves][256];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t r = (int64_t)blockIdx.x * kSwWaves + wv;
+  if (r >= p.rows) return;  // the whole wave leaves; nothing below waits for other waves
+  uint32_t* hist = hist_s[wv];
+  const float* row = p.scores + r * p.ld;
+  const int n = (int)(p.causal ? min(p.ncand, (r % p.period) + p.offset + 1) : p.ncand);
+  const int pb = min(p.n_sink, n);
+  const int pe = max(pb, n - p.n_local);
+  const int npool = pe - pb;
+  int64_t kr64 = p.rden > 0 ? ((int64_t)p.rnum * n + p.rden - 1) / p.rden : (int64_t)p.k;
+  const int kr = (int)max((int64_t)0, min(kr64, (int64_t)npool));
+  const bool take_all = (kr == npool);
+
+  float f[kSwPer];
+#pragma unroll
+  for (int u = 0; u < kSwPer; ++u) {
+    const int i = 64 * u + lane;
+    f[u] = i < n ? row[i] : 0.f;
+  }
+  uint32_t key[kSwPer];
+  bool nan_seen = false;
+#pragma unroll
+  for (int u = 0; u < kSwPer; ++u) {
+    nan_seen |= (64 * u + lane < n) && is_nan(f[u]);
+    key[u] = order_key(f[u]);
+  }
+
+  uint32_t T = 0xffffffffu;
+  int need = 0;  // keys equal to T that are taken
+  if (kr > 0 && !take_all) {
+    uint32_t prefix = 0u, pmask = 0u;
+    uint32_t remaining = (uint32_t)kr;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      wave_lds_sync();
+#pragma unroll
+      for (int x = 0; x < 4; ++x) hist[4 * lane + x] = 0u;
+      wave_lds_sync();
+#pragma unroll
+      for (int u = 0; u < kSwPer; ++u) {
+        const int i = 64 * u + lane;
+        if (i >= pb && i < pe && (key[u] & pmask) == prefix) atomicAdd(&hist[(key[u] >> shift) & 255u], 1u);
+      }
+      wave_lds_sync();
+      uint32_t c[4], loc = 0u;
+#pragma unroll
+      for (int x = 0; x < 4; ++x) {
+        c[x] = hist[255 - 4 * lane - x];
+        loc += c[x];
+      }
+      const uint32_t incl = wave_incl_scan(loc);  // keys with a digit >= 252 - 4*lane
+      const uint32_t above = incl - loc;
+      const bool mine = above < remaining && remaining <= incl;
+      uint32_t dsel = 0u, gt = 0u;
+      if (mine) {
+        uint32_t acc = above;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+          if (acc + c[x] >= remaining) {
+            dsel = (uint32_t)(255 - 4 * lane - x);
+            gt = acc;
+            break;
+          }
+          acc += c[x];
+        }
+      }
+      const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+      dsel = (uint32_t)__shfl((int)dsel, src);
+      gt = (uint32_t)__shfl((int)gt, src);
+      remaining -= gt;
+      prefix |= dsel << shift;
+      pmask |= 255u << shift;
+    }
+    T = prefix;
+    need = (int)remaining;
+  }
+
+  // ---- emission in index order
+  int32_t* out = p.idx + r * p.kmax;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t g_run = 0u, e_run = 0u;  // taken-for-sure and tie counts before this chunk
+#pragma unroll
+  for (int u = 0; u < kSwPer; ++u) {
+    const int i = 64 * u + lane;
+    bool tk = false, tie = false;
+    if (i < n) {
+      if (i < pb || i >= pe) tk = true;
+      else if (kr > 0) {
+        if (take_all) tk = true;
+        else {
+          tk = key[u] > T;
+          tie = key[u] == T;
+        }
+      }
+    }
+    const uint64_t bt = __ballot(tk), be = __ballot(tie);
+    const uint32_t gb = g_run + (uint32_t)__popcll(bt & below);
+    const uint32_t eb = e_run + (uint32_t)__popcll(be & below);
+    if (tk) out[gb + min(eb, (uint32_t)need)] = i;
+    else if (tie && eb < (uint32_t)need) out[gb + eb] = i;
+    g_run += (uint32_t)__popcll(bt);
+    e_run += (uint32_t)__popcll(be);
+  }
+  const int total = (int)g_run + min((int)e_run, need);
+  for (int j = total + lane; j < p.kmax; j += 64) out[j] = -1;
+  const bool any_nan = __any(nan_seen);
+  if (lane == 0) {
+    p.cnt[r] = total;
+    if (any_nan && p.err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(p.err), 1u);
+  }
+}
+
 // Rows of at most 256 candidates (cluster selection): one thread per
 // candidate computes its rank under the total order (higher score first, lower
 // index first on ties) by sweeping the row in LDS; candidates with rank < k are
@@ -667,6 +798,9 @@ hipError_t launch_select(const SelectParams& p, hipStream_t stream) {
   const dim3 grid((unsigned)p.rows);
   if (p.ncand <= 256)
     hipLaunchKernelGGL(k_select_small, grid, dim3(256), 0, stream, p);
+  else if (p.ncand <= kSwMax)
+    hipLaunchKernelGGL(k_select_wave, dim3((unsigned)((p.rows + kSwWaves - 1) / kSwWaves)), dim3(64 * kSwWaves), 0,
+                       stream, p);
   else if (p.ncand <= 4096)
     hipLaunchKernelGGL((k_select<256, true>), grid, dim3(256), 0, stream, p);
   else if (p.ncand <= kBmMax)

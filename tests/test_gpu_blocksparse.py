@@ -48,6 +48,10 @@ SELECT_CASES = [
     (8, 300, "normal", dict(k=0, n_sink=3), 3),
     (8, 300, "normal", dict(k=500, n_local=7), 300),
     (5, 4096, "ties", dict(k=1000), 1000),
+    # one wave per row (257..2048 candidates): a row count that leaves a partial workgroup
+    (7, 1000, "coarse", dict(k=37, n_sink=2, n_local=3), 42),
+    (13, 2000, "ties", dict(ratio=(7, 100), n_sink=1, n_local=2, causal=True, causal_period=13,
+                            causal_offset=1987), 143),
 ]
 
 
@@ -102,6 +106,10 @@ def test_select_ragged_long_rows_and_nan_flag(sa):
     assert err == 0 and all(np.array_equal(idx[r, :cnt[r]], want[r]) for r in range(3))
     s[1, 17] = np.nan
     _, _, err = gpu_select(sa, s, 300, k=300)
+    assert err == 1
+    s = W.score_rows(10, 5, 1500, "normal")     # one wave per row
+    s[3, 1499] = np.nan
+    _, _, err = gpu_select(sa, s, 64, k=60, n_local=4)
     assert err == 1
 
 
