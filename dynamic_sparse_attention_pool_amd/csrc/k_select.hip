@@ -456,7 +456,7 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__global__ __launch_bounds__(64 * kSwWaves) void k_select_wave(SelectParams p) {
+__global__ __launch_bounds__(64 * kSwWaves) __attribute__((amdgpu_waves_per_eu(7))) void k_select_wave(SelectParams p) {
   __shared__ uint32_t hist_s[kSwWaves][256];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t r = (int64_t)blockIdx.x * kSwWaves + wv;
@@ -471,19 +471,17 @@ __global__ __launch_bounds__(64 * kSwWaves) void k_select_wave(SelectParams p) {
   const int kr = (int)max((int64_t)0, min(kr64, (int64_t)npool));
   const bool take_all = (kr == npool);
 
-  float f[kSwPer];
+  // keys straight from the loads (no float copies kept: fewer registers, more
+  // waves per SIMD); a NaN's key lies outside [key(-inf), key(+inf)]
+  uint32_t key[kSwPer];
 #pragma unroll
   for (int u = 0; u < kSwPer; ++u) {
     const int i = 64 * u + lane;
-    f[u] = i < n ? row[i] : 0.f;
+    key[u] = order_key(i < n ? row[i] : 0.f);
   }
-  uint32_t key[kSwPer];
   bool nan_seen = false;
 #pragma unroll
-  for (int u = 0; u < kSwPer; ++u) {
-    nan_seen |= (64 * u + lane < n) && is_nan(f[u]);
-    key[u] = order_key(f[u]);
-  }
+  for (int u = 0; u < kSwPer; ++u) nan_seen |= (64 * u + lane < n) && (key[u] > 0xff800000u || key[u] < 0x007fffffu);
 
   uint32_t T = 0xffffffffu;
   int need = 0;  // keys equal to T that are taken
