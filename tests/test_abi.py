@@ -308,3 +308,20 @@ def test_estimate_and_gather_argument_errors(lib):
     g.mode = F.SA_GATHER_TOKEN
     g.tok_idx, g.n_tok, g.heads_kv = 256, 64, 4                       # 8 heads per KV head
     assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 6
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """No CPU fallback: without libsa.so every entry point raises."""
+    import numpy as np
+    import torch as tt
+
+    import dynamic_sparse_attention_pool_amd as sa
+    from dynamic_sparse_attention_pool_amd import _ffi
+    monkeypatch.setattr(_ffi, "LIB_PATH", "/nonexistent/libsa.so")
+    monkeypatch.setattr(_ffi, "_lib", None)
+    with pytest.raises(ImportError, match="no CPU fallback"):
+        _ffi.load()
+    s = tt.from_numpy(np.zeros((2, 8), np.float32))
+    idx, cnt = tt.zeros((2, 2), dtype=tt.int32), tt.zeros(2, dtype=tt.int32)
+    with pytest.raises(ImportError):
+        sa.sa_select_topk(s, idx, cnt, k=2)
