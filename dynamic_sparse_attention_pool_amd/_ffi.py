@@ -17,7 +17,7 @@ SA_F32, SA_BF16, SA_I32 = 0, 1, 2
 SA_EST_BLOCK_MEANPOOL, SA_EST_VSLASH, SA_EST_CENTROID, SA_EST_INDEXER = 0, 1, 2, 3
 SA_FWD_BLOCK, SA_FWD_VSLASH, SA_FWD_ASHAPE = 0, 1, 2
 SA_GATHER_CLUSTER, SA_GATHER_TOKEN = 0, 1
-ABI_VERSION = 8
+ABI_VERSION = 9
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
                 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_LAUNCH", 8: "SA_ERR_VALUE"}
@@ -33,7 +33,8 @@ class EstimateArgs(C.Structure):
                 ("n_centroids", C.c_int64), ("q_pos0", C.c_int64), ("block_size", C.c_int32),
                 ("last_q", C.c_int32), ("scale", C.c_float), ("reserved0", C.c_int32), ("q", P), ("k", P),
                 ("centroids", P), ("weights", P), ("scores", P), ("scores2", P), ("pooled_q", P),
-                ("pooled_k", P), ("head_list", P), ("n_heads_list", C.c_int32), ("reserved1", C.c_int32)]
+                ("pooled_k", P), ("head_list", P), ("n_heads_list", C.c_int32), ("reserved1", C.c_int32),
+                ("err_flag", P)]
 
 
 class SelectArgs(C.Structure):
@@ -64,8 +65,8 @@ class GatherArgs(C.Structure):
     _fields_ = [("mode", C.c_int32), ("dtype", C.c_int32), ("out_dtype", C.c_int32), ("n_clusters", C.c_int32),
                 ("n_q", C.c_int64), ("heads_q", C.c_int64), ("heads_kv", C.c_int64), ("n_ctx", C.c_int64),
                 ("head_dim", C.c_int64), ("scale", C.c_float), ("n_sel", C.c_int32), ("n_tok", C.c_int32),
-                ("reserved0", C.c_int32), ("q", P), ("k", P), ("v", P), ("cluster_ptr", P), ("sel", P),
-                ("tok_idx", P), ("out", P), ("lse", P)]
+                ("tok_per_head", C.c_int32), ("q", P), ("k", P), ("v", P), ("cluster_ptr", P), ("sel", P),
+                ("tok_idx", P), ("out", P), ("lse", P), ("q_pos", P), ("perm", P)]
 
 
 class ClusterPackArgs(C.Structure):

@@ -66,6 +66,14 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// NaN or +-inf.
+__device__ __forceinline__ bool nonfinite(float f) { return (__float_as_uint(f) & 0x7f800000u) == 0x7f800000u; }
+
+// Bit 0 of the optional device flag: some score the call wrote is not finite.
+__device__ __forceinline__ void flag_nonfinite(int32_t* err, bool bad) {
+  if (bad && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
+}
+
 __device__ __forceinline__ bool is_nan(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu);
@@ -104,6 +112,23 @@ __device__ __forceinline__ void dma16(uint32_t lds_off, const void* gptr) {
 // byte offset, which saves the 64-bit address arithmetic per lane.
 __device__ __forceinline__ void dma16_sb(uint32_t lds_off, const void* base, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds_off), "v"(voff), "s"(base)
+               : "memory", "m0");
+}
+
+// The same two copies at device scope (sc1): the request skips the CU's
+// vector cache and is served by L2.  For read-only tiles that the CU uses once
+// this avoids filling the vector cache with lines nobody reads again; the
+// bytes delivered are identical.
+__device__ __forceinline__ void dma16_dev(uint32_t lds_off, const void* gptr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, off sc1"
+               :
+               : "s"(lds_off), "v"(gptr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma16_sb_dev(uint32_t lds_off, const void* base, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 1\n\tglobal_load_lds_dwordx4 %1, %2 sc1"
                :
                : "s"(lds_off), "v"(voff), "s"(base)
                : "memory", "m0");

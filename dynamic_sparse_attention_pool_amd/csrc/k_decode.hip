@@ -219,8 +219,9 @@ __device__ __forceinline__ void dec_dma_v(uint16_t* vl, const uint16_t* vb, int6
 // them there).  The next tile's K and V are requested right after the current
 // tile's scores, so they are in flight during its softmax and P.V; LDS per
 // wave is 16.5 KB, so two workgroups of four waves share a CU.
-// NQT = query tiles of 32.
-template <int NQT>
+// NQT = query tiles of 32.  CAUSAL: query t only sees packed rows whose
+// context position (perm) is at most q_pos[t].
+template <int NQT, bool CAUSAL>
 __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_split(GatherParams p, float* __restrict__ part, int nsplit) {
   __shared__ __attribute__((aligned(1024))) DecWaveLds L[kDecWaves];
   __shared__ int32_t ptr_s[kDecMaxC + 1];
@@ -280,6 +281,12 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
     const uint16_t* qr = p.q + ((int64_t)t * p.hq + h) * kD + 8 * hf;
 #pragma unroll
     for (int s = 0; s < 8; ++s) qv[nt][s] = as_bf16x8(ldg16(qr + 16 * s));
+  }
+  int qlim[NQT];  // causal bound of this lane's query in each query tile
+#pragma unroll
+  for (int nt = 0; nt < NQT; ++nt) {
+    const int qi = 32 * nt + l32;
+    qlim[nt] = (CAUSAL && qi < nq) ? p.q_pos[qi / grp] : INT_MAX;
   }
 #pragma unroll
   for (int u = 0; u < kPtrPer; ++u) {
@@ -346,6 +353,7 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
   // K operand of tile t: lane row l32, dims 16s + 8hf .. +7 of step s (ordinary
   // loads: the compiler's wait for them also covers the older V copies)
   bf16x8 kr[8];
+  int prow = 0;  // CAUSAL: context position of this lane's row of the fetched tile
   auto fetch = [&](int t, int buf) {
     const int64_t base = p0 + (int64_t)t * kDecRows;
     const int len = (int)min((int64_t)kDecRows, p1 - base);
@@ -353,11 +361,13 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
     const uint16_t* krow = kb + (base + min(l32, len - 1)) * kD + 8 * hf;
 #pragma unroll
     for (int s = 0; s < 8; ++s) kr[s] = as_bf16x8(ldg16(krow + 16 * s));
+    if (CAUSAL) prow = p.perm[(int64_t)g * N + base + min(l32, len - 1)];
   };
 
   int cur = find(w, 0), buf = 0;
   if (cur < ntile) fetch(cur, 0);
   while (cur < ntile) {
+    const int pos_cur = prow;
     f32x16 sc[NQT];
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
@@ -375,6 +385,7 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int i = 0; i < 4; ++i) rmv[4 * j + i] = W.rmask[buf][8 * j + 4 * hf + i];
+
 #pragma unroll
     for (int nt = 0; nt < NQT; ++nt) {
       const int qi = 32 * nt + l32;
@@ -382,7 +393,12 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
       float mx = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const bool keep = qi < nq && ((rmv[r] >> qi) & 1ull);
+        bool keep = qi < nq && ((rmv[r] >> qi) & 1ull);
+        if (CAUSAL) {
+          // every lane takes part in the exchange (lane R holds row R's position)
+          const int rp = __shfl(pos_cur, 8 * (r / 4) + 4 * hf + (r % 4));
+          keep = keep && rp <= qlim[nt];
+        }
         x[r] = keep ? sc[nt][r] : -INFINITY;
         mx = fmaxf(mx, x[r]);
       }
@@ -529,11 +545,12 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
     for (int r = 0; r < 4; ++r) o[dt][r] = 0.f;
   float m = -INFINITY, l = 0.f;
   const int ntile = (p.n_tok + kBlk - 1) / kBlk;
+  const int64_t qlim = p.q_pos != nullptr ? (int64_t)p.q_pos[t] : INT64_MAX;
   for (int tt = 0; tt < ntile; ++tt) {
     const int base = tt * kBlk;
     const int len = min(kBlk, p.n_tok - base);
     int myid = lane < len ? ids[base + lane] : -1;
-    if (myid >= N) myid = -1;  // out-of-range ids are treated as padding
+    if (myid >= N || myid > qlim) myid = -1;  // out-of-range and future ids are treated as padding
     KEYS[w][lane] = myid;
     wave_sync();
     // rows to load (invalid slots read row 0 of a valid key; they are masked)
@@ -634,6 +651,116 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
   if (p.lse != nullptr && qd == 0) p.lse[orow] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
 }
 
+// ================================================================ token gather, any head grouping
+// One wave per (token, query head) over its own list (tok_idx [T, hq, n_tok])
+// or its token's list ([T, n_tok]), any number of query heads per KV head.
+// Per 64-id tile each lane scores one listed key (its 256-byte K row against
+// q from LDS, fp32), the wave takes the tile's max and sum, and the P.V
+// update gives each lane 8 dimensions of every fourth key (V rows read 16
+// bytes per lane, one row per 16 lanes); the four key groups are summed at the
+// end in a fixed order.
+constexpr int kListWaves = 4;
+
+__global__ __launch_bounds__(64 * kListWaves) void k_token_gather_list(GatherParams p) {
+  __shared__ float QS[kListWaves][kD];
+  __shared__ float PS[kListWaves][kBlk];
+  __shared__ int32_t IDS[kListWaves][kBlk];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t item = (int64_t)blockIdx.x * kListWaves + w;  // (t, h)
+  if (item >= (int64_t)p.T * p.hq) return;  // whole waves only: no workgroup barrier below
+  const int t = (int)(item / p.hq), h = (int)(item % p.hq);
+  const int g = h / (p.hq / p.hkv);
+  const int64_t N = p.n_ctx;
+  const uint16_t* kb = p.k + (int64_t)g * N * kD;
+  const uint16_t* vb = p.v + (int64_t)g * N * kD;
+  const int32_t* ids = p.tok_idx + (p.tok_per_head ? item : (int64_t)t) * p.n_tok;
+  const int64_t qlim = p.q_pos != nullptr ? (int64_t)p.q_pos[t] : INT64_MAX;
+  const float sl2 = p.scale * kLog2e;
+  {
+    const uint16_t* qr = p.q + item * kD;
+    QS[w][2 * lane] = bf2f(qr[2 * lane]);
+    QS[w][2 * lane + 1] = bf2f(qr[2 * lane + 1]);
+  }
+  wave_sync();
+  const int kg = lane >> 4, dc = lane & 15;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  for (int base = 0; base < p.n_tok; base += kBlk) {
+    int id = base + lane < p.n_tok ? ids[base + lane] : -1;
+    if (id >= N || id > qlim) id = -1;  // out-of-range and future ids are padding
+    float s = -INFINITY;
+    if (id >= 0) {
+      const uint16_t* kr = kb + (int64_t)id * kD;
+      float acc = 0.f;
+#pragma unroll
+      for (int c = 0; c < kD / 8; ++c) {
+        const u32x4 kv = ldg16(kr + 8 * c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc = fmaf(QS[w][8 * c + 2 * e], __uint_as_float(kv[e] << 16), acc);
+          acc = fmaf(QS[w][8 * c + 2 * e + 1], __uint_as_float(kv[e] & 0xffff0000u), acc);
+        }
+      }
+      s = acc * sl2;
+    }
+    float mx = s;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    const float mnew = fmaxf(m, mx);
+    if (mnew == -INFINITY) continue;  // nothing admissible yet (wave-uniform)
+    const float alpha = fast_exp2(m - mnew);  // m = -inf gives 0
+    const float pr = id >= 0 ? fast_exp2(s - mnew) : 0.f;
+    float ps = pr;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
+    l = l * alpha + ps;
+    m = mnew;
+    PS[w][lane] = pr;
+    IDS[w][lane] = id;
+    wave_sync();
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] *= alpha;
+#pragma unroll 4
+    for (int i = 0; i < kBlk / 4; ++i) {
+      const int j = 4 * i + kg;
+      const int jid = IDS[w][j];
+      if (jid >= 0) {
+        const float pj = PS[w][j];
+        const u32x4 vv = ldg16(vb + (int64_t)jid * kD + 8 * dc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[2 * e] = fmaf(pj, __uint_as_float(vv[e] << 16), o[2 * e]);
+          o[2 * e + 1] = fmaf(pj, __uint_as_float(vv[e] & 0xffff0000u), o[2 * e + 1]);
+        }
+      }
+    }
+    wave_sync();  // PS / IDS are rewritten by the next tile
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    o[e] += __shfl_xor(o[e], 16);
+    o[e] += __shfl_xor(o[e], 32);
+  }
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  if (kg == 0) {
+    if (p.out_bf16) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pk[e] = pack_bf16x2(o[2 * e] * inv, o[2 * e + 1] * inv);
+      stg16(reinterpret_cast<uint16_t*>(p.out) + item * kD + 8 * dc, pk);
+    } else {
+      float* op = reinterpret_cast<float*>(p.out) + item * kD + 8 * dc;
+      f32x4 a = {o[0] * inv, o[1] * inv, o[2] * inv, o[3] * inv};
+      f32x4 b = {o[4] * inv, o[5] * inv, o[6] * inv, o[7] * inv};
+      *reinterpret_cast<f32x4*>(op) = a;
+      *reinterpret_cast<f32x4*>(op + 4) = b;
+    }
+  }
+  if (p.lse != nullptr && lane == 0) p.lse[item] = l > 0.f ? (m + __log2f(l)) * kLn2 : -INFINITY;
+}
+
 size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
@@ -677,10 +804,15 @@ hipError_t launch_cluster_decode(const GatherParams& p, void* ws, hipStream_t st
   float* part = reinterpret_cast<float*>(ws);
   const int nq = p.T * (p.hq / p.hkv);
   const dim3 grid(p.hkv * nsplit);
-  if (nq <= 32)
-    hipLaunchKernelGGL((k_decode_split<1>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
+  const bool causal = p.q_pos != nullptr;
+  if (nq <= 32 && !causal)
+    hipLaunchKernelGGL((k_decode_split<1, false>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
+  else if (nq <= 32)
+    hipLaunchKernelGGL((k_decode_split<1, true>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
+  else if (!causal)
+    hipLaunchKernelGGL((k_decode_split<2, false>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
   else
-    hipLaunchKernelGGL((k_decode_split<2>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
+    hipLaunchKernelGGL((k_decode_split<2, true>), grid, dim3(64 * kDecWaves), 0, stream, p, part, nsplit);
   hipLaunchKernelGGL(k_decode_combine, dim3(p.T * p.hq), dim3(kD), 0, stream, p, part, nsplit);
   return hipGetLastError();
 }
@@ -694,6 +826,12 @@ size_t token_gather_workspace_bytes(int T, int hq, int n_tok) {
 
 hipError_t launch_token_gather(const GatherParams& p, void* ws, hipStream_t stream) {
   (void)ws;
+  if (p.tok_per_head || p.hq != 16 * p.hkv) {
+    const int64_t items = (int64_t)p.T * p.hq;
+    hipLaunchKernelGGL(k_token_gather_list, dim3((unsigned)((items + kListWaves - 1) / kListWaves)),
+                       dim3(64 * kListWaves), 0, stream, p);
+    return hipGetLastError();
+  }
   const int64_t items = (int64_t)p.T * p.hkv;
   hipLaunchKernelGGL(k_token_gather, dim3((unsigned)((items + kGatherWaves - 1) / kGatherWaves)),
                      dim3(64 * kGatherWaves), 0, stream, p);

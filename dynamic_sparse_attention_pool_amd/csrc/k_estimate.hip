@@ -61,10 +61,11 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, int hq, H
 // ---------------------------------------------------------------- k_block_score
 // S[b,h,i,j] = pooled_q[b,h,i] . pooled_k[b,g(h),j] * scale for j <= i.
 // 64x64 output tile per workgroup, 4x4 per thread, fp32 FMAs in dimension
-// order.  Tiles strictly above the diagonal only write -inf.
+// order.  Entries above the diagonal are not written (the causal selection
+// never reads them); tiles strictly above it do nothing.
 __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ pq, const float* __restrict__ pk,
                                                      int hq, int hkv, HeadList hl, int nb, int D, float scale,
-                                                     float* __restrict__ S) {
+                                                     float* __restrict__ S, int32_t* __restrict__ err) {
   __shared__ float Qs[64][33];
   __shared__ float Ks[64][33];
   const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
@@ -76,13 +77,7 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
   listed_row(bh, hq, hl, b, h);
   const int g = (h * hkv) / hq;
   float* Sb = S + (int64_t)bh * nb * nb;
-  if (tj > ti) {
-    for (int e = tid; e < 64 * 64; e += 256) {
-      const int i = ti * 64 + e / 64, j = tj * 64 + e % 64;
-      if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = -INFINITY;
-    }
-    return;
-  }
+  if (tj > ti) return;
   const float* Qb = pq + (int64_t)bh * nb * D;
   const float* Kb = pk + ((int64_t)b * hkv + g) * nb * D;
   float acc[4][4];
@@ -112,13 +107,19 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
     }
     __syncthreads();
   }
+  bool bad = false;
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const int i = ti * 64 + ty + 16 * a, j = tj * 64 + tx + 16 * c;
-      if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = (j <= i) ? acc[a][c] * scale : -INFINITY;
+      if (i < nb && j <= i) {
+        const float v = acc[a][c] * scale;
+        Sb[(int64_t)i * nb + j] = v;
+        bad |= nonfinite(v);
+      }
     }
+  flag_nonfinite(err, bad);
 }
 
 // 128x128 tile of S per workgroup on the fp32 matrix cores
@@ -128,12 +129,12 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
 // of 8 dimensions LDS holds the even ones, then the odd ones: one 16-byte read
 // gives a lane its operands for four steps.  Row pitch 36 floats: sixteen
 // consecutive rows' 16-byte reads hit distinct banks.  Wave (wi, wj) computes
-// the 64x64 quarter (wi, wj) as 2x2 MFMA tiles.  Tiles above the diagonal only
-// write -inf.
+// the 64x64 quarter (wi, wj) as 2x2 MFMA tiles.  Entries above the diagonal are
+// not written; tiles strictly above it do nothing.
 template <int D>
 __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restrict__ pq, const float* __restrict__ pk,
                                                           int hq, int hkv, HeadList hl, int nb, float scale,
-                                                          float* __restrict__ S) {
+                                                          float* __restrict__ S, int32_t* __restrict__ err) {
   constexpr int T = 128, DC = 32, P = DC + 4;
   __shared__ __attribute__((aligned(16))) float Qs[T * P];
   __shared__ __attribute__((aligned(16))) float Ks[T * P];
@@ -146,21 +147,7 @@ __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restric
   listed_row(bh, hq, hl, b, h);
   const int g = (h * hkv) / hq;
   float* Sb = S + (int64_t)bh * nb * nb;
-  if (tj > ti) {
-    if ((nb & 3) == 0 && (reinterpret_cast<uintptr_t>(S) & 15) == 0) {  // 16-byte aligned rows
-      const f32x4 ninf = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      for (int e = tid; e < T * T / 4; e += 256) {
-        const int i = ti * T + e / (T / 4), j = tj * T + 4 * (e % (T / 4));
-        if (i < nb && j < nb) *reinterpret_cast<f32x4*>(Sb + (int64_t)i * nb + j) = ninf;
-      }
-    } else {
-      for (int e = tid; e < T * T; e += 256) {
-        const int i = ti * T + e / T, j = tj * T + e % T;
-        if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = -INFINITY;
-      }
-    }
-    return;
-  }
+  if (tj > ti) return;
   const float* Qb = pq + (int64_t)bh * nb * D;
   const float* Kb = pk + ((int64_t)b * hkv + g) * nb * D;
   const int wi = wv >> 1, wj = wv & 1;
@@ -200,6 +187,7 @@ __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restric
     __syncthreads();
   }
   // element r of tile (m, n): row 64wi + 32m + 8(r/4) + 4hf + r%4, column 64wj + 32n + l32
+  bool bad = false;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -208,8 +196,13 @@ __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restric
       for (int r = 0; r < 16; ++r) {
         const int i = ti * T + 64 * wi + 32 * m + 8 * (r / 4) + 4 * hf + (r % 4);
         const int j = tj * T + 64 * wj + 32 * n + l32;
-        if (i < nb && j < nb) Sb[(int64_t)i * nb + j] = (j <= i) ? acc[m][n][r] * scale : -INFINITY;
+        if (i < nb && j <= i) {
+          const float v = acc[m][n][r] * scale;
+          Sb[(int64_t)i * nb + j] = v;
+          bad |= nonfinite(v);
+        }
       }
+  flag_nonfinite(err, bad);
 }
 
 // ---------------------------------------------------------------- k_centroid_score
@@ -221,7 +214,7 @@ constexpr int kCentChunk = 8;
 template <typename T>
 __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q, const float* __restrict__ cent,
                                                         int T_, int hq, int hkv, int C, int D, float scale,
-                                                        float* __restrict__ out) {
+                                                        float* __restrict__ out, int32_t* __restrict__ err) {
   extern __shared__ float sm[];
   const int grp = hq / hkv;
   const int nq = T_ * grp;
@@ -257,7 +250,9 @@ __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q,
       for (int d = 0; d < D; ++d) acc = fmaf(qr[d], cr[d], acc);
     }
     const int t = qi / grp, h = g * grp + qi % grp;
-    out[((int64_t)t * hq + h) * C + c0 + c] = acc * scale;
+    const float v = acc * scale;
+    out[((int64_t)t * hq + h) * C + c0 + c] = v;
+    flag_nonfinite(err, nonfinite(v));
   }
 }
 
@@ -518,7 +513,7 @@ hipError_t launch_pool(const void* x, int64_t batch, int hq, const HeadList& hl,
 }
 
 hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, const HeadList& hl,
-                              int nb, int head_dim, float scale, float* scores, hipStream_t stream) {
+                              int nb, int head_dim, float scale, float* scores, int32_t* err, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * (hl.n > 0 ? hl.n : hq);
   if (head_dim == 128 || head_dim == 64) {
     const int nbt2 = (nb + 127) / 128;
@@ -526,22 +521,22 @@ hipError_t launch_block_score(const float* pq, const float* pk, int batch, int h
     if (n2 == 0) return hipSuccess;
     if (head_dim == 128)
       hipLaunchKernelGGL((k_block_score_mfma<128>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, hl,
-                         nb, scale, scores);
+                         nb, scale, scores, err);
     else
       hipLaunchKernelGGL((k_block_score_mfma<64>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, hl,
-                         nb, scale, scores);
+                         nb, scale, scores, err);
     return hipGetLastError();
   }
   const int nbt = (nb + 63) / 64;
   const int64_t n = rows * nbt * nbt;
   if (n == 0) return hipSuccess;
   hipLaunchKernelGGL(k_block_score, dim3((unsigned)n), dim3(256), 0, stream, pq, pk, hq, hkv, hl, nb, head_dim,
-                     scale, scores);
+                     scale, scores, err);
   return hipGetLastError();
 }
 
 hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,
-                                 int C, int head_dim, float scale, float* out, hipStream_t stream) {
+                                 int C, int head_dim, float scale, float* out, int32_t* err, hipStream_t stream) {
   const int grp = hq / hkv;
   const size_t lds = (size_t)(kCentChunk + T * grp) * (head_dim + 1) * sizeof(float);
   if (lds > 160 * 1024) return hipErrorInvalidValue;
@@ -549,10 +544,10 @@ hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, 
   const dim3 grid(hkv * nchunk);
   if (q_bf16)
     hipLaunchKernelGGL((k_centroid_score<uint16_t>), grid, dim3(256), lds, stream, (const uint16_t*)q, cent, T,
-                       hq, hkv, C, head_dim, scale, out);
+                       hq, hkv, C, head_dim, scale, out, err);
   else
     hipLaunchKernelGGL((k_centroid_score<float>), grid, dim3(256), lds, stream, (const float*)q, cent, T, hq,
-                       hkv, C, head_dim, scale, out);
+                       hkv, C, head_dim, scale, out, err);
   return hipGetLastError();
 }
 

@@ -36,7 +36,8 @@ namespace {
 
 constexpr int kBlk = 64;
 constexpr int kThreads = 128;
-constexpr int kMetaMax = 2048 + 128;  // staged block list, or column list + intervals
+constexpr int kMetaMax = 2048;        // staged block list, or 64 intervals + up to 1920 columns
+constexpr int kMaxCols = kMetaMax - 128;
 constexpr float kSlack = 8.f;         // lazy-rescale threshold, log2 units
 
 // Tile source: either a contiguous key range or a gathered list of columns.
@@ -57,6 +58,8 @@ struct TileIter {
   const int32_t* col = nullptr;  // ascending column list (optional: without it every column tile is masked)
   int n_iv = 0, cur_iv = 0, cur_off = 0;
   int n_col = 0, col_off = 0;
+  int lim = 0;          // keys at or beyond min(seq, end of the query block) are never loaded
+  int bad_cols = 0;     // some column lies outside [0, seq): mask every gathered tile
 
   __device__ bool next(TileRef& r) {
     if (MODE == 0) {
@@ -69,25 +72,27 @@ struct TileIter {
       r.diag = (j == iblk);
       return true;
     }
-    if (cur_iv < n_iv) {
-      const int s = iv[2 * cur_iv], e = iv[2 * cur_iv + 1];
+    while (cur_iv < n_iv) {
+      // an interval is clipped to [0, lim); an empty one is skipped
+      const int s = max(iv[2 * cur_iv], 0), e = min(iv[2 * cur_iv + 1], lim);
+      if (s + cur_off >= e) {
+        ++cur_iv;
+        cur_off = 0;
+        continue;
+      }
       r.base = s + cur_off;
       r.len = min(kBlk, e - r.base);
       r.gathered = 0;
       // masking only for a short tile or one reaching past the block's first query row
       r.diag = (r.len < kBlk) || (r.base + r.len - 1 > iblk * kBlk);
       cur_off += kBlk;
-      if (s + cur_off >= e) {
-        ++cur_iv;
-        cur_off = 0;
-      }
       return true;
     }
     if (col_off < n_col) {
       r.base = col_off;
       r.len = min(kBlk, n_col - col_off);
       r.gathered = 1;
-      r.diag = (r.len < kBlk) || col == nullptr || (col[r.base + r.len - 1] > iblk * kBlk);
+      r.diag = (r.len < kBlk) || col == nullptr || bad_cols || (col[r.base + r.len - 1] > iblk * kBlk);
       col_off += kBlk;
       return true;
     }
@@ -95,9 +100,15 @@ struct TileIter {
   }
 };
 
-__device__ __forceinline__ int tile_row(const TileRef& r, const int32_t* cols, int slot) {
+// A listed column outside [0, seq) is never loaded: its copy reads row 0 and
+// the key is masked.
+__device__ __forceinline__ bool col_ok(int c, int64_t seq) { return c >= 0 && c < seq; }
+
+__device__ __forceinline__ int tile_row(const TileRef& r, const int32_t* cols, int slot, int64_t seq) {
   const int s = min(slot, r.len - 1);
-  return r.gathered ? cols[r.base + s] : r.base + s;
+  if (!r.gathered) return r.base + s;
+  const int c = cols[r.base + s];
+  return col_ok(c, seq) ? c : 0;
 }
 
 // XOR key of row r: chunk c of row r sits at position c ^ key(r).  For d = 128
@@ -112,20 +123,34 @@ __device__ __forceinline__ int swz_key(int row) {
 }
 
 // One 64-row tile (K or V) -> LDS, row-major, chunk c of row r at position
-// c ^ key(r).  Each wave issues NI copies of 1 KB.
+// c ^ key(r).  Each wave issues NI copies of 1 KB at device scope.  A
+// contiguous tile's first row goes into the 64-bit scalar base, so the lane
+// offsets stay below 16 KB whatever the sequence length; a gathered tile
+// gives every lane its own 64-bit address.
 template <int D>
 __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* gbase, const TileRef& r,
-                                         const int32_t* cols, int w, int lane) {
+                                         const int32_t* cols, int64_t seq, int w, int lane) {
   constexpr int CPR = D / 8;          // 16-byte chunks per row
   constexpr int RPI = 64 / CPR;       // rows per 1 KB copy
   constexpr int NI = kBlk / RPI / 2;  // copies per wave
   const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(lds) + (uint32_t)(w * NI) * 1024u);
+  if (!r.gathered) {
+    const uint16_t* tb = gbase + (int64_t)__builtin_amdgcn_readfirstlane(r.base) * D;
+    const int last = r.len - 1;
+#pragma unroll
+    for (int n = 0; n < NI; ++n) {
+      const int row = (w * NI + n) * RPI + lane / CPR;
+      const int c = (lane % CPR) ^ swz_key<D>(row);
+      const uint32_t off = (uint32_t)min(row, last) * (uint32_t)(D * 2) + (uint32_t)(16 * c);
+      dma16_sb_dev(base + (uint32_t)n * 1024u, tb, off);
+    }
+    return;
+  }
 #pragma unroll
   for (int n = 0; n < NI; ++n) {
     const int row = (w * NI + n) * RPI + lane / CPR;
     const int c = (lane % CPR) ^ swz_key<D>(row);
-    const uint32_t off = (uint32_t)tile_row(r, cols, row) * (uint32_t)(D * 2) + (uint32_t)(16 * c);
-    dma16_sb(base + (uint32_t)n * 1024u, gbase, off);
+    dma16_dev(base + (uint32_t)n * 1024u, gbase + (int64_t)tile_row(r, cols, row, seq) * D + 8 * c);
   }
 }
 
@@ -204,7 +229,7 @@ template <int D, int MODE, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   __shared__ __attribute__((aligned(1024))) uint16_t Kl[kBlk * D];
   __shared__ __attribute__((aligned(1024))) uint16_t Vl[kBlk * D];
-  __shared__ int32_t meta[MODE == 0 ? 2048 : kMetaMax];
+  __shared__ int32_t meta[kMetaMax];  // with K and V: 40 KB, four workgroups per CU
   constexpr int NDMA = D / 16;  // direct-to-LDS copies per wave per tile (K or V)
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, hf = lane >> 5, l32 = lane & 31;
   const Item item = item_at(p, blockIdx.x, gridDim.x, p.order);
@@ -217,15 +242,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   const uint16_t* kb = reinterpret_cast<const uint16_t*>(p.k) + ((int64_t)b * p.heads_kv + g) * N * D;
   const uint16_t* vb = reinterpret_cast<const uint16_t*>(p.v) + ((int64_t)b * p.heads_kv + g) * N * D;
 
-  // ---- stage this row's tile list in LDS (no vector-memory reads inside the pipeline)
+  // ---- stage this row's tile list in LDS (no vector-memory reads inside the pipeline).
+  //      Counts are clipped to the table capacities; intervals are clipped to
+  //      the keys the block can see when they are read, and a column outside
+  //      [0, seq) is loaded as row 0 and masked.
   TileIter<MODE> it;
   const int32_t* cols = nullptr;
+  int bad_col = 0;
   if (MODE == 0) {
     int cnt;
     if (p.ashape) {
       cnt = ashape_list(meta, iblk, p.n_sink, p.n_local, tid, kThreads);
     } else {
-      cnt = min(p.block_cnt[row_id], 2048);
+      cnt = max(0, min(p.block_cnt[row_id], min(p.kmax, 2048)));
       const int32_t* src = p.block_idx + row_id * p.kmax;
       for (int e = tid; e < cnt; e += kThreads) meta[e] = src[e];
     }
@@ -233,16 +262,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
     it.cnt = cnt;
     it.iblk = iblk;
   } else {
-    const int niv = min(p.iv_cnt[row_id], 64);
-    const int ncol = min(p.col_cnt[row_id], kMetaMax - 128);
+    const int niv = max(0, min(p.iv_cnt[row_id], min(p.max_iv, 64)));
+    const int ncol = max(0, min(p.col_cnt[row_id], min(p.max_col, kMaxCols)));
     const int32_t* isrc = p.iv + row_id * p.max_iv * 2;
     const int32_t* csrc = p.col + row_id * p.max_col;
     for (int e = tid; e < 2 * niv; e += kThreads) meta[e] = isrc[e];
-    for (int e = tid; e < ncol; e += kThreads) meta[128 + e] = csrc[e];
+    for (int e = tid; e < ncol; e += kThreads) {
+      const int c = csrc[e];
+      bad_col |= !col_ok(c, N);
+      meta[128 + e] = c;
+    }
     it.iv = meta;
     it.n_iv = niv;
     it.n_col = ncol;
     it.iblk = iblk;
+    it.lim = (int)min(N, (int64_t)iblk * kBlk + kBlk);
     cols = meta + 128;
     it.col = cols;
   }
@@ -257,7 +291,18 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   const int qpos = iblk * kBlk + 32 * w + l32;  // absolute query row of this lane
   const float sl2 = p.scale * kLog2e;
   drain_vmem();  // Q^T resident: from here on the only vector-memory ops are the tile copies
-  __syncthreads();
+  if (MODE == 0) {
+    __syncthreads();
+  } else {
+    // the row's bad-column flag passes through the K tile buffer, which no copy
+    // has touched yet
+    int* flag = reinterpret_cast<int*>(Kl);
+    const int wbad = __any(bad_col);
+    if (lane == 0) flag[w] = wbad;
+    __syncthreads();
+    it.bad_cols = flag[0] | flag[1];
+    __syncthreads();  // both waves read the flags before the first copy lands
+  }
 
   f32x16 o[D / 32];
 #pragma unroll
@@ -269,8 +314,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   TileRef cur, nxt;
   bool have = it.next(cur);
   if (have) {
-    dma_tile<D>(Kl, kb, cur, cols, w, lane);
-    dma_tile<D>(Vl, vb, cur, cols, w, lane);
+    dma_tile<D>(Kl, kb, cur, cols, N, w, lane);
+    dma_tile<D>(Vl, vb, cur, cols, N, w, lane);
   }
   while (have) {
     // ---- K(t) in LDS
@@ -302,7 +347,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();  // both waves are done with K(t)
     const bool more = it.next(nxt);
-    if (more) dma_tile<D>(Kl, kb, nxt, cols, w, lane);
+    if (more) dma_tile<D>(Kl, kb, nxt, cols, N, w, lane);
 
     // ---- online softmax (log2 domain); element r of M tile mt is key slot
     //      32*mt + 8*(r/4) + 4*hf + r%4
@@ -324,7 +369,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
 #pragma unroll
         for (int r = 0; r < 32; ++r) {
           const int slot = 32 * (r / 16) + 8 * ((r % 16) / 4) + 4 * hf + (r % 4);
-          const int key = slot >= cur.len ? INT_MAX : (cur.gathered ? cols[cur.base + slot] : cur.base + slot);
+          int key = INT_MAX;
+          if (slot < cur.len) {
+            key = cur.gathered ? cols[cur.base + slot] : cur.base + slot;
+            if (!col_ok(key, N)) key = INT_MAX;
+          }
           if (key > qpos) x[r] = -INFINITY;
         }
       }
@@ -392,7 +441,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
     }
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();  // both waves are done with V(t)
-    if (more) dma_tile<D>(Vl, vb, nxt, cols, w, lane);
+    if (more) dma_tile<D>(Vl, vb, nxt, cols, N, w, lane);
     cur = nxt;
     have = more;
   }
@@ -454,13 +503,18 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
       __syncthreads();
     } else {
       it.bidx = p.block_idx + row_id * p.kmax;
-      it.cnt = p.block_cnt[row_id];
+      it.cnt = max(0, min(p.block_cnt[row_id], p.kmax));
     }
     it.iblk = iblk;
   } else {
+    // the same clipping as the bf16 kernel: counts to capacities, intervals to
+    // the keys the block can see, columns outside [0, seq) masked
     it.iv = p.iv + row_id * p.max_iv * 2;
-    it.n_iv = p.iv_cnt[row_id];
-    it.n_col = p.col_cnt[row_id];
+    it.n_iv = max(0, min(p.iv_cnt[row_id], p.max_iv));
+    it.n_col = max(0, min(p.col_cnt[row_id], p.max_col));
+    it.iblk = iblk;
+    it.lim = (int)min(N, (int64_t)iblk * kBlk + kBlk);
+    it.bad_cols = 1;  // every gathered key is checked below anyway
     cols = p.col + row_id * p.max_col;
   }
   float q[D], o[D];
@@ -472,12 +526,17 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
   TileRef r;
   while (it.next(r)) {
     __syncthreads();
-    const int row = tile_row(r, cols, tid);
+    const int row = tile_row(r, cols, tid, N);
     for (int d = 0; d < D; d += 4) {
       *reinterpret_cast<f32x4*>(&Ks[tid][d]) = *reinterpret_cast<const f32x4*>(kb + (int64_t)row * D + d);
       *reinterpret_cast<f32x4*>(&Vs[tid][d]) = *reinterpret_cast<const f32x4*>(vb + (int64_t)row * D + d);
     }
-    keyS[tid] = tid < r.len ? (r.gathered ? cols[r.base + tid] : r.base + tid) : INT_MAX;
+    int key = INT_MAX;
+    if (tid < r.len) {
+      key = r.gathered ? cols[r.base + tid] : r.base + tid;
+      if (!col_ok(key, N)) key = INT_MAX;
+    }
+    keyS[tid] = key;
     __syncthreads();
     float s[kBlk];
     float mx = -INFINITY;

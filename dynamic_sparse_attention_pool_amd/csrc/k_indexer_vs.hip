@@ -38,6 +38,34 @@ namespace {
 // (including -0) is a negative int32; finite inputs only (products of bf16).
 __device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
+// The integer ReLU above turns a NaN product with its sign bit set into 0, so
+// a NaN in the indexer's inputs need not reach its scores.  When the caller
+// asks for the flag, this pass sets bit 0 if any element of q, k (bf16, 8 per
+// 16-byte load) or the weights is NaN or infinite.
+__global__ __launch_bounds__(256) void k_idx_scan_inputs(const uint16_t* __restrict__ q, int64_t nq8,
+                                                         const uint16_t* __restrict__ k, int64_t nk8,
+                                                         const float* __restrict__ w, int nw, int32_t* err) {
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t t0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  auto bad2 = [](uint32_t x) { return (x & 0x7f80u) == 0x7f80u || (x & 0x7f800000u) == 0x7f800000u; };
+  bool bad = false;
+  for (int64_t i = t0; i < nq8 + nk8; i += stride) {
+    const u32x4 v = ldg16(i < nq8 ? q + 8 * i : k + 8 * (i - nq8));
+    bad |= bad2(v[0]) || bad2(v[1]) || bad2(v[2]) || bad2(v[3]);
+  }
+  for (int64_t i = t0; i < nw; i += stride) bad |= nonfinite(w[i]);
+  flag_nonfinite(err, bad);
+}
+
+hipError_t scan_indexer_inputs(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
+                               int32_t* err, hipStream_t stream) {
+  if (err == nullptr) return hipSuccess;
+  const int64_t nq8 = (int64_t)T * hi * 64 / 8, nk8 = nk * 64 / 8;
+  const int64_t blocks = std::min<int64_t>(2048, (nq8 + nk8 + 255) / 256 + 1);
+  hipLaunchKernelGGL(k_idx_scan_inputs, dim3((unsigned)blocks), dim3(256), 0, stream, q, nq8, k, nk8, w, hi, err);
+  return hipGetLastError();
+}
+
 constexpr int kIdxWaves = 8;
 constexpr int kIdxD = 64;
 constexpr int kIdxChunk = 8192;  // keys per workgroup
@@ -45,7 +73,8 @@ constexpr int kIdxChunk = 8192;  // keys per workgroup
 template <int HPW>
 __global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
                                                             const float* __restrict__ w, int T, int Hi, int64_t Nk,
-                                                            int64_t pos0, float* __restrict__ out) {
+                                                            int64_t pos0, float* __restrict__ out,
+                                                            int32_t* __restrict__ err) {
   __shared__ float red[kIdxWaves][64 * 33];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, hf = lane >> 5, l32 = lane & 31;
   const int nchunk = (int)((Nk + kIdxChunk - 1) / kIdxChunk);
@@ -66,6 +95,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __re
   }
   const int64_t lim_max = pos0 + std::min(t0 + 31, T - 1);  // largest causal key of the tile's queries
   const int tid = threadIdx.x;
+  bool bad = false;
   for (int64_t s0 = c0; s0 < c1; s0 += 64) {
     const bool live = s0 <= lim_max;
     if (live) {
@@ -123,6 +153,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __re
             for (int ww = 0; ww < kIdxWaves; ++ww) acc += red[ww][key * 33 + qq];
           }
           v4[i] = (s0 + key > lim) ? -INFINITY : acc;
+          bad |= s0 + key <= lim && s0 + key < c1 && nonfinite(acc);
         }
         const int64_t s = s0 + 4 * kq;
         float* op = out + (int64_t)t * Nk + s;
@@ -135,6 +166,7 @@ __global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __re
     }
     __syncthreads();
   }
+  flag_nonfinite(err, bad);
 }
 
 // Heads on the matrix rows.  For a query t the product Q_t . K^T puts the 32
@@ -282,7 +314,11 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
             }
             found[j] += __popcll(m);
           } else {
-            if (hf == 0 && t < T && key < c1) out[(int64_t)t * Nk + key] = key * kstride > pos0 + t ? -INFINITY : tot;
+            if (hf == 0 && t < T && key < c1) {
+              const bool causal = key * kstride <= pos0 + t;
+              out[(int64_t)t * Nk + key] = causal ? tot : -INFINITY;
+              flag_nonfinite(cd.err, causal && nonfinite(tot));
+            }
           }
           sum = 0.f;
         }
@@ -775,7 +811,8 @@ __global__ __launch_bounds__(64) void k_vs_stats_merge(const float* __restrict__
 
 // a_s[o] = sum over the (at most two) tiles whose diagonals reach offset o
 __global__ __launch_bounds__(256) void k_vs_slash(const float* __restrict__ dpart, int64_t N, int rows,
-                                                  float* __restrict__ a_s) {
+                                                  float* __restrict__ a_s, const float* __restrict__ a_v,
+                                                  int32_t* __restrict__ err) {
   const int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (e >= (int64_t)rows * N) return;
   const int64_t bh = e / N, o = e % N;
@@ -790,6 +827,7 @@ __global__ __launch_bounds__(256) void k_vs_slash(const float* __restrict__ dpar
     if (delta >= -63 && delta <= 63) s += dpart[(bh * ntile + tau) * 128 + delta + 63];
   }
   a_s[e] = s;
+  if (err != nullptr) flag_nonfinite(err, nonfinite(s) || nonfinite(a_v[e]));  // a_v has the same layout
 }
 
 size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -797,29 +835,32 @@ size_t a256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
-                          int64_t pos0, float* out, hipStream_t stream) {
+                          int64_t pos0, float* out, int32_t* err, hipStream_t stream) {
   const int nchunk = (int)((nk + kIdxChunk - 1) / kIdxChunk);
+  IdxCand flag{};
+  flag.err = err;  // the dense scores only use the flag
+  if (const hipError_t e = scan_indexer_inputs(q, k, w, T, hi, nk, err, stream); e != hipSuccess) return e;
   if (hi == 32) {
     constexpr int nq = kIdx2Waves * idx2_qpw<1>();
     const dim3 grid2((unsigned)(((T + nq - 1) / nq) * nchunk));
     hipLaunchKernelGGL((k_indexer2<1, false>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, 1, kIdxChunk,
-                       pos0, out, IdxCand{});
+                       pos0, out, flag);
     return hipGetLastError();
   }
   if (hi == 64) {
     constexpr int nq = kIdx2Waves * idx2_qpw<2>();
     const dim3 grid2((unsigned)(((T + nq - 1) / nq) * nchunk));
     hipLaunchKernelGGL((k_indexer2<2, false>), grid2, dim3(64 * kIdx2Waves), 0, stream, q, k, w, T, hi, nk, 1, kIdxChunk,
-                       pos0, out, IdxCand{});
+                       pos0, out, flag);
     return hipGetLastError();
   }
   const dim3 grid((unsigned)(((T + 31) / 32) * nchunk));
   const int hpw = hi / kIdxWaves;
   switch (hpw) {
-    case 1: hipLaunchKernelGGL((k_indexer<1>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
-    case 2: hipLaunchKernelGGL((k_indexer<2>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
-    case 4: hipLaunchKernelGGL((k_indexer<4>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
-    case 8: hipLaunchKernelGGL((k_indexer<8>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out); break;
+    case 1: hipLaunchKernelGGL((k_indexer<1>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
+    case 2: hipLaunchKernelGGL((k_indexer<2>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
+    case 4: hipLaunchKernelGGL((k_indexer<4>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
+    case 8: hipLaunchKernelGGL((k_indexer<8>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -856,6 +897,7 @@ hipError_t launch_indexer_topk(const uint16_t* q, const uint16_t* k, const float
                                hipStream_t stream) {
   if (T == 0) return hipSuccess;
   if (hi != 32 && hi != 64) return hipErrorInvalidValue;
+  if (const hipError_t e = scan_indexer_inputs(q, k, w, T, hi, nk, err, stream); e != hipSuccess) return e;
   const IdxTopkLayout L = idx_topk_layout(T, nk, pos0, kk);
   char* base = static_cast<char*>(ws);
   float* smp = reinterpret_cast<float*>(base);
@@ -902,7 +944,7 @@ size_t vs_workspace_bytes(int64_t rows, int64_t seq) {
 
 hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv,
                               const HeadList& hl, int64_t seq, int head_dim, int last_q, float scale, float* a_v,
-                              float* a_s, void* ws, hipStream_t stream) {
+                              float* a_s, int32_t* err, void* ws, hipStream_t stream) {
   if (last_q != kVsLast) return hipErrorInvalidValue;
   const int rows = batch * (hl.n > 0 ? hl.n : hq);
   const int64_t ntile = (seq + 63) / 64;
@@ -932,7 +974,8 @@ hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, i
     return hipErrorInvalidValue;
   }
   const int64_t n = (int64_t)rows * seq;
-  hipLaunchKernelGGL(k_vs_slash, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dpart, seq, rows, a_s);
+  hipLaunchKernelGGL(k_vs_slash, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, dpart, seq, rows, a_s, a_v,
+                     err);
   return hipGetLastError();
 }
 

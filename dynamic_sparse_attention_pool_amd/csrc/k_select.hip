@@ -681,7 +681,9 @@ __global__ __launch_bounds__(64) void k_vs_build(VsBuildParams p) {
   const int i = (int)(gid % nqb);
   const int32_t* offs = p.slash + r * p.n_slash;
   const int32_t* cols = p.vert + r * p.n_vert;
-  const int ns = p.slash_cnt[r], nv = p.vert_cnt[r];
+  // counts beyond the capacities, negative offsets and columns outside
+  // [0, seq) are ignored, so every table entry names keys that exist
+  const int ns = max(0, min(p.slash_cnt[r], p.n_slash)), nv = max(0, min(p.vert_cnt[r], p.n_vert));
   int32_t* iv = p.iv + gid * p.n_slash * 2;
   int32_t* col = p.col + gid * p.n_vert;
   const int64_t q0 = (int64_t)i * p.bs;
@@ -689,7 +691,7 @@ __global__ __launch_bounds__(64) void k_vs_build(VsBuildParams p) {
   for (int s = ns - 1; s >= 0; --s) {
     const int64_t o = offs[s];
     const int64_t e = q0 - o + p.bs;
-    if (e <= 0) continue;
+    if (o < 0 || e <= 0) continue;
     const int64_t b = max((int64_t)0, q0 - o);
     if (niv > 0 && b <= iv[2 * niv - 1]) {
       if (e > iv[2 * niv - 1]) iv[2 * niv - 1] = (int32_t)e;
@@ -704,6 +706,7 @@ __global__ __launch_bounds__(64) void k_vs_build(VsBuildParams p) {
   for (int c = 0; c < nv; ++c) {
     const int64_t x = cols[c];
     if (x > last) break;
+    if (x < 0) continue;
     while (w < niv && iv[2 * w + 1] <= x) ++w;
     if (w < niv && iv[2 * w] <= x) continue;
     col[nc++] = (int32_t)x;
@@ -731,7 +734,8 @@ __global__ __launch_bounds__(64 * kVbWaves) void k_vs_build_wave(VsBuildParams p
   const int i = (int)(gid % nqb);
   const int32_t* offs = p.slash + r * p.n_slash;
   const int32_t* cols = p.vert + r * p.n_vert;
-  const int ns = min(p.slash_cnt[r], 64), nv = p.vert_cnt[r];
+  // the same clipping as k_vs_build
+  const int ns = max(0, min(p.slash_cnt[r], min(p.n_slash, 64))), nv = max(0, min(p.vert_cnt[r], p.n_vert));
   int32_t* iv = p.iv + gid * p.n_slash * 2;
   int32_t* col = p.col + gid * p.n_vert;
   const int q0 = i * p.bs;
@@ -742,7 +746,7 @@ __global__ __launch_bounds__(64 * kVbWaves) void k_vs_build_wave(VsBuildParams p
   if (lane < ns) {
     const int o = offs[ns - 1 - lane];
     e = q0 - o + p.bs;
-    valid = e > 0;
+    valid = o >= 0 && e > 0;
     b = max(0, q0 - o);
   }
   const int prev_e = __shfl_up(e, 1);  // every lane takes part in the exchanges
@@ -751,8 +755,10 @@ __global__ __launch_bounds__(64 * kVbWaves) void k_vs_build_wave(VsBuildParams p
   const bool starts = valid && (!prev_valid || b > prev_e);
   const uint64_t ms = __ballot(starts);
   const int next_s = __shfl_down((int)starts, 1);
+  const int next_v = __shfl_down((int)valid, 1);
   const bool next_starts = lane < 63 && next_s != 0;
-  const bool ends = valid && (lane == ns - 1 || next_starts);
+  const bool next_valid = lane < 63 && lane + 1 < ns && next_v != 0;
+  const bool ends = valid && (!next_valid || next_starts);
   const int k_here = (int)__popcll(ms & (lt | (1ull << lane))) - 1;  // interval of this lane
   if (starts) {
     iv[2 * k_here] = b;
@@ -777,7 +783,7 @@ __global__ __launch_bounds__(64 * kVbWaves) void k_vs_build_wave(VsBuildParams p
       else hi = mid;
     }
     const bool inside = lo > 0 && x < se[wv][lo - 1];
-    const bool keep = in_range && !inside;
+    const bool keep = x >= 0 && in_range && !inside;
     const uint64_t mk = __ballot(keep);
     if (keep) col[nc + (int)__popcll(mk & lt)] = x;
     nc += (int)__popcll(mk);

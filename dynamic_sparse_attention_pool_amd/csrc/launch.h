@@ -57,17 +57,19 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, 
 // (out compact).
 hipError_t launch_pool(const void* x, int64_t batch, int hq, const HeadList& hl, int64_t seq, int head_dim,
                        bool bf16, int block, float* out, hipStream_t stream);
+// Estimators: err (optional device int32) gets bit 0 when a score they write
+// (outside the masked entries) is NaN or infinite.
 hipError_t launch_block_score(const float* pq, const float* pk, int batch, int hq, int hkv, const HeadList& hl,
-                              int nb, int head_dim, float scale, float* scores, hipStream_t stream);
+                              int nb, int head_dim, float scale, float* scores, int32_t* err, hipStream_t stream);
 hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,
-                                 int C, int head_dim, float scale, float* out, hipStream_t stream);
+                                 int C, int head_dim, float scale, float* out, int32_t* err, hipStream_t stream);
 // centroid scores and a per-row top-k in one pass (query heads per KV head <= 8,
 // clusters <= 1024, head_dim <= 128)
 hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv, int C,
                                 int head_dim, float scale, int k, int kmax, float mass, int k_min, int32_t* idx,
                                 int32_t* cnt, int32_t* err, hipStream_t stream);
 hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, int T, int hi, int64_t nk,
-                          int64_t pos0, float* out, hipStream_t stream);
+                          int64_t pos0, float* out, int32_t* err, hipStream_t stream);
 // Candidate slots of chunk c (keys c*chunk ..) of an indexer row with n causal
 // keys when `expect` kept keys are expected over the row: twice the chunk's
 // share plus 64, rounded up to a multiple of 64, at most the chunk's keys.
@@ -88,7 +90,7 @@ hipError_t launch_indexer_topk(const uint16_t* q, const uint16_t* k, const float
 size_t vs_workspace_bytes(int64_t rows, int64_t seq);
 hipError_t launch_vs_estimate(const uint16_t* q, const uint16_t* k, int batch, int hq, int hkv,
                               const HeadList& hl, int64_t seq, int head_dim, int last_q, float scale, float* a_v,
-                              float* a_s, void* ws, hipStream_t stream);
+                              float* a_s, int32_t* err, void* ws, hipStream_t stream);
 
 // pooled block scores and per-row top-k in one pass (at most 2048 blocks per row)
 constexpr int kBlockTopkMaxBlocks = 2048;
@@ -150,10 +152,13 @@ struct GatherParams {
   const int32_t* cluster_ptr;
   const int32_t* sel;
   const int32_t* tok_idx;
+  const int32_t* q_pos;  // optional [T]: query t sees context positions <= q_pos[t]
+  const int32_t* perm;   // cluster mode with q_pos: context position of each packed row [hkv, n_ctx]
   void* out;
   float* lse;
   int64_t n_ctx;
   int32_t T, hq, hkv, C, n_sel, n_tok;
+  int32_t tok_per_head;  // token mode: lists [T, hq, n_tok] instead of [T, n_tok]
   float scale;
   bool out_bf16;
 };

@@ -242,7 +242,7 @@ int sa_estimate(const sa_estimate_args* a, void* workspace, size_t workspace_byt
         e = sa::launch_pool(a->k, a->batch, (int)a->heads_kv, all, a->seq_k, (int)a->head_dim, bf, kBlock, pk, st);
       if (e == hipSuccess)
         e = sa::launch_block_score(pq, pk, (int)a->batch, (int)a->heads_q, (int)a->heads_kv, hl, (int)nb,
-                                   (int)a->head_dim, a->scale, a->scores, st);
+                                   (int)a->head_dim, a->scale, a->scores, a->err_flag, st);
       return launched(e, "sa_estimate(BLOCK)");
     }
     case SA_EST_VSLASH: {
@@ -250,17 +250,17 @@ int sa_estimate(const sa_estimate_args* a, void* workspace, size_t workspace_byt
       make_head_list(a->head_list, a->n_heads_list, a->heads_q, "sa_estimate(VSLASH)", hl);  // checked above
       return launched(sa::launch_vs_estimate((const uint16_t*)a->q, (const uint16_t*)a->k, (int)a->batch, (int)a->heads_q,
                                              (int)a->heads_kv, hl, a->seq_q, (int)a->head_dim, a->last_q, a->scale,
-                                             a->scores, a->scores2, workspace, st),
+                                             a->scores, a->scores2, a->err_flag, workspace, st),
                       "sa_estimate(VSLASH)");
     }
     case SA_EST_CENTROID:
       return launched(sa::launch_centroid_score(a->q, a->dtype == SA_BF16, a->centroids, (int)a->seq_q, (int)a->heads_q,
                                                 (int)a->heads_kv, (int)a->n_centroids, (int)a->head_dim, a->scale, a->scores,
-                                                st),
+                                                a->err_flag, st),
                       "sa_estimate(CENTROID)");
     case SA_EST_INDEXER:
       return launched(sa::launch_indexer((const uint16_t*)a->q, (const uint16_t*)a->k, a->weights, (int)a->seq_q,
-                                         (int)a->heads_q, a->seq_k, a->q_pos0, a->scores, st),
+                                         (int)a->heads_q, a->seq_k, a->q_pos0, a->scores, a->err_flag, st),
                       "sa_estimate(INDEXER)");
   }
   return fail(SA_ERR_VALUE, "sa_estimate: unknown kind");
@@ -509,8 +509,8 @@ static int check_fwd(const sa_fwd_args* a) {
   } else if (a->mode == SA_FWD_VSLASH) {
     if (!a->iv || !a->iv_cnt || !a->col || !a->col_cnt) return fail(SA_ERR_NULL, "sa_block_sparse_fwd(VSLASH): tables required");
     if (a->max_iv <= 0 || a->max_col <= 0) return fail(SA_ERR_SHAPE, "sa_block_sparse_fwd(VSLASH): capacities must be positive");
-    if (a->dtype == SA_BF16 && (a->max_iv > 64 || a->max_col > 2048))
-      return fail(SA_ERR_UNSUPPORTED, "sa_block_sparse_fwd(VSLASH): bf16 path stages at most 64 intervals and 2048 columns per row");
+    if (a->dtype == SA_BF16 && (a->max_iv > 64 || a->max_col > 1920))
+      return fail(SA_ERR_UNSUPPORTED, "sa_block_sparse_fwd(VSLASH): bf16 path stages at most 64 intervals and 1920 columns per row");
   } else if (a->mode == SA_FWD_ASHAPE) {
     if (a->n_sink < 0 || a->n_local < 0) return fail(SA_ERR_VALUE, "sa_block_sparse_fwd(ASHAPE): n_sink and n_local must be >= 0");
     if ((int64_t)a->n_sink + a->n_local > 2048)
@@ -639,11 +639,12 @@ static int check_gather(const sa_gather_args* a, size_t* ws) {
     if (a->n_q * (a->heads_q / a->heads_kv) > 64)
       return fail(SA_ERR_UNSUPPORTED, "sa_gather_decode(CLUSTER): at most 64 queries per KV head");
     if (a->n_clusters > 1024) return fail(SA_ERR_UNSUPPORTED, "sa_gather_decode(CLUSTER): at most 1024 clusters");
+    if (a->q_pos && !a->perm) return fail(SA_ERR_NULL, "sa_gather_decode(CLUSTER): q_pos needs perm");
     *ws = sa::cluster_decode_workspace_bytes((int)a->n_q, (int)a->heads_q, (int)a->heads_kv, a->n_clusters, a->n_ctx);
   } else if (a->mode == SA_GATHER_TOKEN) {
     if (!a->tok_idx) return fail(SA_ERR_NULL, "sa_gather_decode(TOKEN): tok_idx required");
     if (a->n_tok <= 0) return fail(SA_ERR_SHAPE, "sa_gather_decode(TOKEN): n_tok must be positive");
-    if (a->heads_q / a->heads_kv != 16) return fail(SA_ERR_UNSUPPORTED, "sa_gather_decode(TOKEN): 16 query heads per KV head");
+    if (a->tok_per_head != 0 && a->tok_per_head != 1) return fail(SA_ERR_VALUE, "sa_gather_decode(TOKEN): tok_per_head must be 0 or 1");
     *ws = sa::token_gather_workspace_bytes((int)a->n_q, (int)a->heads_q, a->n_tok);
   } else {
     return fail(SA_ERR_VALUE, "sa_gather_decode: unknown mode %d", a->mode);
@@ -674,6 +675,9 @@ int sa_gather_decode(const sa_gather_args* a, void* workspace, size_t workspace_
   p.cluster_ptr = a->cluster_ptr;
   p.sel = a->sel;
   p.tok_idx = a->tok_idx;
+  p.q_pos = a->q_pos;
+  p.perm = a->perm;
+  p.tok_per_head = a->mode == SA_GATHER_TOKEN ? a->tok_per_head : 0;
   p.out = a->out;
   p.lse = a->lse;
   p.n_ctx = a->n_ctx;

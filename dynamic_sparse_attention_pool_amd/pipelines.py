@@ -76,7 +76,7 @@ class BlockSparseLayer:
                              err_flag=self.err, **budget)
             return
         sa_estimate(BLOCK_MEANPOOL, self.q, self.k, self.scores, scale=self.scale, pooled_q=self.pooled_q,
-                    pooled_k=self.pooled_k, heads=self.heads)
+                    pooled_k=self.pooled_k, heads=self.heads, err_flag=self.err)
 
     def select(self):
         if self.fused:
@@ -130,7 +130,7 @@ class VerticalSlashLayer:
 
     def estimate(self):
         self.ws = sa_estimate(VSLASH, self.q, self.k, self.a_v, scores2=self.a_s, scale=self.scale,
-                              heads=self.heads)
+                              heads=self.heads, workspace=self.ws)
 
     def select(self):
         sa_select_topk(self.a_v.view(self.R, self.N), self.vert, self.vert_cnt, k=self.n_vert)
@@ -314,28 +314,36 @@ class IndexerPrefill:
             self.scores = _t().empty((self.T, self.N), dtype=_t().float32, device=self.qi.device)
         sa_estimate(INDEXER, self.qi, self.ki, self.scores, weights=self.w, q_pos0=self.pos0)
         sa_select_topk(self.scores, self.idx, self.cnt, k=self.k_sel, causal=True, causal_period=self.T,
-                       causal_offset=self.pos0)
+                       causal_offset=self.pos0, err_flag=self.err)
 
-    def index(self, check: bool = False):
+    def index(self, check: bool = True):
         """The index of the full layer.  Fused: one call without the score
-        matrix; with check=True the host reads the error flag (a device sync)
-        and redoes the chunk with two calls when a row's threshold failed."""
+        matrix.  With check=True (the default) the host reads the error flag
+        (one device sync): rows whose sampled threshold failed (flag value 2,
+        cnt = -1) make the whole chunk be recomputed with two calls, and a NaN
+        among the scores (flag value 1) raises.  check=False leaves reading
+        the flag to the caller."""
         if not self.fused:
             self.index_two_call()
-            return
-        self.ws_index = sa_indexer_topk(self.qi, self.ki, self.idx, self.cnt, weights=self.w, q_pos0=self.pos0,
-                                        k=self.k_sel, err_flag=self.err, workspace=self.ws_index)
-        if check and int(self.err.item()) & 2:
-            self.err.zero_()
-            self.index_two_call()
+        else:
+            self.ws_index = sa_indexer_topk(self.qi, self.ki, self.idx, self.cnt, weights=self.w,
+                                            q_pos0=self.pos0, k=self.k_sel, err_flag=self.err,
+                                            workspace=self.ws_index)
+            if check and int(self.err.item()) & 2:
+                self.err.bitwise_and_(~2)   # keep bit 0 (NaN) if the fused call set it
+                self.index_two_call()
+        if check and int(self.err.item()) & 1:
+            raise FloatingPointError("indexer: NaN among the scores; the index is unspecified")
 
     def attend(self, layer: int):
         q, k, v = self.layers[layer]
         self.ws = sa_gather_decode(q, k, v, self.outs[layer], tok_idx=self.idx, scale=self.scale,
                                    workspace=self.ws)
 
-    def step(self, reuse: bool = True):
+    def step(self, reuse: bool = True, check: bool = True):
+        """Every layer: full layers (or all of them without reuse) build the
+        index, checked as in index(); each layer then attends through it."""
         for layer in range(len(self.layers)):
             if layer in self.full or not reuse:
-                self.index()
+                self.index(check=check)
             self.attend(layer)

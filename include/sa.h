@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define SA_ABI_VERSION 8
+#define SA_ABI_VERSION 9
 
 typedef enum sa_status {
   SA_OK = 0,
@@ -59,7 +59,8 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_I32 = 2 } sa_dtype;
  *   q [B,Hq,N,d], k [B,Hkv,N,d] (F32 or BF16), N a multiple of block_size.
  *   scores [B,Hq,nb,nb] float, nb = N/block_size:
  *     scores[b,h,i,j] = mean(q rows of block i) . mean(k rows of block j) * scale
- *     for j <= i, and -INFINITY for j > i.
+ *     for j <= i.  Entries with j > i are not written (sa_select_topk with
+ *     causal = 1 never reads them), which halves the bytes this call stores.
  *   pooled_q [B,Hq,nb,d] / pooled_k [B,Hkv,nb,d]: optional float outputs of the
  *   block means; when NULL the means live in the workspace.
  *
@@ -123,6 +124,11 @@ typedef struct sa_estimate_args {
   const int32_t* head_list; /* BLOCK, VSLASH: optional host array */
   int32_t n_heads_list;
   int32_t reserved1;
+  int32_t* err_flag;      /* optional device int32: bit 0 (value 1) is set when a
+                             score written (masked entries aside) is NaN or
+                             infinite, and for INDEXER also when an element of
+                             q, k or weights is (its ReLU can hide a NaN
+                             product); never cleared by the library */
 } sa_estimate_args;
 
 int sa_estimate_workspace_bytes(const sa_estimate_args* args, size_t* bytes);
@@ -225,13 +231,17 @@ int sa_select_mass(const sa_select_mass_args* args, void* stream);
  * score matrix.
  *
  * "MInference 1.0" article, §方法介紹 (block indices from mean-pooled Q and K)
- * with the selection of sa_select_topk.  The result equals
- * sa_estimate(BLOCK_MEANPOOL) followed by sa_select_topk on its score rows
- * with causal = 1 and causal_period = nb (row i of a head has the candidate
- * blocks 0..i), with the same n_sink / n_local / k or ratio budget, order and
- * output format.  The scores are never written to
- * memory: a workgroup scores 16 consecutive rows, keeps them in registers and
- * selects from them.
+ * with the selection of sa_select_topk: the rule of sa_estimate(BLOCK_MEANPOOL)
+ * followed by sa_select_topk on its score rows with causal = 1 and
+ * causal_period = nb (row i of a head has the candidate blocks 0..i), with the
+ * same n_sink / n_local / k or ratio budget, order and output format.  The
+ * scores are never written to memory: a workgroup scores 16 consecutive rows,
+ * keeps them in registers and selects from them.  Its pooled dot products are
+ * summed in another order than sa_estimate's, so the two results are bit for
+ * bit equal when every product and partial sum is exact in fp32 (e.g.
+ * integer-valued inputs with scale 1); otherwise a row whose cut falls
+ * between scores within fp32 rounding of each other may keep a different,
+ * equally valid set.
  *
  * kind = SA_EST_BLOCK_MEANPOOL: q [B,Hq,N,d], k [B,Hkv,N,d] (F32 or BF16,
  * d = 64 or 128), N a multiple of 64 with N/64 <= 2048.
@@ -301,6 +311,8 @@ int sa_estimate_topk(const sa_estimate_topk_args* args, void* workspace, size_t 
  *       intervals [start, end), ascending; iv_cnt [rows, nqb].
  *   col [rows, nqb, n_vert]: kept columns c <= 64i+63 outside those intervals,
  *       ascending; col_cnt [rows, nqb].
+ * Counts are clipped to [0, n_vert] and [0, n_slash]; negative offsets and
+ * columns outside [0, seq) are ignored.
  * ====================================================================== */
 typedef struct sa_vs_build_args {
   int64_t rows;
@@ -336,9 +348,13 @@ int sa_vs_build(const sa_vs_build_args* args, void* stream);
  * Row r of query block i attends key c only when c <= r (token-causal).
  * mode = SA_FWD_BLOCK: block_idx [B,Hq,nqb,kmax] ascending, -1 padded, and
  *   block_cnt [B,Hq,nqb]; keys = union of blocks [64j, 64j+64).
- *   Every listed block must satisfy 0 <= j <= i.
+ *   Listed blocks outside 0 <= j <= i are skipped; block_cnt is clipped to
+ *   [0, kmax].  bf16 inputs: kmax <= 2048.
  * mode = SA_FWD_VSLASH: the sa_vs_build tables (iv/iv_cnt with capacity
  *   max_iv, col/col_cnt with capacity max_col); keys = intervals ∪ columns.
+ *   Counts are clipped to the capacities, intervals to [0, min(N, 64i+64)),
+ *   and a column outside [0, N) is ignored, so no table entry can make the
+ *   kernel read outside K and V.  bf16 inputs: max_iv <= 64, max_col <= 1920.
  * mode = SA_FWD_ASHAPE ("MInference 1.0" article, §方法介紹, the A-shape
  *   pattern; "稀疏注意力机制解析" explainer, §1.2, global plus local-window
  *   attention): no tables; query block i keeps blocks 0 .. n_sink-1 and the
@@ -405,9 +421,18 @@ int sa_block_sparse_fwd(const sa_fwd_args* args, void* workspace, size_t workspa
  *   layers reuse from the nearest full layer — the index cache is simply the
  *   caller's tok_idx buffer passed to several layers).
  *   q [T,Hq,d] BF16; k, v [Hkv,Nctx,d] BF16 in context order; tok_idx
- *   [T,n_tok] int32, shared by all heads of token t, distinct, -1 padded.
- * d = 128.  out [T,Hq,d] (out_dtype F32 or BF16); lse [T,Hq] optional.
- * Both modes need a workspace.
+ *   [T,n_tok] int32 shared by every head of token t (tok_per_head = 0), or
+ *   [T,Hq,n_tok] with one list per (token, query head) (tok_per_head = 1);
+ *   ids distinct within a list, -1 padded (ids outside [0, Nctx) are padding).
+ *   Shared lists with 16 query heads per KV head run the heads together on
+ *   the matrix cores; other shapes take one wave per (token, head).
+ * q_pos: optional device int32 [T]: query t attends only context positions
+ *   <= q_pos[t] (a causal bound).  Token mode: the position is the id.
+ *   Cluster mode: the position of packed row p of KV head g is perm[g,p]
+ *   (sa_cluster_pack's perm, required with q_pos).  NULL: no bound.
+ * d = 128.  out [T,Hq,d] (out_dtype F32 or BF16); lse [T,Hq] optional.  A
+ * query with no admissible key gets out = 0 and lse = -INFINITY.
+ * Cluster mode needs a workspace; token mode none.
  * ====================================================================== */
 enum { SA_GATHER_CLUSTER = 0, SA_GATHER_TOKEN = 1 };
 
@@ -424,7 +449,7 @@ typedef struct sa_gather_args {
   float scale;
   int32_t n_sel;
   int32_t n_tok;
-  int32_t reserved0;
+  int32_t tok_per_head;   /* TOKEN: 0 = tok_idx [T,n_tok], 1 = [T,Hq,n_tok] */
   const void* q;
   const void* k;
   const void* v;
@@ -433,6 +458,8 @@ typedef struct sa_gather_args {
   const int32_t* tok_idx;
   void* out;
   float* lse;
+  const int32_t* q_pos;   /* optional [T] causal bound */
+  const int32_t* perm;    /* CLUSTER with q_pos: [Hkv,Nctx] */
 } sa_gather_args;
 
 int sa_gather_decode_workspace_bytes(const sa_gather_args* args, size_t* bytes);
@@ -534,9 +561,10 @@ int sa_kmeans(const sa_kmeans_args* args, void* workspace, size_t workspace_byte
  * lies 8 relative spreads below the expected count, the cap 16 above), the
  * row gets cnt = -1 and idx all -1, and bit 1 (value 2) of err_flag is set:
  * the caller recomputes such rows with the two-call path.
- * err_flag bit 0 (value 1): a NaN among the scores the method ranks (the
- * output is then unspecified).  err_flag is optional and never cleared by
- * the library.
+ * err_flag bit 0 (value 1): a NaN among the scores the method ranks, or a
+ * NaN or infinite element of q, k or weights (the output is then
+ * unspecified; the inputs are scanned only when err_flag is given).
+ * err_flag is optional and never cleared by the library.
  *
  * Workspace: sa_indexer_topk_workspace_bytes (T * Nk/16 * 4 bytes of sampled
  * scores when some row exceeds 8192 keys, plus T * (8192 + 128 * Nk/8192) * 8

@@ -43,6 +43,15 @@ def host(t) -> np.ndarray:
     return t.detach().cpu().numpy()
 
 
+def lower_triangle(S: np.ndarray) -> np.ndarray:
+    """Block scores as the oracle states them: the library leaves entries
+    above the diagonal (j > i) unwritten, the oracle holds -inf there."""
+    S = np.array(S, copy=True)
+    nb = S.shape[-1]
+    S[..., np.triu(np.ones((nb, nb), bool), 1)] = -np.inf
+    return S
+
+
 def pad_table(lists, kmax: int):
     """list of index arrays -> (idx [R,kmax] int32 padded with -1, cnt [R])."""
     R = len(lists)
@@ -168,7 +177,7 @@ def fwd_on_oracle_vs(sa, q, k, v, h: int, cols: np.ndarray, offs: np.ndarray, ma
         colc[i] = len(vert)
         col[i, :len(vert)] = vert
     out = t.zeros((B, Hq, N, d), dtype=t.float32, device=q.device)
-    sa.sa_block_sparse_fwd(q, k, v, out, iv=dev_i32(iv[None]), iv_cnt=dev_i32(ivc[None]), col=dev_i32(col[None]),
-                           col_cnt=dev_i32(colc[None]), heads=[h])
+    sa.sa_block_sparse_fwd(q, k, v, out, iv=dev_i32(iv[None, None]), iv_cnt=dev_i32(ivc[None, None]),
+                           col=dev_i32(col[None, None]), col_cnt=dev_i32(colc[None, None]), heads=[h])
     t.cuda.synchronize()
     return host(out[0, h])

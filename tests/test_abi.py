@@ -305,9 +305,53 @@ def test_estimate_and_gather_argument_errors(lib):
     g.n_clusters, g.n_sel = 16, 4
     g.n_q = 32                                                        # 32*4 queries per KV head > 64
     assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 6
+    g.n_q = 8
+    g.q_pos = 256                                                     # a causal bound needs the pack's perm
+    assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 1
     g.mode = F.SA_GATHER_TOKEN
-    g.tok_idx, g.n_tok, g.heads_kv = 256, 64, 4                       # 8 heads per KV head
-    assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 6
+    g.tok_idx, g.n_tok, g.heads_kv = 256, 64, 4
+    g.tok_per_head = 2                                                # neither shared (0) nor per head (1)
+    assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 8
+
+
+def test_binding_rejects_inconsistent_tensors(lib):
+    """Every wrapper checks dtype, shape and device of each tensor against
+    the sizes it passes to the library, before any launch (CPU tensors here,
+    so a consistent call would stop at the device check instead)."""
+    import torch as tt
+
+    import dynamic_sparse_attention_pool_amd as sa
+    bf, f32, i32 = tt.bfloat16, tt.float32, tt.int32
+    q = tt.zeros((1, 4, 256, 128), dtype=bf)
+    k = tt.zeros((1, 2, 256, 128), dtype=bf)
+    out = tt.zeros((1, 4, 256, 128), dtype=f32)
+    idx, cnt = tt.zeros((1, 4, 4, 3), dtype=i32), tt.zeros((1, 4, 4), dtype=i32)
+    cases = [
+        (lambda: sa.sa_block_sparse_fwd(q, k.float(), k, out, block_idx=idx, block_cnt=cnt), "k"),
+        (lambda: sa.sa_block_sparse_fwd(q, k[:, :, :128], k, out, block_idx=idx, block_cnt=cnt), "k"),
+        (lambda: sa.sa_block_sparse_fwd(q, k, k[:, :1], out, block_idx=idx, block_cnt=cnt), "v"),
+        (lambda: sa.sa_block_sparse_fwd(q, k, k, out[:, :2], block_idx=idx, block_cnt=cnt), "out"),
+        (lambda: sa.sa_block_sparse_fwd(q, k, k, out, block_idx=idx.float(), block_cnt=cnt), "block_idx"),
+        (lambda: sa.sa_block_sparse_fwd(q, k, k, out, block_idx=idx, block_cnt=cnt[:, :, :2]), "block_cnt"),
+        (lambda: sa.sa_estimate(sa.BLOCK_MEANPOOL, q, k, tt.zeros((1, 4, 4, 3), dtype=f32)), "scores"),
+        (lambda: sa.sa_estimate(sa.BLOCK_MEANPOOL, q, k, tt.zeros((1, 4, 4, 4), dtype=bf)), "scores"),
+        (lambda: sa.sa_select_topk(tt.zeros((8, 16), dtype=f32), tt.zeros((7, 2), dtype=i32),
+                                   tt.zeros(8, dtype=i32), k=2), "idx"),
+        (lambda: sa.sa_select_topk(tt.zeros((8, 16), dtype=f32), tt.zeros((8, 2), dtype=i32),
+                                   tt.zeros(8, dtype=f32), k=2), "cnt"),
+        (lambda: sa.sa_gather_decode(tt.zeros((2, 32, 128), dtype=bf), tt.zeros((8, 64, 128), dtype=bf),
+                                     tt.zeros((8, 64, 64), dtype=bf), tt.zeros((2, 32, 128), dtype=f32),
+                                     tok_idx=tt.zeros((2, 16), dtype=i32)), "v"),
+        (lambda: sa.sa_gather_decode(tt.zeros((2, 32, 128), dtype=bf), tt.zeros((8, 64, 128), dtype=bf),
+                                     tt.zeros((8, 64, 128), dtype=bf), tt.zeros((2, 32, 128), dtype=f32),
+                                     tok_idx=tt.zeros((2, 31, 16), dtype=i32)), "tok_idx"),
+        (lambda: sa.sa_indexer_topk(tt.zeros((4, 32, 64), dtype=bf), tt.zeros((100, 64), dtype=bf),
+                                    tt.zeros((4, 8), dtype=i32), tt.zeros(4, dtype=i32),
+                                    weights=tt.zeros(16, dtype=f32), q_pos0=96, k=8), "weights"),
+    ]
+    for fn, name in cases:
+        with pytest.raises(ValueError, match=name):
+            fn()
 
 
 def test_missing_library_fails_loudly(monkeypatch):

@@ -8,7 +8,7 @@ import pytest
 import oracle
 import workloads as W
 from gpu_helpers import (assert_attention_close, assert_scores_close, certify_prefill, dev_bf16, dev_f32,
-                         dev_i32, host, pad_table, tie_tolerant_valid, torch)
+                         dev_i32, host, lower_triangle, pad_table, tie_tolerant_valid, torch)
 
 pytestmark = pytest.mark.gpu
 
@@ -114,15 +114,22 @@ def test_select_ragged_long_rows_and_nan_flag(sa):
 
 
 def run_block_estimate(sa, q, k, scale):
+    """Pooled scores with the upper triangle checked untouched (the buffer is
+    pre-filled with a sentinel) and then stated as -inf, like the oracle's."""
     t = torch()
     B, Hq, N, d = q.shape
     nb = N // 64
-    scores = t.empty((B, Hq, nb, nb), dtype=t.float32, device=q.device)
+    scores = t.full((B, Hq, nb, nb), 7777.0, dtype=t.float32, device=q.device)
     pq = t.empty((B, Hq, nb, d), dtype=t.float32, device=q.device)
     pk = t.empty((B, k.shape[1], nb, d), dtype=t.float32, device=q.device)
-    sa.sa_estimate(sa.BLOCK_MEANPOOL, q, k, scores, scale=scale, pooled_q=pq, pooled_k=pk)
+    err = t.zeros(1, dtype=t.int32, device=q.device)
+    sa.sa_estimate(sa.BLOCK_MEANPOOL, q, k, scores, scale=scale, pooled_q=pq, pooled_k=pk, err_flag=err)
     t.cuda.synchronize()
-    return host(scores), host(pq), host(pk)
+    s = host(scores)
+    upper = np.triu(np.ones((nb, nb), bool), 1)
+    assert np.all(s[..., upper] == 7777.0), "entries above the diagonal were written"
+    assert int(host(err)[0]) == 0
+    return lower_triangle(s), host(pq), host(pk)
 
 
 def test_block_estimate_exact_integer_inputs(sa):
@@ -224,7 +231,7 @@ def run_block_layer(sa, q, k, v, n_sink, n_local, kmax, k_fixed=None, ratio=None
     sa.sa_block_sparse_fwd(q, k, v, out, block_idx=idx.view(B, Hq, nb, kmax), block_cnt=cnt.view(B, Hq, nb),
                            scale=scale)
     t.cuda.synchronize()
-    return host(scores), host(idx).reshape(B, Hq, nb, kmax), host(cnt).reshape(B, Hq, nb), host(out)
+    return lower_triangle(host(scores)), host(idx).reshape(B, Hq, nb, kmax), host(cnt).reshape(B, Hq, nb), host(out)
 
 
 def test_end_to_end_sink_diag_top2_fp32(sa):
@@ -272,3 +279,83 @@ def test_determinism_bitwise(sa):
     b = run_block_layer(sa, q, k, v, 1, 4, 12, ratio=(10, 100))
     for x, y in zip(a, b):
         assert np.array_equal(x, y)
+
+
+def test_fwd_out_of_range_block_entries(sa):
+    """Table entries the forward cannot use — negative ids, blocks above the
+    diagonal, counts above kmax or below 0 — are skipped or clipped: the output
+    equals, bit for bit, the forward on the cleaned table, and nothing is read
+    outside K and V."""
+    t = torch()
+    B, Hq, Hkv, N, d = 1, 2, 1, 1024, 128
+    nb = N // 64
+    inp = W.prefill_bf16(61, B, Hq, Hkv, N, d)
+    r = np.random.default_rng(61)
+    clean = [[np.unique(np.concatenate([[0, i], r.choice(i + 1, size=min(i + 1, 3), replace=False)]))
+              for i in range(nb)] for _ in range(Hq)]
+    kmax = 8
+    idx_c, cnt_c = pad_table([x for h in clean for x in h], kmax)
+    idx_b, cnt_b = idx_c.copy(), cnt_c.copy()
+    for row in range(Hq * nb):
+        i = row % nb
+        n = cnt_b[row]
+        junk = [-5, i + 1 + r.integers(0, 50), 10 ** 9, -(10 ** 9)]
+        room = kmax - n
+        if room > 0:
+            idx_b[row, n:n + room] = np.resize(junk, room)   # skipped entries after the kept ones
+            cnt_b[row] = kmax if row % 3 else kmax + 100     # count above kmax is clipped to kmax
+    cnt_b[5] = -7                                           # a negative count keeps nothing
+    cnt_c[5] = 0
+    q, k, v = dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v)
+    outs = []
+    for idx, cnt in ((idx_c, cnt_c), (idx_b, cnt_b)):
+        o = t.empty(q.shape, dtype=t.float32, device=q.device)
+        sa.sa_block_sparse_fwd(q, k, v, o, block_idx=dev_i32(idx).view(B, Hq, nb, kmax),
+                               block_cnt=dev_i32(cnt).view(B, Hq, nb))
+        outs.append(host(o))
+    t.cuda.synchronize()
+    assert np.array_equal(outs[0], outs[1])
+    assert np.all(outs[1][0, 0, 5 * 64:6 * 64] == 0)
+
+
+def test_fwd_rows_beyond_2_pow_32_bytes(sa):
+    """A 16.8M-token head (K and V above 4 GiB each): the last query block
+    attends blocks on both sides of row 2^24, where byte offsets pass 2^32.
+    Compared with the oracle on those keys (the other rows are zero and
+    unread)."""
+    t = torch()
+    d = 128
+    N = (1 << 24) + 2048
+    nb = N // 64
+    i = nb - 1
+    blocks = np.array([0, (1 << 18) - 1, 1 << 18, (1 << 18) + 26, i], np.int64)
+    rows = (blocks[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)
+    rg = W.rng(62, 0)
+    kq = W.f32_to_bf16(rg.standard_normal((64, d), dtype=np.float32))
+    kk = W.f32_to_bf16(rg.standard_normal((rows.size, d), dtype=np.float32))
+    kv = W.f32_to_bf16(rg.standard_normal((rows.size, d), dtype=np.float32))
+    q = t.zeros((1, 1, N, d), dtype=t.bfloat16, device="cuda:0")
+    k = t.zeros_like(q)
+    v = t.zeros_like(q)
+    q[0, 0, i * 64:] = dev_bf16(kq)
+    ridx = t.from_numpy(rows).to("cuda:0")
+    k[0, 0].index_copy_(0, ridx, dev_bf16(kk))
+    v[0, 0].index_copy_(0, ridx, dev_bf16(kv))
+    kmax = 8
+    idx = np.full((nb, kmax), -1, np.int32)
+    cnt = np.zeros(nb, np.int32)
+    idx[i, :blocks.size] = blocks
+    cnt[i] = blocks.size
+    out = t.empty_like(q)
+    sa.sa_block_sparse_fwd(q, k, v, out, block_idx=dev_i32(idx).view(1, 1, nb, kmax),
+                           block_cnt=dev_i32(cnt).view(1, 1, nb))
+    got = host(out[0, 0, i * 64:])
+    t.cuda.synchronize()
+    del q, k, v, out
+    t.cuda.empty_cache()
+    # compact problem: kept keys in ascending order, query positions mapped to
+    # the number of kept keys at or before them (the causal relation is kept)
+    qpos = i * 64 + np.arange(64)
+    want, _ = oracle.attend_rows(W.bf16_to_f32(kq), W.bf16_to_f32(kk), W.bf16_to_f32(kv), np.arange(rows.size),
+                                 1 / math.sqrt(d), row_pos=np.searchsorted(rows, qpos, side="right") - 1)
+    assert_attention_close(got, want, bf16=True, what="rows beyond 2^32 bytes")

@@ -9,6 +9,7 @@ import pytest
 import oracle
 import workloads as W
 from gpu_helpers import (assert_attention_close, assert_scores_close, dev_bf16, fwd_on_oracle_blocks, host,
+                         lower_triangle,
                          tie_tolerant_valid, torch)
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +41,7 @@ def test_block_sparse_layer_full_size(sa, N, ratio, seed):
         f = oracle.forced_set(i + 1, 1, 4)
         per_row.append(f.shape[0] + oracle.budget(i + 1, f.shape[0], None, ratio))
     assert int(cnt.sum()) == 32 * sum(per_row)
-    S_gpu = host(layer.scores)
+    S_gpu = lower_triangle(host(layer.scores))
     rng = np.random.default_rng(0)
     certified = total = 0
     for h in [0, 5, 31]:

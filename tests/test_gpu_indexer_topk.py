@@ -218,6 +218,21 @@ def test_indexer_topk_bracket_failure_is_flagged(sa, sampled_hot):
     got = host(ip.idx)
     for t in range(T):
         assert np.array_equal(got[t], sel[t]), t
+    assert int(ip.err.item()) == 0  # the redo cleared bit 1 and raised nothing else
+    # a whole step takes the same checked path: both layers (the second one
+    # reusing the index) attend through the redone index, exactly as the
+    # two-call pipeline's layers do
+    L2 = W.mqa_layer(94, 1, T, 16, 1, N, 128)
+    layers2 = layers + [(dev_bf16(L2.q), dev_bf16(L2.k), dev_bf16(L2.v))]
+    fu = IndexerPrefill(dev_bf16(qi), dev_bf16(ki), dev_f32(w), pos0, layers2, k_sel=k, fused=True)
+    tc = IndexerPrefill(dev_bf16(qi), dev_bf16(ki), dev_f32(w), pos0, layers2, k_sel=k, fused=False)
+    fu.step(reuse=True)
+    tc.step(reuse=True)
+    torch().cuda.synchronize()
+    assert np.array_equal(host(fu.idx), host(tc.idx)) and np.array_equal(host(fu.idx), sel)
+    for a, b in zip(fu.outs, tc.outs):
+        assert np.array_equal(host(a), host(b))
+    assert int(fu.err.item()) == 0
 
 
 def test_indexer_topk_nan_flag(sa):
@@ -227,6 +242,22 @@ def test_indexer_topk_nan_flag(sa):
     w[3] = np.nan
     _, _, err = run_fused(sa, ind.qi, ind.ki, w, ind.pos0, k)
     assert err & 1
+
+
+@pytest.mark.parametrize("fused", [True, False])
+def test_indexer_pipeline_nan_raises(sa, fused):
+    """A NaN among the indexer scores is reported by the checked index, fused
+    or two-call, instead of reaching the layers."""
+    from dynamic_sparse_attention_pool_amd.pipelines import IndexerPrefill
+    T, Hi, N, k = 24, 32, 9000, 64
+    ind = W.indexer_random(95, T, Hi, 64, N)
+    w = ind.w.copy()
+    w[3] = np.nan
+    L = W.mqa_layer(95, 0, T, 16, 1, N, 128)
+    ip = IndexerPrefill(dev_bf16(ind.qi), dev_bf16(ind.ki), dev_f32(w), ind.pos0,
+                        [(dev_bf16(L.q), dev_bf16(L.k), dev_bf16(L.v))], k_sel=k, fused=fused)
+    with pytest.raises(FloatingPointError):
+        ip.step()
 
 
 def test_indexer_topk_full_size(sa):

@@ -133,7 +133,8 @@ def test_vs_forward_on_oracle_selection(sa):
     r = np.random.default_rng(53)
     sel = [[(np.sort(r.choice(N, size=150, replace=False)), np.sort(r.choice(N, size=12, replace=False)))
             for _ in range(4)]]
-    sel[0][2] = (np.arange(N), np.arange(0, N, 64))   # block-aligned slash tiles cover every causal key
+    # block-aligned slash tiles cover every causal key (1920 columns: the bf16 path's table capacity)
+    sel[0][2] = (np.arange(1920), np.arange(0, N, 64))
     sel[0][3] = (np.sort(r.choice(N, size=5, replace=False)), np.array([1000, 1500]))   # many empty rows
     o, l = run_vs_fwd(sa, inp, sel, N)
     wo, wl = oracle.vs_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), sel, 64, 1 / math.sqrt(d))
@@ -203,3 +204,98 @@ def test_vs_full_size_sampled(sa):
             for i in blocks:
                 rows = slice(64 * i, 64 * i + 64)
                 assert_attention_close(o[rows], wo[0, h, rows], bf16=True, what=f"h{h} block {i}")
+
+
+def test_vs_out_of_range_entries(sa):
+    """Out-of-range selections and tables never reach memory outside K and V.
+    sa_vs_build drops negative offsets and columns outside [0, N) and clips
+    counts to the capacities: its tables equal those built from the valid
+    entries alone.  The forward clips intervals to the block's visible keys,
+    ignores columns outside [0, N) and clips counts: on such tables it equals
+    the oracle on the valid keys."""
+    t = torch()
+    N, d, Hq = 1024, 128, 2
+    nb = N // 64
+    inp = W.prefill_bf16(63, 1, Hq, 1, N, d)
+    r = np.random.default_rng(63)
+    valid = [(np.sort(r.choice(N, size=40, replace=False)), np.sort(r.choice(N, size=6, replace=False)))
+             for _ in range(Hq)]
+    nv, ns = 48, 10
+    # the same selections with junk: negative offsets sort first, columns out of range at both ends
+    vert = np.zeros((Hq, nv), np.int32)
+    slash = np.zeros((Hq, ns), np.int32)
+    vc = np.zeros(Hq, np.int32)
+    sc = np.zeros(Hq, np.int32)
+    for h, (c, o) in enumerate(valid):
+        cj = np.concatenate([[-9, -1], c, [N, N + 7, 10 ** 9]])
+        oj = np.concatenate([[-50, -3], o])
+        vert[h, :cj.size], vc[h] = cj, cj.size + 20     # count above the capacity: clipped to nv
+        slash[h, :oj.size], sc[h] = oj, oj.size
+    vert[:, 45:] = N + 1
+    tables = []
+    for vsel in ((vert, vc, slash, sc), None):
+        if vsel is None:
+            v2 = np.zeros((Hq, nv), np.int32)
+            s2 = np.zeros((Hq, ns), np.int32)
+            for h, (c, o) in enumerate(valid):
+                v2[h, :c.size], s2[h, :o.size] = c, o
+            vsel = (v2, np.array([c.size for c, _ in valid], np.int32), s2,
+                    np.array([o.size for _, o in valid], np.int32))
+        iv = t.empty((1, Hq, nb, ns, 2), dtype=t.int32, device="cuda:0")
+        ivc = t.empty((1, Hq, nb), dtype=t.int32, device="cuda:0")
+        col = t.empty((1, Hq, nb, nv), dtype=t.int32, device="cuda:0")
+        colc = t.empty((1, Hq, nb), dtype=t.int32, device="cuda:0")
+        sa.sa_vs_build(dev_i32(vsel[0]), dev_i32(vsel[1]), dev_i32(vsel[2]), dev_i32(vsel[3]), iv.view(Hq, -1),
+                       ivc.view(Hq, -1), col.view(Hq, -1), colc.view(Hq, -1), seq=N)
+        t.cuda.synchronize()
+        tables.append((host(iv), host(ivc), host(col), host(colc)))
+    (iv_j, ivc_j, col_j, colc_j), (iv_v, ivc_v, col_v, colc_v) = tables
+    assert np.array_equal(ivc_j, ivc_v) and np.array_equal(colc_j, colc_v)
+    for h in range(Hq):
+        for i in range(nb):
+            assert np.array_equal(iv_j[0, h, i, :ivc_j[0, h, i]], iv_v[0, h, i, :ivc_v[0, h, i]])
+            assert np.array_equal(col_j[0, h, i, :colc_j[0, h, i]], col_v[0, h, i, :colc_v[0, h, i]])
+    # forward on hand-made tables with out-of-range entries
+    iv = iv_v.copy()
+    ivc = ivc_v.copy()
+    col = np.full_like(col_v, -1)
+    colc = np.zeros_like(colc_v)
+    for h in range(Hq):
+        for i in range(nb):
+            n = ivc[0, h, i]
+            if n < ns:
+                iv[0, h, i, n] = (64 * i + 64, 64 * i + 5000)   # beyond the block: clipped to nothing
+                ivc[0, h, i] = n + 1
+            good = col_v[0, h, i, :colc_v[0, h, i]]
+            cj = np.concatenate([[-4], good, [N + 3]])[:nv]
+            col[0, h, i, :cj.size] = cj
+            colc[0, h, i] = cj.size + (5 if i % 2 else 0)     # some counts above the capacity
+    # a negative start is clipped to 0; the row's listed columns are kept
+    # disjoint from the widened interval, as the tables' contract requires
+    first_end = iv[0, 0, 3, 0, 1]
+    iv[0, 0, 3, 0, 0] = -100
+    rest = [c for c in col[0, 0, 3, :min(colc[0, 0, 3], nv)] if not (0 <= c < first_end)]
+    col[0, 0, 3] = -1
+    col[0, 0, 3, :len(rest)] = rest
+    colc[0, 0, 3] = len(rest)
+    out = t.empty(inp.q.shape, dtype=t.float32, device="cuda:0")
+    sa.sa_block_sparse_fwd(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), out, iv=dev_i32(iv), iv_cnt=dev_i32(ivc),
+                           col=dev_i32(col), col_cnt=dev_i32(colc))
+    got = host(out)
+    t.cuda.synchronize()
+    q, k, v = inp.f32("q"), inp.f32("k"), inp.f32("v")
+    scale = 1 / math.sqrt(d)
+    want = np.zeros_like(got)
+    for h in range(Hq):
+        for i in range(nb):
+            # the stated clipping, applied to the tables as passed
+            lim = min(N, 64 * i + 64)
+            keys = set()
+            for a, b in iv[0, h, i, :min(ivc[0, h, i], ns)]:
+                keys.update(range(max(int(a), 0), min(int(b), lim)))
+            keys.update(int(c) for c in col[0, h, i, :min(colc[0, h, i], nv)] if 0 <= c < N)
+            rows = np.arange(64 * i, 64 * i + 64)
+            o, _ = oracle.attend_rows(q[0, h, rows], k[0, 0], v[0, 0], np.array(sorted(keys), np.int64), scale,
+                                      row_pos=rows)
+            want[0, h, rows] = o
+    assert_attention_close(got, want, bf16=True, what="vs forward on out-of-range tables")
