@@ -15,7 +15,7 @@ from . import _ffi as F
 from ._ffi import SAError, load  # noqa: F401
 
 __all__ = ["sa_estimate", "sa_select_topk", "sa_select_mass", "sa_vs_build", "sa_block_sparse_fwd",
-           "sa_gather_decode", "sa_cluster_pack", "sa_kmeans", "sa_estimate_topk", "sa_estimate_topk_centroid", "sa_indexer_topk", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
+           "sa_gather_decode", "sa_gather_decode_static", "sa_cluster_pack", "sa_kmeans", "sa_estimate_topk", "sa_estimate_topk_centroid", "sa_indexer_topk", "SAError", "load", "BLOCK_MEANPOOL", "VSLASH", "CENTROID", "INDEXER"]
 
 BLOCK_MEANPOOL, VSLASH, CENTROID, INDEXER = (F.SA_EST_BLOCK_MEANPOOL, F.SA_EST_VSLASH, F.SA_EST_CENTROID,
                                              F.SA_EST_INDEXER)
@@ -417,6 +417,16 @@ def sa_gather_decode(q, k, v, out, *, cluster_ptr=None, sel=None, tok_idx=None, 
     ws, n = _ws(lib.sa_gather_decode_workspace_bytes, a, q, workspace)
     F.check(lib.sa_gather_decode(C.byref(a), _p(ws) if n else None, n, _stream()))
     return ws
+
+
+def sa_gather_decode_static(q, k, v, out, *, cluster_ptr=None, sel=None, tok_idx=None, lse=None, scale=None,
+                            q_pos=None, perm=None):
+    """sa_gather_decode with its scratch in the library's static device array:
+    no workspace and no allocation (usable under graph capture).  Calls that
+    overlap on one GPU race; see sa.h."""
+    lib = load()
+    a = _gather_args(q, k, v, out, cluster_ptr, sel, tok_idx, lse, scale, q_pos, perm)
+    F.check(lib.sa_gather_decode_static(C.byref(a), _stream()))
 
 
 def sa_cluster_pack(labels, cluster_ptr, perm, n_clusters: int, *, k=None, v=None, k_packed=None,

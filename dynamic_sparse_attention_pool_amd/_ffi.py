@@ -18,6 +18,7 @@ SA_EST_BLOCK_MEANPOOL, SA_EST_VSLASH, SA_EST_CENTROID, SA_EST_INDEXER = 0, 1, 2,
 SA_FWD_BLOCK, SA_FWD_VSLASH, SA_FWD_ASHAPE = 0, 1, 2
 SA_GATHER_CLUSTER, SA_GATHER_TOKEN = 0, 1
 ABI_VERSION = 9
+STATIC_SCRATCH_BYTES = 32 << 20   # SA_STATIC_SCRATCH_BYTES
 
 STATUS_NAMES = {0: "SA_OK", 1: "SA_ERR_NULL", 2: "SA_ERR_SHAPE", 3: "SA_ERR_DTYPE", 4: "SA_ERR_ALIGN",
                 5: "SA_ERR_WORKSPACE", 6: "SA_ERR_UNSUPPORTED", 7: "SA_ERR_LAUNCH", 8: "SA_ERR_VALUE"}
@@ -118,6 +119,7 @@ SYMBOLS = {
     "sa_block_sparse_fwd_workspace_bytes": (C.c_int, [C.POINTER(FwdArgs), C.POINTER(C.c_size_t)]),
     "sa_gather_decode": (C.c_int, [C.POINTER(GatherArgs), P, C.c_size_t, P]),
     "sa_gather_decode_workspace_bytes": (C.c_int, [C.POINTER(GatherArgs), C.POINTER(C.c_size_t)]),
+    "sa_gather_decode_static": (C.c_int, [C.POINTER(GatherArgs), P]),
     "sa_cluster_pack": (C.c_int, [C.POINTER(ClusterPackArgs), P, C.c_size_t, P]),
     "sa_cluster_pack_workspace_bytes": (C.c_int, [C.POINTER(ClusterPackArgs), C.POINTER(C.c_size_t)]),
     "sa_kmeans": (C.c_int, [C.POINTER(KmeansArgs), P, C.c_size_t, P]),

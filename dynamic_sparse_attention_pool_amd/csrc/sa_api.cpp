@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "launch.h"
@@ -661,13 +662,7 @@ int sa_gather_decode_workspace_bytes(const sa_gather_args* a, size_t* bytes) {
   return ok();
 }
 
-int sa_gather_decode(const sa_gather_args* a, void* workspace, size_t workspace_bytes, void* stream) {
-  size_t ws = 0;
-  const int rc = check_gather(a, &ws);
-  if (rc) return rc;
-  if (ws > 0 && (!workspace || workspace_bytes < ws))
-    return fail(SA_ERR_WORKSPACE, "sa_gather_decode: workspace of %zu bytes required", ws);
-  if (workspace && !aligned16(workspace)) return fail(SA_ERR_ALIGN, "sa_gather_decode: workspace must be 16-byte aligned");
+static sa::GatherParams gather_params(const sa_gather_args* a) {
   sa::GatherParams p;
   p.q = (const uint16_t*)a->q;
   p.k = (const uint16_t*)a->k;
@@ -689,9 +684,74 @@ int sa_gather_decode(const sa_gather_args* a, void* workspace, size_t workspace_
   p.n_tok = a->n_tok;
   p.scale = a->scale;
   p.out_bf16 = a->out_dtype == SA_BF16;
+  return p;
+}
+
+static int launch_gather(const sa_gather_args* a, void* workspace, void* stream) {
+  const sa::GatherParams p = gather_params(a);
   if (a->mode == SA_GATHER_CLUSTER)
     return launched(sa::launch_cluster_decode(p, workspace, as_stream(stream)), "sa_gather_decode(CLUSTER)");
   return launched(sa::launch_token_gather(p, workspace, as_stream(stream)), "sa_gather_decode(TOKEN)");
+}
+
+int sa_gather_decode(const sa_gather_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  size_t ws = 0;
+  const int rc = check_gather(a, &ws);
+  if (rc) return rc;
+  if (ws > 0 && (!workspace || workspace_bytes < ws))
+    return fail(SA_ERR_WORKSPACE, "sa_gather_decode: workspace of %zu bytes required", ws);
+  if (workspace && !aligned16(workspace)) return fail(SA_ERR_ALIGN, "sa_gather_decode: workspace must be 16-byte aligned");
+  return launch_gather(a, workspace, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------- allocation-free decode
+// Scratch of sa_gather_decode_static: a file-scope device array, one copy per
+// GPU for the life of the process.  On the host the name only identifies the
+// symbol; its device address comes from hipGetSymbolAddress, taken once per
+// device with that device current and kept here.
+namespace {
+static __device__ __align__(256) unsigned char scratch[SA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int static_scratch(void** out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SA_ERR_LAUNCH, "sa_gather_decode_static: hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SA_ERR_UNSUPPORTED, "sa_gather_decode_static: device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    const hipError_t r = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (r != hipSuccess || ptr == nullptr)
+      return fail(SA_ERR_LAUNCH, "sa_gather_decode_static: hipGetSymbolAddress: %s", hipGetErrorString(r));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return SA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+int sa_gather_decode_static(const sa_gather_args* a, void* stream) {
+  size_t ws = 0;
+  const int rc = check_gather(a, &ws);
+  if (rc) return rc;
+  if (ws > SA_STATIC_SCRATCH_BYTES)
+    return fail(SA_ERR_UNSUPPORTED, "sa_gather_decode_static: this call needs %zu bytes of scratch; the static buffer holds %zu",
+                ws, (size_t)SA_STATIC_SCRATCH_BYTES);
+  void* ptr = nullptr;
+  if (ws > 0) {
+    const int r = static_scratch(&ptr);
+    if (r) return r;
+  }
+  (void)as_stream(stream);  // clears an unrelated earlier runtime error, as every entry point does
+  return launch_gather(a, ptr, stream);
 }
 
 // ---------------------------------------------------------------- cluster pack

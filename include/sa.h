@@ -466,6 +466,25 @@ int sa_gather_decode_workspace_bytes(const sa_gather_args* args, size_t* bytes);
 int sa_gather_decode(const sa_gather_args* args, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ======================================================================
+ * sa_gather_decode_static — sa_gather_decode that allocates nothing and takes
+ * no workspace, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * Same arguments, results and errors as sa_gather_decode (bit-identical
+ * outputs).  The scratch the cluster mode needs (the per-range partials,
+ * sa_gather_decode_workspace_bytes) lives in a static device array of
+ * SA_STATIC_SCRATCH_BYTES that each GPU the library runs on holds until the
+ * process ends; its address is looked up once per device, on the first call
+ * with that device current.  A call needing more scratch returns
+ * SA_ERR_UNSUPPORTED before any launch.  Every call on a GPU shares that GPU's
+ * array: calls that overlap in time on one GPU (other streams or threads)
+ * race, so the caller serialises them.  Nothing in the array needs clearing
+ * between calls (each range's partial is written before it is read).
+ * ====================================================================== */
+#define SA_STATIC_SCRATCH_BYTES (32u << 20)
+int sa_gather_decode_static(const sa_gather_args* args, void* stream);
+
+/* ======================================================================
  * sa_cluster_pack — cluster-major layout of a fixed context (offline step).
  *
  * Squeezed Attention page, §技术方案, offline stage: keys are clustered and

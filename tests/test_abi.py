@@ -25,7 +25,8 @@ def lib():
 
 def test_header_declares_the_four_entry_points_and_helpers():
     names = declared_functions()
-    for n in ["sa_estimate", "sa_select_topk", "sa_block_sparse_fwd", "sa_gather_decode", "sa_vs_build",
+    for n in ["sa_estimate", "sa_select_topk", "sa_block_sparse_fwd", "sa_gather_decode", "sa_gather_decode_static",
+              "sa_vs_build",
               "sa_cluster_pack", "sa_select_mass", "sa_kmeans", "sa_estimate_topk", "sa_indexer_topk", "sa_last_error",
               "sa_version",
               "sa_args_size"]:
@@ -312,6 +313,23 @@ def test_estimate_and_gather_argument_errors(lib):
     g.tok_idx, g.n_tok, g.heads_kv = 256, 64, 4
     g.tok_per_head = 2                                                # neither shared (0) nor per head (1)
     assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 8
+
+
+def test_static_decode_rejects_oversized_scratch(lib):
+    """sa_gather_decode_static checks, before any launch, that the cluster
+    partials fit its static scratch (64 KV heads x 2^20 keys need ~1.1 GB)."""
+    from dynamic_sparse_attention_pool_amd import _ffi as F
+    g = F.GatherArgs()
+    g.q = g.k = g.v = g.out = g.cluster_ptr = g.sel = 256
+    g.mode, g.dtype, g.out_dtype, g.head_dim, g.scale = F.SA_GATHER_CLUSTER, F.SA_BF16, F.SA_F32, 128, 0.1
+    g.n_q, g.heads_q, g.heads_kv, g.n_ctx, g.n_clusters, g.n_sel = 1, 64, 64, 1 << 20, 256, 8
+    n = C.c_size_t(0)
+    assert lib.sa_gather_decode_workspace_bytes(C.byref(g), C.byref(n)) == 0
+    assert n.value > F.STATIC_SCRATCH_BYTES
+    assert lib.sa_gather_decode_static(C.byref(g), None) == 6
+    assert "static buffer holds" in _err(lib)
+    g.n_q = 0
+    assert lib.sa_gather_decode_static(C.byref(g), None) == 2   # argument errors as in sa_gather_decode
 
 
 def test_binding_rejects_inconsistent_tensors(lib):
