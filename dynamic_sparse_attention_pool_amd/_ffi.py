@@ -128,6 +128,8 @@ SYMBOLS = {
     "sa_kmeans_workspace_bytes": (C.c_int, [C.POINTER(KmeansArgs), C.POINTER(C.c_size_t)]),
     "sa_indexer_topk": (C.c_int, [C.POINTER(IndexerTopkArgs), P, C.c_size_t, P]),
     "sa_indexer_topk_workspace_bytes": (C.c_int, [C.POINTER(IndexerTopkArgs), C.POINTER(C.c_size_t)]),
+    "sa_peak_mfma_bf16": (C.c_int, [P, C.c_int, C.c_int, C.POINTER(C.c_double), P]),
+    "sa_peak_read": (C.c_int, [P, C.c_size_t, C.c_int, P, C.POINTER(C.c_double), P]),
     "sa_last_error": (C.c_char_p, []),
     "sa_version": (C.c_int, []),
     "sa_args_size": (C.c_size_t, [C.c_int]),

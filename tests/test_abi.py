@@ -9,10 +9,12 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sa.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    """Every function any include/*.h declares."""
+    text = "".join(open(h).read() for h in HEADERS)
     return sorted(set(re.findall(r"^(?:int|const char\*|size_t)\s+(sa_\w+)\s*\(", text, re.M)))
 
 
@@ -29,7 +31,7 @@ def test_header_declares_the_four_entry_points_and_helpers():
               "sa_vs_build",
               "sa_cluster_pack", "sa_select_mass", "sa_kmeans", "sa_estimate_topk", "sa_indexer_topk", "sa_last_error",
               "sa_version",
-              "sa_args_size"]:
+              "sa_args_size", "sa_peak_mfma_bf16", "sa_peak_read"]:
         assert n in names
 
 
@@ -313,6 +315,14 @@ def test_estimate_and_gather_argument_errors(lib):
     g.tok_idx, g.n_tok, g.heads_kv = 256, 64, 4
     g.tok_per_head = 2                                                # neither shared (0) nor per head (1)
     assert lib.sa_gather_decode(C.byref(g), None, 0, None) == 8
+
+
+def test_peak_probes_reject_bad_arguments(lib):
+    d = C.c_double(0)
+    assert lib.sa_peak_mfma_bf16(None, 10, 4, C.byref(d), None) == 1
+    assert lib.sa_peak_mfma_bf16(256, 10, 6, C.byref(d), None) == 1   # waves per CU not a multiple of 4
+    assert lib.sa_peak_read(None, 1 << 20, 1, 256, C.byref(d), None) == 1
+    assert lib.sa_peak_read(264, 1 << 20, 1, 256, C.byref(d), None) == 1   # not 16-byte aligned
 
 
 def test_static_decode_rejects_oversized_scratch(lib):
