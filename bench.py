@@ -134,12 +134,17 @@ class SclkSampler:
             self.stop_ev.wait(0.5)
 
     def __enter__(self):
-        self.th.start()
+        # under a profiler every child process inherits its preloaded library,
+        # so rocm-smi (a script that re-executes its interpreter) is not started
+        profiled = "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+        if not profiled:
+            self.th.start()
         return self
 
     def __exit__(self, *a):
         self.stop_ev.set()
-        self.th.join(timeout=6)
+        if self.th.is_alive():
+            self.th.join(timeout=6)
 
     def summary(self):
         if not self.samples:
