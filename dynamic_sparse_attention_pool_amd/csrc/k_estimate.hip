@@ -470,12 +470,158 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
 
 }  // namespace
 
+// Centroid scores and the fixed top-k of one (token, query head) row per wave,
+// with no workgroup barrier.  Lane l owns centroids l, l+64, ... (NPL of them):
+// it reads their rows (a quarter row per centroid at a time, all loads of a
+// quarter in flight together) and computes each score exactly as
+// k_centroid_score does (fp32 FMAs in dimension order, then the scale), so
+// the selection is bit-identical to sa_estimate(CENTROID) + sa_select_topk.
+// The k-th largest order-preserving key T comes from a 32-step bitwise search
+// (a candidate bit stays when at least k keys reach the prefix), and the
+// emission walks the centroids in index order, 64 per ballot: keys above T,
+// then keys equal to T while the k budget lasts (lower index first).
+namespace {
+// Top-k of one row whose scores a wave holds, NPL per lane (lane l has
+// candidates l, l+64, ...): the k-th largest order-preserving key T by a
+// 32-step bitwise search (a candidate bit stays when at least k keys reach the
+// prefix), then emission in candidate order, 64 per ballot: keys above T and
+// keys equal to T while the budget lasts (lower index first).  NaN scores set
+// bit 0 of err.
+template <int NPL>
+__device__ __forceinline__ void wave_topk_emit(const float* acc, int C, float scale, int k, int kmax, int32_t* out,
+                                               int32_t* cnt_out, int32_t* err, int lane) {
+  uint32_t key[NPL];
+  bool nan_seen = false;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const bool live = 64 * j + lane < C;
+    const float sc = acc[j] * scale;
+    nan_seen |= live && is_nan(sc);
+    key[j] = live ? order_key(sc) : 0u;  // every real key is above 0 (NaN aside)
+  }
+  if (nan_seen && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
+  const int kr = min(k, C);
+  uint32_t Tk = 0u;
+  if (kr > 0) {
+#pragma unroll 1
+    for (int b = 31; b >= 0; --b) {
+      const uint32_t cand = Tk | (1u << b);
+      int n = 0;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) n += __popcll(__ballot(key[j] >= cand));
+      if (n >= kr) Tk = cand;
+    }
+  }
+  int nabove = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) nabove += __popcll(__ballot(kr > 0 && key[j] > Tk));
+  const int need = kr - nabove;
+  const uint64_t lt = (1ull << lane) - 1ull;
+  int base_sel = 0, base_tie = 0;
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) {
+    const bool live = kr > 0 && 64 * j + lane < C;
+    const uint64_t mt = __ballot(live && key[j] == Tk);
+    const int tie_rank = base_tie + (int)__popcll(mt & lt);
+    const bool sel = live && (key[j] > Tk || (((mt >> lane) & 1ull) && tie_rank < need));
+    const uint64_t ms = __ballot(sel);
+    if (sel) out[base_sel + (int)__popcll(ms & lt)] = 64 * j + lane;
+    base_sel += (int)__popcll(ms);
+    base_tie += (int)__popcll(mt);
+  }
+  for (int e = base_sel + lane; e < kmax; e += 64) out[e] = -1;
+  if (lane == 0) *cnt_out = base_sel;
+}
+
+template <typename T, int NPL>
+__global__ __launch_bounds__(64) void k_centroid_topk_wave(const T* __restrict__ q, const float* __restrict__ cent,
+                                                           int hq, int hkv, int C, int D, float scale, int k, int kmax,
+                                                           int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
+                                                           int32_t* err) {
+  __shared__ float qs[128];
+  const int lane = threadIdx.x;
+  // block -> (KV head innermost, so each XCD reads one KV head's centroid table)
+  const int grp = hq / hkv;
+  const int g = blockIdx.x % hkv, rest = blockIdx.x / hkv;
+  const int t = rest / grp, h = g * grp + rest % grp;
+  const int64_t row = (int64_t)t * hq + h;
+  const float* cbase = cent + (int64_t)g * C * D;
+  constexpr int U = NPL <= 4 ? 8 : NPL <= 8 ? 4 : 2;  // 16-byte loads per centroid per chunk: 32 in flight
+  f32x4 mA[NPL][U], mB[NPL][U];
+  auto load_chunk = [&](int d0, f32x4 (&dst)[NPL][U]) {
+#pragma unroll
+    for (int j = 0; j < NPL; ++j) {
+      const int c = min(64 * j + lane, C - 1);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        dst[j][u] = d0 + 4 * u < D ? *reinterpret_cast<const f32x4*>(cbase + (int64_t)c * D + d0 + 4 * u) : f32x4{};
+    }
+  };
+  float acc[NPL];
+#pragma unroll
+  for (int j = 0; j < NPL; ++j) acc[j] = 0.f;
+  auto fma_chunk = [&](int d0, const f32x4 (&m)[NPL][U]) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (d0 + 4 * u >= D) break;
+#pragma unroll
+      for (int j = 0; j < NPL; ++j) {
+        acc[j] = fmaf(qs[d0 + 4 * u], m[j][u][0], acc[j]);
+        acc[j] = fmaf(qs[d0 + 4 * u + 1], m[j][u][1], acc[j]);
+        acc[j] = fmaf(qs[d0 + 4 * u + 2], m[j][u][2], acc[j]);
+        acc[j] = fmaf(qs[d0 + 4 * u + 3], m[j][u][3], acc[j]);
+      }
+    }
+  };
+  // the first chunk's centroid loads go out before the query's, so the two
+  // memory latencies overlap; afterwards the next chunk is in flight while
+  // the current one is multiplied (dimension order is kept)
+  constexpr int CH = 4 * U;  // dimensions per chunk
+  load_chunk(0, mA);
+  for (int d = lane; d < D; d += 64) {
+    const T* qp = q + row * D + d;
+    if constexpr (sizeof(T) == 2) qs[d] = bf2f(*reinterpret_cast<const uint16_t*>(qp));
+    else qs[d] = *reinterpret_cast<const float*>(qp);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  for (int d0 = 0; d0 < D; d0 += 2 * CH) {
+    if (d0 + CH < D) load_chunk(d0 + CH, mB);
+    fma_chunk(d0, mA);
+    if (d0 + CH >= D) break;
+    if (d0 + 2 * CH < D) load_chunk(d0 + 2 * CH, mA);
+    fma_chunk(d0 + CH, mB);
+  }
+  wave_topk_emit<NPL>(acc, C, scale, k, kmax, idx + row * kmax, cnt + row, err, lane);
+}
+
+}  // namespace
+
 hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv, int C,
                                 int head_dim, float scale, int k, int kmax, float mass, int k_min, int32_t* idx,
                                 int32_t* cnt, int32_t* err, hipStream_t stream) {
   if (T == 0) return hipSuccess;
-  // one query head per workgroup: four times the workgroups of one per KV head,
-  // so the centroid rows' loads spread over more CUs
+  if (!(mass > 0.f)) {
+    // fixed budget: one wave per (token, query head)
+    const dim3 gw((unsigned)(T * hq));
+#define SA_CTW_LAUNCH(TQ, NPL)                                                                                        \
+  hipLaunchKernelGGL((k_centroid_topk_wave<TQ, NPL>), gw, dim3(64), 0, stream, (const TQ*)q, cent, hq, hkv, C, head_dim, \
+                     scale, k, kmax, idx, cnt, err)
+    if (q_bf16) {
+      if (C <= 256) SA_CTW_LAUNCH(uint16_t, 4);
+      else if (C <= 512) SA_CTW_LAUNCH(uint16_t, 8);
+      else SA_CTW_LAUNCH(uint16_t, 16);
+    } else {
+      if (C <= 256) SA_CTW_LAUNCH(float, 4);
+      else if (C <= 512) SA_CTW_LAUNCH(float, 8);
+      else SA_CTW_LAUNCH(float, 16);
+    }
+#undef SA_CTW_LAUNCH
+    return hipGetLastError();
+  }
+  // adaptive budget: one query head per workgroup: four times the workgroups
+  // of one per KV head, so the centroid rows' loads spread over more CUs
   const int nsub = hq / hkv;
   const dim3 grid((unsigned)(T * hkv * nsub));
 #define SA_CT_LAUNCH(TQ, M)                                                                                 \
