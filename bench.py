@@ -20,7 +20,7 @@ median and minimum of at least 20 reps:
   5. the token-indexer prefill chunk with index reuse over 4 layers
 Each kernel's rate is reported against the spec peak and against the peak the
 chip sustains in the same run (a matrix-core loop and a streaming read from
-libsa's probes), with the shader clock sampled by rocm-smi.  The CPU oracle is
+libsa's probes), with the shader clock sampled (amdsmi) inside the timed reps.  The CPU oracle is
 timed on a bounded sample of every workload.
 
 python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-extras] [--no-cpu]
@@ -28,13 +28,12 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-extras] [--
 from __future__ import annotations
 
 import argparse
+import contextlib
 import ctypes as C
 import hashlib
 import json
 import math
 import os
-import re
-import subprocess
 import sys
 import threading
 import time
@@ -92,13 +91,15 @@ class Reps:
         b.record()
         self.marks.setdefault(name, []).append((a, b))
 
-    def run(self, reps, parts):
-        """parts: list of (name, fn); one rep = flush, then each part timed."""
-        for _ in range(reps):
-            self.flush()
-            for name, fn in parts:
-                self.span(name, fn)
-        self.torch.cuda.synchronize()
+    def run(self, reps, parts, clock=None):
+        """parts: list of (name, fn); one rep = flush, then each part timed.
+        clock: name of the window the shader clock is sampled in."""
+        with clock_window(clock) if clock else contextlib.nullcontext():
+            for _ in range(reps):
+                self.flush()
+                for name, fn in parts:
+                    self.span(name, fn)
+            self.torch.cuda.synchronize()
 
     def ms(self, name):
         return [a.elapsed_time(b) for a, b in self.marks[name]]
@@ -112,46 +113,85 @@ class Reps:
         return stats(per)
 
 
-class SclkSampler:
-    """Shader clock read from rocm-smi every 0.5 s while running (None where
-    rocm-smi is not available)."""
+class ClockWindows:
+    """Shader clock (amdsmi, read in-process every 10 ms) sampled only inside
+    named timed windows, so idle gaps between workloads do not count."""
 
     def __init__(self):
-        self.samples, self.stop_ev = [], threading.Event()
-        self.th = threading.Thread(target=self._loop, daemon=True)
+        self.samples, self.handle, self.api = {}, None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]
+            self.api = amdsmi
+            self._read()
+        except Exception:  # noqa: BLE001  (the clock is context, not a result)
+            self.handle = None
 
-    def _loop(self):
-        while not self.stop_ev.is_set():
+    def _read(self):
+        """Median over the XCDs of the current gfx clock (MHz) from the GPU
+        metrics table, else its single current / average value."""
+        m = self.api.amdsmi_get_gpu_metrics_info(self.handle)
+        per = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
+        if per:
+            return float(np.median(per))
+        for key in ("current_gfxclk", "average_gfxclk_frequency"):
+            x = m.get(key)
+            if isinstance(x, (int, float)) and 0 < x < 10000:
+                return float(x)
+        raise RuntimeError("no gfx clock in the metrics table")
+
+    def sample_now(self, name):
+        """One sample from the calling thread (while the GPU is known busy)."""
+        if self.handle is not None:
             try:
-                out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=5).stdout
-                for line in out.splitlines():
-                    if "sclk" in line.lower():
-                        m = re.search(r"\((\d+)\s*Mhz\)", line, re.I)
-                        if m:
-                            self.samples.append(int(m.group(1)))
-            except Exception:  # noqa: BLE001  (the clock is context, not a result)
-                return
-            self.stop_ev.wait(0.5)
+                self.samples.setdefault(name, []).append(self._read())
+            except Exception:  # noqa: BLE001
+                pass
 
-    def __enter__(self):
-        # under a profiler every child process inherits its preloaded library,
-        # so rocm-smi (a script that re-executes its interpreter) is not started
-        profiled = "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
-        if not profiled:
-            self.th.start()
-        return self
+    def window(self, name):
+        outer = self
 
-    def __exit__(self, *a):
-        self.stop_ev.set()
-        if self.th.is_alive():
-            self.th.join(timeout=6)
+        class _W:
+            def __enter__(self):
+                self.stop = threading.Event()
+                self.th = None
+                if outer.handle is not None:
+                    self.th = threading.Thread(target=self._loop, daemon=True)
+                    self.th.start()
+                return self
+
+            def _loop(self):
+                while not self.stop.is_set():
+                    try:
+                        outer.samples.setdefault(name, []).append(outer._read())
+                    except Exception:  # noqa: BLE001
+                        return
+                    self.stop.wait(0.01)
+
+            def __exit__(self, *a):
+                self.stop.set()
+                if self.th is not None:
+                    self.th.join(timeout=2)
+        return _W()
 
     def summary(self):
         if not self.samples:
             return None
-        s = np.asarray(self.samples)
-        return {"source": "rocm-smi --showclocks, every 0.5 s", "mhz_median": float(np.median(s)),
-                "mhz_min": int(s.min()), "mhz_max": int(s.max()), "n": int(s.size)}
+        out = {"source": "amdsmi GPU metrics, current gfx clock (median over XCDs), sampled inside the timed reps"}
+        for k, v in self.samples.items():
+            s = np.asarray(v)
+            out[k] = {"mhz_median": float(np.median(s)), "mhz_min": float(s.min()), "mhz_max": float(s.max()),
+                      "n": int(s.size)}
+        return out
+
+
+CLOCK = None
+
+
+def clock_window(name):
+    """Context manager sampling the clock while the body runs."""
+    return CLOCK.window(name) if CLOCK is not None else contextlib.nullcontext()
 
 
 def source_hash(paths):
@@ -242,7 +282,7 @@ def prefill_headline(steps, warmup, reps, seed):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     # the measurement method: reps with a cache flush before each
-    R.run(reps, [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)])
+    R.run(reps, [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)], clock="prefill_128k")
     kept = int(layer.cnt.sum().item())
     assert int(layer.err.item()) == 0, "non-finite block score"
     res = dict(N=N, ms_per_step=ms, kept_blocks=kept, flop=kept * FLOP_PER_BLOCK_128,
@@ -265,7 +305,7 @@ def config1(reps):
     layer.step()
     torch.cuda.synchronize()
     R = Reps()
-    R.run(max(reps, 50), [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)])
+    R.run(max(reps, 50), [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)], clock="c1_1k_fp32")
     kept = int(layer.cnt.sum().item())
     lay = R.total(["estimate", "select", "forward"])
     return {"workload": "block-sparse parity layer: 1024 tokens, 1 head, d64, fp32, blocks of 64 (16x16 grid), "
@@ -288,7 +328,7 @@ def config2(reps, peaks):
         layer.step()
     torch.cuda.synchronize()
     R = Reps()
-    R.run(reps, [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)])
+    R.run(reps, [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)], clock="c2_32k")
     kept = int(layer.cnt.sum().item())
     flop = kept * FLOP_PER_BLOCK_128
     fwd = R.stat("forward")
@@ -330,7 +370,7 @@ def vs_config(reps, inp, peaks):
     layer.step()
     torch.cuda.synchronize()
     R = Reps()
-    R.run(reps, [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)])
+    R.run(reps, [("estimate", layer.estimate), ("select", layer.select), ("forward", layer.forward)], clock="vslash_128k")
     flop = vs_table_keys(layer) * 4 * 64 * 128
     fwd = R.stat("forward")
     tf = flop / (fwd["median"] * 1e-3) / 1e12
@@ -391,6 +431,8 @@ def decode_config(steps, peaks, mass=None):
         ev[0].record()
         graphs[which].replay()
         ev[1].record()
+        if which == 2 and CLOCK is not None:
+            CLOCK.sample_now("decode" if mass is None else "decode_adaptive")
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / (4 * reps_g)
 
@@ -458,7 +500,7 @@ def indexer_config(reps, peaks):
               ("select", lambda: sa.sa_select_topk(ip.scores, ip.idx, ip.cnt, k=k_sel, causal=True, causal_period=T,
                                                    causal_offset=ip.pos0)),
               ("attend", lambda: ip.attend(1)),
-              ("index_fused", lambda: fu.index(check=False))])
+              ("index_fused", lambda: fu.index(check=False))], clock="indexer")
     R.run(max(3, r // 2), [("total_reuse", lambda: ip.step(reuse=True)),
                            ("total_noreuse", lambda: ip.step(reuse=False)),
                            ("total_reuse_fused", lambda: fu.step(reuse=True))])
@@ -708,6 +750,8 @@ def main():
     import dynamic_sparse_attention_pool_amd as sa
     sa.load()
     torch.cuda.init()
+    global CLOCK
+    CLOCK = ClockWindows()
 
     if args.pmc_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -726,9 +770,8 @@ def main():
     if want("peaks"):
         log("[bench] achievable peaks")
         peaks = measured_peaks()
-    with SclkSampler() as clk:
-        log("[bench] 128K block-sparse layer")
-        main_res = prefill_headline(args.steps, args.warmup, reps, seed=3)
+    log("[bench] 128K block-sparse layer")
+    main_res = prefill_headline(args.steps, args.warmup, reps, seed=3)
     ms = main_res["ms_per_step"]
     value = main_res["flop"] / (ms * 1e-3) / 1e12
     fwd_ms = main_res["contract_ms"]["forward"]
@@ -751,7 +794,7 @@ def main():
                    "ms_estimate_median": main_res["parts"]["estimate"]["median"],
                    "ms_select_median": main_res["parts"]["select"]["median"],
                    "TFLOP_per_s_layer_median": main_res["flop"] / (main_res["layer"]["median"] * 1e-3) / 1e12},
-        "clock": clk.summary(),
+        "clock": CLOCK.summary() if CLOCK is not None else None,
         "peaks": {"mfma_bf16_spec_TFLOP_per_s": PEAK_BF16_TFLOPS, "hbm_spec_GB_per_s": PEAK_HBM_GBS, **peaks},
         "roofline": {"bound": "mfma", "kernel": "k_fwd_bf16<128,block>", "achieved": round(fwd_tflops, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(fwd_tflops / PEAK_BF16_TFLOPS, 4),

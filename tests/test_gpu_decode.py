@@ -234,8 +234,12 @@ def test_decode_end_to_end_full_size_fused_estimate(sa):
     sel = oracle.cluster_select(s, ksel)
     for t, h in rows:
         assert np.array_equal(got[t, h], sel[t][h]), (t, h)
+    # every other row: a valid top-64 up to near-ties of the fp64 scores
+    for t in range(T):
+        for h in range(Hq):
+            assert tie_tolerant_valid(np.sort(got[t, h]), s[t, h], ksel, none), (t, h)
+    # all outputs against the oracle's decode over the clusters the GPU chose
+    gsel = [[np.sort(got[t, h]) for h in range(Hq)] for t in range(T)]
     wo, _ = oracle.cluster_decode(W.bf16_to_f32(inp.q), W.bf16_to_f32(inp.k), W.bf16_to_f32(inp.v), inp.labels,
-                                  sel, scale)
-    o = host(dc.out)
-    idx = np.array(rows)
-    assert_attention_close(o[idx[:, 0], idx[:, 1]], wo[idx[:, 0], idx[:, 1]], bf16=True, what="fused decode")
+                                  gsel, scale)
+    assert_attention_close(host(dc.out), wo, bf16=True, what="fused decode")
