@@ -118,12 +118,14 @@ class ClockWindows:
     named timed windows, so idle gaps between workloads do not count."""
 
     def __init__(self):
-        self.samples, self.handle, self.api = {}, None, None
+        self.samples, self.handle, self.api, self.errors, self.raw = {}, None, None, [], None
         try:
             import amdsmi
             amdsmi.amdsmi_init()
             self.handle = amdsmi.amdsmi_get_processor_handles()[0]
             self.api = amdsmi
+            m = amdsmi.amdsmi_get_gpu_metrics_info(self.handle)
+            self.raw = {k: m.get(k) for k in ("current_gfxclk", "average_gfxclk_frequency", "current_gfxclks")}
             self._read()
         except Exception:  # noqa: BLE001  (the clock is context, not a result)
             self.handle = None
@@ -146,8 +148,12 @@ class ClockWindows:
         if self.handle is not None:
             try:
                 self.samples.setdefault(name, []).append(self._read())
-            except Exception:  # noqa: BLE001
-                pass
+            except Exception as e:  # noqa: BLE001
+                self._err(name, e)
+
+    def _err(self, name, e):
+        if len(self.errors) < 4:
+            self.errors.append(f"{name}: {type(e).__name__}: {e}"[:200])
 
     def window(self, name):
         outer = self
@@ -165,7 +171,8 @@ class ClockWindows:
                 while not self.stop.is_set():
                     try:
                         outer.samples.setdefault(name, []).append(outer._read())
-                    except Exception:  # noqa: BLE001
+                    except Exception as e:  # noqa: BLE001
+                        outer._err(name, e)
                         return
                     self.stop.wait(0.01)
 
@@ -176,9 +183,11 @@ class ClockWindows:
         return _W()
 
     def summary(self):
-        if not self.samples:
+        if not self.samples and not self.errors:
             return None
-        out = {"source": "amdsmi GPU metrics, current gfx clock (median over XCDs), sampled inside the timed reps"}
+        out = {"errors": self.errors} if self.errors else {}
+        out["metrics_at_start"] = str(self.raw)[:300]
+        out.update({"source": "amdsmi GPU metrics, current gfx clock (median over XCDs), sampled inside the timed reps"})
         for k, v in self.samples.items():
             s = np.asarray(v)
             out[k] = {"mhz_median": float(np.median(s)), "mhz_min": float(s.min()), "mhz_max": float(s.max()),

@@ -173,11 +173,14 @@ __global__ __launch_bounds__(64 * kIdxWaves) void k_indexer(const uint16_t* __re
 // heads of a head group on the rows of v_mfma_f32_32x32x16_bf16 and 32 keys on
 // its columns, so each lane holds 16 heads of one key: the ReLU and the
 // weighted sum over heads are 16 in-register FMAs and one exchange with the
-// lane holding the other 16 heads.  A workgroup (8 waves x 4 queries) walks
-// its key range in tiles of 64 keys copied once into LDS (double-buffered) and
-// shared by all waves; there is no cross-wave reduction.  Queries per wave:
-// 4 with one head group, 3 with two (the query operands then fill 96 registers).
-constexpr int kIdx2Waves = 8;
+// lane holding the other 16 heads (v_permlane32_swap, no LDS round trip).  A
+// workgroup (4 waves x 4 queries, two workgroups per CU) walks its key range
+// in tiles of 64 keys copied once into LDS (double-buffered) and shared by all
+// waves; there is no cross-wave reduction.  Queries per wave: 4 with one head
+// group, 3 with two (the query operands then fill 96 registers).  Within a
+// tile the products of the next (key half, query, head group) unit run on the
+// matrix cores while the VALU finishes the current one.
+constexpr int kIdx2Waves = 4;
 template <int HG>
 constexpr int idx2_qpw() { return HG == 1 ? 4 : 3; }
 
@@ -198,7 +201,7 @@ struct IdxCand {
 };
 
 template <int HG, bool CAND>
-__global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __restrict__ q,
+__global__ __launch_bounds__(64 * kIdx2Waves, 2) void k_indexer2(const uint16_t* __restrict__ q,
                                                                const uint16_t* __restrict__ k,
                                                                const float* __restrict__ w, int T, int Hi,
                                                                int64_t Nk, int kstride, int chunk, int64_t pos0,
@@ -253,12 +256,16 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
 
   const int64_t s_end = std::min(c1, lim_max + 1);  // keys past every query's limit are only written
   const int ntile = s_end > c0 ? (int)((s_end - c0 + 63) / 64) : 0;
-  // one 1 KB copy per wave: rows 8wv .. 8wv+7 of the tile
+  // 1 KB copies (8 rows each), 8 / kIdx2Waves per wave: rows 8wq .. 8wq+7
   auto copy = [&](int tl, int buf) {
-    const int r = 8 * wv + lane / 8, c = lane % 8;
-    const int64_t row = std::min(c0 + 64 * (int64_t)tl + r, Nk - 1) * kstride;
-    const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[buf][0]) + (uint32_t)wv * 1024u);
-    dma16(dst, k + row * kIdxD + 8 * (c ^ ((r >> 1) & 7)));
+#pragma unroll
+    for (int n = 0; n < 8 / kIdx2Waves; ++n) {
+      const int wq = wv + n * kIdx2Waves;
+      const int r = 8 * wq + lane / 8, c = lane % 8;
+      const int64_t row = std::min(c0 + 64 * (int64_t)tl + r, Nk - 1) * kstride;
+      const uint32_t dst = __builtin_amdgcn_readfirstlane(lds_addr(&Kt[buf][0]) + (uint32_t)wq * 1024u);
+      dma16(dst, k + row * kIdxD + 8 * (c ^ ((r >> 1) & 7)));
+    }
   };
   if (ntile > 0) copy(0, 0);
   for (int tl = 0; tl < ntile; ++tl) {
@@ -267,61 +274,63 @@ __global__ __launch_bounds__(64 * kIdx2Waves) void k_indexer2(const uint16_t* __
     __syncthreads();  // tile tl landed for every wave; buffer buf^1 is free
     if (tl + 1 < ntile) copy(tl + 1, buf ^ 1);
     const int64_t s0 = c0 + 64 * (int64_t)tl;
+    // both 32-key halves of the tile; unit u = (half hv, query j, head group g)
+    bf16x8 kb[2][4];
 #pragma unroll
-    for (int hv = 0; hv < 2; ++hv) {
-      bf16x8 kb[4];
+    for (int hv = 0; hv < 2; ++hv)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
-        kb[s4] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kt[buf][idx2_swz(32 * hv + l32, 2 * s4 + hf)]));
-      const int64_t key = s0 + 32 * hv + l32;
-      // units u = (query j, head group g); the products of unit u+1 run on the
-      // matrix cores while the ReLU-weighted sum of unit u runs on the VALU
-      constexpr int U = kIdx2Qpw * HG;
-      f32x16 acc[2];
-      auto prod = [&](int u, f32x16& a) {
-        const int j = u / HG, g = u % HG;
-        a = mfma32x32x16(qa[j][g][0], kb[0], f32x16{});
+        kb[hv][s4] = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kt[buf][idx2_swz(32 * hv + l32, 2 * s4 + hf)]));
+    constexpr int UH = kIdx2Qpw * HG, U = 2 * UH;
+    f32x16 acc[2];
+    auto prod = [&](int u, f32x16& a) {
+      const int hv = u / UH, j = (u / HG) % kIdx2Qpw, g = u % HG;
+      a = mfma32x32x16(qa[j][g][0], kb[hv][0], f32x16{});
 #pragma unroll
-        for (int s4 = 1; s4 < 4; ++s4) a = mfma32x32x16(qa[j][g][s4], kb[s4], a);
-      };
-      prod(0, acc[0]);
-      float sum = 0.f;
+      for (int s4 = 1; s4 < 4; ++s4) a = mfma32x32x16(qa[j][g][s4], kb[hv][s4], a);
+    };
+    // the products of unit u+1 run on the matrix cores while the ReLU-weighted
+    // sum of unit u runs on the VALU
+    prod(0, acc[0]);
+    float sum = 0.f;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int j = u / HG, g = u % HG;
-        if (u + 1 < U) prod(u + 1, acc[(u + 1) & 1]);
+    for (int u = 0; u < U; ++u) {
+      const int hv = u / UH, j = (u / HG) % kIdx2Qpw, g = u % HG;
+      if (u + 1 < U) prod(u + 1, acc[(u + 1) & 1]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sum = fmaf(wr[g][r], relu_bits(acc[u & 1][r]), sum);
-        if (u + 1 < U) {
+      for (int r = 0; r < 16; ++r) sum = fmaf(wr[g][r], relu_bits(acc[u & 1][r]), sum);
+      if (u + 1 < U) {
 #pragma unroll
-          for (int x = 0; x < 4; ++x) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
-            __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);  // eight VALU
+        for (int x = 0; x < 4; ++x) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one product
+          __builtin_amdgcn_sched_group_barrier(0x402, 8, 0);  // eight VALU
+        }
+      }
+      if (g == HG - 1) {
+        // lane l < 32 adds the partial sum of lane l + 32 (the other 16 heads)
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(sum), __float_as_uint(sum), false, false);
+        const float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+        const int t = t0 + kIdx2Qpw * wv + j;
+        const int64_t key = s0 + 32 * hv + l32;
+        if constexpr (CAND) {
+          // lanes 0..31 hold keys s0+32hv .. +31 in order: a ballot ranks
+          // the kept ones, so every chunk's run is stored ascending.  A NaN
+          // score is kept (the exact select reports it).
+          const bool take = hf == 0 && (int)key <= lim[j] && !(tot < thr[j]);
+          const uint64_t m = __ballot(take);
+          if (take) {
+            const int pos = found[j] + (int)__builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u);
+            if (pos < nslot[j]) run[j][pos] = make_int2((int)key, __float_as_int(tot));
+          }
+          found[j] += __popcll(m);
+        } else {
+          if (hf == 0 && t < T && key < c1) {
+            const bool causal = key * kstride <= pos0 + t;
+            out[(int64_t)t * Nk + key] = causal ? tot : -INFINITY;
+            flag_nonfinite(cd.err, causal && nonfinite(tot));
           }
         }
-        if (g == HG - 1) {
-          const float tot = sum + __shfl_xor(sum, 32);
-          const int t = t0 + kIdx2Qpw * wv + j;
-          if constexpr (CAND) {
-            // lanes 0..31 hold keys s0+32hv .. +31 in order: a ballot ranks
-            // the kept ones, so every chunk's run is stored ascending.  A NaN
-            // score is kept (the exact select reports it).
-            const bool take = hf == 0 && (int)key <= lim[j] && !(tot < thr[j]);
-            const uint64_t m = __ballot(take);
-            if (take) {
-              const int pos = found[j] + (int)__builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u);
-              if (pos < nslot[j]) run[j][pos] = make_int2((int)key, __float_as_int(tot));
-            }
-            found[j] += __popcll(m);
-          } else {
-            if (hf == 0 && t < T && key < c1) {
-              const bool causal = key * kstride <= pos0 + t;
-              out[(int64_t)t * Nk + key] = causal ? tot : -INFINITY;
-              flag_nonfinite(cd.err, causal && nonfinite(tot));
-            }
-          }
-          sum = 0.f;
-        }
+        sum = 0.f;
       }
     }
   }
