@@ -12,6 +12,9 @@
  *     *_workspace_bytes() call returns (0 is a valid answer).
  *   - Tensors are dense, row-major, in the documented shape order; the last
  *     dimension is contiguous.  q, k, v, out pointers must be 16-byte aligned.
+ *     There is no strided-tensor descriptor: every kernel copies whole rows at
+ *     the dense pitch, so a strided view must be made contiguous by the
+ *     caller (the binding rejects non-contiguous tensors).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *     default stream).  No call synchronises the host.
  *   - The return value is an sa_status.  Argument errors are detected on the
