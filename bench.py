@@ -28,14 +28,12 @@ python bench.py [--gpus 1] [--steps K] [--warmup W] [--reps R] [--no-extras] [--
 from __future__ import annotations
 
 import argparse
-import contextlib
 import ctypes as C
 import hashlib
 import json
 import math
 import os
 import sys
-import threading
 import time
 
 import numpy as np
@@ -94,12 +92,12 @@ class Reps:
     def run(self, reps, parts, clock=None):
         """parts: list of (name, fn); one rep = flush, then each part timed.
         clock: name of the window the shader clock is sampled in."""
-        with clock_window(clock) if clock else contextlib.nullcontext():
-            for _ in range(reps):
-                self.flush()
-                for name, fn in parts:
-                    self.span(name, fn)
-            self.torch.cuda.synchronize()
+        for _ in range(reps):
+            self.flush()
+            for name, fn in parts:
+                self.span(name, fn)
+            clock_sample(clock)
+        self.torch.cuda.synchronize()
 
     def ms(self, name):
         return [a.elapsed_time(b) for a, b in self.marks[name]]
@@ -114,8 +112,9 @@ class Reps:
 
 
 class ClockWindows:
-    """Shader clock (amdsmi, read in-process every 10 ms) sampled only inside
-    named timed windows, so idle gaps between workloads do not count."""
+    """Shader clock read in-process (amdsmi's GPU metrics table, median over
+    the XCDs) from the launching thread right after each timed rep is
+    enqueued, while the GPU is still running it."""
 
     def __init__(self):
         self.samples, self.handle, self.api, self.errors, self.raw = {}, None, None, [], None
@@ -131,8 +130,6 @@ class ClockWindows:
             self.handle = None
 
     def _read(self):
-        """Median over the XCDs of the current gfx clock (MHz) from the GPU
-        metrics table, else its single current / average value."""
         m = self.api.amdsmi_get_gpu_metrics_info(self.handle)
         per = [x for x in (m.get("current_gfxclks") or []) if isinstance(x, (int, float)) and 0 < x < 10000]
         if per:
@@ -144,63 +141,33 @@ class ClockWindows:
         raise RuntimeError("no gfx clock in the metrics table")
 
     def sample_now(self, name):
-        """One sample from the calling thread (while the GPU is known busy)."""
         if self.handle is not None:
             try:
                 self.samples.setdefault(name, []).append(self._read())
             except Exception as e:  # noqa: BLE001
-                self._err(name, e)
-
-    def _err(self, name, e):
-        if len(self.errors) < 4:
-            self.errors.append(f"{name}: {type(e).__name__}: {e}"[:200])
-
-    def window(self, name):
-        outer = self
-
-        class _W:
-            def __enter__(self):
-                self.stop = threading.Event()
-                self.th = None
-                if outer.handle is not None:
-                    self.th = threading.Thread(target=self._loop, daemon=True)
-                    self.th.start()
-                return self
-
-            def _loop(self):
-                while not self.stop.is_set():
-                    try:
-                        outer.samples.setdefault(name, []).append(outer._read())
-                    except Exception as e:  # noqa: BLE001
-                        outer._err(name, e)
-                        return
-                    self.stop.wait(0.01)
-
-            def __exit__(self, *a):
-                self.stop.set()
-                if self.th is not None:
-                    self.th.join(timeout=2)
-        return _W()
+                if len(self.errors) < 4:
+                    self.errors.append(f"{name}: {type(e).__name__}: {e}"[:200])
 
     def summary(self):
         if not self.samples and not self.errors:
             return None
         out = {"errors": self.errors} if self.errors else {}
         out["metrics_at_start"] = str(self.raw)[:300]
-        out.update({"source": "amdsmi GPU metrics, current gfx clock (median over XCDs), sampled inside the timed reps"})
+        out["source"] = ("amdsmi GPU metrics, current gfx clock (median over XCDs), one sample right after each "
+                         "timed rep is enqueued")
         for k, v in self.samples.items():
-            s = np.asarray(v)
-            out[k] = {"mhz_median": float(np.median(s)), "mhz_min": float(s.min()), "mhz_max": float(s.max()),
-                      "n": int(s.size)}
+            a = np.asarray(v)
+            out[k] = {"mhz_median": float(np.median(a)), "mhz_min": float(a.min()), "mhz_max": float(a.max()),
+                      "n": int(a.size)}
         return out
 
 
 CLOCK = None
 
 
-def clock_window(name):
-    """Context manager sampling the clock while the body runs."""
-    return CLOCK.window(name) if CLOCK is not None else contextlib.nullcontext()
+def clock_sample(name):
+    if CLOCK is not None and name:
+        CLOCK.sample_now(name)
 
 
 def source_hash(paths):
@@ -440,8 +407,8 @@ def decode_config(steps, peaks, mass=None):
         ev[0].record()
         graphs[which].replay()
         ev[1].record()
-        if which == 2 and CLOCK is not None:
-            CLOCK.sample_now("decode" if mass is None else "decode_adaptive")
+        if which == 2:
+            clock_sample("decode" if mass is None else "decode_adaptive")
         torch.cuda.synchronize()
         return ev[0].elapsed_time(ev[1]) / (4 * reps_g)
 
