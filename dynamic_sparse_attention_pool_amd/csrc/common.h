@@ -74,6 +74,19 @@ __device__ __forceinline__ void flag_nonfinite(int32_t* err, bool bad) {
   if (bad && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
 }
 
+// a + b and max(a, b) of a value with the one in lane l ^ 32, through
+// v_permlane32_swap (a register exchange between the two wave halves, no LDS
+// round trip).  Both operations are symmetric, so every lane gets exactly what
+// op(v, __shfl_xor(v, 32)) gives.
+__device__ __forceinline__ float xor32_add(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 __device__ __forceinline__ bool is_nan(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x7f800000u) == 0x7f800000u && (u & 0x7fffffu);

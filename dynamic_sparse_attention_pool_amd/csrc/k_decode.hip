@@ -402,7 +402,7 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
         x[r] = keep ? sc[nt][r] : -INFINITY;
         mx = fmaxf(mx, x[r]);
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+      mx = xor32_max(mx) * sl2;
       const float mnew = fmaxf(m[nt], mx);
       const float muse = (mnew == -INFINITY) ? 0.f : mnew;
       float ps = 0.f;
@@ -411,7 +411,7 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
         x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
         ps += x[r];
       }
-      ps += __shfl_xor(ps, 32);
+      ps = xor32_add(ps);
       const float alpha = fast_exp2(m[nt] - muse);
       l[nt] = l[nt] * alpha + ps;
       m[nt] = mnew;
@@ -597,7 +597,7 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
     mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xor32_max(mx);
     const float mnew = fmaxf(m, mx);
     const float muse = (mnew == -INFINITY) ? 0.f : mnew;
     const float alpha = fast_exp2(m - muse);
@@ -608,7 +608,7 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
       ps += x[r];
     }
     ps += __shfl_xor(ps, 16);
-    ps += __shfl_xor(ps, 32);
+    ps = xor32_add(ps);
     l = l * alpha + ps;
     m = mnew;
     // P^T for k-step ks: registers of M tiles 2ks and 2ks+1
@@ -741,7 +741,7 @@ __global__ __launch_bounds__(64 * kListWaves) void k_token_gather_list(GatherPar
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     o[e] += __shfl_xor(o[e], 16);
-    o[e] += __shfl_xor(o[e], 32);
+    o[e] = xor32_add(o[e]);
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   if (kg == 0) {

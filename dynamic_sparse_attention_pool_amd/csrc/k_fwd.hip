@@ -381,7 +381,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
     float mx = x[0];
 #pragma unroll
     for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+    mx = xor32_max(mx) * sl2;
     // Lazy rescaling: the reference maximum m only moves when the tile's
     // maximum exceeds it by more than kSlack (log2 units), so probabilities
     // stay below 2^kSlack and O / l are rescaled only on such jumps.  The
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
       pp[r & 3] += x[r];
     }
     float ps = (pp[0] + pp[1]) + (pp[2] + pp[3]);
-    ps += __shfl_xor(ps, 32);
+    ps = xor32_add(ps);
     lsum += ps;
 
     // ---- P^T operand for k-step ks = the 8 consecutive registers x[8ks .. 8ks+7]

@@ -681,13 +681,13 @@ __global__ __launch_bounds__(64 * kVsWaves) void k_vs_pass(const uint16_t* __res
           float mx = acc[0];
 #pragma unroll
           for (int r = 1; r < 16; ++r) mx = fmaxf(mx, acc[r]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32)) * sl2;
+          mx = xor32_max(mx) * sl2;
           const float mnew = fmaxf(m[qt], mx);
           const float muse = mnew == -INFINITY ? 0.f : mnew;
           float ps = 0.f;
 #pragma unroll
           for (int r = 0; r < 16; ++r) ps += fast_exp2(fmaf(acc[r], sl2, -muse));
-          ps += __shfl_xor(ps, 32);
+          ps = xor32_add(ps);
           l[qt] = l[qt] * fast_exp2(m[qt] - muse) + ps;
           m[qt] = mnew;
         }
@@ -714,7 +714,7 @@ __global__ __launch_bounds__(64 * kVsWaves) void k_vs_pass(const uint16_t* __res
             *reinterpret_cast<f32x4*>(&Pl[js][32 * kh + l32][32 * qt + 8 * r4 + 4 * hf]) =
                 f32x4{pv[4 * r4], pv[4 * r4 + 1], pv[4 * r4 + 2], pv[4 * r4 + 3]};
         }
-        cs += __shfl_xor(cs, 32);
+        cs = xor32_add(cs);
         if (hf == 0) av_s[js][tl * 64 + 32 * kh + l32] = cs;
       }
     }
@@ -743,8 +743,8 @@ __global__ __launch_bounds__(64 * kVsWaves) void k_vs_pass(const uint16_t* __res
             else sb += v[u];
           }
         }
-        sa += __shfl_xor(sa, 32);
-        sb += __shfl_xor(sb, 32);
+        sa = xor32_add(sa);
+        sb = xor32_add(sb);
         if (hf == 0) {
           dp_s[jj][tl][pc + 63] = sa;           // d = pc
           if (pc > 0) dp_s[jj][tl][pc - 1] = sb;  // d = pc - 64
