@@ -50,9 +50,10 @@ struct TileRef {
 
 template <int MODE>
 struct TileIter {
-  // block mode
+  // block mode; `pre` holds entry t, read one call ahead so the LDS latency
+  // of the next index is hidden behind a whole tile
   const int32_t* bidx = nullptr;
-  int cnt = 0, t = 0, iblk = 0;
+  int cnt = 0, t = 0, iblk = 0, pre = -1;
   // vertical-slash mode
   const int32_t* iv = nullptr;
   const int32_t* col = nullptr;  // ascending column list (optional: without it every column tile is masked)
@@ -64,7 +65,11 @@ struct TileIter {
   __device__ bool next(TileRef& r) {
     if (MODE == 0) {
       int j = -1;
-      while (t < cnt && (j < 0 || j > iblk)) j = bidx[t++];  // entries outside 0..i are skipped
+      while (t < cnt && (j < 0 || j > iblk)) {  // entries outside 0..i are skipped
+        j = pre;
+        ++t;
+        pre = t < cnt ? bidx[t] : -1;
+      }
       if (j < 0 || j > iblk) return false;
       r.base = j * kBlk;
       r.len = kBlk;
@@ -293,6 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   drain_vmem();  // Q^T resident: from here on the only vector-memory ops are the tile copies
   if (MODE == 0) {
     __syncthreads();
+    it.pre = it.cnt > 0 ? meta[0] : -1;
   } else {
     // the row's bad-column flag passes through the K tile buffer, which no copy
     // has touched yet
