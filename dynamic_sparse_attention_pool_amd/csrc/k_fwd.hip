@@ -62,6 +62,10 @@ struct TileIter {
   int lim = 0;          // keys at or beyond min(seq, end of the query block) are never loaded
   int bad_cols = 0;     // some column lies outside [0, seq): mask every gathered tile
 
+  // block mode: read the first entry once bidx and cnt are set (and the list,
+  // when staged in LDS, is visible to the whole workgroup)
+  __device__ void start_blocks() { pre = cnt > 0 ? bidx[0] : -1; }
+
   __device__ bool next(TileRef& r) {
     if (MODE == 0) {
       int j = -1;
@@ -298,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
   drain_vmem();  // Q^T resident: from here on the only vector-memory ops are the tile copies
   if (MODE == 0) {
     __syncthreads();
-    it.pre = it.cnt > 0 ? meta[0] : -1;
+    it.start_blocks();
   } else {
     // the row's bad-column flag passes through the K tile buffer, which no copy
     // has touched yet
@@ -512,6 +516,7 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
       it.cnt = max(0, min(p.block_cnt[row_id], p.kmax));
     }
     it.iblk = iblk;
+    it.start_blocks();
   } else {
     // the same clipping as the bf16 kernel: counts to capacities, intervals to
     // the keys the block can see, columns outside [0, seq) masked
