@@ -340,7 +340,7 @@ static int check_centroid_topk(const sa_estimate_topk_args* a) {
     return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk(CENTROID): heads_q must be 1..8 times heads_kv");
   if (a->head_dim > 128 || a->head_dim % 4) return fail(SA_ERR_UNSUPPORTED, "sa_estimate_topk(CENTROID): head_dim must be a multiple of 4, at most 128");
   if (a->n_centroids < 1 || a->n_centroids > 1024) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): n_centroids must lie in [1, 1024]");
-  if (a->seq * a->heads_kv > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): too many queries");
+  if (a->seq * a->heads_q > 0x7fffffff) return fail(SA_ERR_SHAPE, "sa_estimate_topk(CENTROID): too many query rows");
   if (!(a->scale > 0.f)) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): scale must be > 0");
   if (a->k < 0) return fail(SA_ERR_VALUE, "sa_estimate_topk(CENTROID): k must be >= 0");
   if (a->mass != 0.f) {
