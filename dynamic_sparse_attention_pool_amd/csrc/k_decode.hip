@@ -30,6 +30,18 @@
 namespace sa {
 namespace {
 
+// a + b and max(a, b) with lane l ^ 16 (v_permlane16_swap: rows of 16 lanes trade
+// places inside each half of the wave).
+__device__ __forceinline__ float xor16_add(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float xor16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+
 constexpr int kBlk = 64;
 constexpr int kD = 128;
 constexpr int kVS = kBlk + 8;  // V^T row stride (elements)
@@ -596,7 +608,7 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
     float mx = x[0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) mx = fmaxf(mx, x[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = xor16_max(mx);
     mx = xor32_max(mx);
     const float mnew = fmaxf(m, mx);
     const float muse = (mnew == -INFINITY) ? 0.f : mnew;
@@ -607,7 +619,7 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
       x[r] = fast_exp2(x[r] - muse);
       ps += x[r];
     }
-    ps += __shfl_xor(ps, 16);
+    ps = xor16_add(ps);
     ps = xor32_add(ps);
     l = l * alpha + ps;
     m = mnew;
@@ -740,7 +752,7 @@ __global__ __launch_bounds__(64 * kListWaves) void k_token_gather_list(GatherPar
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    o[e] += __shfl_xor(o[e], 16);
+    o[e] = xor16_add(o[e]);
     o[e] = xor32_add(o[e]);
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
