@@ -122,71 +122,69 @@ __global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ p
   flag_nonfinite(err, bad);
 }
 
-// 128x128 tile of S per workgroup on the fp32 matrix cores
-// (v_mfma_f32_32x32x2_f32: fp32 products, fp32 accumulation).  The pooled Q
-// and K rows of the tile pass through LDS 32 dimensions at a time.  Step kk of
-// the product takes dimension 2kk + hf from lane half hf, so within each group
-// of 8 dimensions LDS holds the even ones, then the odd ones: one 16-byte read
-// gives a lane its operands for four steps.  Row pitch 36 floats: sixteen
-// consecutive rows' 16-byte reads hit distinct banks.  Wave (wi, wj) computes
-// the 64x64 quarter (wi, wj) as 2x2 MFMA tiles.  Entries above the diagonal are
-// not written; tiles strictly above it do nothing.
+// One wave per 64x64 tile of S at or below the diagonal (four waves per
+// workgroup, tiles enumerated row by row over the lower triangle), operands
+// straight from memory: the contraction over d is split between the two lane
+// halves (half hf takes dimensions hf*D/2 .. +D/2-1, step kk its kk-th), so a
+// lane reads 16 consecutive floats of its row per 16 steps with four 16-byte
+// loads; the next 16 steps' operands are in flight while the current ones run
+// on v_mfma_f32_32x32x2_f32 (fp32 products and accumulation) over four
+// independent accumulators.  Entries above the diagonal are not written.
 template <int D>
-__global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restrict__ pq, const float* __restrict__ pk,
-                                                          int hq, int hkv, HeadList hl, int nb, float scale,
-                                                          float* __restrict__ S, int32_t* __restrict__ err) {
-  constexpr int T = 128, DC = 32, P = DC + 4;
-  __shared__ __attribute__((aligned(16))) float Qs[T * P];
-  __shared__ __attribute__((aligned(16))) float Ks[T * P];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, l32 = lane & 31;
-  const int nbt = (nb + T - 1) / T;
-  const int bh = blockIdx.x / (nbt * nbt);
-  const int tile = blockIdx.x % (nbt * nbt);
-  const int ti = tile / nbt, tj = tile % nbt;
+__global__ __launch_bounds__(256) void k_block_score_direct(const float* __restrict__ pq, const float* __restrict__ pk,
+                                                            int hq, int hkv, HeadList hl, int64_t rows, int nb,
+                                                            float scale, float* __restrict__ S,
+                                                            int32_t* __restrict__ err) {
+  constexpr int HALF = D / 2, NCH = HALF / 16;
+  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31;
+  const int nbt = (nb + 63) / 64;
+  const int64_t per_head = (int64_t)nbt * (nbt + 1) / 2;
+  const int64_t wid = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (wid >= rows * per_head) return;  // whole waves only; no workgroup barrier below
+  const int64_t bh = wid / per_head;
+  const int t = (int)(wid % per_head);
+  int ti = (int)((sqrtf(8.f * (float)t + 1.f) - 1.f) * 0.5f);
+  while ((int64_t)(ti + 1) * (ti + 2) / 2 <= t) ++ti;
+  while ((int64_t)ti * (ti + 1) / 2 > t) --ti;
+  const int tj = t - ti * (ti + 1) / 2;
   int b, h;
   listed_row(bh, hq, hl, b, h);
   const int g = (h * hkv) / hq;
-  float* Sb = S + (int64_t)bh * nb * nb;
-  if (tj > ti) return;
-  const float* Qb = pq + (int64_t)bh * nb * D;
-  const float* Kb = pk + ((int64_t)b * hkv + g) * nb * D;
-  const int wi = wv >> 1, wj = wv & 1;
-  f32x16 acc[2][2] = {};
-  for (int d0 = 0; d0 < D; d0 += DC) {
-    for (int e = tid; e < T * (DC / 4); e += 256) {
-      const int rr = e / (DC / 4), c4 = e % (DC / 4);
-      const int qi = ti * T + rr, kj = tj * T + rr;
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      const f32x4 vq = qi < nb ? *reinterpret_cast<const f32x4*>(Qb + (int64_t)qi * D + d0 + 4 * c4) : z;
-      const f32x4 vk = kj < nb ? *reinterpret_cast<const f32x4*>(Kb + (int64_t)kj * D + d0 + 4 * c4) : z;
+  const float* Qb = pq + bh * (int64_t)nb * D;
+  const float* Kb = pk + ((int64_t)b * hkv + g) * (int64_t)nb * D;
+  const float* qr[2];
+  const float* kr[2];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const int j = 4 * c4 + x, pos = (j & ~7) + 4 * (j & 1) + ((j & 7) >> 1);  // even dims, then odd ones
-        Qs[rr * P + pos] = vq[x];
-        Ks[rr * P + pos] = vk[x];
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int k8 = 0; k8 < DC / 8; ++k8) {
-      // steps 4k8 .. 4k8+3: dimensions 8k8 + 2x + hf
-      f32x4 qa[2], kb[2];
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        qa[m] = *reinterpret_cast<const f32x4*>(&Qs[(64 * wi + 32 * m + l32) * P + 8 * k8 + 4 * hf]);  // A: row l32
-        kb[m] = *reinterpret_cast<const f32x4*>(&Ks[(64 * wj + 32 * m + l32) * P + 8 * k8 + 4 * hf]);  // B: column l32
-      }
-#pragma unroll
-      for (int x = 0; x < 4; ++x)
-#pragma unroll
-        for (int m = 0; m < 2; ++m)
-#pragma unroll
-          for (int n = 0; n < 2; ++n)
-            acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(qa[m][x], kb[n][x], acc[m][n], 0, 0, 0);
-    }
-    __syncthreads();
+  for (int m = 0; m < 2; ++m) {
+    qr[m] = Qb + (int64_t)min(64 * ti + 32 * m + l32, nb - 1) * D + HALF * hf;
+    kr[m] = Kb + (int64_t)min(64 * tj + 32 * m + l32, nb - 1) * D + HALF * hf;
   }
-  // element r of tile (m, n): row 64wi + 32m + 8(r/4) + 4hf + r%4, column 64wj + 32n + l32
+  f32x4 A[2][2][4], B[2][2][4];
+  auto load = [&](int c, int buf) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        A[buf][m][v] = *reinterpret_cast<const f32x4*>(qr[m] + 16 * c + 4 * v);
+        B[buf][m][v] = *reinterpret_cast<const f32x4*>(kr[m] + 16 * c + 4 * v);
+      }
+  };
+  f32x16 acc[2][2] = {};
+  load(0, 0);
+#pragma unroll
+  for (int c = 0; c < NCH; ++c) {
+    if (c + 1 < NCH) load(c + 1, (c + 1) & 1);
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int n = 0; n < 2; ++n)
+          acc[m][n] = __builtin_amdgcn_mfma_f32_32x32x2f32(A[c & 1][m][u / 4][u % 4], B[c & 1][n][u / 4][u % 4],
+                                                          acc[m][n], 0, 0, 0);
+  }
+  // element r of tile (m, n): row 64ti + 32m + 8(r/4) + 4hf + r%4, column 64tj + 32n + l32
+  float* Sb = S + bh * (int64_t)nb * nb;
   bool bad = false;
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -194,8 +192,8 @@ __global__ __launch_bounds__(256) void k_block_score_mfma(const float* __restric
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int i = ti * T + 64 * wi + 32 * m + 8 * (r / 4) + 4 * hf + (r % 4);
-        const int j = tj * T + 64 * wj + 32 * n + l32;
+        const int i = 64 * ti + 32 * m + 8 * (r / 4) + 4 * hf + (r % 4);
+        const int j = 64 * tj + 32 * n + l32;
         if (i < nb && j <= i) {
           const float v = acc[m][n][r] * scale;
           Sb[(int64_t)i * nb + j] = v;
@@ -662,15 +660,16 @@ hipError_t launch_block_score(const float* pq, const float* pk, int batch, int h
                               int nb, int head_dim, float scale, float* scores, int32_t* err, hipStream_t stream) {
   const int64_t rows = (int64_t)batch * (hl.n > 0 ? hl.n : hq);
   if (head_dim == 128 || head_dim == 64) {
-    const int nbt2 = (nb + 127) / 128;
-    const int64_t n2 = rows * nbt2 * nbt2;
-    if (n2 == 0) return hipSuccess;
+    const int64_t nbt = (nb + 63) / 64;
+    const int64_t waves = rows * (nbt * (nbt + 1) / 2);  // 64x64 tiles at or below the diagonal
+    if (waves == 0) return hipSuccess;
+    const dim3 grid((unsigned)((waves + 3) / 4));
     if (head_dim == 128)
-      hipLaunchKernelGGL((k_block_score_mfma<128>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, hl,
-                         nb, scale, scores, err);
+      hipLaunchKernelGGL((k_block_score_direct<128>), grid, dim3(256), 0, stream, pq, pk, hq, hkv, hl, rows, nb, scale,
+                         scores, err);
     else
-      hipLaunchKernelGGL((k_block_score_mfma<64>), dim3((unsigned)n2), dim3(256), 0, stream, pq, pk, hq, hkv, hl,
-                         nb, scale, scores, err);
+      hipLaunchKernelGGL((k_block_score_direct<64>), grid, dim3(256), 0, stream, pq, pk, hq, hkv, hl, rows, nb, scale,
+                         scores, err);
     return hipGetLastError();
   }
   const int nbt = (nb + 63) / 64;
