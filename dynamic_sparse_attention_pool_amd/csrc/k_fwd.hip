@@ -409,24 +409,11 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
       m = mnew;
     }
     const float muse = (m == -INFINITY) ? 0.f : m;
-    float pp[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
-#pragma unroll
-    for (int r = 0; r < 32; ++r) {
-      x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
-      pp[r & 3] += x[r];
-    }
-    float ps = (pp[0] + pp[1]) + (pp[2] + pp[3]);
-    ps = xor32_add(ps);
-    lsum += ps;
 
-    // ---- P^T operand for k-step ks = the 8 consecutive registers x[8ks .. 8ks+7]
-    bf16x8 pv[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pv[ks][e] = (__bf16)x[8 * ks + e];
-
-    // ---- V(t) in LDS
+    // ---- V(t) in LDS: the probabilities are made one k-step at a time, each
+    //      step's P^T operand (8 consecutive registers x[8ks .. 8ks+7]) going
+    //      straight into its products, so the exps of step ks+1 run on the VALU
+    //      while the matrix core works on step ks
     if (more) wait_vmcnt<NDMA>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
@@ -434,8 +421,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
     // 16ks + 8 + 4hf + e) comes from two transposing reads: in each 16-lane group,
     // lane j points at V[key0 + j/4][dim0 + 4(j%4) .. +3]
     const int gl = lane & 15, gsub = (lane >> 4) & 1;
+    float pp[4] = {0.f, 0.f, 0.f, 0.f};  // four partial sums: short dependency chains
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 pvk;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int r = 8 * ks + e;
+        x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
+        pp[r & 3] += x[r];
+        pvk[e] = (__bf16)x[r];
+      }
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {  // independent accumulators back to back
         const int dim = 32 * dt + 16 * gsub + 4 * (gl & 3);
@@ -446,9 +442,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
         const v4i16 lo = lds_read_tr16(Vl + a0);
         const v4i16 hi = lds_read_tr16(Vl + a1);
         const short __attribute__((ext_vector_type(8))) ab = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ab), pv[ks], o[dt]);
+        o[dt] = mfma32x32x16(__builtin_bit_cast(bf16x8, ab), pvk, o[dt]);
       }
     }
+    float ps = (pp[0] + pp[1]) + (pp[2] + pp[3]);
+    ps = xor32_add(ps);
+    lsum += ps;
     wait_lgkm0();
     __builtin_amdgcn_s_barrier();  // both waves are done with V(t)
     if (more) dma_tile<D>(Vl, vb, nxt, cols, N, w, lane);
