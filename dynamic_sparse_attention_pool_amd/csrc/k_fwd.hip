@@ -338,20 +338,20 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
       s1[r] = 0.f;
     }
     {
-      // operands of step st+1 are read while step st runs on the matrix core
-      bf16x8 a0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(l32, hf)]));
-      bf16x8 a1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 + l32, hf)]));
+      // keys 0..31 first, then 32..63 (operands of step st+1 read while step st
+      // runs): the first half's scores are ready while the second half is
+      // still on the matrix core
 #pragma unroll
-      for (int st = 0; st < D / 16; ++st) {
-        bf16x8 n0 = a0, n1 = a1;
-        if (st + 1 < D / 16) {
-          n0 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(l32, 2 * (st + 1) + hf)]));
-          n1 = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 + l32, 2 * (st + 1) + hf)]));
+      for (int half = 0; half < 2; ++half) {
+        f32x16& acc = half ? s1 : s0;
+        bf16x8 a = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 * half + l32, hf)]));
+#pragma unroll
+        for (int st = 0; st < D / 16; ++st) {
+          bf16x8 n = a;
+          if (st + 1 < D / 16) n = as_bf16x8(*reinterpret_cast<const u32x4*>(&Kl[swz<D>(32 * half + l32, 2 * (st + 1) + hf)]));
+          acc = mfma32x32x16(a, qv[st], acc);
+          a = n;
         }
-        s0 = mfma32x32x16(a0, qv[st], s0);
-        s1 = mfma32x32x16(a1, qv[st], s1);
-        a0 = n0;
-        a1 = n1;
       }
     }
     wait_lgkm0();
