@@ -388,6 +388,17 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
         }
       }
     }
+    // Block mode: the first half's probabilities are made with the current
+    // reference before the maximum is known (the lazy rescale below rarely
+    // moves it), so these exps overlap the second half's products; they are
+    // redone if the reference moves.
+    constexpr bool SPEC = (MODE == 0);
+    const float mspec = (m == -INFINITY) ? 0.f : m;
+    float xs[SPEC ? 16 : 1];
+    if constexpr (SPEC) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xs[r] = fast_exp2(fmaf(x[r], sl2, -mspec));
+    }
     float mx = x[0];
 #pragma unroll
     for (int r = 1; r < 32; ++r) mx = fmaxf(mx, x[r]);
@@ -409,6 +420,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
       m = mnew;
     }
     const float muse = (m == -INFINITY) ? 0.f : m;
+    if constexpr (SPEC) {
+      if (__any(muse != mspec)) {  // the reference moved: redo the first half
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[r] = fast_exp2(fmaf(x[r], sl2, -muse));
+      }
+    }
 
     // ---- V(t) in LDS: the probabilities are made one k-step at a time, each
     //      step's P^T operand (8 consecutive registers x[8ks .. 8ks+7]) going
@@ -428,7 +445,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = 8 * ks + e;
-        x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
+        if (SPEC && r < 16) x[r] = xs[SPEC ? r : 0];
+        else x[r] = fast_exp2(fmaf(x[r], sl2, -muse));
         pp[r & 3] += x[r];
         pvk[e] = (__bf16)x[r];
       }
