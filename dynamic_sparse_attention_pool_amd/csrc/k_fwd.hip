@@ -16,16 +16,20 @@
 //   S^T[key][query] = K_tile . Q^T          (v_mfma_f32_32x32x16_bf16, K from LDS,
 //                                            Q^T resident in VGPRs)
 //   online softmax along keys: every lane holds one query column, so the row
-//   statistics need a single exchange with lane^32
+//   statistics need a single exchange with lane^32 (a register lane swap)
 //   O^T[d][query] += V^T . P^T               (V^T read with ds_read_b64_tr_b16, which
 //                                            transposes 4-key x 16-dim blocks on the
 //                                            way out of LDS; P^T comes straight from
 //                                            the S^T accumulators, no shuffles)
-// K(t+1) is fetched while the softmax and P.V of tile t run, V(t+1) while the
-// next S^T runs: one LDS buffer each (40 KB per workgroup, four workgroups per
-// CU), four barriers per tile.  The tile fills, not the matrix cores, bound this
-// kernel: every kept (head, query block, key block) brings its own 32 KB of K
-// and V through L2.
+// The probabilities of each 8-key step are made just before that step's P.V
+// products, so the exps overlap the matrix core; in block mode the first half
+// of them is made with the current reference maximum before the tile's own
+// maximum is known.  K(t+1) is fetched while the softmax and P.V of tile t
+// run, V(t+1) while the next S^T runs: one LDS buffer each (40 KB per
+// workgroup, four workgroups per CU), four barriers per tile.  Every kept
+// (head, query block, key block) brings its own 32 KB of K and V through L2;
+// with all of them L2 hits the loop still takes most of the time, its VALU
+// softmax and its products overlapping only in part.
 #include <climits>
 
 #include "common.h"
