@@ -172,9 +172,11 @@ __device__ __forceinline__ void dma_tile(uint16_t* lds, const uint16_t* gbase, c
 //          when batch x KV heads == 8).
 // order 1: every XCD works on the same KV head at the same time, so the K/V
 //          being read stays in the 256 MB Infinity Cache even when all heads'
-//          K/V do not fit; each XCD takes runs of 8 consecutive query blocks
-//          (neighbouring rows share their local blocks in that XCD's L2).
-//          Needs nqb % 64 == 0 and the item count a multiple of 8.
+//          K/V do not fit; each XCD takes runs of 4 consecutive query blocks
+//          (neighbouring rows share their local blocks in that XCD's L2, and
+//          all XCDs stay on nearby query blocks; runs of 2, 8, 16 and 32
+//          measured slower or equal).  Needs nqb % 64 == 0 and the item count
+//          a multiple of 8.
 __device__ __forceinline__ void item_of(int bid, int n_items, int grp, int nqb, int order, int& hh, int& ii,
                                         int& bg) {
   if (order == 1) {
@@ -183,9 +185,9 @@ __device__ __forceinline__ void item_of(int bid, int n_items, int grp, int nqb, 
     bg = slot / per_bg;
     const int rem = slot % per_bg;
     hh = rem % grp;
-    const int r8 = (rem / grp) % 8;
-    const int cidx = rem / (8 * grp);
-    ii = (cidx * kXcds + x) * 8 + r8;
+    const int r4 = (rem / grp) % 4;
+    const int cidx = rem / (4 * grp);
+    ii = (cidx * kXcds + x) * 4 + r4;
     return;
   }
   int rest = xcd_remap(bid, n_items);
