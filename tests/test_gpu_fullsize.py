@@ -29,9 +29,15 @@ def test_block_sparse_layer_full_size(sa, N, ratio, seed):
     inp = W.prefill_bf16(seed, 1, 32, 8, N, 128)
     layer = BlockSparseLayer(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), n_sink=1, n_local=4, ratio=ratio,
                              out_dtype=torch().bfloat16, with_lse=True)
+    # every (head, query block) of the launch writes its rows, whatever order the
+    # workgroups take them in: no NaN planted before the launch may survive
+    layer.out.fill_(float("nan"))
+    layer.lse.fill_(float("nan"))
     layer.step()
     torch().cuda.synchronize()
     assert int(host(layer.err)[0]) == 0
+    assert bool(torch().isfinite(layer.out).all()), "some output rows were not written"
+    assert bool(torch().isfinite(layer.lse).all()), "some lse rows were not written"
     nb = N // 64
     scale = 1 / math.sqrt(128)
     idx, cnt = host(layer.idx), host(layer.cnt)

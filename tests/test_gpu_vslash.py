@@ -176,8 +176,10 @@ def test_vs_full_size_sampled(sa):
     inp = W.prefill_bf16(W.CONFIG_SEEDS[3], 1, 32, 8, N, d)
     layer = VerticalSlashLayer(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), n_vert=1000, n_slash=64,
                                out_dtype=torch().float32)
+    layer.out.fill_(float("nan"))   # every row of the launch must be written
     layer.step()
     torch().cuda.synchronize()
+    assert bool(torch().isfinite(layer.out).all()), "some output rows were not written"
     scale = 1 / math.sqrt(d)
     vh, sh = host(layer.vert), host(layer.slash)
     av_all, as_all = host(layer.a_v), host(layer.a_s)
