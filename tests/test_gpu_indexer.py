@@ -90,8 +90,14 @@ def test_indexer_full_size_sampled_rows(sa):
     L = W.mqa_layer(seed, 0, T, 16, 1, N, 128)
     layers = [(dev_bf16(L.q), dev_bf16(L.k), dev_bf16(L.v))]
     ip = IndexerPrefill(dev_bf16(ind.qi), dev_bf16(ind.ki), dev_f32(ind.w), ind.pos0, layers, k_sel=k)
+    # every score (causal ones and the -inf beyond each query's position) and
+    # every output row is written: no NaN planted before the launch survives
+    ip.scores.fill_(float("nan"))
+    ip.outs[0].fill_(float("nan"))
     ip.step()
     torch().cuda.synchronize()
+    assert not bool(torch().isnan(ip.scores).any()), "some indexer scores were not written"
+    assert bool(torch().isfinite(ip.outs[0]).all()), "some gathered-attention rows were not written"
     rows = np.array([0, 1, 777, 2048, 4000, 4095])
     scores = host(ip.scores[rows.tolist()])
     idx = host(ip.idx)[rows]
