@@ -227,6 +227,10 @@ def test_estimate_topk_argument_errors(lib):
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 2
     c.kmax, c.n_centroids = 64, 2000
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 2
+    c.n_centroids = 1025                                                         # one past the cap
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 2
+    c.n_centroids = 1024                                                         # the cap itself
+    assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 0
     c.n_centroids, c.heads_q = 256, 80                                           # 10 query heads per KV head
     assert lib.sa_estimate_topk_workspace_bytes(C.byref(c), C.byref(n)) == 6
     c.heads_q, c.n_sink = 32, 1
