@@ -199,6 +199,28 @@ def test_fwd_bf16_on_oracle_sets(sa, d, out_bf16):
     assert np.max(np.abs(l - wl)) < 1e-3
 
 
+def test_fwd_bf16_row_at_table_capacity(sa):
+    """At 131072 tokens a row may list all 2048 blocks, the most the bf16 path
+    stages per row: that row, a row of every other block, a half-length dense
+    row and diagonal-only rows, sampled against the oracle."""
+    B, Hq, Hkv, N, d = 1, 1, 1, 131072, 128
+    nb = N // 64
+    inp = W.prefill_bf16(15, B, Hq, Hkv, N, d)
+    kept = [[[np.array([i]) for i in range(nb)]]]
+    kept[0][0][nb - 1] = np.arange(nb)
+    kept[0][0][nb - 2] = np.arange(0, nb - 1, 2)
+    kept[0][0][1000] = np.arange(1001)
+    print(f"capacity row: kmax {nb}, N {N}", flush=True)
+    o, l = run_fwd(sa, dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), kept, nb)
+    rows = [0, 999, 1000, nb - 2, nb - 1]
+    wo, wl = oracle.block_sparse_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), kept, 64, 1 / math.sqrt(d),
+                                           blocks=rows)
+    for i in rows:
+        r = slice(64 * i, 64 * i + 64)
+        assert_attention_close(o[:, :, r], wo[:, :, r], bf16=True, what=f"capacity rows, block {i}")
+        assert np.max(np.abs(l[:, :, r] - wl[:, :, r])) < 1e-3
+
+
 def test_fwd_bf16_empty_and_single_block_rows(sa):
     B, Hq, Hkv, N, d = 1, 2, 1, 512, 128
     inp = W.prefill_bf16(14, B, Hq, Hkv, N, d)
