@@ -149,12 +149,16 @@ def test_token_gather_lists_and_causal_bound(sa, Hq, Hkv, per_head, causal):
     assert np.max(np.abs(gl[fin] - wl[fin])) < 1e-3
 
 
-def test_cluster_decode_causal_bound(sa):
+@pytest.mark.parametrize("T,qpos", [(4, [4095, 2000, 10, 900]),
+                                    (12, [4095, 0, 3000, 17, 2048, 4000, 1, 512, 3999, 64, 100, 2500])])
+def test_cluster_decode_causal_bound(sa, T, qpos):
     """Cluster mode with q_pos: packed rows map back to context positions
     through the pack's perm; query t attends the tokens of its selected
-    clusters at or before q_pos[t] (none for some)."""
+    clusters at or before q_pos[t] (none for some).  T = 12 puts 48 query
+    rows on each KV head (the two-tile form of the gather)."""
     t = torch()
-    T, Hq, Hkv, N, d, C, ks = 4, 8, 2, 4096, 128, 64, 8
+    Hq, Hkv, N, d, C, ks = 8, 2, 4096, 128, 64, 8
+    print(f"causal cluster decode T{T}", flush=True)
     dec = W.decode_clustered(75, T, Hq, Hkv, N, d, C)
     ptr = t.empty((Hkv, C + 1), dtype=t.int32, device="cuda:0")
     perm = t.empty((Hkv, N), dtype=t.int32, device="cuda:0")
@@ -165,7 +169,7 @@ def test_cluster_decode_causal_bound(sa):
     scale = 1 / math.sqrt(d)
     sel = oracle.cluster_select(oracle.centroid_scores(W.bf16_to_f32(dec.q), dec.centroids, scale), ks)
     sel_np = np.array([[s for s in row] for row in sel], np.int32)
-    qpos = np.array([4095, 2000, 10, 900], np.int32)
+    qpos = np.array(qpos, np.int32)
     out = t.empty((T, Hq, d), dtype=t.float32, device="cuda:0")
     lse = t.empty((T, Hq), dtype=t.float32, device="cuda:0")
     sa.sa_gather_decode(dev_bf16(dec.q), kp, vp, out, cluster_ptr=ptr, sel=dev_i32(sel_np), lse=lse,
