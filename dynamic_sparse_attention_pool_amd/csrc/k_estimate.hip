@@ -58,70 +58,8 @@ __global__ __launch_bounds__(256) void k_pool(const T* __restrict__ x, int hq, H
   }
 }
 
-// ---------------------------------------------------------------- k_block_score
+// ---------------------------------------------------------------- k_block_score_direct
 // S[b,h,i,j] = pooled_q[b,h,i] . pooled_k[b,g(h),j] * scale for j <= i.
-// 64x64 output tile per workgroup, 4x4 per thread, fp32 FMAs in dimension
-// order.  Entries above the diagonal are not written (the causal selection
-// never reads them); tiles strictly above it do nothing.
-__global__ __launch_bounds__(256) void k_block_score(const float* __restrict__ pq, const float* __restrict__ pk,
-                                                     int hq, int hkv, HeadList hl, int nb, int D, float scale,
-                                                     float* __restrict__ S, int32_t* __restrict__ err) {
-  __shared__ float Qs[64][33];
-  __shared__ float Ks[64][33];
-  const int tid = threadIdx.x, tx = tid % 16, ty = tid / 16;
-  const int nbt = (nb + 63) / 64;
-  const int bh = blockIdx.x / (nbt * nbt);
-  const int tile = blockIdx.x % (nbt * nbt);
-  const int ti = tile / nbt, tj = tile % nbt;
-  int b, h;
-  listed_row(bh, hq, hl, b, h);
-  const int g = (h * hkv) / hq;
-  float* Sb = S + (int64_t)bh * nb * nb;
-  if (tj > ti) return;
-  const float* Qb = pq + (int64_t)bh * nb * D;
-  const float* Kb = pk + ((int64_t)b * hkv + g) * nb * D;
-  float acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[a][c] = 0.f;
-  for (int d0 = 0; d0 < D; d0 += 32) {
-    for (int e = tid; e < 64 * 32; e += 256) {
-      const int rr = e / 32, dd = e % 32;
-      const int qi = ti * 64 + rr, kj = tj * 64 + rr;
-      Qs[rr][dd] = qi < nb ? Qb[(int64_t)qi * D + d0 + dd] : 0.f;
-      Ks[rr][dd] = kj < nb ? Kb[(int64_t)kj * D + d0 + dd] : 0.f;
-    }
-    __syncthreads();
-#pragma unroll 8
-    for (int dd = 0; dd < 32; ++dd) {
-      float qv[4], kv[4];
-#pragma unroll
-      for (int a = 0; a < 4; ++a) qv[a] = Qs[ty + 16 * a][dd];
-#pragma unroll
-      for (int c = 0; c < 4; ++c) kv[c] = Ks[tx + 16 * c][dd];
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[a][c] = fmaf(qv[a], kv[c], acc[a][c]);
-    }
-    __syncthreads();
-  }
-  bool bad = false;
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int i = ti * 64 + ty + 16 * a, j = tj * 64 + tx + 16 * c;
-      if (i < nb && j <= i) {
-        const float v = acc[a][c] * scale;
-        Sb[(int64_t)i * nb + j] = v;
-        bad |= nonfinite(v);
-      }
-    }
-  flag_nonfinite(err, bad);
-}
-
 // One wave per 64x64 tile of S at or below the diagonal (four waves per
 // workgroup, tiles enumerated row by row over the lower triangle), operands
 // straight from memory: the contraction over d is split between the two lane
@@ -255,68 +193,53 @@ __global__ __launch_bounds__(256) void k_centroid_score(const T* __restrict__ q,
 }
 
 // ---------------------------------------------------------------- k_centroid_topk
-// Centroid scores and the per-row top-k in one pass, for decode: a workgroup
-// covers nrow query heads of one token that share a KV head (one head per
-// workgroup at launch, which spreads the centroid rows' loads over four times
-// as many CUs as one workgroup per KV head).  Thread c owns centroids c, c+256,
-// ...: it reads each centroid row (its loads issued together) and computes its
-// score for every row (dimension order, fp32, as k_centroid_score), keeping
-// order-preserving keys in LDS.  Per row, an
-// MSB-first radix select (8-bit digits, LDS histograms, 32 threads per row for
-// the digit) finds the k-th key T; candidates above T and the lowest-index
-// keys equal to T are written in cluster order.
+// Centroid scores and the adaptive budget in one pass, for decode: one
+// workgroup per (token, query head).  Thread c owns centroids c, c+256, ...: it
+// reads each centroid row (its loads issued together) and computes the row's
+// score (dimension order, fp32, as k_centroid_score), keeping order-preserving
+// keys in LDS; the adaptive budget of sa_select_mass (mass_select_lds) then
+// runs on those keys, with k as the upper clamp.  The fixed budget takes
+// k_centroid_topk_wave.
 constexpr int kCtThreads = 256;
-constexpr int kCtMaxRows = 8;
 constexpr int kCtMaxC = 1024;
 
-// MASS: one row per workgroup; instead of the fixed top-k, the adaptive
-// budget of sa_select_mass (mass_select_lds) on the row's keys, with k as the
-// upper clamp.
-template <typename T, bool MASS>
+template <typename T>
 __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restrict__ q, const float* __restrict__ cent,
                                                               int hq, int hkv, int C, int D, float scale, int k,
-                                                              int kmax, int nsub, float mass, int k_min,
+                                                              int kmax, float mass, int k_min,
                                                               int32_t* __restrict__ idx, int32_t* __restrict__ cnt,
                                                               int32_t* err) {
-  __shared__ float qs[kCtMaxRows][128];
-  __shared__ uint32_t keys[kCtMaxRows][kCtMaxC];
-  __shared__ uint32_t hist[kCtMaxRows][256];
-  __shared__ uint32_t s_digit[kCtMaxRows][2];
-  __shared__ int32_t s_need[kCtMaxRows];
-  __shared__ uint32_t s_wave[kCtThreads / 64][kCtMaxRows][2];
+  __shared__ float qs[128];
+  __shared__ uint32_t keys[kCtMaxC];
+  __shared__ uint64_t kv[kCtMaxC];
+  __shared__ uint32_t bm[kCtMaxC / 32];
+  __shared__ uint64_t wtmp[kCtThreads / 64];
+  __shared__ uint32_t utmp[kCtThreads / 64];
   __shared__ uint32_t s_nan;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  // workgroup (t, s, g): token t, KV head g (innermost, so one KV head's
-  // centroid rows stay in one XCD's L2), rows s*nrow .. of the g's query heads
-  const int grp = hq / hkv, nrow = grp / nsub;
+  const int tid = threadIdx.x;
+  // workgroup (t, h): KV head innermost, so one KV head's centroid rows stay
+  // in one XCD's L2
+  const int grp = hq / hkv;
   const int g = blockIdx.x % hkv, ts = blockIdx.x / hkv;
-  const int t = ts / nsub, h0 = g * grp + (ts % nsub) * nrow;
-  const int kr = min(k, C);
+  const int t = ts / grp, h = g * grp + ts % grp;
+  const int64_t row = (int64_t)t * hq + h;
   if (tid == 0) s_nan = 0u;
-  for (int e = tid; e < nrow * D; e += kCtThreads) {
-    const int hh = e / D, d = e % D;
-    const T* qp = q + ((int64_t)t * hq + h0 + hh) * D + d;
-    if constexpr (sizeof(T) == 2) qs[hh][d] = bf2f(*reinterpret_cast<const uint16_t*>(qp));
-    else qs[hh][d] = *reinterpret_cast<const float*>(qp);
+  for (int d = tid; d < D; d += kCtThreads) {
+    const T* qp = q + row * D + d;
+    if constexpr (sizeof(T) == 2) qs[d] = bf2f(*reinterpret_cast<const uint16_t*>(qp));
+    else qs[d] = *reinterpret_cast<const float*>(qp);
   }
-  if (tid < nrow) s_need[tid] = kr;
   __syncthreads();
   // ---- scores -> keys
   bool nan_seen = false;
   for (int c = tid; c < C; c += kCtThreads) {
     const float* cr = cent + ((int64_t)g * C + c) * D;
-    float acc[kCtMaxRows];
-#pragma unroll
-    for (int hh = 0; hh < kCtMaxRows; ++hh) acc[hh] = 0.f;
+    float acc = 0.f;
     auto fma4 = [&](int d0, const f32x4& m4) {
-#pragma unroll
-      for (int hh = 0; hh < kCtMaxRows; ++hh)
-        if (hh < nrow) {
-          acc[hh] = fmaf(qs[hh][d0], m4[0], acc[hh]);
-          acc[hh] = fmaf(qs[hh][d0 + 1], m4[1], acc[hh]);
-          acc[hh] = fmaf(qs[hh][d0 + 2], m4[2], acc[hh]);
-          acc[hh] = fmaf(qs[hh][d0 + 3], m4[3], acc[hh]);
-        }
+      acc = fmaf(qs[d0], m4[0], acc);
+      acc = fmaf(qs[d0 + 1], m4[1], acc);
+      acc = fmaf(qs[d0 + 2], m4[2], acc);
+      acc = fmaf(qs[d0 + 3], m4[3], acc);
     };
     // the row's loads are issued before its products (16 in flight), so one
     // memory latency covers a 64-dimension half instead of one per 4 dimensions
@@ -329,140 +252,18 @@ __global__ __launch_bounds__(kCtThreads) void k_centroid_topk(const T* __restric
       for (int u = 0; u < 16; ++u) fma4(d0 + 4 * u, m4[u]);
     }
     for (; d0 < D; d0 += 4) fma4(d0, *reinterpret_cast<const f32x4*>(cr + d0));
-#pragma unroll
-    for (int hh = 0; hh < kCtMaxRows; ++hh)
-      if (hh < nrow) {
-        const float sc = acc[hh] * scale;
-        nan_seen |= is_nan(sc);
-        keys[hh][c] = order_key(sc);
-      }
+    const float sc = acc * scale;
+    nan_seen |= is_nan(sc);
+    keys[c] = order_key(sc);
   }
   if (nan_seen) atomicOr(&s_nan, 1u);
-  if constexpr (MASS) {
-    // one row: (key << 32 | ~index) pairs, padded to a power of two, then the adaptive budget
-    __shared__ uint64_t kv[kCtMaxC];
-    __shared__ uint32_t bm[kCtMaxC / 32];
-    __shared__ uint64_t wtmp[kCtThreads / 64];
-    __shared__ uint32_t utmp[kCtThreads / 64];
-    __syncthreads();
-    int P = 64;
-    while (P < C) P <<= 1;
-    for (int c = tid; c < P; c += kCtThreads)
-      kv[c] = c < C ? (((uint64_t)keys[0][c] << 32) | (uint64_t)(~(uint32_t)c)) : 0ull;
-    __syncthreads();
-    const int64_t row = (int64_t)t * hq + h0;
-    mass_select_lds<kCtThreads>(kv, bm, wtmp, utmp, C, P, mass, k_min, k, idx + row * kmax, kmax, cnt + row);
-    if (tid == 0 && s_nan && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
-    return;
-  }
-  // ---- radix select: T[hh] = the kr-th largest key of row hh
-  uint32_t Tk[kCtMaxRows];
-#pragma unroll
-  for (int hh = 0; hh < kCtMaxRows; ++hh) Tk[hh] = 0u;
-  constexpr int TPR = kCtThreads / kCtMaxRows;  // 32 threads per row in the digit search
-#pragma unroll 1
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    const uint32_t hmask = shift == 24 ? 0u : ~((1u << (shift + 8)) - 1u);
-    for (int e = tid; e < kCtMaxRows * 256; e += kCtThreads) (&hist[0][0])[e] = 0u;
-    __syncthreads();
-    for (int c = tid; c < C; c += kCtThreads)
-#pragma unroll
-      for (int hh = 0; hh < kCtMaxRows; ++hh)
-        if (hh < nrow) {
-          const uint32_t key = keys[hh][c];
-          if ((key & hmask) == (Tk[hh] & hmask)) atomicAdd(&hist[hh][(key >> shift) & 255u], 1u);
-        }
-    __syncthreads();
-    {
-      const int row = tid / TPR, seg = tid % TPR;
-      if (row < nrow) {
-        const int rneed = s_need[row];
-        uint32_t loc = 0u;
-#pragma unroll
-        for (int x = 0; x < 8; ++x) loc += hist[row][8 * seg + x];
-        uint32_t incl = loc;
-#pragma unroll
-        for (int off = 1; off < TPR; off <<= 1) {
-          const uint32_t o = __shfl_down(incl, off, TPR);
-          if (seg + off < TPR) incl += o;
-        }
-        const uint32_t above = incl - loc;
-        if (rneed == 0) {
-          if (seg == TPR - 1) {
-            s_digit[row][0] = 255u;
-            s_digit[row][1] = 0u;
-          }
-        } else if (above < (uint32_t)rneed && (uint32_t)rneed <= incl) {
-          uint32_t acc = above;
-          for (int dg = 8 * seg + 7; dg >= 8 * seg; --dg) {
-            const uint32_t hc = hist[row][dg];
-            if (acc + hc >= (uint32_t)rneed) {
-              s_digit[row][0] = (uint32_t)dg;
-              s_digit[row][1] = acc;
-              break;
-            }
-            acc += hc;
-          }
-        }
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hh = 0; hh < kCtMaxRows; ++hh)
-      if (hh < nrow) Tk[hh] |= s_digit[hh][0] << shift;
-    if (tid < nrow) s_need[tid] -= (int)s_digit[tid][1];  // read again after two more barriers
-  }
   __syncthreads();
-  // ---- emission in cluster order: chunks of 256 candidates, ballots per wave
-  const uint64_t lt = (1ull << lane) - 1ull;
-  int base_f[kCtMaxRows], base_t[kCtMaxRows];
-#pragma unroll
-  for (int hh = 0; hh < kCtMaxRows; ++hh) base_f[hh] = base_t[hh] = 0;
-  for (int c0 = 0; c0 < C; c0 += kCtThreads) {
-    const int c = c0 + tid;
-    uint64_t mf[kCtMaxRows], mt[kCtMaxRows];
-#pragma unroll
-    for (int hh = 0; hh < kCtMaxRows; ++hh) {
-      const uint32_t key = (c < C && hh < nrow) ? keys[hh][c] : 0u;
-      const bool live = c < C && hh < nrow;
-      mf[hh] = __ballot(live && key > Tk[hh]);
-      mt[hh] = __ballot(live && key == Tk[hh]);
-      if (lane == 0) {
-        s_wave[wv][hh][0] = (uint32_t)__popcll(mf[hh]);
-        s_wave[wv][hh][1] = (uint32_t)__popcll(mt[hh]);
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int hh = 0; hh < kCtMaxRows; ++hh) {
-      if (hh >= nrow) continue;
-      int wf = 0, wt = 0, af = 0, at = 0;
-      for (int x = 0; x < kCtThreads / 64; ++x) {
-        const int f = (int)s_wave[x][hh][0], e = (int)s_wave[x][hh][1];
-        if (x < wv) {
-          wf += f;
-          wt += e;
-        }
-        af += f;
-        at += e;
-      }
-      const int need = s_need[hh];
-      const int fb = base_f[hh] + wf + (int)__popcll(mf[hh] & lt);
-      const int tb = base_t[hh] + wt + (int)__popcll(mt[hh] & lt);
-      int32_t* out = idx + ((int64_t)t * hq + h0 + hh) * kmax;
-      if ((mf[hh] >> lane) & 1ull) out[fb + min(tb, need)] = c;
-      else if (((mt[hh] >> lane) & 1ull) && tb < need) out[fb + tb] = c;
-      base_f[hh] += af;
-      base_t[hh] += at;
-    }
-    __syncthreads();
-  }
-  for (int e = tid; e < nrow * kmax; e += kCtThreads) {
-    const int hh = e / kmax, pos = e % kmax;
-    const int64_t row = (int64_t)t * hq + h0 + hh;
-    if (pos >= kr) idx[row * kmax + pos] = -1;
-    if (pos == 0) cnt[row] = kr;
-  }
+  // (key << 32 | ~index) pairs, padded to a power of two, then the adaptive budget
+  int P = 64;
+  while (P < C) P <<= 1;
+  for (int c = tid; c < P; c += kCtThreads) kv[c] = c < C ? (((uint64_t)keys[c] << 32) | (uint64_t)(~(uint32_t)c)) : 0ull;
+  __syncthreads();
+  mass_select_lds<kCtThreads>(kv, bm, wtmp, utmp, C, P, mass, k_min, k, idx + row * kmax, kmax, cnt + row);
   if (tid == 0 && s_nan && err != nullptr) atomicOr(reinterpret_cast<unsigned int*>(err), 1u);
 }
 
@@ -618,21 +419,14 @@ hipError_t launch_centroid_topk(const void* q, bool q_bf16, const float* cent, i
 #undef SA_CTW_LAUNCH
     return hipGetLastError();
   }
-  // adaptive budget: one query head per workgroup: four times the workgroups
-  // of one per KV head, so the centroid rows' loads spread over more CUs
-  const int nsub = hq / hkv;
-  const dim3 grid((unsigned)(T * hkv * nsub));
-#define SA_CT_LAUNCH(TQ, M)                                                                                 \
-  hipLaunchKernelGGL((k_centroid_topk<TQ, M>), grid, dim3(kCtThreads), 0, stream, (const TQ*)q, cent, hq, hkv, C, \
-                     head_dim, scale, k, kmax, nsub, mass, k_min, idx, cnt, err)
-  if (q_bf16) {
-    if (mass > 0.f) SA_CT_LAUNCH(uint16_t, true);
-    else SA_CT_LAUNCH(uint16_t, false);
-  } else {
-    if (mass > 0.f) SA_CT_LAUNCH(float, true);
-    else SA_CT_LAUNCH(float, false);
-  }
-#undef SA_CT_LAUNCH
+  // adaptive budget: one workgroup per (token, query head)
+  const dim3 grid((unsigned)(T * hq));
+  if (q_bf16)
+    hipLaunchKernelGGL((k_centroid_topk<uint16_t>), grid, dim3(kCtThreads), 0, stream, (const uint16_t*)q, cent, hq, hkv,
+                       C, head_dim, scale, k, kmax, mass, k_min, idx, cnt, err);
+  else
+    hipLaunchKernelGGL((k_centroid_topk<float>), grid, dim3(kCtThreads), 0, stream, (const float*)q, cent, hq, hkv, C,
+                       head_dim, scale, k, kmax, mass, k_min, idx, cnt, err);
   return hipGetLastError();
 }
 
@@ -672,12 +466,7 @@ hipError_t launch_block_score(const float* pq, const float* pk, int batch, int h
                          scores, err);
     return hipGetLastError();
   }
-  const int nbt = (nb + 63) / 64;
-  const int64_t n = rows * nbt * nbt;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_block_score, dim3((unsigned)n), dim3(256), 0, stream, pq, pk, hq, hkv, hl, nb, head_dim,
-                     scale, scores, err);
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_centroid_score(const void* q, bool q_bf16, const float* cent, int T, int hq, int hkv,

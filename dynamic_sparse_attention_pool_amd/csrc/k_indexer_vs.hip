@@ -863,15 +863,23 @@ hipError_t launch_indexer(const uint16_t* q, const uint16_t* k, const float* w, 
                        pos0, out, flag);
     return hipGetLastError();
   }
+  // the other multiples of 8 up to 64 heads: hi / 8 heads per wave
   const dim3 grid((unsigned)(((T + 31) / 32) * nchunk));
   const int hpw = hi / kIdxWaves;
+#define SA_IDX_CASE(H_)                                                                                              \
+  case H_:                                                                                                           \
+    hipLaunchKernelGGL((k_indexer<H_>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); \
+    break;
   switch (hpw) {
-    case 1: hipLaunchKernelGGL((k_indexer<1>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
-    case 2: hipLaunchKernelGGL((k_indexer<2>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
-    case 4: hipLaunchKernelGGL((k_indexer<4>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
-    case 8: hipLaunchKernelGGL((k_indexer<8>), grid, dim3(64 * kIdxWaves), 0, stream, q, k, w, T, hi, nk, pos0, out, err); break;
+    SA_IDX_CASE(1)
+    SA_IDX_CASE(2)
+    SA_IDX_CASE(3)
+    SA_IDX_CASE(5)
+    SA_IDX_CASE(6)
+    SA_IDX_CASE(7)
     default: return hipErrorInvalidValue;
   }
+#undef SA_IDX_CASE
   return hipGetLastError();
 }
 

@@ -126,7 +126,8 @@ int check_estimate(const sa_estimate_args* a, size_t* ws) {
       if (a->dtype != SA_BF16) return fail(SA_ERR_DTYPE, "sa_estimate(INDEXER): dtype must be BF16");
       if (!a->weights) return fail(SA_ERR_NULL, "sa_estimate(INDEXER): weights required");
       if (a->head_dim != 64) return fail(SA_ERR_UNSUPPORTED, "sa_estimate(INDEXER): head_dim must be 64");
-      if (a->heads_q % 8) return fail(SA_ERR_UNSUPPORTED, "sa_estimate(INDEXER): indexer heads must be a multiple of 8");
+      if (a->heads_q % 8 || a->heads_q > 64)
+        return fail(SA_ERR_UNSUPPORTED, "sa_estimate(INDEXER): indexer heads must be a multiple of 8, at most 64");
       if (a->heads_kv != 1) return fail(SA_ERR_SHAPE, "sa_estimate(INDEXER): one indexer key head");
       if (a->q_pos0 < 0) return fail(SA_ERR_VALUE, "sa_estimate(INDEXER): q_pos0 must be >= 0");
       if (a->seq_k > ((int64_t)1 << 31) - 64) return fail(SA_ERR_SHAPE, "sa_estimate(INDEXER): seq_k too large");

@@ -89,7 +89,7 @@ typedef enum sa_dtype { SA_F32 = 0, SA_BF16 = 1, SA_I32 = 2 } sa_dtype;
  *   q [T,Hi,di] (BF16; heads_q = Hi, head_dim = di, seq_q = T),
  *   k [Nk,di] (BF16; seq_k = Nk, heads_kv = 1), weights [Hi] float.
  *   scores [T,Nk] float, -INFINITY where s > q_pos0 + t.  No scale.
- *   di must be 64; Hi a multiple of 8.
+ *   di must be 64; Hi a multiple of 8, at most 64.
  *
  * Head list (BLOCK_MEANPOOL and VSLASH; "MInference 1.0" article, §方法介紹:
  * each head runs the estimate of its own pattern): head_list, when not NULL,

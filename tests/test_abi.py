@@ -301,6 +301,10 @@ def test_estimate_and_gather_argument_errors(lib):
     e.head_dim = 32
     e.weights = 256
     assert lib.sa_estimate(C.byref(e), None, 0, None) == 6
+    e.head_dim, e.heads_kv, e.heads_q = 64, 1, 72                     # more than 64 indexer heads
+    assert lib.sa_estimate(C.byref(e), None, 0, None) == 6
+    e.heads_q = 20                                                    # not a multiple of 8
+    assert lib.sa_estimate(C.byref(e), None, 0, None) == 6
     e.kind = 9
     assert lib.sa_estimate(C.byref(e), None, 0, None) == 8
     g = F.GatherArgs()

@@ -174,9 +174,10 @@ def run_fwd(sa, q, k, v, kept_lists, kmax, out_bf16=False, scale=None):
     return host(out), host(lse)
 
 
-def test_fwd_fp32_sink_diag_top2_on_oracle_sets(sa):
-    inp = W.prefill_fp32(W.CONFIG_SEEDS[1], 1, 1, 1024, 64)
-    scale = 1 / 8.0
+@pytest.mark.parametrize("d", [64, 128])
+def test_fwd_fp32_sink_diag_top2_on_oracle_sets(sa, d):
+    inp = W.prefill_fp32(W.CONFIG_SEEDS[1], 1, 1, 1024, d)
+    scale = 1 / math.sqrt(d)
     S = oracle.block_scores(inp.q, inp.k, 64, scale)
     kept = oracle.block_select(S, n_sink=1, n_local=1, k=2)
     o, l = run_fwd(sa, dev_f32(inp.q), dev_f32(inp.k), dev_f32(inp.v), kept, 4, scale=scale)
@@ -185,7 +186,7 @@ def test_fwd_fp32_sink_diag_top2_on_oracle_sets(sa):
     assert np.max(np.abs(l - wl)) < 1e-5
 
 
-@pytest.mark.parametrize("d,out_bf16", [(128, False), (128, True), (64, False)])
+@pytest.mark.parametrize("d,out_bf16", [(128, False), (128, True), (64, False), (64, True)])
 def test_fwd_bf16_on_oracle_sets(sa, d, out_bf16):
     B, Hq, Hkv, N = 1, 4, 2, 1024
     inp = W.prefill_bf16(13, B, Hq, Hkv, N, d)

@@ -166,7 +166,7 @@ def test_token_gather_mqa(sa, T, N, ntok):
 
 @pytest.mark.parametrize("T,Hq,Hkv,C,k,dt", [(8, 32, 8, 256, 64, "bf16"), (3, 6, 2, 1000, 37, "f32"),
                                             (2, 8, 1, 300, 400, "bf16"), (5, 4, 4, 17, 5, "f32"),
-                                            (4, 8, 2, 1024, 100, "bf16")])
+                                            (4, 8, 2, 1024, 100, "bf16"), (3, 8, 2, 400, 50, "f32")])
 def test_fused_centroid_topk_matches_oracle_and_separate_path(sa, T, Hq, Hkv, C, k, dt):
     """sa_estimate_topk(CENTROID) keeps the oracle's clusters on certified rows
     and equals the separate scores + selection bit for bit (same arithmetic)."""

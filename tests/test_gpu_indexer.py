@@ -29,10 +29,12 @@ def gpu_indexer(sa, qi, ki, w, pos0):
     return host(out)
 
 
-def test_indexer_exact_integer_inputs(sa):
+@pytest.mark.parametrize("Hi", [64, 24])
+def test_indexer_exact_integer_inputs(sa, Hi):
     """Integers in [-4,4] and weights m/64: every product, ReLU and weighted
-    sum is exact in fp32, so the GPU equals the fp64 oracle bit for bit."""
-    T, Hi, di, N = 64, 64, 64, 16384 + 512
+    sum is exact in fp32, so the GPU equals the fp64 oracle bit for bit (64
+    heads on the matrix-core rows, 24 heads split over eight waves)."""
+    T, di, N = 64, 64, 16384 + 512
     qi = W.integer_bf16(41, (T, Hi, di), -4, 4, 0)
     ki = W.integer_bf16(41, (N, di), -4, 4, 1)
     w = (np.random.default_rng(41).integers(0, 65, size=Hi) / 64.0).astype(np.float32)
@@ -42,7 +44,8 @@ def test_indexer_exact_integer_inputs(sa):
     assert np.array_equal(got, want)
 
 
-@pytest.mark.parametrize("T,Hi,N", [(80, 64, 20000), (64, 32, 9000), (32, 16, 8192), (7, 8, 4096)])
+@pytest.mark.parametrize("T,Hi,N", [(80, 64, 20000), (64, 32, 9000), (32, 16, 8192), (7, 8, 4096), (33, 24, 5000),
+                                    (20, 40, 4100), (9, 48, 3000), (40, 56, 8200)])
 def test_indexer_random(sa, T, Hi, N):
     ind = W.indexer_random(42, T, Hi, 64, N)
     got = gpu_indexer(sa, ind.qi, ind.ki, ind.w, ind.pos0)

@@ -71,7 +71,7 @@ def check_head(X, init, iters, cent, labels, exact_frac=0.99):
     return mu, lab
 
 
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
 def test_kmeans_separated_mixture(sa, dtype, d):
     """Keys drawn around C means; the table starts near the means: every key is
     far from any other centroid, so all labels and centroids must match."""

@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads as W
-from gpu_helpers import (assert_attention_close, assert_scores_close, dev_bf16, dev_i32, fwd_on_oracle_vs, host,
+from gpu_helpers import (dev_f32, assert_attention_close, assert_scores_close, dev_bf16, dev_i32, fwd_on_oracle_vs, host,
                          tie_tolerant_valid, torch)
 
 pytestmark = pytest.mark.gpu
@@ -99,7 +99,7 @@ def test_vs_build_tables_exact(sa, ns):
             assert np.array_equal(colh[rr, i, :colch[rr, i]], vert_i)
 
 
-def run_vs_fwd(sa, inp, sel, N):
+def run_vs_fwd(sa, inp, sel, N, out_bf16=False):
     """forward in tile-list mode on tables built by the library from sel."""
     t = torch()
     B, Hq = inp.q.shape[:2]
@@ -119,10 +119,10 @@ def run_vs_fwd(sa, inp, sel, N):
     colc = t.empty((B, Hq, nb), dtype=t.int32, device="cuda:0")
     sa.sa_vs_build(dev_i32(vert), dev_i32(cv), dev_i32(slash), dev_i32(cs), iv.view(Hq, -1), ivc.view(Hq, -1),
                    col.view(Hq, -1), colc.view(Hq, -1), seq=N)
-    out = t.empty(inp.q.shape, dtype=t.float32, device="cuda:0")
+    out = t.empty(inp.q.shape, dtype=t.bfloat16 if out_bf16 else t.float32, device="cuda:0")
     lse = t.empty((B, Hq, N), dtype=t.float32, device="cuda:0")
-    sa.sa_block_sparse_fwd(dev_bf16(inp.q), dev_bf16(inp.k), dev_bf16(inp.v), out, iv=iv, iv_cnt=ivc, col=col,
-                           col_cnt=colc, lse=lse)
+    up = dev_bf16 if inp.dtype == "bf16" else dev_f32
+    sa.sa_block_sparse_fwd(up(inp.q), up(inp.k), up(inp.v), out, iv=iv, iv_cnt=ivc, col=col, col_cnt=colc, lse=lse)
     t.cuda.synchronize()
     return host(out), host(lse)
 
@@ -142,6 +142,24 @@ def test_vs_forward_on_oracle_selection(sa):
     assert np.array_equal(np.isneginf(l), np.isneginf(wl))
     fin = np.isfinite(wl)
     assert np.max(np.abs(l[fin] - wl[fin])) < 1e-3
+
+
+@pytest.mark.parametrize("d,dtype,out_bf16", [(128, "bf16", True), (64, "bf16", False), (64, "bf16", True),
+                                             (64, "f32", False), (128, "f32", False)])
+def test_vs_forward_head_dims_and_dtypes(sa, d, dtype, out_bf16):
+    """The tile-list forward for each head size, input type and output type
+    on random vertical and slash selections, against the oracle."""
+    N, H = 1024, 2
+    inp = W.prefill_bf16(54, 1, H, H, N, d) if dtype == "bf16" else W.prefill_fp32(54, 1, H, N, d)
+    r = np.random.default_rng(54)
+    sel = [[(np.sort(r.choice(N, size=90, replace=False)), np.sort(r.choice(N, size=9, replace=False)))
+            for _ in range(H)]]
+    o, l = run_vs_fwd(sa, inp, sel, N, out_bf16=out_bf16)
+    wo, wl = oracle.vs_attention(inp.f32("q"), inp.f32("k"), inp.f32("v"), sel, 64, 1 / math.sqrt(d))
+    assert_attention_close(o, wo, bf16=dtype == "bf16", what=f"vs forward d{d} {dtype} out_bf16={out_bf16}")
+    assert np.array_equal(np.isneginf(l), np.isneginf(wl))
+    fin = np.isfinite(wl)
+    assert np.max(np.abs(l[fin] - wl[fin])) < (1e-3 if dtype == "bf16" else 1e-5)
 
 
 def test_vs_end_to_end_planted_certified(sa):
