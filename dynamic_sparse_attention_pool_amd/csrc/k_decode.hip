@@ -244,6 +244,32 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
   const int nq = p.T * grp;
   const int64_t N = p.n_ctx;
   const int C = p.C;
+  const uint16_t* kb = p.k + (int64_t)g * N * kD;
+  const uint16_t* vb = p.v + (int64_t)g * N * kD;
+  const int64_t p0 = (int64_t)split * kRowsPerSplit;
+  const int64_t p1 = min(N, p0 + kRowsPerSplit);
+  const int ntile = (int)((p1 - p0 + kDecRows - 1) / kDecRows);
+  DecWaveLds& W = L[w];
+  // K operand of tile t: lane row l32, dims 16s + 8hf .. +7 of step s (ordinary
+  // loads: the compiler's wait for them also covers the older V copies)
+  bf16x8 kr[8];
+  int prow = 0;  // CAUSAL: context position of this lane's row of the fetched tile
+  auto fetch = [&](int t, int buf) {
+    const int64_t base = p0 + (int64_t)t * kDecRows;
+    const int len = (int)min((int64_t)kDecRows, p1 - base);
+    dec_dma_v(W.v[buf], vb, base, len, lane);
+    const uint16_t* krow = kb + (base + min(l32, len - 1)) * kD + 8 * hf;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) kr[s] = as_bf16x8(ldg16(krow + 16 * s));
+    if (CAUSAL) prow = p.perm[(int64_t)g * N + base + min(l32, len - 1)];
+  };
+  // This wave's first tile is fetched before the set-up below: at decode sizes
+  // nearly every tile is selected, so its copy travels with the set-up loads.
+  // If the wave's first selected tile is another one, that fetch refills the
+  // same buffer and registers (a wave's loads complete in order, so the later
+  // copy lands last).
+  const bool spec = w < ntile;
+  if (spec) fetch(w, 0);
   // Set-up: the cluster pointers, the selected cluster ids and Q are all
   // requested before the first of them is used, so the workgroup waits for one
   // memory latency instead of one per loop trip.
@@ -312,11 +338,6 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
     sel_load(e0, cv);
     sel_mark(e0, cv);
   }
-  const uint16_t* kb = p.k + (int64_t)g * N * kD;
-  const uint16_t* vb = p.v + (int64_t)g * N * kD;
-  const int64_t p0 = (int64_t)split * kRowsPerSplit;
-  const int64_t p1 = min(N, p0 + kRowsPerSplit);
-  const int ntile = (int)((p1 - p0 + kDecRows - 1) / kDecRows);
   const float sl2 = p.scale * kLog2e;
   __syncthreads();
 
@@ -331,7 +352,6 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[nt][dt][r] = 0.f;
   }
-  DecWaveLds& W = L[w];
 
   // cluster of this lane's row: last c with ptr[c] <= row.  Rows only grow
   // along a wave's tiles, so after one binary search the cluster index
@@ -362,22 +382,8 @@ __global__ __launch_bounds__(64 * kDecWaves, NQT == 1 ? 2 : 1) void k_decode_spl
     }
     return ntile;
   };
-  // K operand of tile t: lane row l32, dims 16s + 8hf .. +7 of step s (ordinary
-  // loads: the compiler's wait for them also covers the older V copies)
-  bf16x8 kr[8];
-  int prow = 0;  // CAUSAL: context position of this lane's row of the fetched tile
-  auto fetch = [&](int t, int buf) {
-    const int64_t base = p0 + (int64_t)t * kDecRows;
-    const int len = (int)min((int64_t)kDecRows, p1 - base);
-    dec_dma_v(W.v[buf], vb, base, len, lane);
-    const uint16_t* krow = kb + (base + min(l32, len - 1)) * kD + 8 * hf;
-#pragma unroll
-    for (int s = 0; s < 8; ++s) kr[s] = as_bf16x8(ldg16(krow + 16 * s));
-    if (CAUSAL) prow = p.perm[(int64_t)g * N + base + min(l32, len - 1)];
-  };
-
   int cur = find(w, 0), buf = 0;
-  if (cur < ntile) fetch(cur, 0);
+  if (cur < ntile && !(spec && cur == w)) fetch(cur, 0);
   while (cur < ntile) {
     const int pos_cur = prow;
     f32x16 sc[NQT];
