@@ -564,10 +564,16 @@ __global__ __launch_bounds__(64 * kGatherWaves) void k_token_gather(GatherParams
   float m = -INFINITY, l = 0.f;
   const int ntile = (p.n_tok + kBlk - 1) / kBlk;
   const int64_t qlim = p.q_pos != nullptr ? (int64_t)p.q_pos[t] : INT64_MAX;
+  // the next tile's ids are requested one tile ahead, so a tile waits for one
+  // memory latency (its K and V rows) instead of two
+  int id_next = ntile > 0 && lane < min(kBlk, p.n_tok) ? ids[lane] : -1;
   for (int tt = 0; tt < ntile; ++tt) {
     const int base = tt * kBlk;
-    const int len = min(kBlk, p.n_tok - base);
-    int myid = lane < len ? ids[base + lane] : -1;
+    int myid = id_next;
+    if (tt + 1 < ntile) {
+      const int nbase = base + kBlk;
+      id_next = lane < min(kBlk, p.n_tok - nbase) ? ids[nbase + lane] : -1;
+    }
     if (myid >= N || myid > qlim) myid = -1;  // out-of-range and future ids are treated as padding
     KEYS[w][lane] = myid;
     wave_sync();
