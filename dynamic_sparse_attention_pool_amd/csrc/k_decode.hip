@@ -711,8 +711,10 @@ __global__ __launch_bounds__(64 * kListWaves) void k_token_gather_list(GatherPar
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = 0.f;
   float m = -INFINITY, l = 0.f;
+  int id_next = lane < p.n_tok ? ids[lane] : -1;  // the next tile's ids, read one tile ahead
   for (int base = 0; base < p.n_tok; base += kBlk) {
-    int id = base + lane < p.n_tok ? ids[base + lane] : -1;
+    int id = id_next;
+    if (base + kBlk < p.n_tok) id_next = base + kBlk + lane < p.n_tok ? ids[base + kBlk + lane] : -1;
     if (id >= N || id > qlim) id = -1;  // out-of-range and future ids are padding
     float s = -INFINITY;
     if (id >= 0) {
