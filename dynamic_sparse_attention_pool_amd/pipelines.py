@@ -127,14 +127,22 @@ class VerticalSlashLayer:
         self.col_cnt = torch.empty((B, nh, self.nb), dtype=torch.int32, device=dev)
         self.out, self.lse = _out_buffers(q, out_dtype, with_lse, out, lse)
         self.ws = None
+        self.side = torch.cuda.Stream(device=dev)  # default priority
 
     def estimate(self):
         self.ws = sa_estimate(VSLASH, self.q, self.k, self.a_v, scores2=self.a_s, scale=self.scale,
                               heads=self.heads, workspace=self.ws)
 
     def select(self):
+        # the two selections run side by side: each has one workgroup per row,
+        # too few to fill the GPU alone
+        torch = _t()
+        cur = torch.cuda.current_stream(self.a_v.device)
+        self.side.wait_stream(cur)
+        with torch.cuda.stream(self.side):
+            sa_select_topk(self.a_s.view(self.R, self.N), self.slash, self.slash_cnt, k=self.n_slash)
         sa_select_topk(self.a_v.view(self.R, self.N), self.vert, self.vert_cnt, k=self.n_vert)
-        sa_select_topk(self.a_s.view(self.R, self.N), self.slash, self.slash_cnt, k=self.n_slash)
+        cur.wait_stream(self.side)
         sa_vs_build(self.vert, self.vert_cnt, self.slash, self.slash_cnt, self.iv.view(self.R, -1),
                     self.iv_cnt.view(self.R, -1), self.col.view(self.R, -1), self.col_cnt.view(self.R, -1),
                     seq=self.N)
