@@ -231,7 +231,7 @@ __global__ __launch_bounds__(NT) void k_select_long(SelectParams p) {
   __shared__ int32_t bi[kBand];
   __shared__ uint32_t selbm[kWords];
   __shared__ uint32_t tiebm[kWords];
-  __shared__ uint32_t hist[256];
+  __shared__ uint32_t hist[512];
   __shared__ uint32_t tmp[NT];
   __shared__ uint32_t shv[4];
 
@@ -279,12 +279,12 @@ __global__ __launch_bounds__(NT) void k_select_long(SelectParams p) {
     const int64_t rk_hi = max((int64_t)1, (int64_t)frac - margin);
     const int64_t rk_lo = min((int64_t)ns, (int64_t)ceil(frac) + margin);
     uint32_t hi, lo;
-    int64_t dummy;
-    radix_kth<NT>([&](int64_t i) { return keys[i]; }, 0, ns, rk_hi, hist, tmp, shv, hi, dummy);
-    radix_kth<NT>([&](int64_t i) { return keys[i]; }, 0, ns, rk_lo, hist, tmp, shv, lo, dummy);
+    radix_kth2<NT>([&](int64_t i) { return keys[i]; }, 0, ns, rk_hi, rk_lo, hist, tmp, shv, hi, lo);
     if (tid == 0) {
       shv[0] = 0u;  // keys > hi
       shv[1] = 0u;  // keys in [lo, hi]
+      shv[2] = 0u;  // the NaN flag below (the bracket search used it)
+      shv[3] = 0u;
     }
     __syncthreads();
     // ---- the one pass over the pool.  Per key: its order key, a running

@@ -87,6 +87,59 @@ __device__ void radix_kth(KeyAt key_at, int64_t b, int64_t e, int64_t k, uint32_
   need = remaining;
 }
 
+// The k1-th and k2-th largest keys of [b, e) at once: the same digit search as
+// radix_kth for each rank, with both ranks' histograms built in one sweep per
+// pass (hist holds 512 bins, tmp 8 entries), so the two searches share their
+// barriers.  Needs NT >= 512.
+template <int NT, typename KeyAt>
+__device__ void radix_kth2(KeyAt key_at, int64_t b, int64_t e, int64_t k1, int64_t k2, uint32_t* hist, uint32_t* tmp,
+                           uint32_t* shv, uint32_t& T1, uint32_t& T2) {
+  static_assert(NT >= 512, "two 256-digit scans run side by side");
+  const int tid = threadIdx.x;
+  uint32_t pmask = 0u, prefix1 = 0u, prefix2 = 0u;
+  int64_t rem1 = k1, rem2 = k2;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int d = tid; d < 512; d += NT) hist[d] = 0u;
+    __syncthreads();
+    for (int64_t i = b + tid; i < e; i += NT) {
+      const uint32_t kk = key_at(i);
+      const uint32_t dg = (kk >> shift) & 255u;
+      if ((kk & pmask) == prefix1) atomicAdd(&hist[dg], 1u);
+      if ((kk & pmask) == prefix2) atomicAdd(&hist[256 + dg], 1u);
+    }
+    __syncthreads();
+    // threads 0..255 scan rank 1's digits, 256..511 rank 2's (keys with digit >= 255 - t)
+    const int r = tid >> 8, t = tid & 255;
+    uint32_t v = 0u, incl = 0u;
+    if (tid < 512) {
+      v = hist[256 * r + 255 - t];
+      incl = wave_incl_scan(v);
+      if ((tid & 63) == 63) tmp[tid >> 6] = incl;
+    }
+    __syncthreads();
+    if (tid < 512) {
+      uint32_t before = 0u;
+      for (int j = 4 * r; j < (tid >> 6); ++j) before += tmp[j];
+      const uint32_t ge = before + incl;
+      const uint32_t gt = ge - v;
+      const int64_t rem = r == 0 ? rem1 : rem2;
+      if (gt < (uint32_t)rem && (uint32_t)rem <= ge) {
+        shv[2 * r] = 255u - t;
+        shv[2 * r + 1] = gt;
+      }
+    }
+    __syncthreads();
+    rem1 -= shv[1];
+    rem2 -= shv[3];
+    prefix1 |= shv[0] << shift;
+    prefix2 |= shv[2] << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  T1 = prefix1;
+  T2 = prefix2;
+}
+
 __device__ __forceinline__ float key_float(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k ^ 0x80000000u) : ~k);
 }
