@@ -508,22 +508,38 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ fp32 inputs
-// One workgroup of 64 threads per (batch, head, query block); each thread owns
-// one query row and folds the tile's keys one by one (fp32 throughout).
+// One workgroup of 256 threads per (batch, head, query block): four threads per
+// query row, each owning a quarter of the head dimensions (fp32 throughout).
+// Per 64-key tile a thread forms its partial dot products with the tile's keys,
+// the row's four partials are summed by two quad exchanges in a fixed order
+// (so the four threads hold identical scores), and the online softmax and the
+// P.V products run on the thread's quarter of the output.
+constexpr int kF32Threads = 256;
+
+// v + the value of lane l ^ X within each quad (X = 1 or 2), by DPP quad permute.
+template <int X>
+__device__ __forceinline__ float quad_xor_add(float v) {
+  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  const int o = __builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false);
+  return v + __int_as_float(o);
+}
+
 template <int D, int MODE>
-__global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
-  __shared__ float Ks[kBlk][D];
-  __shared__ float Vs[kBlk][D];
+__global__ __launch_bounds__(kF32Threads) void k_fwd_f32(FwdParams p) {
+  constexpr int DQ = D / 4;  // dimensions per thread
+  constexpr int C4 = D / 4;  // 16-byte chunks per row
+  __shared__ __attribute__((aligned(16))) float Ks[kBlk][D];
+  __shared__ __attribute__((aligned(16))) float Vs[kBlk][D];
   __shared__ int32_t keyS[kBlk];
   __shared__ int32_t ash[MODE == 0 ? 2048 : 1];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, rw = tid >> 2, part = tid & 3;
   const Item item = item_at(p, blockIdx.x, gridDim.x, 0);
   const int b = item.b, h = item.h, iblk = item.iblk;
   const int g = h / (p.heads_q / p.heads_kv);
   const int64_t N = p.seq;
   const int64_t row_id = item.trow;
-  const int qpos = iblk * kBlk + tid;
-  const float* qr = reinterpret_cast<const float*>(p.q) + (((int64_t)b * p.heads_q + h) * N + qpos) * D;
+  const int qpos = iblk * kBlk + rw;
+  const float* qr = reinterpret_cast<const float*>(p.q) + (((int64_t)b * p.heads_q + h) * N + qpos) * D + part * DQ;
   const float* kb = reinterpret_cast<const float*>(p.k) + ((int64_t)b * p.heads_kv + g) * N * D;
   const float* vb = reinterpret_cast<const float*>(p.v) + ((int64_t)b * p.heads_kv + g) * N * D;
 
@@ -531,7 +547,7 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
   const int32_t* cols = nullptr;
   if (MODE == 0) {
     if (p.ashape) {
-      it.cnt = ashape_list(ash, iblk, p.n_sink, p.n_local, tid, 64);
+      it.cnt = ashape_list(ash, iblk, p.n_sink, p.n_local, tid, kF32Threads);
       it.bidx = ash;
       __syncthreads();
     } else {
@@ -551,32 +567,47 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
     it.bad_cols = 1;  // every gathered key is checked below anyway
     cols = p.col + row_id * p.max_col;
   }
-  float q[D], o[D];
-  for (int d = 0; d < D; ++d) {
-    q[d] = qr[d];
-    o[d] = 0.f;
+  float q[DQ], o[DQ];
+#pragma unroll
+  for (int d = 0; d < DQ; d += 4) {
+    const f32x4 v4 = *reinterpret_cast<const f32x4*>(qr + d);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      q[d + e] = v4[e];
+      o[d + e] = 0.f;
+    }
   }
   float m = -INFINITY, l = 0.f;
   TileRef r;
   while (it.next(r)) {
-    __syncthreads();
-    const int row = tile_row(r, cols, tid, N);
-    for (int d = 0; d < D; d += 4) {
-      *reinterpret_cast<f32x4*>(&Ks[tid][d]) = *reinterpret_cast<const f32x4*>(kb + (int64_t)row * D + d);
-      *reinterpret_cast<f32x4*>(&Vs[tid][d]) = *reinterpret_cast<const f32x4*>(vb + (int64_t)row * D + d);
+    __syncthreads();  // the previous tile's K and V are no longer read
+    for (int e = tid; e < kBlk * C4; e += kF32Threads) {
+      const int slot = e / C4, c = e % C4;
+      const int64_t row = tile_row(r, cols, slot, N);
+      *reinterpret_cast<f32x4*>(&Ks[slot][4 * c]) = *reinterpret_cast<const f32x4*>(kb + row * D + 4 * c);
+      *reinterpret_cast<f32x4*>(&Vs[slot][4 * c]) = *reinterpret_cast<const f32x4*>(vb + row * D + 4 * c);
     }
-    int key = INT_MAX;
-    if (tid < r.len) {
-      key = r.gathered ? cols[r.base + tid] : r.base + tid;
-      if (!col_ok(key, N)) key = INT_MAX;
+    if (tid < kBlk) {
+      int key = INT_MAX;
+      if (tid < r.len) {
+        key = r.gathered ? cols[r.base + tid] : r.base + tid;
+        if (!col_ok(key, N)) key = INT_MAX;
+      }
+      keyS[tid] = key;
     }
-    keyS[tid] = key;
     __syncthreads();
     float s[kBlk];
     float mx = -INFINITY;
+#pragma unroll
     for (int c = 0; c < kBlk; ++c) {
       float acc = 0.f;
-      for (int d = 0; d < D; ++d) acc = fmaf(q[d], Ks[c][d], acc);
+#pragma unroll
+      for (int d = 0; d < DQ; d += 4) {
+        const f32x4 k4 = *reinterpret_cast<const f32x4*>(&Ks[c][part * DQ + d]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc = fmaf(q[d + e], k4[e], acc);
+      }
+      acc = quad_xor_add<2>(quad_xor_add<1>(acc));  // (p0 + p1) + (p2 + p3) on all four lanes
       s[c] = keyS[c] > qpos ? -INFINITY : acc * p.scale;
       mx = fmaxf(mx, s[c]);
     }
@@ -584,19 +615,27 @@ __global__ __launch_bounds__(64) void k_fwd_f32(FwdParams p) {
     if (mnew == -INFINITY) continue;
     const float alpha = expf(m - mnew);
     l *= alpha;
-    for (int d = 0; d < D; ++d) o[d] *= alpha;
+#pragma unroll
+    for (int d = 0; d < DQ; ++d) o[d] *= alpha;
+#pragma unroll
     for (int c = 0; c < kBlk; ++c) {
       const float pc = expf(s[c] - mnew);
       l += pc;
-      for (int d = 0; d < D; ++d) o[d] = fmaf(pc, Vs[c][d], o[d]);
+#pragma unroll
+      for (int d = 0; d < DQ; d += 4) {
+        const f32x4 v4 = *reinterpret_cast<const f32x4*>(&Vs[c][part * DQ + d]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[d + e] = fmaf(pc, v4[e], o[d + e]);
+      }
     }
     m = mnew;
   }
   const float inv = l > 0.f ? 1.f / l : 0.f;
   const int64_t orow = ((int64_t)b * p.heads_q + h) * N + qpos;
-  if (p.lse != nullptr) p.lse[orow] = l > 0.f ? m + logf(l) : -INFINITY;
-  float* op = reinterpret_cast<float*>(p.out) + orow * D;
-  for (int d = 0; d < D; d += 4) {
+  if (p.lse != nullptr && part == 0) p.lse[orow] = l > 0.f ? m + logf(l) : -INFINITY;
+  float* op = reinterpret_cast<float*>(p.out) + orow * D + part * DQ;
+#pragma unroll
+  for (int d = 0; d < DQ; d += 4) {
     f32x4 v4 = {o[d] * inv, o[d + 1] * inv, o[d + 2] * inv, o[d + 3] * inv};
     *reinterpret_cast<f32x4*>(op + d) = v4;
   }
@@ -634,7 +673,7 @@ hipError_t launch_fwd(const FwdParams& p, int head_dim, int mode, bool in_bf16, 
   if (out_bf16) return hipErrorInvalidValue;
 #define SA_FWD32_CASE(D_, M_)                                                   \
   if (head_dim == D_ && mode == M_) {                                           \
-    hipLaunchKernelGGL((k_fwd_f32<D_, M_>), grid, dim3(64), 0, stream, p);      \
+    hipLaunchKernelGGL((k_fwd_f32<D_, M_>), grid, dim3(kF32Threads), 0, stream, p); \
     return hipGetLastError();                                                   \
   }
   SA_FWD32_CASE(64, 0)
