@@ -289,7 +289,7 @@ def config1(reps):
             "kept_blocks": kept, "flop": kept * 4 * 64 * 64 * 64,
             "us_layer_median": lay["median"] * 1e3, "us_layer_min": lay["min"] * 1e3,
             "us_forward_median": R.stat("forward")["median"] * 1e3, "reps": lay["n"],
-            "bound": "launch latency (parity configuration; no roofline claim)", "inputs": inp}
+            "bound": "16 workgroups, one per query block: the serial work per tile (parity configuration; no roofline claim)", "inputs": inp}
 
 
 def config2(reps, peaks):
