@@ -202,34 +202,43 @@ __global__ __launch_bounds__(64 * kKmWaves) void k_km_assign_mfma(const uint16_t
   }
 }
 
-// One workgroup per (KV head, cluster), one thread per dimension.
+// One workgroup per (KV head, cluster), one thread per dimension.  The
+// cluster's row ids are staged in LDS (2048 at a time), then each thread sums
+// its dimension over the rows in token order with 32 rows' loads in flight, so
+// the largest cluster costs one memory latency per 32 rows.
+constexpr int kKmStage = 2048;
+constexpr int kKmInFlight = 32;
+
 template <typename T, int D>
-__global__ __launch_bounds__(D) void k_km_update(const T* __restrict__ keys, const int32_t* __restrict__ ptr,
+__global__ __launch_bounds__(D) __attribute__((amdgpu_waves_per_eu(1, 4))) void k_km_update(const T* __restrict__ keys, const int32_t* __restrict__ ptr,
                                                  const int32_t* __restrict__ perm, int64_t n, int C,
                                                  float* __restrict__ cent) {
+  __shared__ int32_t rs[kKmStage];
   const int g = blockIdx.x / C, c = blockIdx.x % C, d = threadIdx.x;
   const int32_t b = ptr[(int64_t)g * (C + 1) + c], e = ptr[(int64_t)g * (C + 1) + c + 1];
-  if (e <= b) return;  // empty cluster: the centroid stays
-  const T* kg = keys + (int64_t)g * n * D;
+  if (e <= b) return;  // empty cluster: the centroid stays (the whole workgroup leaves)
+  const T* kg = keys + (int64_t)g * n * D + d;
   const int32_t* pg = perm + (int64_t)g * n;
-  auto val = [&](int64_t row) -> float {
-    if constexpr (sizeof(T) == 2) return bf2f(kg[row * D + d]);
-    else return kg[row * D + d];
+  auto val = [&](int32_t row) -> float {
+    if constexpr (sizeof(T) == 2) return bf2f(kg[(int64_t)row * D]);
+    else return kg[(int64_t)row * D];
   };
-  // 8 rows' loads in flight at a time; the sum still runs in token order
   float s = 0.f;
-  int32_t r = b;
-  for (; r + 8 <= e; r += 8) {
-    int64_t rows[8];
+  for (int32_t cb = b; cb < e; cb += kKmStage) {
+    const int nn = min(kKmStage, e - cb);
+    __syncthreads();  // the previous chunk's ids are consumed
+    for (int i = d; i < nn; i += D) rs[i] = pg[cb + i];
+    __syncthreads();
+    int r = 0;
+    for (; r + kKmInFlight <= nn; r += kKmInFlight) {
+      float v[kKmInFlight];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) rows[x] = pg[r + x];
-    float v[8];
+      for (int x = 0; x < kKmInFlight; ++x) v[x] = val(rs[r + x]);
 #pragma unroll
-    for (int x = 0; x < 8; ++x) v[x] = val(rows[x]);
-#pragma unroll
-    for (int x = 0; x < 8; ++x) s += v[x];
+      for (int x = 0; x < kKmInFlight; ++x) s += v[x];
+    }
+    for (; r < nn; ++r) s += val(rs[r]);
   }
-  for (; r < e; ++r) s += val(pg[r]);
   cent[((int64_t)g * C + c) * D + d] = s / (float)(e - b);
 }
 
