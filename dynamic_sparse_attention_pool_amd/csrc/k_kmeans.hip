@@ -144,7 +144,15 @@ __global__ __launch_bounds__(64 * kKmWaves) void k_km_assign_mfma(const uint16_t
                                                                  const float* __restrict__ nrm, int64_t n, int C,
                                                                  int32_t* __restrict__ labels) {
   constexpr int NS = D / 16;
-  const int lane = threadIdx.x & 63, hf = lane >> 5, l32 = lane & 31, wv = threadIdx.x >> 6;
+  constexpr int RS = 3 * D + 8;            // LDS row of one centroid's three parts, padded by 16 bytes
+  constexpr int CPR = 3 * D / 8;           // 16-byte chunks per centroid row
+  constexpr int CPT = 32 * CPR;            // per tile of 32 centroids
+  constexpr int NT = 64 * kKmWaves;
+  constexpr int PER = (CPT + NT - 1) / NT;
+  __shared__ __attribute__((aligned(16))) uint16_t cs[2][32 * RS];
+  __shared__ float cn[2][32];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, hf = lane >> 5, l32 = lane & 31, wv = tid >> 6;
   constexpr int kPerWg = kKmWaves * kKmKeysPerWave;
   const int64_t nblk = (n + kPerWg - 1) / kPerWg;
   const int g = (int)(blockIdx.x / nblk);
@@ -159,38 +167,67 @@ __global__ __launch_bounds__(64 * kKmWaves) void k_km_assign_mfma(const uint16_t
   }
   const uint16_t* pg = parts + (int64_t)g * C * 3 * D;
   const float* ng = nrm + (int64_t)g * C;
+  // one tile of 32 centroids (three bf16 parts each, and the squared norms)
+  // goes global -> registers -> LDS, shared by the workgroup's four waves
+  u32x4 rg[PER];
+  float rn = 0.f;
+  auto fetch = [&](int ct) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * NT;
+      if (q < CPT) {
+        const int crow = std::min(32 * ct + q / CPR, C - 1);
+        rg[u] = ldg16(pg + (int64_t)crow * 3 * D + 8 * (q % CPR));
+      }
+    }
+    if (tid < 32) rn = ng[std::min(32 * ct + tid, C - 1)];
+  };
+  auto put = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int q = tid + u * NT;
+      if (q < CPT) *reinterpret_cast<u32x4*>(&cs[buf][(q / CPR) * RS + 8 * (q % CPR)]) = rg[u];
+    }
+    if (tid < 32) cn[buf][tid] = rn;
+  };
   float best[2] = {INFINITY, INFINITY};
   int arg[2] = {0, 0};
   const int nct = (C + 31) / 32;
+  fetch(0);
+  put(0);
+  __syncthreads();
   for (int ct = 0; ct < nct; ++ct) {
-    const int crow = std::min(32 * ct + l32, C - 1);
-    const uint16_t* pr = pg + (int64_t)crow * 3 * D + 8 * hf;
+    const int buf = ct & 1;
+    const bool nx = ct + 1 < nct;
+    if (nx) fetch(ct + 1);  // in flight during this tile's products
+    const uint16_t* cr = &cs[buf][l32 * RS + 8 * hf];
     f32x16 acc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int part = 0; part < 3; ++part) {
       bf16x8 a[NS];
 #pragma unroll
-      for (int s4 = 0; s4 < NS; ++s4) a[s4] = as_bf16x8(ldg16(pr + part * D + 16 * s4));
+      for (int s4 = 0; s4 < NS; ++s4) a[s4] = as_bf16x8(*reinterpret_cast<const u32x4*>(cr + part * D + 16 * s4));
 #pragma unroll
       for (int s4 = 0; s4 < NS; ++s4)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt) acc[kt] = mfma32x32x16(a[s4], xb[kt][s4], acc[kt]);
     }
-    float nr[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) nr[r] = ng[std::min(32 * ct + 8 * (r / 4) + 4 * hf + (r % 4), C - 1)];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int c = 32 * ct + 8 * (r / 4) + 4 * hf + (r % 4);
+      const int cl = 8 * (r / 4) + 4 * hf + (r % 4);
+      const int c = 32 * ct + cl;
+      const float nr = cn[buf][cl];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const float dist = fmaf(-2.f, acc[kt][r], nr[r]);
+        const float dist = fmaf(-2.f, acc[kt][r], nr);
         if (c < C && dist < best[kt]) {
           best[kt] = dist;
           arg[kt] = c;
         }
       }
     }
+    if (nx) put(buf ^ 1);
+    __syncthreads();  // the next tile is in LDS; this one is no longer read
   }
 #pragma unroll
   for (int kt = 0; kt < 2; ++kt) {
