@@ -47,7 +47,7 @@ constexpr int kD = 128;
 constexpr int kVS = kBlk + 8;  // V^T row stride (elements)
 
 // ================================================================ cluster pack
-constexpr int kSeg = 2048;
+constexpr int kSeg = 512;  // tokens per pack segment
 
 __global__ __launch_bounds__(256) void k_pack_count(const int32_t* __restrict__ labels, int64_t n, int C, int nseg,
                                                     int32_t* __restrict__ segcnt, int32_t* err) {
@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_scan(int C, int nseg, int
 // Each thread owns clusters; walking the segment in token order keeps the sort stable.
 __global__ __launch_bounds__(256) void k_pack_scatter(const int32_t* __restrict__ labels, int64_t n, int C, int nseg,
                                                       const int32_t* __restrict__ seg, int32_t* __restrict__ perm) {
-  __shared__ int32_t lab[kSeg];
+  __shared__ __attribute__((aligned(16))) int32_t lab[kSeg];
   const int g = blockIdx.x / nseg, s = blockIdx.x % nseg;
   const int64_t t0 = (int64_t)s * kSeg, t1 = min(n, t0 + kSeg);
   const int len = (int)(t1 - t0);
@@ -123,8 +123,17 @@ __global__ __launch_bounds__(256) void k_pack_scatter(const int32_t* __restrict_
   __syncthreads();
   for (int c = threadIdx.x; c < C; c += blockDim.x) {
     int32_t pos = seg[((int64_t)g * nseg + s) * C + c];
-    for (int t = 0; t < len; ++t)
-      if (lab[t] == c) perm[(int64_t)g * n + pos++] = (int32_t)(t0 + t);
+    int32_t* pg = perm + (int64_t)g * n;
+    int t = 0;
+    for (; t + 4 <= len; t += 4) {  // four labels per LDS read
+      const int4 l4 = *reinterpret_cast<const int4*>(&lab[t]);
+      if (l4.x == c) pg[pos++] = (int32_t)(t0 + t);
+      if (l4.y == c) pg[pos++] = (int32_t)(t0 + t + 1);
+      if (l4.z == c) pg[pos++] = (int32_t)(t0 + t + 2);
+      if (l4.w == c) pg[pos++] = (int32_t)(t0 + t + 3);
+    }
+    for (; t < len; ++t)
+      if (lab[t] == c) pg[pos++] = (int32_t)(t0 + t);
   }
 }
 
