@@ -112,6 +112,57 @@ __global__ __launch_bounds__(kScanThreads) void k_pack_scan(int C, int nseg, int
   if (tid == 0) ptr[(int64_t)g * (C + 1) + C] = all;
 }
 
+// With C <= kScanThreads clusters: thread t takes cluster t % C and the t / C-th
+// of Q = kScanThreads / C consecutive ranges of its segments, so for each
+// segment the wave reads consecutive clusters (coalesced); the runs are then
+// scanned in (cluster, range) order through LDS.
+__global__ __launch_bounds__(kScanThreads) void k_pack_scan_cm(int C, int nseg, int32_t* __restrict__ seg,
+                                                               int32_t* __restrict__ ptr) {
+  __shared__ int32_t buf[kScanThreads];
+  __shared__ int32_t wsum[kScanThreads / 64];
+  const int g = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int Q = kScanThreads / C;
+  const int c = tid % C, q = tid / C;
+  const bool act = q < Q;
+  const int per = (nseg + Q - 1) / Q;
+  const int s0 = act ? min(nseg, q * per) : 0, s1 = act ? min(nseg, s0 + per) : 0;
+  int32_t* sg = seg + (int64_t)g * nseg * C;
+  int32_t run = 0;
+  for (int s = s0; s < s1; ++s) run += sg[(int64_t)s * C + c];
+  const int o = act ? c * Q + q : tid;  // position in (cluster, range) order
+  buf[o] = run;
+  __syncthreads();
+  const int32_t v = buf[tid];
+  int32_t incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int32_t u = __shfl_up(incl, off);
+    if (lane >= off) incl += u;
+  }
+  if (lane == 63) wsum[wv] = incl;
+  __syncthreads();
+  int32_t ex = incl - v, all = 0;
+#pragma unroll
+  for (int x = 0; x < kScanThreads / 64; ++x) {
+    const int32_t w = wsum[x];
+    ex += x < wv ? w : 0;
+    all += w;
+  }
+  buf[tid] = ex;
+  __syncthreads();
+  if (act) {
+    int32_t base = buf[o];
+    if (q == 0) ptr[(int64_t)g * (C + 1) + c] = base;
+    for (int s = s0; s < s1; ++s) {
+      int32_t& cell = sg[(int64_t)s * C + c];
+      const int32_t x = cell;
+      cell = base;
+      base += x;
+    }
+  }
+  if (tid == 0) ptr[(int64_t)g * (C + 1) + C] = all;
+}
+
 // Each thread owns clusters; walking the segment in token order keeps the sort stable.
 __global__ __launch_bounds__(256) void k_pack_scatter(const int32_t* __restrict__ labels, int64_t n, int C, int nseg,
                                                       const int32_t* __restrict__ seg, int32_t* __restrict__ perm) {
@@ -813,7 +864,10 @@ hipError_t launch_cluster_pack(const int32_t* labels, int64_t hkv, int64_t n, in
   int32_t* seg = reinterpret_cast<int32_t*>(ws);
   const dim3 grid((unsigned)(hkv * nseg));
   hipLaunchKernelGGL(k_pack_count, grid, dim3(256), (size_t)C * 4, stream, labels, n, C, nseg, seg, err);
-  hipLaunchKernelGGL(k_pack_scan, dim3((unsigned)hkv), dim3(kScanThreads), 0, stream, C, nseg, seg, ptr);
+  if (C <= kScanThreads)
+    hipLaunchKernelGGL(k_pack_scan_cm, dim3((unsigned)hkv), dim3(kScanThreads), 0, stream, C, nseg, seg, ptr);
+  else
+    hipLaunchKernelGGL(k_pack_scan, dim3((unsigned)hkv), dim3(kScanThreads), 0, stream, C, nseg, seg, ptr);
   hipLaunchKernelGGL(k_pack_scatter, grid, dim3(256), 0, stream, labels, n, C, nseg, seg, perm);
   if (kp != nullptr) {
     const int row_bytes = head_dim * elem_bytes;
