@@ -508,31 +508,33 @@ __global__ __launch_bounds__(kThreads, 2) void k_fwd_bf16(FwdParams p) {
 }
 
 // ------------------------------------------------------------------ fp32 inputs
-// One workgroup of 256 threads per (batch, head, query block): four threads per
-// query row, each owning a quarter of the head dimensions (fp32 throughout).
+// One workgroup of 512 threads per (batch, head, query block): eight threads per
+// query row, each owning an eighth of the head dimensions (fp32 throughout).
 // Per 64-key tile a thread forms its partial dot products with the tile's keys,
-// the row's four partials are summed by two quad exchanges in a fixed order
-// (so the four threads hold identical scores), and the online softmax and the
-// P.V products run on the thread's quarter of the output.
-constexpr int kF32Threads = 256;
+// the row's eight partials are summed by three lane exchanges in a fixed order
+// (so the eight threads hold identical scores), and the online softmax and the
+// P.V products run on the thread's eighth of the output.
+constexpr int kF32Threads = 512;
 
-// v + the value of lane l ^ X within each quad (X = 1 or 2), by DPP quad permute.
+// X = 1 or 2: v + the value of lane l ^ X within each quad (DPP quad permute).
+// X = 4: v + the value of lane 7 - l within each group of 8 (row_half_mirror),
+// which after the two quad steps holds the other quad's sum.
 template <int X>
 __device__ __forceinline__ float quad_xor_add(float v) {
-  constexpr int ctrl = X == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  constexpr int ctrl = X == 1 ? 0xB1 : (X == 2 ? 0x4E : 0x141);  // quad_perm [1,0,3,2] / [2,3,0,1] / row_half_mirror
   const int o = __builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, false);
   return v + __int_as_float(o);
 }
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kF32Threads) void k_fwd_f32(FwdParams p) {
-  constexpr int DQ = D / 4;  // dimensions per thread
+  constexpr int DQ = D / 8;  // dimensions per thread
   constexpr int C4 = D / 4;  // 16-byte chunks per row
   __shared__ __attribute__((aligned(16))) float Ks[kBlk][D];
   __shared__ __attribute__((aligned(16))) float Vs[kBlk][D];
   __shared__ int32_t keyS[kBlk];
   __shared__ int32_t ash[MODE == 0 ? 2048 : 1];
-  const int tid = threadIdx.x, rw = tid >> 2, part = tid & 3;
+  const int tid = threadIdx.x, rw = tid >> 3, part = tid & 7;
   const Item item = item_at(p, blockIdx.x, gridDim.x, 0);
   const int b = item.b, h = item.h, iblk = item.iblk;
   const int g = h / (p.heads_q / p.heads_kv);
@@ -607,7 +609,7 @@ __global__ __launch_bounds__(kF32Threads) void k_fwd_f32(FwdParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc = fmaf(q[d + e], k4[e], acc);
       }
-      acc = quad_xor_add<2>(quad_xor_add<1>(acc));  // (p0 + p1) + (p2 + p3) on all four lanes
+      acc = quad_xor_add<4>(quad_xor_add<2>(quad_xor_add<1>(acc)));  // ((p0 + p1) + (p2 + p3)) + (...) on all eight lanes
       s[c] = keyS[c] > qpos ? -INFINITY : acc * p.scale;
       mx = fmaxf(mx, s[c]);
     }
